@@ -1,0 +1,207 @@
+"""CPU oracle of the MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package's smoke check and the benchmark's CPU-baseline
+leg may import this module. The product path (the HIP library and its Python
+binding) never does, and this module imports nothing from it.
+
+Plain numpy in float64, written step by step from the pages:
+  * gate: a lightweight linear layer scoring every token against every expert
+    (EP tutorial "专家并行：混合专家模型的分布式训练方案", section 1.1);
+  * the gate's output is a per-token expert-assignment probability
+    (fine-grained EP deployment guide "细粒度专家并行部署实践与优化指南",
+    section 5 step 3); softmax is the reading taken for "probability";
+  * top-K expert selection, only chosen experts compute (EP tutorial 1.1,
+    2.1 step 1; deployment guide section 7 example, topk of gate_probs, k=2);
+  * capacity = round((total tokens / experts) x capacity factor), tokens over
+    capacity dropped (EP tutorial, section 2.2);
+  * dispatch plan, tokens grouped contiguously per expert (EP tutorial 2.1
+    step 2 and 5.3);
+  * per-expert FFN: up-projection w1, activation, down-projection w2
+    (ETP expert-parallel page "ETP专家并行加速MoE模型", the ETP section:
+    4096 -> 16384 -> 4096, w1 split by columns, w2 by rows); GELU-tanh is the
+    activation this workload names, written from its textbook definition;
+  * combine: results returned to their original token positions (EP tutorial
+    2.1 step 5), weighted by the gate probabilities;
+  * L_aux = alpha * num_experts * sum_i f_i * P_i (EP tutorial, section 5.1).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * probabilities are a softmax over all E logits, taken before top-k;
+  * experts are ranked on their logits rounded to float32 (the precision the
+    kernels rank in), larger first, ties to the lower expert index; the
+    combine weight of a chosen expert is its softmax probability (not
+    renormalised unless `renorm`);
+  * the capacity formula's "total tokens" is n = T (the tokens entering the
+    layer); round() is round-half-even; cf <= 0 disables dropping;
+  * dropping keeps, per expert, the first C assignments in token order;
+    a dropped assignment contributes 0 and surviving weights are not
+    renormalised;
+  * f_i counts router assignments before dropping, divided by T*k;
+    P_i is the mean over all T tokens of the full softmax.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode(a, dtype: str) -> np.ndarray:
+    """Input tensor -> float64. bf16 is the upper half of a binary32 word."""
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def capacity(n_tokens: int, n_experts: int, cf: float) -> int:
+    """Expert capacity = round((total tokens / experts) x capacity factor)
+    (EP tutorial, section 2.2). Python's round() is round-half-even.
+    cf <= 0 means no dropping and returns -1."""
+    if cf <= 0:
+        return -1
+    return int(round((n_tokens / n_experts) * cf))
+
+
+def gate_logits(x64: np.ndarray, wg64: np.ndarray, bias=None) -> np.ndarray:
+    """l[t, e] = sum_c x[t, c] * Wg[e, c] + b[e] (EP tutorial 1.1: the gate is
+    a linear layer over the token representation)."""
+    l = x64 @ wg64.T
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float64)[None, :]
+    return l
+
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """Row-wise softmax, max-subtracted."""
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk(logits: np.ndarray, probs: np.ndarray, k: int, renorm: bool = False):
+    """Top-k experts per token (EP tutorial 1.1 and 2.1 step 1).
+
+    Key: float32(logit) descending, then expert index ascending. Slot j holds
+    the j-th best expert. Weight = the expert's softmax probability.
+    Returns (idx [T,k] int64, w [T,k] float64)."""
+    T, E = logits.shape
+    l32 = logits.astype(np.float32)
+    eidx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((eidx, -l32), axis=-1)   # primary key is the last one
+    idx = order[:, :k].astype(np.int64)
+    w = np.take_along_axis(probs, idx, axis=1)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+def dispatch(topk_idx: np.ndarray, n_experts: int, cap: int):
+    """Capacity-limited dispatch plan (EP tutorial 2.1 step 2, 2.2, 5.3).
+
+    Assignments are visited in token order (t, then slot j); each expert hands
+    out positions 0, 1, 2, ... in that order and keeps the assignment iff its
+    position is below the capacity. Kept rows are laid out expert by expert.
+
+    Returns counts[E] (assignments before dropping), offsets[E+1] (exclusive
+    scan of kept rows), dest[T,k] (row in the grouped layout, or -1 when
+    dropped) and src[R] (token of each grouped row)."""
+    T, k = topk_idx.shape
+    fill = np.zeros(n_experts, dtype=np.int64)
+    pos = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(topk_idx[t, j])
+            pos[t, j] = fill[e]
+            fill[e] += 1
+    counts = fill
+    kept = counts.copy() if cap < 0 else np.minimum(counts, cap)
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    keep = np.ones((T, k), dtype=bool) if cap < 0 else pos < cap
+    dest = np.where(keep, offsets[topk_idx] + pos, -1)
+    src = np.empty(int(offsets[-1]), dtype=np.int64)
+    tok = np.broadcast_to(np.arange(T)[:, None], (T, k))
+    src[dest[keep]] = tok[keep]
+    return counts, offsets, dest, src
+
+
+def gelu_tanh(z: np.ndarray) -> np.ndarray:
+    """GELU, tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))."""
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def expert_ffn(x_rows: np.ndarray, w1_e: np.ndarray, w2_e: np.ndarray) -> np.ndarray:
+    """One expert's FFN on a block of rows: gelu(X W1^T) W2^T, where W1 is
+    [d_ff, d] and W2 is [d, d_ff] (ETP page: up-projection w1, down w2)."""
+    return gelu_tanh(x_rows @ w1_e.T) @ w2_e.T
+
+
+def combine(y_perm: np.ndarray, dest: np.ndarray, topk_w: np.ndarray, T: int) -> np.ndarray:
+    """y[t] = sum over kept slots j of w[t,j] * y_perm[dest[t,j]]; a token with
+    no kept slot gets 0 (EP tutorial 2.1 step 5 and 2.2)."""
+    d = y_perm.shape[1] if y_perm.ndim == 2 else 0
+    y = np.zeros((T, d), dtype=np.float64)
+    for j in range(dest.shape[1]):
+        keep = dest[:, j] >= 0
+        y[keep] += topk_w[keep, j][:, None] * y_perm[dest[keep, j]]
+    return y
+
+
+def aux_loss(probs: np.ndarray, counts: np.ndarray, k: int, alpha: float) -> float:
+    """L_aux = alpha * E * sum_i f_i * P_i (EP tutorial, section 5.1), with
+    f_i = counts_i / (T k) and P_i the mean gate probability of expert i."""
+    T, E = probs.shape
+    if T == 0:
+        return 0.0
+    f = counts / float(T * k)
+    P = probs.mean(axis=0)
+    return float(alpha * E * np.sum(f * P))
+
+
+def route(x, w_gate, bias, dtype: str, k: int, renorm: bool = False):
+    """Gate -> softmax -> top-k on the given input bits."""
+    l = gate_logits(decode(x, dtype), decode(w_gate, dtype), bias)
+    p = softmax(l)
+    idx, w = topk(l, p, k, renorm)
+    return {"logits": l, "probs": p, "topk_idx": idx, "topk_w": w}
+
+
+def forward(inp: dict, dtype: str, k: int, cf: float, alpha: float = 0.01,
+            renorm: bool = False, sample_tokens=None) -> dict:
+    """The whole layer: route (unless `inp` carries topk_idx/topk_w), dispatch,
+    expert FFN, combine, aux loss.
+
+    With `sample_tokens` (an index array) the FFN and combine are evaluated
+    for those tokens only: `y` then has one row per sampled token, and only
+    the grouped rows listed in `y_perm_rows` of `y_perm` are filled."""
+    x = inp["x"]
+    T = x.shape[0]
+    E = inp["w1"].shape[0]
+    out = {}
+    if inp.get("w_gate") is not None:
+        out.update(route(x, inp["w_gate"], inp.get("bias"), dtype, k, renorm))
+    else:
+        out["topk_idx"] = np.asarray(inp["topk_idx"], dtype=np.int64)
+        out["topk_w"] = np.asarray(inp["topk_w"], dtype=np.float64)
+        k = out["topk_idx"].shape[1]
+    C = capacity(T, E, cf)
+    counts, offsets, dest, src = dispatch(out["topk_idx"], E, C)
+    out.update(capacity=C, counts=counts, offsets=offsets, dest=dest, src=src)
+    if "probs" in out:
+        out["aux"] = aux_loss(out["probs"], counts, k, alpha)
+
+    toks = np.arange(T) if sample_tokens is None else np.asarray(sample_tokens)
+    need = dest[toks]
+    rows = np.unique(need[need >= 0])                       # grouped rows needed
+    d = inp["w2"].shape[1]
+    y_perm = np.zeros((int(offsets[-1]), d))
+    for e in range(E):
+        sel = rows[(rows >= offsets[e]) & (rows < offsets[e + 1])]
+        if sel.size:
+            y_perm[sel] = expert_ffn(decode(x[src[sel]], dtype),
+                                     decode(inp["w1"][e], dtype),
+                                     decode(inp["w2"][e], dtype))
+    out["y_perm"] = y_perm
+    out["y_perm_rows"] = rows
+    out["y"] = combine(y_perm, need, out["topk_w"][toks], toks.size)
+    return out

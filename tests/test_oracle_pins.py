@@ -1,0 +1,309 @@
+"""Pins for the CPU oracle: it is checked against hand-worked cases, closed
+forms, independent library routines (scipy, torch) and brute force on tiny
+inputs -- never against itself."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import moe_oracle as O
+from mixture_experts_layer_49_amd import inputs as I
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- capacity --
+def test_capacity_hand_cases():
+    for c in gold("capacity_hand.json")["cases"]:
+        assert O.capacity(c["n"], c["E"], c["cf"]) == c["C"], c
+
+
+def test_capacity_of_the_five_workloads():
+    want = [80, 256, 320, 1280, 1280]
+    for cfg, c in zip(I.CONFIGS, want):
+        assert O.capacity(cfg.T, cfg.E, cfg.cf) == c
+
+
+# -------------------------------------------------------------------- gate --
+def test_gate_hand_example():
+    g = gold("gate_hand.json")
+    l = O.gate_logits(np.array(g["x"], float), np.array(g["w_gate"], float), g["bias"])
+    np.testing.assert_array_equal(l, np.array(g["logits"]))
+
+
+def test_gate_vs_brute_force_loops():
+    rng = np.random.default_rng(5)
+    x, wg, b = rng.normal(size=(3, 5)), rng.normal(size=(4, 5)), rng.normal(size=4)
+    l = O.gate_logits(x, wg, b)
+    for t in range(3):
+        for e in range(4):
+            s = b[e]
+            for c in range(5):
+                s += x[t, c] * wg[e, c]
+            assert abs(l[t, e] - s) < 1e-12
+
+
+def test_gate_vs_torch_linear():
+    rng = np.random.default_rng(6)
+    x, wg, b = rng.normal(size=(17, 40)), rng.normal(size=(9, 40)), rng.normal(size=9)
+    ref = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(wg),
+                                     torch.from_numpy(b)).numpy()
+    np.testing.assert_allclose(O.gate_logits(x, wg, b), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_bf16_exact_values():
+    # bf16 bit patterns: 0x3f80 = 1.0, 0xc000 = -2.0, 0x3e80 = 0.25, 0x0000 = 0
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0000], dtype=np.uint16)
+    np.testing.assert_array_equal(O.decode(bits, "bf16"), [1.0, -2.0, 0.25, 0.0])
+    a = np.random.default_rng(1).normal(size=100).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.decode(I.to_bf16_bits(a), "bf16"), ref)
+
+
+# ----------------------------------------------------------------- softmax --
+def test_softmax_exact_and_library():
+    p = O.softmax(np.array([[0.0, math.log(3.0)]]))
+    np.testing.assert_allclose(p, [[0.25, 0.75]], rtol=1e-15)
+    l = np.random.default_rng(2).normal(size=(50, 7)) * 5
+    np.testing.assert_allclose(O.softmax(l), scipy.special.softmax(l, axis=1), rtol=1e-13)
+    # max-subtraction: huge shifts stay finite and shift-invariant
+    np.testing.assert_allclose(O.softmax(l + 1000.0), O.softmax(l), rtol=1e-12)
+
+
+# -------------------------------------------------------------------- topk --
+def test_topk_hand_order_and_ties():
+    g = gold("topk_hand.json")
+    l = np.array(g["logits"], float)
+    p = O.softmax(l)
+    for k in range(1, 5):
+        idx, w = O.topk(l, p, k)
+        np.testing.assert_array_equal(idx, np.array(g["order"])[:, :k])
+        np.testing.assert_array_equal(w, np.take_along_axis(p, idx, 1))
+
+
+def _brute_topk(row, k):
+    """The unique k-subset whose every member outranks every non-member under
+    (value desc, index asc); members listed best first."""
+    E = len(row)
+    better = lambda a, b: row[a] > row[b] or (row[a] == row[b] and a < b)
+    for S in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in S]
+        if all(better(a, b) for a in S for b in rest):
+            # order members: a member precedes another iff it outranks it
+            return sorted(S, key=lambda a: sum(better(b, a) for b in S))
+    raise AssertionError("no dominating subset")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_vs_brute_force_subsets(seed):
+    rng = np.random.default_rng(seed)
+    E = 5
+    l = rng.integers(-2, 3, size=(12, E)).astype(float)   # many exact ties
+    l32 = l.astype(np.float32)
+    p = O.softmax(l)
+    for k in range(1, E + 1):
+        idx, _ = O.topk(l, p, k)
+        for t in range(12):
+            assert list(idx[t]) == _brute_topk(l32[t], k)
+
+
+def test_topk_ranks_in_float32():
+    # two logits that differ only below float32 resolution tie -> lower index
+    l = np.array([[1.0, 1.0 + 1e-12, 0.0]])
+    idx, _ = O.topk(l, O.softmax(l), 1)
+    assert idx[0, 0] == 0
+
+
+def test_topk_renorm_sums_to_one():
+    l = np.random.default_rng(3).normal(size=(20, 8))
+    _, w = O.topk(l, O.softmax(l), 3, renorm=True)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- dispatch --
+def test_dispatch_hand_example():
+    g = gold("dispatch_hand.json")
+    idx = np.array(g["topk_idx"])
+    for c in g["cases"]:
+        counts, offsets, dest, src = O.dispatch(idx, g["E"], c["C"])
+        np.testing.assert_array_equal(counts, c["counts"])
+        np.testing.assert_array_equal(offsets, c["offsets"])
+        np.testing.assert_array_equal(dest, c["dest"])
+        np.testing.assert_array_equal(src, c["src"])
+
+
+def _random_routes(rng, T, E, k, skew):
+    w = np.array([(e + 1.0) ** -skew for e in range(E)])
+    w /= w.sum()
+    return np.stack([rng.choice(E, size=k, replace=False, p=w) for _ in range(T)])
+
+
+@pytest.mark.parametrize("T,E,k,C", [(40, 4, 2, 9), (64, 8, 1, 3), (33, 5, 3, 0),
+                                     (50, 6, 2, -1), (25, 3, 3, 100)])
+def test_dispatch_invariants_and_per_expert_filter(T, E, k, C):
+    rng = np.random.default_rng(T + E)
+    idx = _random_routes(rng, T, E, k, 1.3)
+    counts, offsets, dest, src = O.dispatch(idx, E, C)
+    assert counts.sum() == T * k
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    kept = counts if C < 0 else np.minimum(counts, C)
+    np.testing.assert_array_equal(np.diff(offsets), kept)
+    R = offsets[-1]
+    assert sorted(dest[dest >= 0].tolist()) == list(range(R))   # bijection onto [0,R)
+    assert ((dest >= 0).sum(1) <= k).all()
+    # independent formulation: per expert, the tokens that chose it in ascending
+    # order; the first C of them are kept, in that order, as the expert's rows
+    for e in range(E):
+        toks = [t for t in range(T) if e in idx[t]]
+        keep = toks if C < 0 else toks[:C]
+        assert src[offsets[e]:offsets[e + 1]].tolist() == keep
+        for t in toks:
+            j = list(idx[t]).index(e)
+            r = dest[t, j]
+            if t in keep:
+                assert r == offsets[e] + keep.index(t)
+            else:
+                assert r == -1
+
+
+# -------------------------------------------------------------------- gelu --
+def test_gelu_vs_torch_and_identities():
+    z = np.linspace(-8, 8, 2001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(z), ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(O.gelu_tanh(z) - O.gelu_tanh(-z), z, atol=1e-14)
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(O.gelu_tanh(np.array([1.0]))[0] - 0.8411919906082768) < 1e-15
+
+
+# --------------------------------------------------------------------- ffn --
+def test_expert_ffn_brute_force():
+    rng = np.random.default_rng(7)
+    d, dff = 3, 4
+    x, w1, w2 = rng.normal(size=(2, d)), rng.normal(size=(dff, d)), rng.normal(size=(d, dff))
+    o = O.expert_ffn(x, w1, w2)
+    for r in range(2):
+        h = []
+        for j in range(dff):
+            z = sum(w1[j, c] * x[r, c] for c in range(d))
+            h.append(0.5 * z * (1 + math.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3))))
+        for c in range(d):
+            assert abs(o[r, c] - sum(w2[c, j] * h[j] for j in range(dff))) < 1e-12
+
+
+# ----------------------------------------------------------------- combine --
+def test_combine_hand_example():
+    g = gold("combine_hand.json")
+    y = O.combine(np.array(g["y_perm"], float), np.array(g["dest"]),
+                  np.array(g["topk_w"]), 3)
+    np.testing.assert_array_equal(y, np.array(g["y"]))
+
+
+# --------------------------------------------------------------------- aux --
+def test_aux_hand_cases():
+    g = gold("aux_hand.json")
+    for c in g["cases"]:
+        got = O.aux_loss(np.array(c["probs"]), np.array(c["counts"]), c["k"], g["alpha"])
+        assert abs(got - c["loss"]) < 1e-15
+
+
+def test_aux_closed_forms():
+    T, E, alpha = 64, 8, 0.01
+    # uniform probabilities and perfectly balanced counts -> alpha
+    assert abs(O.aux_loss(np.full((T, E), 1 / E), np.full(E, T * 2 // E), 2, alpha) - alpha) < 1e-15
+    # every token puts all probability on expert 0, k=1 -> alpha * E
+    p = np.zeros((T, E)); p[:, 0] = 1
+    c = np.zeros(E, int); c[0] = T
+    assert abs(O.aux_loss(p, c, 1, alpha) - alpha * E) < 1e-15
+
+
+# --------------------------------------------------------- whole layer pins --
+def _np_inputs(rng, T, d, dff, E):
+    return {"x": rng.normal(size=(T, d)).astype(np.float32),
+            "w_gate": rng.normal(size=(E, d)).astype(np.float32),
+            "bias": None,
+            "w1": (rng.normal(size=(E, dff, d)) / math.sqrt(d)).astype(np.float32),
+            "w2": (rng.normal(size=(E, d, dff)) / math.sqrt(dff)).astype(np.float32)}
+
+
+def test_layer_single_expert_is_plain_mlp():
+    """E=1, k=1, no dropping: softmax weight is 1 and the layer is the MLP."""
+    rng = np.random.default_rng(8)
+    inp = _np_inputs(rng, 20, 12, 24, 1)
+    out = O.forward(inp, "f32", k=1, cf=0.0)
+    x = torch.from_numpy(inp["x"]).double()
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.gelu(torch.nn.functional.linear(x, torch.from_numpy(inp["w1"][0]).double()),
+                                 approximate="tanh"),
+        torch.from_numpy(inp["w2"][0]).double()).numpy()
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_layer_no_drop_equals_dense_masked_sum(k):
+    """No dropping: y[t] = sum_e [e in topk(t)] p[t,e] FFN_e(x_t), every expert
+    evaluated densely on every token (torch, no dispatch at all)."""
+    rng = np.random.default_rng(9 + k)
+    T, d, dff, E = 30, 10, 14, 5
+    inp = _np_inputs(rng, T, d, dff, E)
+    out = O.forward(inp, "f32", k=k, cf=0.0)
+    x = torch.from_numpy(inp["x"]).double()
+    logits = torch.nn.functional.linear(x, torch.from_numpy(inp["w_gate"]).double())
+    p = torch.softmax(logits, dim=1)
+    y = torch.zeros(T, d, dtype=torch.float64)
+    l32 = logits.float()
+    for t in range(T):
+        chosen = sorted(range(E), key=lambda e: (-float(l32[t, e]), e))[:k]
+        for e in chosen:
+            h = torch.nn.functional.gelu(x[t] @ torch.from_numpy(inp["w1"][e]).double().T,
+                                         approximate="tanh")
+            y[t] += p[t, e] * (h @ torch.from_numpy(inp["w2"][e]).double().T)
+    np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_layer_linear_in_combine_weight_and_drop_zeroes():
+    rng = np.random.default_rng(11)
+    T, d, dff, E = 24, 8, 16, 4
+    inp = _np_inputs(rng, T, d, dff, E)
+    inp.pop("w_gate")
+    inp["topk_idx"] = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    inp["topk_w"] = rng.uniform(size=(T, 1))
+    a = O.forward(dict(inp), "f32", k=1, cf=0.5)        # C = round(24/4*0.5) = 3
+    inp2 = dict(inp, topk_w=inp["topk_w"] * 2.0)
+    b = O.forward(inp2, "f32", k=1, cf=0.5)
+    np.testing.assert_allclose(b["y"], 2.0 * a["y"], rtol=1e-14)
+    dropped = a["dest"][:, 0] < 0
+    assert dropped.any() and (a["y"][dropped] == 0).all()
+    assert (a["counts"] == np.bincount(inp["topk_idx"][:, 0], minlength=E)).all()
+
+
+def test_layer_sampled_equals_full():
+    rng = np.random.default_rng(12)
+    inp = _np_inputs(rng, 40, 8, 12, 4)
+    full = O.forward(inp, "f32", k=2, cf=1.0)
+    s = np.array([0, 5, 17, 39])
+    part = O.forward(inp, "f32", k=2, cf=1.0, sample_tokens=s)
+    np.testing.assert_allclose(part["y"], full["y"][s], rtol=1e-14)
+
+
+def test_generator_is_deterministic_and_shaped():
+    cfg = I.small(T=50, d=16, d_ff=24, E=4)
+    a, b = I.make_inputs(cfg), I.make_inputs(cfg)
+    for key in ("x", "w_gate", "w1", "w2"):
+        assert a[key].shape == b[key].shape and (a[key] == b[key]).all()
+    assert a["w1"].shape == (4, 24, 16) and a["w2"].shape == (4, 16, 24)
+    r = I.make_inputs(I.small(name="r", T=64, d=16, d_ff=24, E=8, k=1, routed=False))
+    counts = np.bincount(r["topk_idx"][:, 0], minlength=8)
+    np.testing.assert_array_equal(counts, I.zipf_counts(64, 8, 1.2))
+    np.testing.assert_array_equal(I.zipf_counts(8192, 8, 1.2),
+                                  [3511, 1528, 940, 665, 509, 409, 340, 290])
