@@ -1,0 +1,175 @@
+/*
+ * moe.h -- C ABI of the single-GPU Mixture-of-Experts layer forward
+ *          (gfx950 / CDNA4, HIP).
+ *
+ * The layer replaces a Transformer FFN with a gate, a set of expert FFNs and
+ * sparse top-K activation (EP tutorial "专家并行：混合专家模型的分布式训练方案",
+ * section 1.1). One forward is five calls, in the order the pages give:
+ *
+ *   moe_router_topk  gate linear -> softmax -> top-k          (tutorial 1.1, 2.1 step 1;
+ *                    deployment guide "细粒度专家并行部署实践与优化指南", section 5 step 3)
+ *   moe_dispatch     capacity-limited dispatch plan + permute  (tutorial 2.1 step 2, 2.2, 5.3)
+ *   moe_grouped_ffn  per-expert up-proj, GELU-tanh, down-proj  (ETP page "ETP专家并行加速MoE模型",
+ *                    the w1 / w2 up- and down-projection example; tutorial 2.1 step 4)
+ *   moe_combine      weighted return to token order            (tutorial 2.1 step 5)
+ *   moe_aux_loss     L_aux = alpha * E * sum_i f_i * P_i       (tutorial 5.1)
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers, row-major, densely packed, owned
+ *    by the caller. The library never allocates, frees or synchronises; every
+ *    call validates its arguments on the host, enqueues its kernels on
+ *    `stream` and returns. Results are ready once the caller synchronises.
+ *  - dtype codes: MOE_F32 (IEEE binary32) or MOE_BF16 (bfloat16, RNE).
+ *    bf16 tensors need 16-byte aligned base pointers and a row length that is
+ *    a multiple of 8 elements; f32 tensors need 16-byte alignment and a row
+ *    length that is a multiple of 4.
+ *  - Return value: MOE_OK, or a negative moe_status. On an argument error
+ *    nothing is enqueued; moe_last_error() gives a text for the calling thread.
+ *    A launch failure returns MOE_ERR_HIP. A fault inside a kernel surfaces at
+ *    the caller's next synchronisation, as with any stream API.
+ *  - T == 0 is a valid no-op for every call (aux loss writes 0).
+ *  - Values are not checked: NaN/Inf inputs give unspecified routing.
+ *  - The library keeps no state apart from the thread-local error text and a
+ *    per-device cache of the compute-unit count; calls are re-entrant.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,       /* null pointer, negative or inconsistent size   */
+  MOE_ERR_DTYPE = -2,     /* unsupported dtype code                         */
+  MOE_ERR_SHAPE = -3,     /* size outside what the kernels support          */
+  MOE_ERR_WORKSPACE = -4, /* workspace missing or smaller than required     */
+  MOE_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed     */
+  MOE_ERR_ALIGN = -6      /* pointer or row length breaks the 16-B rule     */
+} moe_status;
+
+#define MOE_MAX_E 256   /* experts per layer                      */
+#define MOE_MAX_K 8     /* experts per token                      */
+#define MOE_RENORM 0x1u /* router flag: rescale the k weights to sum to 1 */
+
+/* Expert capacity (EP tutorial section 2.2): round((n_tokens / n_experts) x
+ * capacity_factor), computed in double, round-half-even. A factor <= 0 means
+ * "no dropping" and returns -1 (ms-swift page, section 4.1, drop switch off).
+ * n_tokens < 0 or n_experts < 1 returns -2. Host-only, no GPU needed. */
+int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, double capacity_factor);
+
+/* Rows of the grouped (expert-major) buffers x_perm / h / y_perm:
+ * min(T*k, E*capacity), or T*k when capacity < 0. Host-only. */
+int64_t moe_rows_max(int64_t T, int32_t k, int32_t E, int64_t capacity);
+
+/* Gate, softmax and top-k (EP tutorial 1.1: a linear gate scores each token
+ * against every expert and picks the Top-K; deployment guide section 5
+ * step 3: the gate outputs per-token assignment probabilities).
+ *   x        [T, d]  dtype        token representations
+ *   w_gate   [E, d]  dtype        gate weight (row e scores expert e)
+ *   bias     [E]     f32 or NULL  added to the logits
+ *   topk_idx [T, k]  int32 out    chosen experts, best first; ties between
+ *                                 equal float32 logits go to the lower index
+ *   topk_w   [T, k]  f32   out    softmax probability of each chosen expert
+ *                                 (rescaled to sum 1 iff flags & MOE_RENORM)
+ *   probs    [T, E]  f32   out    full softmax, or NULL when not wanted
+ * Logits and softmax are float32 (bf16 products accumulate in float32).
+ * Limits: 1 <= E <= MOE_MAX_E, 1 <= k <= min(E, MOE_MAX_K). */
+int moe_router_topk(const void* x, const void* w_gate, const float* bias,
+                    int64_t T, int64_t d, int32_t E, int32_t k, int32_t dtype,
+                    uint32_t flags, int32_t* topk_idx, float* topk_w, float* probs,
+                    hipStream_t stream);
+
+/* Bytes of device workspace moe_dispatch needs (0 when T == 0). */
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E);
+
+/* Dispatch plan with capacity dropping, then the permute (EP tutorial 2.1
+ * step 2: map each token to its target expert; 2.2: assignments beyond an
+ * expert's capacity are dropped; 5.3: tokens packed so each expert's rows are
+ * contiguous). Assignments are ranked inside their expert in token order
+ * (token t, then slot j); the first `capacity` of them are kept
+ * (capacity < 0: all kept).
+ *   topk_idx [T, k] int32 in   expert of each slot; ids outside [0, E) and a
+ *                              repeat of an expert already named earlier in the
+ *                              same token are ignored (not counted, dest -1)
+ *   x        [T, d] dtype in   token rows to permute
+ *   counts   [E]    int32 out  assignments per expert before dropping
+ *   offsets  [E+1]  int32 out  exclusive scan of kept rows per expert;
+ *                              offsets[E] = R, the total kept rows
+ *   dest     [T, k] int32 out  grouped row of each slot, or -1 if dropped
+ *   src      [rows_max] int32 out   token of each grouped row (first R valid)
+ *   x_perm   [rows_max, d] dtype out x_perm[r] = x[src[r]] for r < R
+ *   workspace / workspace_bytes: device scratch of at least
+ *             moe_dispatch_workspace_bytes(T, k, E) bytes, 4-byte aligned.
+ * rows_max = moe_rows_max(T, k, E, capacity). Deterministic: no atomics on
+ * any output. Requires T * k < 2^31. */
+int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                 int64_t capacity, const void* x, int64_t d, int32_t dtype,
+                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                 void* x_perm, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Grouped expert FFN over the expert-major segments given by `offsets`
+ * (ETP page: up-projection w1 then down-projection w2, e.g.
+ * 4096 -> 16384 -> 4096; EP tutorial 2.1 step 4: each expert computes on its
+ * own tokens). For every expert e and row r in [offsets[e], offsets[e+1]):
+ *   h[r]      = gelu_tanh(W1[e] . x_perm[r])    (stored in dtype; bf16 = RNE)
+ *   y_perm[r] = W2[e] . h[r]                     (float32)
+ * with gelu_tanh(z) = z / 2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
+ *   x_perm [rows_max, d]      dtype    w1 [E, d_ff, d] dtype (K contiguous)
+ *   h      [rows_max, d_ff]   dtype    w2 [E, d, d_ff] dtype (K contiguous)
+ *   y_perm [rows_max, d]      f32
+ *   offsets [E+1] int32, device: read by the kernels, never by the host.
+ * Products accumulate in float32. Rows >= offsets[E] are not touched. */
+int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E,
+                    int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                    const void* w2, int32_t dtype, void* h, float* y_perm,
+                    hipStream_t stream);
+
+/* The two halves of moe_grouped_ffn, callable on their own (same arguments,
+ * same layouts): the up-projection with its GELU-tanh epilogue, and the
+ * down-projection. moe_grouped_ffn == up then down on the same stream. */
+int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E,
+                       int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                       int32_t dtype, void* h, hipStream_t stream);
+int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
+                    int64_t rows_max, int64_t d, int64_t d_ff, const void* w2,
+                    int32_t dtype, float* y_perm, hipStream_t stream);
+
+/* Weighted combine back to token order (EP tutorial 2.1 step 5; 2.2: a
+ * dropped slot takes no part):
+ *   y[t] = sum over j with dest[t,j] >= 0 of topk_w[t,j] * y_perm[dest[t,j]],
+ * summed in slot order; a token with no kept slot gets zeros.
+ *   y_perm [rows, d] f32, dest [T, k] int32, topk_w [T, k] f32,
+ *   y [T, d] in out_dtype (MOE_F32 or MOE_BF16). Deterministic, no atomics. */
+int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
+                int64_t T, int32_t k, int64_t d, void* y, int32_t out_dtype,
+                hipStream_t stream);
+
+/* Bytes of device workspace moe_aux_loss needs. */
+size_t moe_aux_loss_workspace_bytes(int64_t T, int32_t E);
+
+/* Auxiliary load-balance loss (EP tutorial 5.1):
+ *   L = alpha * E * sum_i f_i * P_i,  f_i = counts[i] / (T * k),
+ *   P_i = (1/T) * sum_t probs[t, i].
+ * counts are the pre-drop assignment counts moe_dispatch writes.
+ *   probs [T, E] f32, counts [E] int32, loss: one f32 written on the device.
+ * Sums run in double in a fixed order: bit-identical from run to run. */
+int moe_aux_loss(const float* probs, const int32_t* counts, int64_t T, int32_t E,
+                 int32_t k, float alpha, float* loss, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

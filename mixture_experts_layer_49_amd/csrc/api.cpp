@@ -1,0 +1,266 @@
+// C ABI of the MoE layer forward: argument validation, capacity arithmetic,
+// workspace sizing and kernel launches. Every check runs on the host before
+// anything is enqueued; see include/moe.h for the contract of each call.
+#include "moe.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+int check_dtype(int32_t dtype) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16)
+    return fail(MOE_ERR_DTYPE, "dtype %d is neither MOE_F32 (0) nor MOE_BF16 (1)", dtype);
+  return MOE_OK;
+}
+
+// Row length rule for vector access: bf16 rows are a multiple of 8 elements,
+// f32 rows a multiple of 4 (16 bytes either way).
+int check_row(const char* name, int64_t len, int32_t dtype) {
+  const int64_t q = dtype == MOE_BF16 ? 8 : 4;
+  if (len % q != 0)
+    return fail(MOE_ERR_ALIGN, "%s = %lld must be a multiple of %lld for this dtype", name,
+                static_cast<long long>(len), static_cast<long long>(q));
+  return MOE_OK;
+}
+
+int check_ptr16(const char* name, const void* p) {
+  if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define MOE_TRY(x)            \
+  do {                        \
+    const int _rc = (x);      \
+    if (_rc != MOE_OK) return _rc; \
+  } while (0)
+
+#define MOE_NONNULL(p) \
+  do { if ((p) == nullptr) return fail(MOE_ERR_ARG, "%s must not be NULL", #p); } while (0)
+
+int check_experts(int32_t E, int32_t k) {
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, MOE_MAX_E);
+  if (k < 1 || k > E || k > MOE_MAX_K)
+    return fail(MOE_ERR_SHAPE, "k = %d outside [1, min(E=%d, %d)]", k, E, MOE_MAX_K);
+  return MOE_OK;
+}
+
+int check_ffn(const void* a, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,
+              int64_t d_ff, const void* w, int32_t dtype, const void* out) {
+  MOE_TRY(check_dtype(dtype));
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, MOE_MAX_E);
+  if (rows_max < 0 || d <= 0 || d_ff <= 0)
+    return fail(MOE_ERR_ARG, "need rows_max >= 0, d > 0, d_ff > 0 (got %lld, %lld, %lld)",
+                static_cast<long long>(rows_max), static_cast<long long>(d),
+                static_cast<long long>(d_ff));
+  if (d > (1 << 30) || d_ff > (1 << 30) || rows_max > 0x7fffffffLL)
+    return fail(MOE_ERR_SHAPE, "d, d_ff or rows_max too large for 32-bit row indexing");
+  MOE_TRY(check_row("d", d, dtype));
+  MOE_TRY(check_row("d_ff", d_ff, dtype));
+  if (rows_max == 0) return MOE_OK;
+  MOE_NONNULL(a);
+  MOE_NONNULL(offsets);
+  MOE_NONNULL(w);
+  MOE_NONNULL(out);
+  MOE_TRY(check_ptr16("activation", a));
+  MOE_TRY(check_ptr16("weight", w));
+  MOE_TRY(check_ptr16("output", out));
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, double capacity_factor) {
+  if (n_tokens < 0 || n_experts < 1) return -2;
+  if (!(capacity_factor > 0.0)) return -1;
+  const double c = (static_cast<double>(n_tokens) / n_experts) * capacity_factor;
+  return static_cast<int64_t>(std::nearbyint(c));   // default mode: round-half-even
+}
+
+int64_t moe_rows_max(int64_t T, int32_t k, int32_t E, int64_t capacity) {
+  if (T < 0 || k < 1 || E < 1) return -1;
+  const int64_t tk = T * k;
+  if (capacity < 0) return tk;
+  const int64_t ec = static_cast<int64_t>(E) * capacity;
+  return tk < ec ? tk : ec;
+}
+
+int moe_router_topk(const void* x, const void* w_gate, const float* bias, int64_t T, int64_t d,
+                    int32_t E, int32_t k, int32_t dtype, uint32_t flags, int32_t* topk_idx,
+                    float* topk_w, float* probs, hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  MOE_TRY(check_experts(E, k));
+  if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
+  if (T > (1LL << 31) / MOE_MAX_K) return fail(MOE_ERR_SHAPE, "T too large");
+  if (flags & ~MOE_RENORM) return fail(MOE_ERR_ARG, "unknown flag bits 0x%x", flags);
+  MOE_TRY(check_row("d", d, dtype));
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(x);
+  MOE_NONNULL(w_gate);
+  MOE_NONNULL(topk_idx);
+  MOE_NONNULL(topk_w);
+  MOE_TRY(check_ptr16("x", x));
+  MOE_TRY(check_ptr16("w_gate", w_gate));
+  return hip_status(moe::launch_router(x, w_gate, bias, T, d, E, k, dtype, flags, topk_idx, topk_w,
+                                       probs, stream),
+                    "moe_router_topk launch");
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  (void)k;
+  if (T <= 0 || E < 1) return 0;
+  return moe::dispatch_ws_ints(T, E) * sizeof(int32_t);
+}
+
+int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,
+                 const void* x, int64_t d, int32_t dtype, int32_t* counts, int32_t* offsets,
+                 int32_t* dest, int32_t* src, void* x_perm, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  MOE_TRY(check_experts(E, k));
+  if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
+  if (T * k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T * k must stay below 2^31");
+  MOE_TRY(check_row("d", d, dtype));
+  MOE_NONNULL(counts);
+  MOE_NONNULL(offsets);
+  if (T > 0) {
+    MOE_NONNULL(topk_idx);
+    MOE_NONNULL(x);
+    MOE_NONNULL(dest);
+    MOE_NONNULL(src);
+    MOE_NONNULL(x_perm);
+    MOE_TRY(check_ptr16("x", x));
+    MOE_TRY(check_ptr16("x_perm", x_perm));
+    const size_t need = moe_dispatch_workspace_bytes(T, k, E);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                  workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
+      return fail(MOE_ERR_ALIGN, "workspace is not 4-byte aligned");
+  }
+  const int64_t rows_max = moe_rows_max(T, k, E, capacity);
+  return hip_status(moe::launch_dispatch(topk_idx, T, k, E, capacity, x, d, elem_bytes(dtype),
+                                         rows_max, counts, offsets, dest, src, x_perm,
+                                         static_cast<int32_t*>(workspace), stream),
+                    "moe_dispatch launch");
+}
+
+int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E, int64_t rows_max,
+                       int64_t d, int64_t d_ff, const void* w1, int32_t dtype, void* h,
+                       hipStream_t stream) {
+  MOE_TRY(check_ffn(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h));
+  return hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h, stream),
+                    "moe_expert_up_gelu launch");
+}
+
+int moe_expert_down(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,
+                    int64_t d_ff, const void* w2, int32_t dtype, float* y_perm,
+                    hipStream_t stream) {
+  MOE_TRY(check_ffn(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm));
+  return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm, stream),
+                    "moe_expert_down launch");
+}
+
+int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E, int64_t rows_max,
+                    int64_t d, int64_t d_ff, const void* w1, const void* w2, int32_t dtype,
+                    void* h, float* y_perm, hipStream_t stream) {
+  MOE_TRY(check_ffn(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h));
+  MOE_TRY(check_ffn(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm));
+  MOE_TRY(hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h, stream),
+                     "moe_grouped_ffn up-projection launch"));
+  return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm, stream),
+                    "moe_grouped_ffn down-projection launch");
+}
+
+int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w, int64_t T,
+                int32_t k, int64_t d, void* y, int32_t out_dtype, hipStream_t stream) {
+  MOE_TRY(check_dtype(out_dtype));
+  if (T < 0 || d <= 0 || k < 1 || k > MOE_MAX_K)
+    return fail(MOE_ERR_ARG, "need T >= 0, d > 0, 1 <= k <= %d", MOE_MAX_K);
+  if (d % 4 != 0) return fail(MOE_ERR_ALIGN, "d = %lld must be a multiple of 4", static_cast<long long>(d));
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(dest);
+  MOE_NONNULL(topk_w);
+  MOE_NONNULL(y);
+  MOE_NONNULL(y_perm);
+  MOE_TRY(check_ptr16("y_perm", y_perm));
+  if (out_dtype == MOE_BF16) {
+    if ((reinterpret_cast<uintptr_t>(y) & 7u) != 0) return fail(MOE_ERR_ALIGN, "y is not 8-byte aligned");
+  } else {
+    MOE_TRY(check_ptr16("y", y));
+  }
+  return hip_status(moe::launch_combine(y_perm, dest, topk_w, T, k, d, y, out_dtype, stream),
+                    "moe_combine launch");
+}
+
+size_t moe_aux_loss_workspace_bytes(int64_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return moe::aux_ws_doubles(T, E) * sizeof(double);
+}
+
+int moe_aux_loss(const float* probs, const int32_t* counts, int64_t T, int32_t E, int32_t k,
+                 float alpha, float* loss, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  MOE_TRY(check_experts(E, k));
+  if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
+  MOE_NONNULL(loss);
+  MOE_NONNULL(counts);
+  if (T > 0) MOE_NONNULL(probs);
+  const size_t need = moe_aux_loss_workspace_bytes(T, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+    return fail(MOE_ERR_ALIGN, "workspace is not 8-byte aligned");
+  return hip_status(moe::launch_aux_loss(probs, counts, T, E, k, alpha, loss,
+                                         static_cast<double*>(workspace), stream),
+                    "moe_aux_loss launch");
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

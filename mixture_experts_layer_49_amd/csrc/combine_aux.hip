@@ -1,0 +1,141 @@
+// Weighted combine and auxiliary load-balance loss.
+//
+// Combine (EP tutorial "专家并行：混合专家模型的分布式训练方案", section 2.1
+// step 5: expert outputs return to their tokens' original positions; section
+// 2.2: a dropped assignment takes no part): written in gather form -- each
+// output row reads its <= k grouped rows, weights them and sums in slot order
+// -- so it needs no atomics and no zero-fill pass and is deterministic.
+//
+// Aux loss (same tutorial, section 5.1): L = alpha * E * sum_i f_i * P_i with
+// f_i = counts_i / (T k) and P_i the mean gate probability of expert i. The
+// column sums of probs run in double, in a fixed two-level order.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// One workgroup per token row (grid-stride), float4 lanes over d.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ dest,
+                                                      const float* __restrict__ topk_w, int64_t T,
+                                                      int k, int64_t d, void* __restrict__ y) {
+  const int64_t dv = d / 4;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    int32_t rows[kMaxK];
+    float w[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      rows[j] = j < k ? dest[t * k + j] : -1;
+      w[j] = j < k ? topk_w[t * k + j] : 0.f;
+    }
+    for (int64_t v = threadIdx.x; v < dv; v += blockDim.x) {
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (rows[j] >= 0) {
+          const float4 o = reinterpret_cast<const float4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[v];
+          acc.x = fmaf(w[j], o.x, acc.x);
+          acc.y = fmaf(w[j], o.y, acc.y);
+          acc.z = fmaf(w[j], o.z, acc.z);
+          acc.w = fmaf(w[j], o.w, acc.w);
+        }
+      }
+      if (BF16_OUT) {
+        ushort4 b;
+        b.x = f32_to_bf16(acc.x); b.y = f32_to_bf16(acc.y);
+        b.z = f32_to_bf16(acc.z); b.w = f32_to_bf16(acc.w);
+        reinterpret_cast<ushort4*>(static_cast<uint16_t*>(y) + t * d)[v] = b;
+      } else {
+        reinterpret_cast<float4*>(static_cast<float*>(y) + t * d)[v] = acc;
+      }
+    }
+  }
+}
+
+constexpr int kAuxBlocks = 256;    // partial-sum workgroups
+constexpr int kAuxThreads = 256;
+
+// Partial column sums: workgroup b takes tokens [b*chunk, (b+1)*chunk); thread
+// (e = tid % E, g = tid / E) sums tokens t = g, g + G, ... of the chunk; the
+// G per-thread sums are then added in g order. Fixed order -> deterministic.
+__global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float* __restrict__ probs,
+                                                                  int64_t T, int E, int64_t chunk,
+                                                                  double* __restrict__ part) {
+  __shared__ double s[kAuxThreads];
+  const int tid = threadIdx.x;
+  const int G = kAuxThreads / E;   // E <= 256 -> G >= 1
+  const int e = tid % E, g = tid / E;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t t1 = min(t0 + chunk, T);
+  double acc = 0.0;
+  if (g < G)
+    for (int64_t t = t0 + g; t < t1; t += G) acc += static_cast<double>(probs[t * E + e]);
+  s[tid] = acc;
+  __syncthreads();
+  if (tid < E) {
+    double tot = 0.0;
+    for (int gg = 0; gg < G; ++gg) tot += s[gg * E + tid];
+    part[static_cast<int64_t>(blockIdx.x) * E + tid] = tot;
+  }
+}
+
+__global__ __launch_bounds__(kMaxE) void aux_final_kernel(const double* __restrict__ part,
+                                                          int nblocks,
+                                                          const int32_t* __restrict__ counts,
+                                                          int64_t T, int E, int k, float alpha,
+                                                          float* __restrict__ loss) {
+  __shared__ double s[kMaxE];
+  const int e = threadIdx.x;
+  double term = 0.0;
+  if (e < E && T > 0) {
+    double col = 0.0;
+    for (int b = 0; b < nblocks; ++b) col += part[static_cast<int64_t>(b) * E + e];
+    const double P = col / static_cast<double>(T);
+    const double f = static_cast<double>(counts[e]) / (static_cast<double>(T) * k);
+    term = f * P;
+  }
+  s[e] = term;
+  __syncthreads();
+  for (int o = kMaxE / 2; o > 0; o >>= 1) {
+    if (e < o) s[e] += s[e + o];
+    __syncthreads();
+  }
+  if (e == 0) loss[0] = static_cast<float>(static_cast<double>(alpha) * E * s[0]);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w, int64_t T,
+                          int k, int64_t d, void* y, int out_dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t grid = T < 65536 ? T : 65536;
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                       y_perm, dest, topk_w, T, k, d, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                       y_perm, dest, topk_w, T, k, d, y);
+  return hipGetLastError();
+}
+
+size_t aux_ws_doubles(int64_t T, int E) {
+  (void)T;
+  return static_cast<size_t>(kAuxBlocks) * E;
+}
+
+hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T, int E, int k,
+                           float alpha, float* loss, double* ws, hipStream_t s) {
+  int nblocks = 0;
+  if (T > 0) {
+    const int64_t chunk = (T + kAuxBlocks - 1) / kAuxBlocks;
+    nblocks = static_cast<int>((T + chunk - 1) / chunk);
+    hipLaunchKernelGGL(aux_partial_kernel, dim3(nblocks), dim3(kAuxThreads), 0, s, probs, T, E,
+                       chunk, ws);
+  }
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(kMaxE), 0, s, ws, nblocks, counts, T, E, k,
+                     alpha, loss);
+  return hipGetLastError();
+}
+
+}  // namespace moe

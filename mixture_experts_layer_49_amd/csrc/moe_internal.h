@@ -1,0 +1,60 @@
+// Internal declarations shared by the kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+constexpr int kDispatchTok = 256;   // tokens per dispatch workgroup
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Launchers (host). Arguments are validated by the C-ABI layer before these
+// run; each enqueues on `s` and returns the launch status.
+hipError_t launch_router(const void* x, const void* wg, const float* bias, int64_t T,
+                         int64_t d, int E, int k, int dtype, uint32_t flags,
+                         int32_t* topk_idx, float* topk_w, float* probs, hipStream_t s);
+
+hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                           const void* x, int64_t d, int elem_bytes, int64_t rows_max,
+                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                           void* x_perm, int32_t* ws, hipStream_t s);
+
+hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,
+                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h,
+                          hipStream_t s);
+
+hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max,
+                       int64_t d, int64_t d_ff, const void* w2, int dtype, float* y_perm,
+                       hipStream_t s);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
+                          int64_t T, int k, int64_t d, void* y, int out_dtype, hipStream_t s);
+
+hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T, int E, int k,
+                           float alpha, float* loss, double* ws, hipStream_t s);
+
+size_t dispatch_ws_ints(int64_t T, int E);
+size_t aux_ws_doubles(int64_t T, int E);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace moe

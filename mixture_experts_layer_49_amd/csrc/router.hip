@@ -1,0 +1,216 @@
+// Gate linear + softmax + top-k, fused (EP tutorial "专家并行：混合专家模型的
+// 分布式训练方案", section 1.1 and 2.1 step 1; deployment guide
+// "细粒度专家并行部署实践与优化指南", section 5 step 3: the gate outputs each
+// token's expert-assignment probabilities).
+//
+// One workgroup = 4 waves = 16 tokens. The logits l = x . Wg^T (+ b) are a
+// [16 x d] x [d x E] contraction: bf16 inputs go through
+// v_mfma_f32_16x16x32_bf16 with each wave taking every 4th 128-wide slice of d;
+// the four partial tiles meet in LDS and are summed in a fixed order. Softmax
+// and top-k then run with 16 lanes per token, each lane owning experts
+// e = lane%16 + 16*i, so a token's E logits never leave registers.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTok = 16;      // tokens per workgroup
+constexpr int kThreads = 256;
+constexpr int kChunk = 128;   // d-elements one wave consumes per step
+
+// Softmax + top-k for one token held by a 16-lane group; lane q owns experts
+// e = q + 16*i (i < NT). Invalid experts (e >= E) carry -inf and are skipped.
+template <int NT>
+__device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int64_t t,
+                            int q, int32_t* topk_idx, float* topk_w, float* probs) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) m = fmaxf(m, lg[i]);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float ex[NT];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int e = q + 16 * i;
+    ex[i] = (e < E) ? expf(lg[i] - m) : 0.f;
+    s += ex[i];
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+  const float inv_s = 1.0f / s;
+  if (probs) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = q + 16 * i;
+      if (e < E) probs[t * E + e] = ex[i] * inv_s;
+    }
+  }
+  // k rounds of a (logit desc, index asc) arg-max over the unchosen experts.
+  uint32_t chosen = 0;
+  float wsel[kMaxK];
+  int esel[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) break;
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = q + 16 * i;
+      if (e < E && !((chosen >> i) & 1u)) {
+        if (lg[i] > bv || (lg[i] == bv && e < be)) { bv = lg[i]; be = e; }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oe = __shfl_xor(be, o);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if (be != 0x7fffffff) {
+      if ((be & 15) == q) chosen |= 1u << (be >> 4);
+      esel[j] = be;
+      wsel[j] = expf(bv - m) * inv_s;   // same arithmetic as probs[t, be]
+    } else {                            // only NaN logits were left
+      esel[j] = -1;
+      wsel[j] = 0.f;
+    }
+  }
+  if (q == 0) {
+    float norm = 1.f;
+    if (flags & 1u) {
+      float tot = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k) tot += wsel[j];
+      norm = 1.0f / tot;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        topk_idx[t * k + j] = esel[j];
+        topk_w[t * k + j] = (flags & 1u) ? wsel[j] * norm : wsel[j];
+      }
+    }
+  }
+}
+
+// bf16: MFMA logits, LDS reduction over the four d-slices, then softmax/top-k.
+template <int NT>
+__global__ __launch_bounds__(kThreads) void router_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
+    const float* __restrict__ bias, int64_t T, int64_t d, int E, int k, uint32_t flags,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ probs) {
+  __shared__ float red[4][kTok][NT * 16];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  const int64_t trow = min(t0 + r, T - 1);   // tail rows re-read the last token
+  const uint16_t* xrow = x + trow * d;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* wrow[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) wrow[n] = wg + static_cast<int64_t>(min(n * 16 + r, E - 1)) * d;
+
+  for (int64_t c0 = static_cast<int64_t>(wave) * kChunk; c0 < d; c0 += 4 * kChunk) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t col = c0 + g * 32 + s * 8;
+      if (col < d) a[s] = *reinterpret_cast<const bf16x8*>(xrow + col);
+      else a[s] = bf16x8{};
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t col = c0 + g * 32 + s * 8;
+        bf16x8 b = bf16x8{};
+        if (col < d) b = *reinterpret_cast<const bf16x8*>(wrow[n] + col);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc[n], 0, 0, 0);
+      }
+    }
+  }
+  // D layout of a 16x16 tile: lane holds rows 4*(lane/16)+i, column lane%16.
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][g * 4 + i][n * 16 + r] = acc[n][i];
+  __syncthreads();
+
+  const int tok = tid >> 4, q = tid & 15;
+  const int64_t t = t0 + tok;
+  float lg[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int e = q + 16 * i;
+    float v = red[0][tok][e] + red[1][tok][e] + red[2][tok][e] + red[3][tok][e];
+    if (bias != nullptr && e < E) v += bias[e];
+    lg[i] = (e < E) ? v : -INFINITY;
+  }
+  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs);
+}
+
+// f32: plain FMA dot products, one (token, expert) pair per lane and step.
+template <int NT>
+__global__ __launch_bounds__(kThreads) void router_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    int64_t T, int64_t d, int E, int k, uint32_t flags, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ probs) {
+  const int tid = threadIdx.x;
+  const int tok = tid >> 4, q = tid & 15;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + tok;
+  const float* xr = x + min(t, T - 1) * d;
+  float lg[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int e = q + 16 * i;
+    if (e < E) {
+      const float* wr = wg + static_cast<int64_t>(e) * d;
+      float v = 0.f;
+      for (int64_t c = 0; c < d; ++c) v = fmaf(xr[c], wr[c], v);
+      if (bias != nullptr) v += bias[e];
+      lg[i] = v;
+    } else {
+      lg[i] = -INFINITY;
+    }
+  }
+  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs);
+}
+
+template <int NT>
+hipError_t launch_nt(const void* x, const void* wg, const float* bias, int64_t T, int64_t d,
+                     int E, int k, int dtype, uint32_t flags, int32_t* idx, float* w,
+                     float* probs, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok)), block(kThreads);
+  if (dtype == 1)
+    hipLaunchKernelGGL(router_bf16_kernel<NT>, grid, block, 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias,
+                       T, d, E, k, flags, idx, w, probs);
+  else
+    hipLaunchKernelGGL(router_f32_kernel<NT>, grid, block, 0, s, static_cast<const float*>(x),
+                       static_cast<const float*>(wg), bias, T, d, E, k, flags, idx, w, probs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router(const void* x, const void* wg, const float* bias, int64_t T, int64_t d,
+                         int E, int k, int dtype, uint32_t flags, int32_t* topk_idx,
+                         float* topk_w, float* probs, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nt = (E + 15) / 16;
+  if (nt <= 1) return launch_nt<1>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
+  if (nt <= 2) return launch_nt<2>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
+  if (nt <= 4) return launch_nt<4>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
+  if (nt <= 8) return launch_nt<8>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
+  return launch_nt<16>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
+}
+
+}  // namespace moe
