@@ -120,22 +120,28 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
  * (ETP page: up-projection w1 then down-projection w2, e.g.
  * 4096 -> 16384 -> 4096; EP tutorial 2.1 step 4: each expert computes on its
  * own tokens). For every expert e and row r in [offsets[e], offsets[e+1]):
- *   h[r]      = gelu_tanh(W1[e] . x_perm[r])    (stored in dtype; bf16 = RNE)
+ *   h[r]      = gelu_tanh(W1[e] . x_perm[r])
  *   y_perm[r] = W2[e] . h[r]                     (float32)
  * with gelu_tanh(z) = z / 2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
  *   x_perm [rows_max, d]      dtype    w1 [E, d_ff, d] dtype (K contiguous)
- *   h      [rows_max, d_ff]   dtype    w2 [E, d, d_ff] dtype (K contiguous)
+ *   h      [rows_max, d_ff]   hidden   w2 [E, d, d_ff] dtype (K contiguous)
  *   y_perm [rows_max, d]      f32
  *   offsets [E+1] int32, device: read by the kernels, never by the host.
- * Products accumulate in float32. Rows >= offsets[E] are not touched. */
+ * Hidden-activation storage: f32 when dtype is MOE_F32; IEEE fp16 (RNE) when
+ * dtype is MOE_BF16 -- the same two bytes as bf16 with three more significand
+ * bits; the down-projection then runs fp16 x fp16 with W2's bf16 values
+ * converted exactly to fp16. This needs |h| and |W2| below 65504.
+ * Products accumulate in float32. Rows >= offsets[E] are not touched.
+ * Limits: d, d_ff <= 2^22. */
 int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E,
                     int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
                     const void* w2, int32_t dtype, void* h, float* y_perm,
                     hipStream_t stream);
 
 /* The two halves of moe_grouped_ffn, callable on their own (same arguments,
- * same layouts): the up-projection with its GELU-tanh epilogue, and the
- * down-projection. moe_grouped_ffn == up then down on the same stream. */
+ * same layouts, `dtype` is the layer's dtype in both): the up-projection with
+ * its GELU-tanh epilogue, and the down-projection. moe_grouped_ffn == up then
+ * down on the same stream. */
 int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E,
                        int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
                        int32_t dtype, void* h, hipStream_t stream);

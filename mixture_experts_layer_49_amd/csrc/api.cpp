@@ -76,8 +76,8 @@ int check_ffn(const void* a, const int32_t* offsets, int32_t E, int64_t rows_max
     return fail(MOE_ERR_ARG, "need rows_max >= 0, d > 0, d_ff > 0 (got %lld, %lld, %lld)",
                 static_cast<long long>(rows_max), static_cast<long long>(d),
                 static_cast<long long>(d_ff));
-  if (d > (1 << 30) || d_ff > (1 << 30) || rows_max > 0x7fffffffLL)
-    return fail(MOE_ERR_SHAPE, "d, d_ff or rows_max too large for 32-bit row indexing");
+  if (d > (1 << 22) || d_ff > (1 << 22) || rows_max > 0x7fffffffLL)
+    return fail(MOE_ERR_SHAPE, "d and d_ff must be <= 2^22 and rows_max < 2^31");
   MOE_TRY(check_row("d", d, dtype));
   MOE_TRY(check_row("d_ff", d_ff, dtype));
   if (rows_max == 0) return MOE_OK;

@@ -10,7 +10,13 @@
 //   down: A = h [R, d_ff],    B = W2[e] [d, d_ff], C -> y_perm (f32)
 //
 // bf16 path (gfx950 MFMA): 256x256x64 workgroup tiles, 4 waves in a 2x2 grid,
-// each wave owning a 128x128 sub-tile = 4x4 v_mfma_f32_32x32x16_bf16 tiles.
+// each wave owning a 128x128 sub-tile = 4x4 32x32x16 MFMA tiles. The hidden
+// activation h is kept as IEEE fp16, not bf16: same size, three more
+// significand bits, which cuts the rounding error it adds to the layer output
+// about eight-fold. So the up-projection is bf16 x bf16 (v_mfma_f32_32x32x16_bf16)
+// with a GELU -> fp16 epilogue, and the down-projection is fp16 h x fp16 W2
+// (v_mfma_f32_32x32x16_f16), W2's bf16 values being converted exactly to
+// fp16 on their way into LDS.
 // Global -> register -> LDS staging, double-buffered (2 x 64 KiB), with the
 // 16-byte chunk of row r, column-chunk c stored at chunk (c ^ (r & 7)) so both
 // the row-wise writes and the MFMA fragment reads are free of bank conflicts.
@@ -81,6 +87,19 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z / (1.0f + __expf(-2.0f * u));
 }
 
+// Two bf16 values (one 32-bit word) -> two IEEE fp16 values, round to nearest
+// even. Exact for every bf16 value inside the fp16 normal range.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  const f16x2 h = {static_cast<_Float16>(__uint_as_float(v << 16)),
+                   static_cast<_Float16>(__uint_as_float(v & 0xffff0000u))};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  return uint4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+               bf16x2_to_f16x2(v.w)};
+}
+
 // ------------------------------------------------------------ bf16 MFMA --
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
@@ -91,8 +110,10 @@ constexpr int kAChunks = BM * BK / 8 / kThreads;   // 16-byte chunks per thread
 constexpr int kBChunks = BN * BK / 8 / kThreads;
 constexpr int kStageChunks = (BM + BN) * BK / 8;   // uint4 per LDS stage
 
+// UP:   A = x_perm (bf16), B = W1 (bf16), C = fp16 gelu_tanh(acc)
+// DOWN: A = h (fp16),      B = W2 (bf16 -> fp16 in the loader), C = f32 acc
 template <bool UP>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int N, int K,
     const uint16_t* __restrict__ B, void* __restrict__ Cout) {
   __shared__ uint4 lds[2][kStageChunks];
@@ -157,7 +178,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
 #pragma unroll
       for (int i = 0; i < kAChunks; ++i) lds[buf][st0 + 256 * i] = ra[i];
 #pragma unroll
-      for (int i = 0; i < kBChunks; ++i) lds[buf][BM * 8 + st0 + 256 * i] = rb[i];
+      for (int i = 0; i < kBChunks; ++i)
+        lds[buf][BM * 8 + st0 + 256 * i] = UP ? rb[i] : bf16x8_to_f16x8(rb[i]);
     };
 
     f32x16 acc[MI][NI];
@@ -178,22 +200,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int c = kk * 2 + hl;
-        bf16x8 af[MI], bfr[NI];
+        uint4 af[MI], bfr[NI];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const int row = wm * (BM / WM) + i * 32 + l32;
-          af[i] = __builtin_bit_cast(bf16x8, lds[cur][row * 8 + (c ^ (row & 7))]);
+          af[i] = lds[cur][row * 8 + (c ^ (row & 7))];
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           const int row = wn * (BN / WN) + j * 32 + l32;
-          bfr[j] = __builtin_bit_cast(bf16x8, lds[cur][BM * 8 + row * 8 + (c ^ (row & 7))]);
+          bfr[j] = lds[cur][BM * 8 + row * 8 + (c ^ (row & 7))];
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < NI; ++j) {
+            if (UP)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(f16x8, af[i]), __builtin_bit_cast(f16x8, bfr[j]), acc[i][j], 0, 0, 0);
+          }
       }
       if (kt + 1 < nk) lstore(cur ^ 1);
       __syncthreads();
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(
           if (row < seg1) {
             const int64_t o = static_cast<int64_t>(row) * N + col;
             if (UP)
-              static_cast<uint16_t*>(Cout)[o] = f32_to_bf16(gelu_tanh(acc[i][j][r]));
+              static_cast<_Float16*>(Cout)[o] = static_cast<_Float16>(gelu_tanh(acc[i][j][r]));
             else
               static_cast<float*>(Cout)[o] = acc[i][j][r];
           }
@@ -295,7 +323,7 @@ hipError_t launch_gemm(const void* A, const int32_t* offsets, int E, int64_t row
     int64_t g = device_cu_count();
     if (upper < g) g = upper;
     g = (g + 7) / 8 * 8;
-    hipLaunchKernelGGL(grouped_gemm_bf16<UP>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(grouped_gemm_mfma<UP>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
                        s, static_cast<const uint16_t*>(A), offsets, E, N, K,
                        static_cast<const uint16_t*>(B), C);
   } else {

@@ -95,6 +95,12 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def hidden_dtype(dt: torch.dtype) -> torch.dtype:
+    """Storage of the FFN hidden activation h: f32 for f32 layers, fp16 for
+    bf16 layers (see moe_grouped_ffn in include/moe.h)."""
+    return torch.float32 if dt == torch.float32 else torch.float16
+
+
 # ------------------------------------------------------------------ calls --
 def moe_capacity(n_tokens: int, n_experts: int, capacity_factor: float) -> int:
     return int(lib().moe_capacity(n_tokens, n_experts, capacity_factor))
@@ -143,9 +149,9 @@ def moe_dispatch(topk_idx, E: int, capacity: int, x, counts=None, offsets=None, 
 
 def moe_expert_up_gelu(x_perm, offsets, w1, rows_max: int, h=None, stream=None):
     E, d_ff, d = w1.shape
-    h = _empty((max(rows_max, 1), d_ff), x_perm.dtype, x_perm) if h is None else h
+    h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x_perm) if h is None else h
     _check(lib().moe_expert_up_gelu(_ptr(x_perm), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
-                                    dtype_code(x_perm.dtype), _ptr(h), _stream(stream)))
+                                    dtype_code(w1.dtype), _ptr(h), _stream(stream)))
     return h
 
 
@@ -153,13 +159,13 @@ def moe_expert_down(h, offsets, w2, rows_max: int, y_perm=None, stream=None):
     E, d, d_ff = w2.shape
     y_perm = _empty((max(rows_max, 1), d), torch.float32, h) if y_perm is None else y_perm
     _check(lib().moe_expert_down(_ptr(h), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w2),
-                                 dtype_code(h.dtype), _ptr(y_perm), _stream(stream)))
+                                 dtype_code(w2.dtype), _ptr(y_perm), _stream(stream)))
     return y_perm
 
 
 def moe_grouped_ffn(x_perm, offsets, w1, w2, rows_max: int, h=None, y_perm=None, stream=None):
     E, d_ff, d = w1.shape
-    h = _empty((max(rows_max, 1), d_ff), x_perm.dtype, x_perm) if h is None else h
+    h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x_perm) if h is None else h
     y_perm = _empty((max(rows_max, 1), d), torch.float32, x_perm) if y_perm is None else y_perm
     _check(lib().moe_grouped_ffn(_ptr(x_perm), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
                                  _ptr(w2), dtype_code(x_perm.dtype), _ptr(h), _ptr(y_perm),
@@ -208,7 +214,7 @@ class MoEBuffers:
         self.dest = z((T, k), torch.int32)
         self.src = z((R,), torch.int32)
         self.x_perm = z((R, d), dtype)
-        self.h = z((R, d_ff), dtype)
+        self.h = z((R, d_ff), hidden_dtype(dtype))
         self.y_perm = z((R, d), torch.float32)
         self.y = z((T, d), torch.float32)
         self.loss = z((1,), torch.float32)
