@@ -1,0 +1,200 @@
+"""Benchmark: one MoE layer forward per step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is the whole forward -- gate + softmax + top-k, dispatch (index build +
+permute), grouped expert FFN (up-projection + GELU, down-projection), weighted
+combine, aux loss -- over one batch of synthetic tokens already resident in
+HBM. Default workload: large-experts-e8 (T=8192 tokens, d=4096,
+d_ff=16384, E=8, top-2, capacity factor 1.25, bf16).
+
+Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
+kernel (timed live with HIP events on the launch stream), a per-call
+breakdown, and the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE fwd tokens/s on 1 GPU + expert GEMM % bf16 MFMA peak, HBM % peak"
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large-experts-e8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args(argv)
+
+
+def cpu_baseline(inp, cfg):
+    """The CPU oracle, as it stands, on the full batch of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    O.forward(inp, cfg.dtype, cfg.k, cfg.cf, cfg.alpha)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "full batch: %d tokens, every step (gate, softmax, top-k, dispatch, "
+                      "FFN on all kept rows, combine, aux) in float64 numpy; %.1f s wall"
+                      % (cfg.T, dt), "seconds": dt}
+
+
+def main(argv=None) -> int:
+    args = parse(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_49_amd import inputs as I
+    from mixture_experts_layer_49_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    cfg = I.config(args.workload)
+    t0 = time.perf_counter()
+    inp = I.make_inputs(cfg)
+    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+
+    def dev(a, bf16):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf16 else t).to("cuda:0")
+
+    bf = cfg.dtype == "bf16"
+    x, w1, w2 = dev(inp["x"], bf), dev(inp["w1"], bf), dev(inp["w2"], bf)
+    wg = dev(inp["w_gate"], bf) if cfg.routed else None
+    bias = dev(inp["bias"], False) if cfg.routed and inp["bias"] is not None else None
+    given_idx = dev(inp["topk_idx"], False) if not cfg.routed else None
+    given_w = dev(inp["topk_w"], False) if not cfg.routed else None
+    C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed)
+    stream = torch.cuda.current_stream()
+
+    names = ["router", "dispatch", "up_gelu", "down", "combine", "aux"]
+    # one set of boundary events per timed step, all on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        if cfg.routed:
+            ops.moe_router_topk(x, wg, bias, cfg.k, 0, True, b.topk_idx, b.topk_w, b.probs)
+            idx, w = b.topk_idx, b.topk_w
+        else:
+            idx, w = given_idx, given_w
+        rec(1)
+        ops.moe_dispatch(idx, cfg.E, C, x, b.counts, b.offsets, b.dest, b.src, b.x_perm,
+                         b.ws_dispatch)
+        rec(2)
+        ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h)
+        rec(3)
+        ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm)
+        rec(4)
+        ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
+        rec(5)
+        if cfg.routed:
+            ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
+        rec(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
+
+    counts = b.counts.cpu().numpy()
+    R = int(b.offsets.cpu().numpy()[-1])
+    T, d, dff, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
+    s = 2 if bf else 4
+    flops_up = 2.0 * R * d * dff
+    flops_down = 2.0 * R * dff * d
+    bytes_router = T * d * s + E * d * s + T * k * 8 + T * E * 4 if cfg.routed else 0
+    bytes_dispatch = T * k * 4 * 2 + 2 * R * d * s + R * 4
+    bytes_combine = R * d * 4 + T * d * 4 + T * k * 8
+    bytes_aux = T * E * 4 if cfg.routed else 0
+    us = dict(zip(names, (per * 1e3).tolist()))
+    breakdown = {
+        "router": {"us": us["router"], "GB/s": bytes_router / (per[0] * 1e-3) / 1e9 if per[0] else None},
+        "dispatch": {"us": us["dispatch"], "GB/s": bytes_dispatch / (per[1] * 1e-3) / 1e9},
+        "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (per[2] * 1e-3) / 1e12},
+        "down": {"us": us["down"], "TFLOP/s": flops_down / (per[3] * 1e-3) / 1e12},
+        "combine": {"us": us["combine"], "GB/s": bytes_combine / (per[4] * 1e-3) / 1e9},
+        "aux": {"us": us["aux"]},
+    }
+    for key, v in breakdown.items():
+        if "GB/s" in v and v["GB/s"] is not None:
+            v["hbm_frac"] = v["GB/s"] / PEAK_HBM_GBS
+        if "TFLOP/s" in v:
+            v["mfma_frac"] = v["TFLOP/s"] / PEAK_MFMA_TFLOPS
+    dom = "up_gelu" if per[2] >= per[3] else "down"
+    achieved = breakdown[dom]["TFLOP/s"]
+    ffn_tflops = (flops_up + flops_down) / ((per[2] + per[3]) * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": T * args.steps / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded; inputs resident in HBM before timing)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
+                   "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
+                   "max_over_mean_load": float(counts.max() / counts.mean()),
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else "down"),
+                     "bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
+                     "launch_us": us[dom]},
+        "ffn_mfma_frac": ffn_tflops / PEAK_MFMA_TFLOPS,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(inp, cfg)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -86,15 +86,27 @@ __global__ __launch_bounds__(kMaxE) void aux_final_kernel(const double* __restri
                                                           int64_t T, int E, int k, float alpha,
                                                           float* __restrict__ loss) {
   __shared__ double s[kMaxE];
-  const int e = threadIdx.x;
+  __shared__ double g_part[kMaxE];
+  const int tid = threadIdx.x;
+  // Thread (e = tid % E, g = tid / E) adds partials b = g, g + G, ...; the G
+  // group sums of each expert are then added in g order.
+  const int G = kMaxE / E;
+  const int e_t = tid % E, g_t = tid / E;
+  double acc = 0.0;
+  if (g_t < G)
+    for (int b = g_t; b < nblocks; b += G) acc += part[static_cast<int64_t>(b) * E + e_t];
+  g_part[tid] = acc;
+  __syncthreads();
+  const int e = tid;
   double term = 0.0;
   if (e < E && T > 0) {
     double col = 0.0;
-    for (int b = 0; b < nblocks; ++b) col += part[static_cast<int64_t>(b) * E + e];
+    for (int g = 0; g < G; ++g) col += g_part[g * E + e];
     const double P = col / static_cast<double>(T);
     const double f = static_cast<double>(counts[e]) / (static_cast<double>(T) * k);
     term = f * P;
   }
+  __syncthreads();
   s[e] = term;
   __syncthreads();
   for (int o = kMaxE / 2; o > 0; o >>= 1) {

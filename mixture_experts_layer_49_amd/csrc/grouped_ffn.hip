@@ -6,20 +6,26 @@
 // Both projections are one segmented "NT" GEMM, C[m, n] = sum_k A[m, k] B[n, k]
 // with A and B K-contiguous, over the expert-major row segments that
 // offsets[] describes:
-//   up:   A = x_perm [R, d],  B = W1[e] [d_ff, d], C = gelu_tanh(.) -> h (dtype)
+//   up:   A = x_perm [R, d],  B = W1[e] [d_ff, d], C = gelu_tanh(.) -> h
 //   down: A = h [R, d_ff],    B = W2[e] [d, d_ff], C -> y_perm (f32)
 //
 // bf16 path (gfx950 MFMA): 256x256x64 workgroup tiles, 4 waves in a 2x2 grid,
-// each wave owning a 128x128 sub-tile = 4x4 32x32x16 MFMA tiles. The hidden
-// activation h is kept as IEEE fp16, not bf16: same size, three more
-// significand bits, which cuts the rounding error it adds to the layer output
-// about eight-fold. So the up-projection is bf16 x bf16 (v_mfma_f32_32x32x16_bf16)
-// with a GELU -> fp16 epilogue, and the down-projection is fp16 h x fp16 W2
-// (v_mfma_f32_32x32x16_f16), W2's bf16 values being converted exactly to
-// fp16 on their way into LDS.
-// Global -> register -> LDS staging, double-buffered (2 x 64 KiB), with the
-// 16-byte chunk of row r, column-chunk c stored at chunk (c ^ (r & 7)) so both
-// the row-wise writes and the MFMA fragment reads are free of bank conflicts.
+// each wave owning a 128x128 sub-tile = 4x4 32x32x16 MFMA tiles, accumulators
+// in AGPRs. The hidden activation h is kept as IEEE fp16, not bf16: same
+// size, three more significand bits, which cuts the rounding error it adds to
+// the layer output about eight-fold. So the up-projection is bf16 x bf16
+// (v_mfma_f32_32x32x16_bf16) with a GELU -> fp16 epilogue, and the
+// down-projection is fp16 h x fp16 W2 (v_mfma_f32_32x32x16_f16), W2's bf16
+// values being converted exactly to fp16 on their way into LDS.
+//
+// Staging: global -> LDS with buffer_load_dwordx4 ... lds (no VGPR round trip)
+// wherever the bytes go to LDS unchanged; W2 of the down-projection goes
+// through VGPRs for its conversion. Two 64 KiB LDS stages: stage k+1 streams
+// in while the MFMAs consume stage k, and each wave prefetches the next
+// k-slice's fragments into a second register set. The 16-byte chunk c of tile
+// row r lives at chunk c ^ (r & 7) of that row, so the MFMA fragment reads
+// (eight rows, same c) hit eight different bank groups.
+//
 // Persistent: one workgroup per CU walks the tile list, which it derives on
 // the device from offsets[] (no host read-back). Tiles are ordered expert,
 // n-panel, m-tile, and each round of gridDim tiles is laid out so that the 32
@@ -30,6 +36,8 @@
 
 namespace moe {
 namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // ----------------------------------------------------------- tile list --
 // s_pref[e] = number of m-tiles of experts < e (e = 0..E).
@@ -103,15 +111,18 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
 // ------------------------------------------------------------ bf16 MFMA --
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int WM = 2, WN = 2;                 // waves per dimension
-constexpr int MI = BM / WM / 32;              // 32x32 tiles per wave along M
-constexpr int NI = BN / WN / 32;              // ... along N
-constexpr int kAChunks = BM * BK / 8 / kThreads;   // 16-byte chunks per thread
-constexpr int kBChunks = BN * BK / 8 / kThreads;
-constexpr int kStageChunks = (BM + BN) * BK / 8;   // uint4 per LDS stage
+constexpr int kWaves = kThreads / kWave;
+constexpr int WM = 2, WN = 2;                     // waves per dimension
+constexpr int MI = BM / WM / 32;                  // 32x32 tiles per wave along M
+constexpr int NI = BN / WN / 32;                  // ... along N
+constexpr int kRowsPerInstr = kWave / 8;          // one wave-wide 16-B load = 8 rows
+constexpr int kLoadsA = BM / kRowsPerInstr / kWaves;   // per wave per stage
+constexpr int kLoadsB = BN / kRowsPerInstr / kWaves;
+constexpr int kStageChunks = (BM + BN) * BK / 8;  // uint4 per LDS stage
+constexpr int kRegB = BN * BK / 8 / kThreads;     // register-staged W2 chunks per thread
 
 // UP:   A = x_perm (bf16), B = W1 (bf16), C = fp16 gelu_tanh(acc)
-// DOWN: A = h (fp16),      B = W2 (bf16 -> fp16 in the loader), C = f32 acc
+// DOWN: A = h (fp16),      B = W2 (bf16 -> fp16 through VGPRs), C = f32 acc
 template <bool UP>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int N, int K,
@@ -125,19 +136,34 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(
   const int64_t total = static_cast<int64_t>(s_pref[E]) * tiles_n;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // The wave index is uniform across the wave; say so, so that the LDS-DMA
+  // destination (M0) is computed in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hl = lane >> 5;
   const int nk = (K + BK - 1) / BK;
+  const bool k_tail = (K % BK) != 0;
 
-  const int G = gridDim.x;                    // multiple of 8
+  const int G = gridDim.x;                        // multiple of 8
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // Loader role: chunk q = tid + kThreads*i holds row (tid/8) + 32*i, column
-  // chunk tid%8 of a tile; its LDS slot is therefore slot0 + 256*i.
-  const int ld_row = tid >> 3, ld_c = tid & 7;
-  const int st0 = ld_row * 8 + (ld_c ^ (ld_row & 7));
+  // Loader: wave-wide load j of wave w fills LDS chunks [64 (4j + w), +64) =
+  // rows 8 (4j + w) .. +8. Lane l lands in chunk slot l of that block: row
+  // offset l/8, physical chunk l%8, hence logical chunk (l%8) ^ (l/8) (the
+  // block starts on a multiple of 8 rows, so row & 7 = l/8).
   const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
+  const int ld_r = lane >> 3, ld_c = (lane & 7) ^ (lane >> 3);
+  const uint32_t ld_voff = ld_r * row_bytes + ld_c * 16u;
+  // Register-staged W2 loader (down only): 16-byte chunk q = tid + 256 i is
+  // row q/8 = tid/8 + 32 i, logical chunk tid%8, stored at st0 + 256 i.
+  const int rs_row = tid >> 3, rs_c = tid & 7;
+  const int rs_st0 = rs_row * 8 + (rs_c ^ (rs_row & 7));
+  const uint32_t rs_voff = rs_row * row_bytes + rs_c * 16u;
+
+  // Fragment reads: row l32 of each 32-row sub-tile, chunk (2 kk + hl) ^ (l32 & 7).
+  const int a_base = (wm * (BM / WM) + l32) * 8;
+  const int b_base = BM * 8 + (wn * (BN / WN) + l32) * 8;
+  const int sw = l32 & 7;
 
   for (int64_t base = 0;; base += G) {
     const int64_t id = base + slot;
@@ -155,31 +181,58 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(B + (static_cast<int64_t>(tl.e) * N + n0) * K), 0,
         static_cast<int>(b_rows * row_bytes), 0x00020000);
-    const uint32_t voff = ld_row * row_bytes + ld_c * 16u;
 
-    uint4 ra[kAChunks], rb[kBChunks];
-    auto gload = [&](int kt) {
-      const int k0 = kt * BK;
-      const bool ok = (k0 + BK) <= K || (k0 + ld_c * 8) < K;   // K tail -> zeros
+    uint4 rb[UP ? 1 : kRegB];
+    // Issue every load of stage kt into LDS buffer `buf`; nothing waits here.
+    auto issue = [&](int kt, int buf) {
+      const uint32_t k_bytes = static_cast<uint32_t>(kt) * BK * 2u;
 #pragma unroll
-      for (int i = 0; i < kAChunks; ++i) {
-        const uint32_t so = i * 32u * row_bytes + k0 * 2u;
-        ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, voff, so, 0));
-        if (!ok) ra[i] = uint4{0, 0, 0, 0};
+      for (int j = 0; j < kLoadsA; ++j) {
+        const int blk = j * kWaves + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_ptr_t)(&lds[buf][blk * kWave]), 16, ld_voff,
+            blk * kRowsPerInstr * row_bytes + k_bytes, 0, 0);
       }
+      if (UP) {
 #pragma unroll
-      for (int i = 0; i < kBChunks; ++i) {
-        const uint32_t so = i * 32u * row_bytes + k0 * 2u;
-        rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, voff, so, 0));
-        if (!ok) rb[i] = uint4{0, 0, 0, 0};
+        for (int j = 0; j < kLoadsB; ++j) {
+          const int blk = j * kWaves + wave;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              b_rsrc, (lds_ptr_t)(&lds[buf][BM * 8 + blk * kWave]), 16, ld_voff,
+              blk * kRowsPerInstr * row_bytes + k_bytes, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRegB; ++i)
+          rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                b_rsrc, rs_voff, i * 32u * row_bytes + k_bytes, 0));
       }
     };
-    auto lstore = [&](int buf) {
+    // Down only: convert the staged W2 chunks and write them to LDS.
+    auto store_b = [&](int buf) {
+      if (!UP) {
 #pragma unroll
-      for (int i = 0; i < kAChunks; ++i) lds[buf][st0 + 256 * i] = ra[i];
+        for (int i = 0; i < kRegB; ++i)
+          lds[buf][BM * 8 + rs_st0 + 256 * i] = bf16x8_to_f16x8(rb[i]);
+      }
+    };
+    // After a stage has landed: zero the chunks past K (only the last stage,
+    // only when K is not a multiple of 64).
+    auto zero_tail = [&](int kt, int buf) {
+      const int k0 = kt * BK;
+      for (int p = tid; p < kStageChunks; p += kThreads) {
+        const int c = (p & 7) ^ ((p >> 3) & 7);
+        if (k0 + c * 8 >= K) lds[buf][p] = uint4{0, 0, 0, 0};
+      }
+    };
+
+    uint4 fa[2][MI], fb[2][NI];
+    auto read_frags = [&](int buf, int kk, int sl) {
+      const int c = (kk * 2 + hl) ^ sw;
 #pragma unroll
-      for (int i = 0; i < kBChunks; ++i)
-        lds[buf][BM * 8 + st0 + 256 * i] = UP ? rb[i] : bf16x8_to_f16x8(rb[i]);
+      for (int i = 0; i < MI; ++i) fa[sl][i] = lds[buf][a_base + i * 32 * 8 + c];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) fb[sl][j] = lds[buf][b_base + j * 32 * 8 + c];
     };
 
     f32x16 acc[MI][NI];
@@ -190,41 +243,50 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    __syncthreads();   // previous tile's readers are done with lds
-    gload(0);
-    lstore(0);
+    __syncthreads();   // previous tile's readers are done with both buffers
+    issue(0, 0);
+    store_b(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (k_tail && nk == 1) {
+      zero_tail(0, 0);
+      __syncthreads();
+    }
+    read_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
+      const bool more = kt + 1 < nk;
+      if (more) issue(kt + 1, cur ^ 1);
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const int c = kk * 2 + hl;
-        uint4 af[MI], bfr[NI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int row = wm * (BM / WM) + i * 32 + l32;
-          af[i] = lds[cur][row * 8 + (c ^ (row & 7))];
-        }
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const int row = wn * (BN / WN) + j * 32 + l32;
-          bfr[j] = lds[cur][BM * 8 + row * 8 + (c ^ (row & 7))];
-        }
+        const int sl = kk & 1;
+        if (kk + 1 < BK / 16) read_frags(cur, kk + 1, sl ^ 1);   // prefetch next k-slice
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
             if (UP)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8, fa[sl][i]), __builtin_bit_cast(bf16x8, fb[sl][j]),
+                  acc[i][j], 0, 0, 0);
             else
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  __builtin_bit_cast(f16x8, af[i]), __builtin_bit_cast(f16x8, bfr[j]), acc[i][j], 0, 0, 0);
+                  __builtin_bit_cast(f16x8, fa[sl][i]), __builtin_bit_cast(f16x8, fb[sl][j]),
+                  acc[i][j], 0, 0, 0);
           }
       }
-      if (kt + 1 < nk) lstore(cur ^ 1);
+      if (more) {
+        store_b(cur ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       __syncthreads();
+      if (more) {
+        if (k_tail && kt + 2 == nk) {
+          zero_tail(kt + 1, cur ^ 1);
+          __syncthreads();
+        }
+        read_frags(cur ^ 1, 0, 0);
+      }
     }
 
     // Epilogue. 32x32 D layout: lane holds column lane%32 and, for register r,
