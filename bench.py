@@ -41,7 +41,37 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large-experts-e8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps, as a "
+                         "known-size reference for memory-traffic counters")
     return ap.parse_args(argv)
+
+
+GEMM_SOURCES = ["mixture_experts_layer_49_amd/csrc/gemm_mfma.hip",
+                "mixture_experts_layer_49_amd/csrc/ffn_common.h",
+                "mixture_experts_layer_49_amd/csrc/moe_internal.h"]
+
+
+def measured_traffic(which: str, workload: str):
+    """HBM bytes per launch of the up/down GEMM from the committed rocprofv3
+    summary (profiles/gemm_mfma_<which>_<workload>.md), or None when there is
+    none or the kernel source changed after the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "gemm_mfma_%s_%s.md" % (which, workload))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            key, val = line.split(":", 1)
+            fields[key] = val.strip()
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(inp, cfg):
@@ -123,6 +153,14 @@ def main(argv=None) -> int:
             ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
         rec(6)
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src_probe = torch.ones(n // 4, dtype=torch.float32, device=x.device)
+        dst_probe = torch.empty_like(src_probe)
+        torch.cuda.synchronize()
+        dst_probe.copy_(src_probe)
+        torch.cuda.synchronize()
+        del src_probe, dst_probe
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -183,7 +221,8 @@ def main(argv=None) -> int:
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else "down"),
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
+                     "traffic": measured_traffic("up" if dom == "up_gelu" else "down", cfg.name),
                      "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
                      "launch_us": us[dom]},
         "ffn_mfma_frac": ffn_tflops / PEAK_MFMA_TFLOPS,

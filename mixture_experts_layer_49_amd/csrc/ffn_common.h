@@ -1,0 +1,89 @@
+// Pieces shared by the grouped expert-FFN kernels: the device-side tile list
+// over the expert segments, GELU-tanh and the bf16 -> fp16 conversion.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace ffn {
+
+// s_pref[e] = number of BM-row tiles of experts < e (e = 0..E), from the
+// segment bounds offsets[] (device memory); every thread of the block calls.
+__device__ inline void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int BM,
+                                         int* s_pref, int* s_tmp) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kMaxE; e += blockDim.x) {
+    int mt = 0;
+    if (e < E) {
+      const int rows = offsets[e + 1] - offsets[e];
+      mt = (rows + BM - 1) / BM;
+    }
+    s_tmp[e] = mt;
+  }
+  __syncthreads();
+  // Inclusive scan over kMaxE entries (Hillis-Steele, ping-pong s_tmp/s_pref).
+  int* in = s_tmp;
+  int* out = s_pref + 1;
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    for (int e = tid; e < kMaxE; e += blockDim.x) out[e] = in[e] + (e >= o ? in[e - o] : 0);
+    __syncthreads();
+    int* t = in;
+    in = out;
+    out = t;
+  }
+  // 8 steps (even): the result is back in s_tmp.
+  for (int e = tid; e < kMaxE; e += blockDim.x) s_pref[e + 1] = in[e];
+  if (tid == 0) s_pref[0] = 0;
+  __syncthreads();
+}
+
+struct Tile {
+  int e, mi, nt;
+};
+
+// Tiles are numbered expert by expert; inside an expert, n-panel by n-panel,
+// and inside an n-panel, m-tile by m-tile.
+__device__ __forceinline__ Tile find_tile(const int* s_pref, int E, int tiles_n, int64_t id) {
+  int lo = 0, hi = E;   // largest e with s_pref[e] * tiles_n <= id
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<int64_t>(s_pref[mid]) * tiles_n <= id) lo = mid;
+    else hi = mid;
+  }
+  const int mt = s_pref[lo + 1] - s_pref[lo];
+  const int64_t local = id - static_cast<int64_t>(s_pref[lo]) * tiles_n;
+  Tile t;
+  t.e = lo;
+  t.nt = static_cast<int>(local / mt);
+  t.mi = static_cast<int>(local % mt);
+  return t;
+}
+
+// gelu_tanh(z) = z/2 (1 + tanh(u)) = z * sigmoid(2u), u = sqrt(2/pi)(z + 0.044715 z^3)
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float u = 0.7978845608028654f * fmaf(0.044715f * z, z * z, z);
+  return z / (1.0f + __expf(-2.0f * u));
+}
+
+// The same function with hardware exp2 and reciprocal (about 1e-6 relative
+// error), for results that are rounded to 16-bit floats anyway.
+__device__ __forceinline__ float gelu_tanh_fast(float z) {
+  const float u = 0.7978845608028654f * fmaf(0.044715f * z, z * z, z);
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+}
+
+// Two bf16 values (one 32-bit word) -> two IEEE fp16 values, round to nearest
+// even. Exact for every bf16 value inside the fp16 normal range.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  const f16x2 h = {static_cast<_Float16>(__uint_as_float(v << 16)),
+                   static_cast<_Float16>(__uint_as_float(v & 0xffff0000u))};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  return uint4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+               bf16x2_to_f16x2(v.w)};
+}
+
+}  // namespace ffn
+}  // namespace moe

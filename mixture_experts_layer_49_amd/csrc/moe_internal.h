@@ -47,6 +47,10 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
                        int64_t d, int64_t d_ff, const void* w2, int dtype, float* y_perm,
                        hipStream_t s);
 
+// bf16 layers: the segmented MFMA GEMM (up: GELU -> fp16 h; down: f32 out).
+hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets, int E, int64_t rows_max,
+                           int N, int K, const void* B, void* C, hipStream_t s);
+
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                           int64_t T, int k, int64_t d, void* y, int out_dtype, hipStream_t s);
 
