@@ -37,8 +37,10 @@ def log(*a):
 def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # The clocks ramp up over the first few launches after idle; 20 steps
+    # (about 60 ms of work) reach the sustained state.
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large-experts-e8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -143,9 +145,9 @@ def main(argv=None) -> int:
         ops.moe_dispatch(idx, cfg.E, C, x, b.counts, b.offsets, b.dest, b.src, b.x_perm,
                          b.ws_dispatch)
         rec(2)
-        ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h)
+        ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
         rec(3)
-        ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm)
+        ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
         rec(4)
         ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
         rec(5)

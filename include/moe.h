@@ -132,11 +132,18 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
  * bits; the down-projection then runs fp16 x fp16 with W2's bf16 values
  * converted exactly to fp16. This needs |h| and |W2| below 65504.
  * Products accumulate in float32. Rows >= offsets[E] are not touched.
- * Limits: d, d_ff <= 2^22. */
+ * Limits: d, d_ff <= 2^22.
+ * workspace / workspace_bytes: device scratch of at least
+ *   moe_ffn_workspace_bytes(dtype) bytes (16-byte aligned), or NULL. With it,
+ *   output tiles of a short last round of work are split along K over idle
+ *   compute units and their float32 partial sums added up in a fixed order
+ *   (results stay deterministic); with NULL, no tile is split. Calls that
+ *   share one workspace must not overlap in time (same stream, or ordered).
+ * Errors: MOE_ERR_WORKSPACE when a non-NULL workspace is smaller than needed. */
 int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E,
                     int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
                     const void* w2, int32_t dtype, void* h, float* y_perm,
-                    hipStream_t stream);
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The two halves of moe_grouped_ffn, callable on their own (same arguments,
  * same layouts, `dtype` is the layer's dtype in both): the up-projection with
@@ -144,10 +151,17 @@ int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E,
  * down on the same stream. */
 int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E,
                        int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
-                       int32_t dtype, void* h, hipStream_t stream);
+                       int32_t dtype, void* h, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
                     int64_t rows_max, int64_t d, int64_t d_ff, const void* w2,
-                    int32_t dtype, float* y_perm, hipStream_t stream);
+                    int32_t dtype, float* y_perm, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Bytes of expert-FFN workspace for the current device: one 256 x 256 float32
+ * partial tile and one counter per compute unit (64 MiB + 1 KiB on a
+ * 256-CU MI355X) for MOE_BF16; 0 for MOE_F32 (whose kernels never split). */
+size_t moe_ffn_workspace_bytes(int32_t dtype);
 
 /* Weighted combine back to token order (EP tutorial 2.1 step 5; 2.2: a
  * dropped slot takes no part):

@@ -91,6 +91,14 @@ int check_ffn(const void* a, const int32_t* offsets, int32_t E, int64_t rows_max
   return MOE_OK;
 }
 
+int check_ffn_ws(int32_t dtype, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr || dtype != MOE_BF16) return MOE_OK;
+  const size_t need = moe::ffn_workspace_bytes(dtype);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "expert-FFN workspace needs %zu bytes, got %zu", need, ws_bytes);
+  return check_ptr16("workspace", ws);
+}
+
 }  // namespace
 
 namespace moe {
@@ -191,29 +199,41 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
 
 int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E, int64_t rows_max,
                        int64_t d, int64_t d_ff, const void* w1, int32_t dtype, void* h,
-                       hipStream_t stream) {
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_ffn(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h));
-  return hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h, stream),
+  MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
+  return hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h,
+                                        workspace, stream),
                     "moe_expert_up_gelu launch");
 }
 
 int moe_expert_down(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,
-                    int64_t d_ff, const void* w2, int32_t dtype, float* y_perm,
-                    hipStream_t stream) {
+                    int64_t d_ff, const void* w2, int32_t dtype, float* y_perm, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_ffn(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm));
-  return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm, stream),
+  MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
+  return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm,
+                                     workspace, stream),
                     "moe_expert_down launch");
 }
 
 int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E, int64_t rows_max,
                     int64_t d, int64_t d_ff, const void* w1, const void* w2, int32_t dtype,
-                    void* h, float* y_perm, hipStream_t stream) {
+                    void* h, float* y_perm, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
   MOE_TRY(check_ffn(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h));
   MOE_TRY(check_ffn(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm));
-  MOE_TRY(hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h, stream),
+  MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
+  MOE_TRY(hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h,
+                                         workspace, stream),
                      "moe_grouped_ffn up-projection launch"));
-  return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm, stream),
+  return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm,
+                                     workspace, stream),
                     "moe_grouped_ffn down-projection launch");
+}
+
+size_t moe_ffn_workspace_bytes(int32_t dtype) {
+  return dtype == MOE_BF16 ? moe::ffn_workspace_bytes(dtype) : 0;
 }
 
 int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w, int64_t T,

@@ -87,9 +87,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
 
 template <bool UP>
 hipError_t launch_gemm(const void* A, const int32_t* offsets, int E, int64_t rows_max, int N,
-                       int K, const void* B, int dtype, void* C, hipStream_t s) {
+                       int K, const void* B, int dtype, void* C, void* ws, hipStream_t s) {
   if (rows_max == 0) return hipSuccess;
-  if (dtype == 1) return launch_ffn_mfma(UP, A, offsets, E, rows_max, N, K, B, C, s);
+  if (dtype == 1) return launch_ffn_mfma(UP, A, offsets, E, rows_max, N, K, B, C, ws, s);
   const int64_t tiles_n = (N + FN - 1) / FN;
   int64_t g = (rows_max / FM + E) * tiles_n;
   if (g > 65535) g = 65535;
@@ -102,16 +102,19 @@ hipError_t launch_gemm(const void* A, const int32_t* offsets, int E, int64_t row
 }  // namespace
 
 hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,
-                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h,
+                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* ws,
                           hipStream_t s) {
   return launch_gemm<true>(x_perm, offsets, E, rows_max, static_cast<int>(d_ff),
-                           static_cast<int>(d), w1, dtype, h, s);
+                           static_cast<int>(d), w1, dtype, h, ws, s);
 }
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
-                       int64_t d_ff, const void* w2, int dtype, float* y_perm, hipStream_t s) {
+                       int64_t d_ff, const void* w2, int dtype, float* y_perm, void* ws,
+                       hipStream_t s) {
   return launch_gemm<false>(h, offsets, E, rows_max, static_cast<int>(d), static_cast<int>(d_ff),
-                            w2, dtype, y_perm, s);
+                            w2, dtype, y_perm, ws, s);
 }
+
+size_t ffn_workspace_bytes(int dtype) { return dtype == 1 ? ffn_mfma_workspace_bytes() : 0; }
 
 }  // namespace moe

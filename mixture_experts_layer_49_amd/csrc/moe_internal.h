@@ -39,17 +39,23 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E, int
                            int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                            void* x_perm, int32_t* ws, hipStream_t s);
 
+// ws: the expert-FFN workspace (ffn_workspace_bytes(dtype) bytes) or null.
 hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,
-                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h,
+                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* ws,
                           hipStream_t s);
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max,
                        int64_t d, int64_t d_ff, const void* w2, int dtype, float* y_perm,
-                       hipStream_t s);
+                       void* ws, hipStream_t s);
 
 // bf16 layers: the segmented MFMA GEMM (up: GELU -> fp16 h; down: f32 out).
+// With a workspace, output tiles of a short last round are split along K.
 hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets, int E, int64_t rows_max,
-                           int N, int K, const void* B, void* C, hipStream_t s);
+                           int N, int K, const void* B, void* C, void* ws, hipStream_t s);
+
+// Workspace bytes of the expert FFN on the current device (0 for f32 layers).
+size_t ffn_workspace_bytes(int dtype);
+size_t ffn_mfma_workspace_bytes();
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                           int64_t T, int k, int64_t d, void* y, int out_dtype, hipStream_t s);

@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
-           "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_last_error"]
+           "moe_ffn_workspace_bytes", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -54,9 +54,10 @@ def lib() -> ctypes.CDLL:
         "moe_router_topk": (ctypes.c_int, [P, P, P, I64, I64, I32, I32, I32, U32, P, P, P, P]),
         "moe_dispatch_workspace_bytes": (SZ, [I64, I32, I32]),
         "moe_dispatch": (ctypes.c_int, [P, I64, I32, I32, I64, P, I64, I32, P, P, P, P, P, P, SZ, P]),
-        "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P]),
-        "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P]),
-        "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P]),
+        "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P, SZ, P]),
+        "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
+        "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
+        "moe_ffn_workspace_bytes": (SZ, [I32]),
         "moe_combine": (ctypes.c_int, [P, P, P, I64, I32, I64, P, I32, P]),
         "moe_aux_loss_workspace_bytes": (SZ, [I64, I32]),
         "moe_aux_loss": (ctypes.c_int, [P, P, I64, I32, I32, F32, P, P, SZ, P]),
@@ -147,29 +148,42 @@ def moe_dispatch(topk_idx, E: int, capacity: int, x, counts=None, offsets=None, 
     return counts, offsets, dest, src, x_perm
 
 
-def moe_expert_up_gelu(x_perm, offsets, w1, rows_max: int, h=None, stream=None):
+def moe_ffn_workspace_bytes(dtype) -> int:
+    return int(lib().moe_ffn_workspace_bytes(dtype_code(dtype)))
+
+
+def _ws_size(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def moe_expert_up_gelu(x_perm, offsets, w1, rows_max: int, h=None, workspace=None, stream=None):
+    """workspace: a device buffer of moe_ffn_workspace_bytes(dtype) bytes, or
+    None (then no output tile is split along K)."""
     E, d_ff, d = w1.shape
     h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x_perm) if h is None else h
     _check(lib().moe_expert_up_gelu(_ptr(x_perm), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
-                                    dtype_code(w1.dtype), _ptr(h), _stream(stream)))
+                                    dtype_code(w1.dtype), _ptr(h), _ptr(workspace),
+                                    _ws_size(workspace), _stream(stream)))
     return h
 
 
-def moe_expert_down(h, offsets, w2, rows_max: int, y_perm=None, stream=None):
+def moe_expert_down(h, offsets, w2, rows_max: int, y_perm=None, workspace=None, stream=None):
     E, d, d_ff = w2.shape
     y_perm = _empty((max(rows_max, 1), d), torch.float32, h) if y_perm is None else y_perm
     _check(lib().moe_expert_down(_ptr(h), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w2),
-                                 dtype_code(w2.dtype), _ptr(y_perm), _stream(stream)))
+                                 dtype_code(w2.dtype), _ptr(y_perm), _ptr(workspace),
+                                 _ws_size(workspace), _stream(stream)))
     return y_perm
 
 
-def moe_grouped_ffn(x_perm, offsets, w1, w2, rows_max: int, h=None, y_perm=None, stream=None):
+def moe_grouped_ffn(x_perm, offsets, w1, w2, rows_max: int, h=None, y_perm=None, workspace=None,
+                    stream=None):
     E, d_ff, d = w1.shape
     h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x_perm) if h is None else h
     y_perm = _empty((max(rows_max, 1), d), torch.float32, x_perm) if y_perm is None else y_perm
     _check(lib().moe_grouped_ffn(_ptr(x_perm), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
                                  _ptr(w2), dtype_code(x_perm.dtype), _ptr(h), _ptr(y_perm),
-                                 _stream(stream)))
+                                 _ptr(workspace), _ws_size(workspace), _stream(stream)))
     return h, y_perm
 
 
@@ -220,6 +234,8 @@ class MoEBuffers:
         self.loss = z((1,), torch.float32)
         self.ws_dispatch = z((max(moe_dispatch_workspace_bytes(T, k, E), 4),), torch.uint8)
         self.ws_aux = z((max(moe_aux_loss_workspace_bytes(T, E), 8),), torch.uint8)
+        nb = moe_ffn_workspace_bytes(dtype)
+        self.ws_ffn = z((nb,), torch.uint8) if nb > 0 else None
 
 
 def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_idx=None,
@@ -241,7 +257,8 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
         idx, w = topk_idx, topk_w
     moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                  bufs.x_perm, bufs.ws_dispatch, stream)
-    moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm, stream)
+    moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
+                    bufs.ws_ffn, stream)
     moe_combine(bufs.y_perm, bufs.dest, w, d, torch.float32, bufs.y, stream)
     if routed and bufs.probs is not None:
         moe_aux_loss(bufs.probs, bufs.counts, k, alpha, bufs.loss, bufs.ws_aux, stream)

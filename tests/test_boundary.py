@@ -107,14 +107,21 @@ def test_dispatch_argument_errors():
 
 def test_ffn_combine_aux_argument_errors():
     L = ops.lib()
-    assert L.moe_grouped_ffn(FAKE, FAKE, 0, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None) == -3
-    assert L.moe_grouped_ffn(FAKE, FAKE, 8, 10, 60, 128, FAKE, FAKE, 1, FAKE, FAKE, None) == -6
-    assert L.moe_grouped_ffn(FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, 3, FAKE, FAKE, None) == -2
-    assert L.moe_grouped_ffn(None, FAKE, 8, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None) == -1
-    assert L.moe_grouped_ffn(FAKE, FAKE, 8, -1, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None) == -1
-    assert L.moe_grouped_ffn(None, None, 8, 0, 64, 128, None, None, 1, None, None, None) == 0
-    assert L.moe_expert_up_gelu(FAKE, FAKE, 8, 10, 64, 130, FAKE, 1, FAKE, None) == -6
-    assert L.moe_expert_down(FAKE, None, 8, 10, 64, 128, FAKE, 1, FAKE, None) == -1
+    assert L.moe_grouped_ffn(FAKE, FAKE, 0, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None, 0, None) == -3
+    assert L.moe_grouped_ffn(FAKE, FAKE, 8, 10, 60, 128, FAKE, FAKE, 1, FAKE, FAKE, None, 0, None) == -6
+    assert L.moe_grouped_ffn(FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, 3, FAKE, FAKE, None, 0, None) == -2
+    assert L.moe_grouped_ffn(None, FAKE, 8, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None, 0, None) == -1
+    assert L.moe_grouped_ffn(FAKE, FAKE, 8, -1, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None, 0, None) == -1
+    assert L.moe_grouped_ffn(None, None, 8, 0, 64, 128, None, None, 1, None, None, None, 0, None) == 0
+    assert L.moe_expert_up_gelu(FAKE, FAKE, 8, 10, 64, 130, FAKE, 1, FAKE, None, 0, None) == -6
+    assert L.moe_expert_down(FAKE, None, 8, 10, 64, 128, FAKE, 1, FAKE, None, 0, None) == -1
+    # the FFN workspace is optional, but a given one must be large enough and 16-B aligned
+    need = L.moe_ffn_workspace_bytes(1)
+    assert L.moe_expert_down(FAKE, FAKE, 8, 10, 64, 128, FAKE, 1, FAKE, FAKE, need - 1, None) == -4
+    assert L.moe_expert_up_gelu(FAKE, FAKE, 8, 10, 64, 128, FAKE, 1, FAKE, FAKE, need - 1, None) == -4
+    assert L.moe_grouped_ffn(FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None) == -4
+    assert L.moe_expert_down(FAKE, FAKE, 8, 10, 64, 128, FAKE, 1, FAKE,
+                             ctypes.c_void_p((1 << 20) + 8), need, None) == -6
     assert L.moe_combine(FAKE, FAKE, FAKE, 10, 9, 64, FAKE, 0, None) == -1
     assert L.moe_combine(FAKE, FAKE, FAKE, 10, 2, 62, FAKE, 0, None) == -6
     assert L.moe_combine(FAKE, None, FAKE, 10, 2, 64, FAKE, 0, None) == -1
@@ -122,6 +129,14 @@ def test_ffn_combine_aux_argument_errors():
     assert L.moe_aux_loss(FAKE, FAKE, 10, 8, 2, 0.01, FAKE, None, 0, None) == -4
     assert L.moe_aux_loss(FAKE, FAKE, 10, 8, 2, 0.01, None, FAKE, 1 << 20, None) == -1
     assert L.moe_aux_loss(FAKE, FAKE, 10, 8, 9, 0.01, FAKE, FAKE, 1 << 20, None) == -3
+
+
+def test_ffn_workspace_bytes():
+    L = ops.lib()
+    assert L.moe_ffn_workspace_bytes(0) == 0           # f32 kernels never split a tile
+    n = L.moe_ffn_workspace_bytes(1)
+    # one 256 x 256 f32 partial tile and one int counter per workgroup slot
+    assert n > 0 and n % (256 * 256 * 4 + 4) == 0, n
 
 
 def test_binding_raises_typed_errors():

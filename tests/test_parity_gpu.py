@@ -33,6 +33,9 @@ SMALL = [
     I.small("receiver", T=700, d=128, d_ff=256, E=8, k=1, cf=1.25, routed=False, seed=14),
     I.small("single-token", T=1, d=64, d_ff=64, E=4, k=2, cf=1.25, seed=15),
     I.small("multi-tile", T=1200, d=512, d_ff=576, E=3, k=2, cf=1.25, seed=16),
+    # few tiles, long K: output tiles split along K (2-way with a K tail, and 8-way)
+    I.small("split-k2-ragged", T=300, d=1024, d_ff=1032, E=2, k=2, cf=1.25, seed=17),
+    I.small("split-k8", T=200, d=4096, d_ff=256, E=1, k=1, cf=1.25, seed=18),
 ]
 FULL = list(I.CONFIGS)              # the five workloads at their real sizes
 FULL_ORACLE_FFN = {"tiny-fp32", "e16-zipf-bias"}   # oracle FFN on every token
@@ -287,10 +290,49 @@ def test_ffn_halves_equal_whole():
     C = g["C"]
     _, off, _, _, xp = ops.moe_dispatch(idx, cfg.E, C, x)
     rows = ops.moe_rows_max(cfg.T, cfg.k, cfg.E, C)
-    h1, y1 = ops.moe_grouped_ffn(xp, off, t["w1"], t["w2"], rows)
-    h2 = ops.moe_expert_up_gelu(xp, off, t["w1"], rows)
-    y2 = ops.moe_expert_down(h2, off, t["w2"], rows)
+    ws = torch.empty(ops.moe_ffn_workspace_bytes(torch.bfloat16), dtype=torch.uint8, device="cuda:0")
+    h1, y1 = ops.moe_grouped_ffn(xp, off, t["w1"], t["w2"], rows, workspace=ws)
+    h2 = ops.moe_expert_up_gelu(xp, off, t["w1"], rows, workspace=ws)
+    y2 = ops.moe_expert_down(h2, off, t["w2"], rows, workspace=ws)
     torch.cuda.synchronize()
     R = g["R"]
     assert torch.equal(h1[:R], h2[:R]) and torch.equal(y1[:R], y2[:R])
     assert np.array_equal(host(y1)[:R], g["y_perm"])
+
+
+@pytest.mark.parametrize("name", ["split-k2-ragged", "split-k8"])
+def test_split_tiles_match_unsplit(name):
+    """Tiles split along K (workspace given) against the same GEMMs unsplit
+    (no workspace): equal up to float32 summation order, and the split result
+    is the same on every call."""
+    cfg = next(c for c in SMALL if c.name == name)
+    inp = I.make_inputs(cfg)
+    g, t = gpu_forward(inp, cfg)
+    idx = dev(g["topk_idx"].astype(np.int32), "f32")
+    _, off, _, _, xp = ops.moe_dispatch(idx, cfg.E, g["C"], t["x"])
+    rows = g["rows_max"]
+    ws = torch.empty(ops.moe_ffn_workspace_bytes(torch.bfloat16), dtype=torch.uint8, device="cuda:0")
+    ws.fill_(0xA5)   # the counters must not depend on the workspace's old contents
+    hs, ys = ops.moe_grouped_ffn(xp, off, t["w1"], t["w2"], rows, workspace=ws)
+    hs2, ys2 = ops.moe_grouped_ffn(xp, off, t["w1"], t["w2"], rows, workspace=ws)
+    hu, yu = ops.moe_grouped_ffn(xp, off, t["w1"], t["w2"], rows)
+    torch.cuda.synchronize()
+    R = g["R"]
+    assert torch.equal(hs[:R], hs2[:R]) and torch.equal(ys[:R], ys2[:R])
+    # h is stored in fp16. A different float32 summation order changes the
+    # pre-activation by a few float32 ulps of the summed terms (not of the
+    # result, which may be small after cancellation); after rounding to fp16
+    # that is at most one fp16 ulp (2^-10 relative) or a tiny absolute
+    # amount, and only for few values.
+    a, b = host(hs)[:R], host(hu)[:R]
+    rms = float(np.sqrt(np.mean(b ** 2)))
+    bound = np.maximum(np.abs(a), np.abs(b)) * 2.0 ** -10 + 1e-5 * rms
+    moved = np.abs(a - b) > 0
+    say("  h split vs unsplit: %d of %d values differ, worst %.2f of the bound" % (
+        int(moved.sum()), a.size, float(np.max(np.abs(a - b) / bound))))
+    assert (np.abs(a - b) <= bound).all() and moved.mean() < 1e-2
+    a, b = host(ys)[:R], host(yu)[:R]
+    err = float(np.max(np.abs(a - b))) / float(np.sqrt(np.mean(b ** 2)))
+    say("  y_perm split vs unsplit: max|diff|/rms = %.2e" % err)
+    assert err <= 1e-3, err
+    assert np.array_equal(host(ys)[:R], g["y_perm"])
