@@ -128,7 +128,7 @@ def main(argv=None) -> int:
     b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed)
     stream = torch.cuda.current_stream()
 
-    names = ["router", "dispatch", "up_gelu", "down", "combine", "aux"]
+    names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]
     # one set of boundary events per timed step, all on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
@@ -142,18 +142,19 @@ def main(argv=None) -> int:
         else:
             idx, w = given_idx, given_w
         rec(1)
-        ops.moe_dispatch(idx, cfg.E, C, x, b.counts, b.offsets, b.dest, b.src, b.x_perm,
-                         b.ws_dispatch)
+        ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
         rec(2)
-        ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
+        ops.moe_permute(x, b.src, b.offsets, b.rows_max, b.x_perm)
         rec(3)
-        ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
+        ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
         rec(4)
-        ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
+        ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
         rec(5)
+        ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
+        rec(6)
         if cfg.routed:
             ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
-        rec(6)
+        rec(7)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
@@ -183,16 +184,19 @@ def main(argv=None) -> int:
     flops_up = 2.0 * R * d * dff
     flops_down = 2.0 * R * dff * d
     bytes_router = T * d * s + E * d * s + T * k * 8 + T * E * 4 if cfg.routed else 0
-    bytes_dispatch = T * k * 4 * 2 + 2 * R * d * s + R * 4
+    bytes_plan = T * k * 4 * 2 + R * 4 + 2 * E * 4
+    bytes_permute = 2 * R * d * s + R * 4
     bytes_combine = R * d * 4 + T * d * 4 + T * k * 8
     bytes_aux = T * E * 4 if cfg.routed else 0
     us = dict(zip(names, (per * 1e3).tolist()))
     breakdown = {
         "router": {"us": us["router"], "GB/s": bytes_router / (per[0] * 1e-3) / 1e9 if per[0] else None},
-        "dispatch": {"us": us["dispatch"], "GB/s": bytes_dispatch / (per[1] * 1e-3) / 1e9},
-        "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (per[2] * 1e-3) / 1e12},
-        "down": {"us": us["down"], "TFLOP/s": flops_down / (per[3] * 1e-3) / 1e12},
-        "combine": {"us": us["combine"], "GB/s": bytes_combine / (per[4] * 1e-3) / 1e9},
+        # the plan is integer work of a few hundred KB: latency, reported in us only
+        "dispatch_plan": {"us": us["dispatch_plan"], "bytes": bytes_plan},
+        "permute": {"us": us["permute"], "GB/s": bytes_permute / (per[2] * 1e-3) / 1e9},
+        "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (per[3] * 1e-3) / 1e12},
+        "down": {"us": us["down"], "TFLOP/s": flops_down / (per[4] * 1e-3) / 1e12},
+        "combine": {"us": us["combine"], "GB/s": bytes_combine / (per[5] * 1e-3) / 1e9},
         "aux": {"us": us["aux"]},
     }
     for key, v in breakdown.items():
@@ -200,9 +204,9 @@ def main(argv=None) -> int:
             v["hbm_frac"] = v["GB/s"] / PEAK_HBM_GBS
         if "TFLOP/s" in v:
             v["mfma_frac"] = v["TFLOP/s"] / PEAK_MFMA_TFLOPS
-    dom = "up_gelu" if per[2] >= per[3] else "down"
+    dom = "up_gelu" if per[3] >= per[4] else "down"
     achieved = breakdown[dom]["TFLOP/s"]
-    ffn_tflops = (flops_up + flops_down) / ((per[2] + per[3]) * 1e-3) / 1e12
+    ffn_tflops = (flops_up + flops_down) / ((per[3] + per[4]) * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,

@@ -116,6 +116,21 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
                  void* x_perm, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/* The two halves of moe_dispatch, callable on their own (same arguments and
+ * layouts as above; moe_dispatch == plan then permute on the same stream).
+ * moe_dispatch_plan: the integer plan only -- counts, offsets, dest, src
+ *   (EP tutorial 2.1 step 2, 2.2); bit-exact and deterministic.
+ * moe_permute: x_perm[r] = x[src[r]] for r < offsets[E] (EP tutorial 5.3);
+ *   offsets and src as written by moe_dispatch_plan, rows_max the row count of
+ *   the x_perm buffer (moe_rows_max); rows past offsets[E] are not touched. */
+int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                      int64_t capacity, int32_t* counts, int32_t* offsets,
+                      int32_t* dest, int32_t* src, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+int moe_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
+                const int32_t* offsets, int32_t E, int64_t rows_max, void* x_perm,
+                hipStream_t stream);
+
 /* Grouped expert FFN over the expert-major segments given by `offsets`
  * (ETP page: up-projection w1 then down-projection w2, e.g.
  * 4096 -> 16384 -> 4096; EP tutorial 2.1 step 4: each expert computes on its

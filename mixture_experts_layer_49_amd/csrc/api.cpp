@@ -164,25 +164,20 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   return moe::dispatch_ws_ints(T, E) * sizeof(int32_t);
 }
 
-int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,
-                 const void* x, int64_t d, int32_t dtype, int32_t* counts, int32_t* offsets,
-                 int32_t* dest, int32_t* src, void* x_perm, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
-  MOE_TRY(check_dtype(dtype));
+namespace {
+
+int check_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t* counts,
+               int32_t* offsets, int32_t* dest, int32_t* src, const void* workspace,
+               size_t workspace_bytes) {
   MOE_TRY(check_experts(E, k));
-  if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
+  if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
   if (T * k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T * k must stay below 2^31");
-  MOE_TRY(check_row("d", d, dtype));
   MOE_NONNULL(counts);
   MOE_NONNULL(offsets);
   if (T > 0) {
     MOE_NONNULL(topk_idx);
-    MOE_NONNULL(x);
     MOE_NONNULL(dest);
     MOE_NONNULL(src);
-    MOE_NONNULL(x_perm);
-    MOE_TRY(check_ptr16("x", x));
-    MOE_TRY(check_ptr16("x_perm", x_perm));
     const size_t need = moe_dispatch_workspace_bytes(T, k, E);
     if (workspace == nullptr || workspace_bytes < need)
       return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
@@ -190,10 +185,61 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
     if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
       return fail(MOE_ERR_ALIGN, "workspace is not 4-byte aligned");
   }
+  return MOE_OK;
+}
+
+int check_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
+                  const int32_t* offsets, int32_t E, int64_t rows_max, const void* x_perm) {
+  MOE_TRY(check_dtype(dtype));
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, MOE_MAX_E);
+  if (d <= 0 || rows_max < 0) return fail(MOE_ERR_ARG, "need d > 0 and rows_max >= 0");
+  MOE_TRY(check_row("d", d, dtype));
+  if (rows_max == 0) return MOE_OK;
+  MOE_NONNULL(x);
+  MOE_NONNULL(src);
+  MOE_NONNULL(offsets);
+  MOE_NONNULL(x_perm);
+  MOE_TRY(check_ptr16("x", x));
+  MOE_TRY(check_ptr16("x_perm", x_perm));
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,
+                      int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_plan(topk_idx, T, k, E, counts, offsets, dest, src, workspace, workspace_bytes));
+  return hip_status(moe::launch_dispatch_plan(topk_idx, T, k, E, capacity, counts, offsets, dest,
+                                              src, static_cast<int32_t*>(workspace), stream),
+                    "moe_dispatch_plan launch");
+}
+
+int moe_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
+                const int32_t* offsets, int32_t E, int64_t rows_max, void* x_perm,
+                hipStream_t stream) {
+  MOE_TRY(check_permute(x, d, dtype, src, offsets, E, rows_max, x_perm));
+  return hip_status(moe::launch_permute(x, d, elem_bytes(dtype), src, offsets, E, rows_max,
+                                        x_perm, stream),
+                    "moe_permute launch");
+}
+
+int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,
+                 const void* x, int64_t d, int32_t dtype, int32_t* counts, int32_t* offsets,
+                 int32_t* dest, int32_t* src, void* x_perm, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  MOE_TRY(check_plan(topk_idx, T, k, E, counts, offsets, dest, src, workspace, workspace_bytes));
+  if (d <= 0) return fail(MOE_ERR_ARG, "need d > 0");
+  MOE_TRY(check_row("d", d, dtype));
   const int64_t rows_max = moe_rows_max(T, k, E, capacity);
-  return hip_status(moe::launch_dispatch(topk_idx, T, k, E, capacity, x, d, elem_bytes(dtype),
-                                         rows_max, counts, offsets, dest, src, x_perm,
-                                         static_cast<int32_t*>(workspace), stream),
+  if (T > 0) MOE_TRY(check_permute(x, d, dtype, src, offsets, E, rows_max, x_perm));
+  MOE_TRY(hip_status(moe::launch_dispatch_plan(topk_idx, T, k, E, capacity, counts, offsets, dest,
+                                               src, static_cast<int32_t*>(workspace), stream),
+                     "moe_dispatch launch"));
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_permute(x, d, elem_bytes(dtype), src, offsets, E, rows_max,
+                                        x_perm, stream),
                     "moe_dispatch launch");
 }
 

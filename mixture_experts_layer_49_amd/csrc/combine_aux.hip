@@ -14,40 +14,59 @@
 namespace moe {
 namespace {
 
-// One workgroup per token row (grid-stride), float4 lanes over d.
-template <bool BF16_OUT>
+// One workgroup per token row (grid-stride), float4 lanes over d. Each thread
+// takes U float4 columns per step and issues all their loads (U x KM rows)
+// before it sums, so several round trips to memory overlap. KM >= k bounds
+// the slots held in registers (2 for top-1/top-2, else kMaxK).
+template <bool BF16_OUT, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ topk_w, int64_t T,
                                                       int k, int64_t d, void* __restrict__ y) {
+  constexpr int U = KM <= 2 ? 4 : 1;
   const int64_t dv = d / 4;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    int32_t rows[kMaxK];
-    float w[kMaxK];
+    int32_t rows[KM];
+    float w[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       rows[j] = j < k ? dest[t * k + j] : -1;
       w[j] = j < k ? topk_w[t * k + j] : 0.f;
     }
-    for (int64_t v = threadIdx.x; v < dv; v += blockDim.x) {
-      float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t v0 = threadIdx.x; v0 < dv; v0 += U * static_cast<int64_t>(blockDim.x)) {
+      float4 o[U][KM];
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (rows[j] >= 0) {
-          const float4 o = reinterpret_cast<const float4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[v];
-          acc.x = fmaf(w[j], o.x, acc.x);
-          acc.y = fmaf(w[j], o.y, acc.y);
-          acc.z = fmaf(w[j], o.z, acc.z);
-          acc.w = fmaf(w[j], o.w, acc.w);
-        }
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + static_cast<int64_t>(u) * blockDim.x;
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          o[u][j] = (v < dv && rows[j] >= 0)
+                        ? reinterpret_cast<const float4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[v]
+                        : float4{0.f, 0.f, 0.f, 0.f};
       }
-      if (BF16_OUT) {
-        ushort4 b;
-        b.x = f32_to_bf16(acc.x); b.y = f32_to_bf16(acc.y);
-        b.z = f32_to_bf16(acc.z); b.w = f32_to_bf16(acc.w);
-        reinterpret_cast<ushort4*>(static_cast<uint16_t*>(y) + t * d)[v] = b;
-      } else {
-        reinterpret_cast<float4*>(static_cast<float*>(y) + t * d)[v] = acc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + static_cast<int64_t>(u) * blockDim.x;
+        if (v >= dv) break;
+        // Slot order; a dropped slot is skipped (not added as zero).
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (rows[j] >= 0) {
+            acc.x = fmaf(w[j], o[u][j].x, acc.x);
+            acc.y = fmaf(w[j], o[u][j].y, acc.y);
+            acc.z = fmaf(w[j], o[u][j].z, acc.z);
+            acc.w = fmaf(w[j], o[u][j].w, acc.w);
+          }
+        }
+        if (BF16_OUT) {
+          ushort4 bb;
+          bb.x = f32_to_bf16(acc.x); bb.y = f32_to_bf16(acc.y);
+          bb.z = f32_to_bf16(acc.z); bb.w = f32_to_bf16(acc.w);
+          reinterpret_cast<ushort4*>(static_cast<uint16_t*>(y) + t * d)[v] = bb;
+        } else {
+          reinterpret_cast<float4*>(static_cast<float*>(y) + t * d)[v] = acc;
+        }
       }
     }
   }
@@ -122,12 +141,14 @@ hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float*
                           int k, int64_t d, void* y, int out_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t grid = T < 65536 ? T : 65536;
-  if (out_dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                       y_perm, dest, topk_w, T, k, d, y);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                       y_perm, dest, topk_w, T, k, d, y);
+  const dim3 g(static_cast<unsigned>(grid)), b(256);
+  if (k <= 2) {
+    if (out_dtype == 1) hipLaunchKernelGGL((combine_kernel<true, 2>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
+    else hipLaunchKernelGGL((combine_kernel<false, 2>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
+  } else {
+    if (out_dtype == 1) hipLaunchKernelGGL((combine_kernel<true, kMaxK>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
+    else hipLaunchKernelGGL((combine_kernel<false, kMaxK>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
+  }
   return hipGetLastError();
 }
 

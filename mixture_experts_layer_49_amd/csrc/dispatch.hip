@@ -150,10 +150,9 @@ size_t dispatch_ws_ints(int64_t T, int E) {
   return static_cast<size_t>(2 * nchunks * E);
 }
 
-hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
-                           const void* x, int64_t d, int elem_bytes, int64_t rows_max,
-                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
-                           void* x_perm, int32_t* ws, hipStream_t s) {
+hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                                int32_t* ws, hipStream_t s) {
   if (T == 0) {
     // Nothing routed: zero counts and offsets so later calls see empty
     // segments (a fill kernel, not a memset node, so the call can be captured).
@@ -170,13 +169,18 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E, int
                      cap, counts, offsets);
   hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
                      chunk_base, offsets, dest, src);
-  if (rows_max > 0) {
-    const int64_t row_vecs = d * elem_bytes / 16;
-    const int64_t grid = rows_max < 16384 ? rows_max : 16384;
-    hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                       static_cast<const uint4*>(x), src, offsets, E, row_vecs,
-                       static_cast<uint4*>(x_perm));
-  }
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, int64_t d, int elem_bytes, const int32_t* src,
+                          const int32_t* offsets, int E, int64_t rows_max, void* x_perm,
+                          hipStream_t s) {
+  if (rows_max <= 0) return hipSuccess;
+  const int64_t row_vecs = d * elem_bytes / 16;
+  const int64_t grid = rows_max < 16384 ? rows_max : 16384;
+  hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), src, offsets, E, row_vecs,
+                     static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 

@@ -34,10 +34,13 @@ hipError_t launch_router(const void* x, const void* wg, const float* bias, int64
                          int64_t d, int E, int k, int dtype, uint32_t flags,
                          int32_t* topk_idx, float* topk_w, float* probs, hipStream_t s);
 
-hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
-                           const void* x, int64_t d, int elem_bytes, int64_t rows_max,
-                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
-                           void* x_perm, int32_t* ws, hipStream_t s);
+hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                                int32_t* ws, hipStream_t s);
+
+hipError_t launch_permute(const void* x, int64_t d, int elem_bytes, const int32_t* src,
+                          const int32_t* offsets, int E, int64_t rows_max, void* x_perm,
+                          hipStream_t s);
 
 // ws: the expert-FFN workspace (ffn_workspace_bytes(dtype) bytes) or null.
 hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,

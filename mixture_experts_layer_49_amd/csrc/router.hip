@@ -118,24 +118,33 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
 #pragma unroll
   for (int n = 0; n < NT; ++n) wrow[n] = wg + static_cast<int64_t>(min(n * 16 + r, E - 1)) * d;
 
-  for (int64_t c0 = static_cast<int64_t>(wave) * kChunk; c0 < d; c0 += 4 * kChunk) {
-    bf16x8 a[4];
+  // U slices per step, all their loads issued before the MFMAs that use
+  // them (one slice per step would leave each wave with one round trip to
+  // memory in flight); fewer for wide gates, whose W fragments need more
+  // registers.
+  constexpr int U = NT <= 2 ? 4 : (NT <= 4 ? 2 : 1);
+  for (int64_t c00 = static_cast<int64_t>(wave) * kChunk; c00 < d; c00 += 4 * U * kChunk) {
+    bf16x8 a[U][4], b[U][NT][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t col = c0 + g * 32 + s * 8;
-      if (col < d) a[s] = *reinterpret_cast<const bf16x8*>(xrow + col);
-      else a[s] = bf16x8{};
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    for (int u = 0; u < U; ++u) {
+      const int64_t c0 = c00 + static_cast<int64_t>(u) * 4 * kChunk;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int64_t col = c0 + g * 32 + s * 8;
-        bf16x8 b = bf16x8{};
-        if (col < d) b = *reinterpret_cast<const bf16x8*>(wrow[n] + col);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc[n], 0, 0, 0);
+        const bool in = col < d;
+        a[u][s] = in ? *reinterpret_cast<const bf16x8*>(xrow + col) : bf16x8{};
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          b[u][n][s] = in ? *reinterpret_cast<const bf16x8*>(wrow[n] + col) : bf16x8{};
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s], b[u][n][s], acc[n], 0, 0, 0);
   }
   // D layout of a 16x16 tile: lane holds rows 4*(lane/16)+i, column lane%16.
 #pragma unroll

@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_dispatch_workspace_bytes",
-           "moe_dispatch", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
+           "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_last_error"]
 
 
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         "moe_router_topk": (ctypes.c_int, [P, P, P, I64, I64, I32, I32, I32, U32, P, P, P, P]),
         "moe_dispatch_workspace_bytes": (SZ, [I64, I32, I32]),
         "moe_dispatch": (ctypes.c_int, [P, I64, I32, I32, I64, P, I64, I32, P, P, P, P, P, P, SZ, P]),
+        "moe_dispatch_plan": (ctypes.c_int, [P, I64, I32, I32, I64, P, P, P, P, P, SZ, P]),
+        "moe_permute": (ctypes.c_int, [P, I64, I32, P, P, I32, I64, P, P]),
         "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P, SZ, P]),
         "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
         "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
@@ -146,6 +148,31 @@ def moe_dispatch(topk_idx, E: int, capacity: int, x, counts=None, offsets=None, 
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
     return counts, offsets, dest, src, x_perm
+
+
+def moe_dispatch_plan(topk_idx, E: int, capacity: int, counts=None, offsets=None, dest=None,
+                      src=None, workspace=None, stream=None):
+    T, k = topk_idx.shape
+    rows = moe_rows_max(T, k, E, capacity)
+    counts = _empty((E,), torch.int32, topk_idx) if counts is None else counts
+    offsets = _empty((E + 1,), torch.int32, topk_idx) if offsets is None else offsets
+    dest = _empty((T, k), torch.int32, topk_idx) if dest is None else dest
+    src = _empty((max(rows, 1),), torch.int32, topk_idx) if src is None else src
+    if workspace is None:
+        workspace = _empty((max(moe_dispatch_workspace_bytes(T, k, E), 4),), torch.uint8, topk_idx)
+    _check(lib().moe_dispatch_plan(_ptr(topk_idx), T, k, E, capacity, _ptr(counts), _ptr(offsets),
+                                   _ptr(dest), _ptr(src), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return counts, offsets, dest, src
+
+
+def moe_permute(x, src, offsets, rows_max: int, x_perm=None, stream=None):
+    d = x.shape[1]
+    E = offsets.numel() - 1
+    x_perm = _empty((max(rows_max, 1), d), x.dtype, x) if x_perm is None else x_perm
+    _check(lib().moe_permute(_ptr(x), d, dtype_code(x.dtype), _ptr(src), _ptr(offsets), E, rows_max,
+                             _ptr(x_perm), _stream(stream)))
+    return x_perm
 
 
 def moe_ffn_workspace_bytes(dtype) -> int:

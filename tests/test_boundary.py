@@ -105,6 +105,33 @@ def test_dispatch_argument_errors():
     assert L.moe_dispatch(*a) == -1
 
 
+def test_plan_and_permute_argument_errors():
+    L = ops.lib()
+    need = L.moe_dispatch_workspace_bytes(100, 2, 8)
+    ok = [FAKE, 100, 2, 8, 30, FAKE, FAKE, FAKE, FAKE, FAKE, need, None]
+
+    def plan(i, v):
+        a = list(ok); a[i] = v
+        return L.moe_dispatch_plan(*a)
+    assert plan(3, 0) == -3                      # E = 0
+    assert plan(2, 9) == -3                      # k > E
+    assert plan(1, -1) == -1                     # T < 0
+    assert plan(5, None) == -1                   # counts
+    assert plan(0, None) == -1                   # topk_idx with T > 0
+    assert plan(10, need - 1) == -4              # workspace too small
+    assert plan(9, ctypes.c_void_p((1 << 20) + 2)) == -6
+    a = list(ok); a[1] = 0; a[0] = None; a[7] = None; a[8] = None; a[9] = None; a[10] = 0; a[5] = None
+    assert L.moe_dispatch_plan(*a) == -1         # T == 0 still needs counts and offsets
+    # moe_permute(x, d, dtype, src, offsets, E, rows_max, x_perm, stream)
+    assert L.moe_permute(FAKE, 64, 1, FAKE, FAKE, 8, 10, FAKE, None) != -1
+    assert L.moe_permute(FAKE, 60, 1, FAKE, FAKE, 8, 10, FAKE, None) == -6
+    assert L.moe_permute(FAKE, 64, 7, FAKE, FAKE, 8, 10, FAKE, None) == -2
+    assert L.moe_permute(None, 64, 1, FAKE, FAKE, 8, 10, FAKE, None) == -1
+    assert L.moe_permute(FAKE, 64, 1, FAKE, FAKE, 0, 10, FAKE, None) == -3
+    assert L.moe_permute(None, 64, 1, None, None, 8, 0, None, None) == 0
+    assert L.moe_permute(FAKE, 64, 1, FAKE, FAKE, 8, 10, ctypes.c_void_p((1 << 20) + 4), None) == -6
+
+
 def test_ffn_combine_aux_argument_errors():
     L = ops.lib()
     assert L.moe_grouped_ffn(FAKE, FAKE, 0, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, None, 0, None) == -3

@@ -168,6 +168,28 @@ def test_dispatch_bitexact_on_oracle_topk(cfg):
     check_dispatch(inp, cfg, idx)
 
 
+@pytest.mark.parametrize("cfg", [c for c in SMALL if c.name in ("ragged-bf16", "max-experts", "receiver", "small-f32")],
+                         ids=lambda c: c.name)
+def test_plan_then_permute_equals_dispatch(cfg):
+    """moe_dispatch_plan + moe_permute give exactly moe_dispatch's outputs."""
+    inp = I.make_inputs(cfg)
+    t = gpu_tensors(inp, cfg)
+    if cfg.routed:
+        idx, _, _ = ops.moe_router_topk(t["x"], t["w_gate"], t["bias"], cfg.k, 0)
+    else:
+        idx = t["topk_idx"]
+    C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    rows = ops.moe_rows_max(cfg.T, cfg.k, cfg.E, C)
+    ref = ops.moe_dispatch(idx, cfg.E, C, t["x"])
+    counts, offsets, dest, src = ops.moe_dispatch_plan(idx, cfg.E, C)
+    xp = ops.moe_permute(t["x"], src, offsets, rows)
+    torch.cuda.synchronize()
+    R = int(host(offsets)[-1])
+    for a, b in ((counts, ref[0]), (offsets, ref[1]), (dest, ref[2])):
+        assert torch.equal(a, b)
+    assert torch.equal(src[:R], ref[3][:R]) and torch.equal(xp[:R], ref[4][:R])
+
+
 def test_dispatch_ignores_invalid_and_repeated_ids():
     """Ids outside [0,E) and repeats inside a token are skipped. Expected plan:
     the oracle's, with every skipped slot sent to an extra expert E placed
