@@ -42,6 +42,10 @@ class MoEConfig:
     gate_bias  "none" | "zipf": per-expert logit bias log Zipf(s) (hot expert 0)
     routed     False for a receiver share: no gate, labels and weights are given
     recv_zipf_s  Zipf exponent of the per-expert received-row counts
+    etp, etp_rank  expert tensor parallelism: this GPU holds slice etp_rank of
+               etp equal slices of the hidden width -- rows of W1, columns of
+               W2 -- of a layer whose hidden width is d_ff * etp (the weights
+               are drawn for that layer, then sliced); its y is a partial sum
     """
 
     name: str
@@ -58,6 +62,8 @@ class MoEConfig:
     routed: bool = True
     recv_zipf_s: float = 1.2
     seed: int = 0
+    etp: int = 1
+    etp_rank: int = 0
 
 
 CONFIGS = [
@@ -72,10 +78,19 @@ CONFIGS = [
 ]
 
 
+# Workloads beyond the five above. The ETP share: one GPU's quarter of the
+# large-experts layer's 4096 -> 16384 -> 4096 experts at ETP 4, W1 split by
+# output columns and W2 by input columns (ETP expert-parallel page, ETP
+# section); same tokens, gate and routing as large-experts-e8.
+EXTRA_CONFIGS = [
+    MoEConfig("etp4-share-e8", 8192, 4096, 4096, 8, 2, 1.25, BF16, seed=3, etp=4, etp_rank=0),
+]
+
+
 def config(i_or_name) -> MoEConfig:
     if isinstance(i_or_name, int):
         return CONFIGS[i_or_name]
-    for c in CONFIGS:
+    for c in CONFIGS + EXTRA_CONFIGS:
         if c.name == i_or_name:
             return c
     raise KeyError(i_or_name)
@@ -135,7 +150,8 @@ def make_inputs(cfg: MoEConfig, seed: int | None = None) -> dict:
       topk_idx [T, 1] int32, topk_w [T, 1] f32   (receiver share only)
     """
     rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
-    T, d, dff, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
+    T, d, E = cfg.T, cfg.d, cfg.E
+    dff = cfg.d_ff * cfg.etp   # drawn for the whole layer; an ETP share is sliced below
     out = {"cfg": cfg}
     out["x"] = _normal(rng, (T, d), 1.0, cfg.dtype)
     if cfg.routed:
@@ -146,6 +162,10 @@ def make_inputs(cfg: MoEConfig, seed: int | None = None) -> dict:
         w1[e] = _normal(rng, (dff, d), 1.0 / math.sqrt(d), cfg.dtype)
     for e in range(E):
         w2[e] = _normal(rng, (d, dff), 1.0 / math.sqrt(dff), cfg.dtype)
+    if cfg.etp > 1:
+        lo, hi = cfg.etp_rank * cfg.d_ff, (cfg.etp_rank + 1) * cfg.d_ff
+        w1 = np.ascontiguousarray(w1[:, lo:hi, :])
+        w2 = np.ascontiguousarray(w2[:, :, lo:hi])
     out["w1"], out["w2"] = w1, w2
     if cfg.routed:
         out["bias"] = zipf_log_bias(E, cfg.zipf_s) if cfg.gate_bias == "zipf" else None

@@ -307,3 +307,32 @@ def test_generator_is_deterministic_and_shaped():
     np.testing.assert_array_equal(counts, I.zipf_counts(64, 8, 1.2))
     np.testing.assert_array_equal(I.zipf_counts(8192, 8, 1.2),
                                   [3511, 1528, 940, 665, 509, 409, 340, 290])
+
+
+def test_etp_shares_sum_to_the_whole_layer():
+    """ETP (ETP expert-parallel page, ETP section): W1 split by output columns
+    and W2 by input columns over the hidden width. Each share's output is a
+    partial sum; the shares add up to the whole layer (the FFN is separable
+    over hidden units because GELU acts elementwise)."""
+    import dataclasses
+    share = I.small("etp", T=60, d=16, d_ff=8, E=4, k=2, cf=1.25, dtype="f32", seed=21, etp=4)
+    whole = dataclasses.replace(share, d_ff=32, etp=1)
+    ref = O.forward(I.make_inputs(whole), "f32", k=2, cf=1.25)
+    tot = 0.0
+    for r in range(4):
+        inp = I.make_inputs(dataclasses.replace(share, etp_rank=r))
+        out = O.forward(inp, "f32", k=2, cf=1.25)
+        np.testing.assert_array_equal(out["dest"], ref["dest"])   # same routing
+        tot = tot + out["y"]
+    np.testing.assert_allclose(tot, ref["y"], rtol=1e-12, atol=1e-12)
+    # a share with one hidden unit per expert is a rank-1 update per expert
+    one = dataclasses.replace(share, d_ff=1, etp=32, etp_rank=5)
+    inp = I.make_inputs(one)
+    out = O.forward(inp, "f32", k=2, cf=1.25)
+    r = out["src"]
+    x = inp["x"].astype(np.float64)
+    for e in range(4):
+        rows = np.arange(out["offsets"][e], out["offsets"][e + 1])
+        z = x[r[rows]] @ inp["w1"][e, 0].astype(np.float64)
+        g = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+        np.testing.assert_allclose(out["y_perm"][rows], np.outer(g, inp["w2"][e, :, 0]), rtol=1e-12, atol=1e-14)

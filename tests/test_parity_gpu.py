@@ -263,6 +263,34 @@ def test_layer_full(cfg):
     check_layer(inp, cfg, sample)
 
 
+def test_layer_etp_share_full_size():
+    """One GPU's ETP-4 share of the large-experts layer (d_ff 16384 / 4),
+    against the oracle on sampled tokens."""
+    cfg = I.config("etp4-share-e8")
+    inp = cached_inputs(cfg)
+    rng = np.random.default_rng(1000 + cfg.seed)
+    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 40, replace=False)]))
+    check_layer(inp, cfg, sample)
+
+
+def test_etp_shares_sum_to_whole_layer():
+    """The four ETP shares' partial outputs add up to the whole layer's output
+    (same routing); bf16, with a K tail in the down-projection of the shares."""
+    import dataclasses
+    share = I.small("etp-sum", T=700, d=512, d_ff=264, E=4, k=2, cf=1.25, seed=23, etp=4)
+    whole = dataclasses.replace(share, d_ff=4 * 264, etp=1)
+    g_whole, _ = gpu_forward(I.make_inputs(whole), whole)
+    tot = None
+    for r in range(4):
+        g, _ = gpu_forward(I.make_inputs(dataclasses.replace(share, etp_rank=r)), share)
+        assert np.array_equal(g["dest"], g_whole["dest"])
+        tot = g["y"].astype(np.float64) if tot is None else tot + g["y"]
+    ref = g_whole["y"].astype(np.float64)
+    err = float(np.max(np.abs(tot - ref))) / float(np.sqrt(np.mean(ref ** 2)))
+    say("  sum of 4 shares vs whole: max|diff|/rms = %.2e" % err)
+    assert err <= 1e-4, err
+
+
 def test_layer_is_deterministic():
     for cfg in (I.small("det", T=900, d=256, d_ff=320, E=8, k=2, seed=41), FULL[1]):
         inp = cached_inputs(cfg) if cfg in FULL else I.make_inputs(cfg)
