@@ -37,6 +37,12 @@ Readings where the pages are silent (each also listed in the design notes):
     renormalised;
   * f_i counts router assignments before dropping, divided by T*k;
     P_i is the mean over all T tokens of the full softmax.
+  * routing knobs against hot experts: the SP/EP page (EP section) adjusts
+    the routing temperature and adds a random perturbation, the ETP page
+    names a routing z-loss; none gives a formula. Read as: scores
+    s = (l + noise) / temperature replace the logits in softmax and top-k
+    (the caller draws the noise), and the z-loss is the mean over tokens of
+    (log sum_e exp(s[t, e]))^2, the usual router z-loss.
 """
 from __future__ import annotations
 
@@ -158,12 +164,38 @@ def aux_loss(probs: np.ndarray, counts: np.ndarray, k: int, alpha: float) -> flo
     return float(alpha * E * np.sum(f * P))
 
 
-def route(x, w_gate, bias, dtype: str, k: int, renorm: bool = False):
-    """Gate -> softmax -> top-k on the given input bits."""
+def balance_scores(logits: np.ndarray, temperature: float = 1.0, noise=None) -> np.ndarray:
+    """Routing scores with the pages' balancing knobs (SP/EP page, EP section:
+    routing temperature and a random perturbation):
+    s = (l + noise) / temperature; temperature 1 and no noise give l."""
+    s = logits if noise is None else logits + np.asarray(noise, dtype=np.float64)
+    return s / float(temperature)
+
+
+def z_loss_terms(scores: np.ndarray) -> np.ndarray:
+    """Per-token term of the router z-loss (ETP page: routing z-loss spreads
+    the gate's attention): (log sum_e exp(s[t, e]))^2, max-subtracted."""
+    m = scores.max(axis=1)
+    lse = m + np.log(np.exp(scores - m[:, None]).sum(axis=1))
+    return lse ** 2
+
+
+def z_loss(scores: np.ndarray, coeff: float) -> float:
+    """Router z-loss = coeff * mean over tokens of z_loss_terms."""
+    if scores.shape[0] == 0:
+        return 0.0
+    return float(coeff * z_loss_terms(scores).mean())
+
+
+def route(x, w_gate, bias, dtype: str, k: int, renorm: bool = False, temperature: float = 1.0,
+          noise=None):
+    """Gate -> (balancing knobs) -> softmax -> top-k on the given input bits.
+    `logits` in the result are the scores that softmax and top-k see."""
     l = gate_logits(decode(x, dtype), decode(w_gate, dtype), bias)
-    p = softmax(l)
-    idx, w = topk(l, p, k, renorm)
-    return {"logits": l, "probs": p, "topk_idx": idx, "topk_w": w}
+    s = balance_scores(l, temperature, noise)
+    p = softmax(s)
+    idx, w = topk(s, p, k, renorm)
+    return {"logits": s, "probs": p, "topk_idx": idx, "topk_w": w, "zsq": z_loss_terms(s)}
 
 
 def forward(inp: dict, dtype: str, k: int, cf: float, alpha: float = 0.01,

@@ -336,3 +336,41 @@ def test_etp_shares_sum_to_the_whole_layer():
         z = x[r[rows]] @ inp["w1"][e, 0].astype(np.float64)
         g = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
         np.testing.assert_allclose(out["y_perm"][rows], np.outer(g, inp["w2"][e, :, 0]), rtol=1e-12, atol=1e-14)
+
+
+def test_routing_temperature_and_perturbation():
+    """Scores (l + noise) / temperature (SP/EP page, EP section knobs)."""
+    rng = np.random.default_rng(31)
+    l = rng.standard_normal((50, 6)) * 3
+    # E = 2: the probability of expert 0 is a logistic function of the gap
+    two = O.balance_scores(l[:, :2], temperature=2.5)
+    np.testing.assert_allclose(O.softmax(two)[:, 0],
+                               scipy.special.expit((l[:, 0] - l[:, 1]) / 2.5), rtol=1e-13)
+    # the ranking does not depend on a positive temperature
+    for tau in (0.3, 1.0, 7.0):
+        s = O.balance_scores(l, temperature=tau)
+        i1, _ = O.topk(s, O.softmax(s), 3)
+        i0, _ = O.topk(l, O.softmax(l), 3)
+        assert (i1 == i0).all()
+    # very high temperature -> uniform probabilities
+    s = O.balance_scores(l, temperature=1e9)
+    np.testing.assert_allclose(O.softmax(s), 1 / 6, rtol=1e-7)
+    # a perturbation decides the choice (hand case)
+    s = O.balance_scores(np.array([[1.0, 2.0, 3.0]]), noise=np.array([[5.0, 0.0, 0.0]]))
+    i, _ = O.topk(s, O.softmax(s), 1)
+    assert i[0, 0] == 0
+    np.testing.assert_allclose(O.softmax(s), scipy.special.softmax([[6.0, 2.0, 3.0]], axis=1), rtol=1e-14)
+
+
+def test_router_z_loss_closed_forms():
+    """z-loss = coeff * mean_t (log sum_e exp s[t,e])^2 (ETP page names it)."""
+    E = 8
+    s = np.full((4, E), 0.7)                       # equal scores: lse = c + log E
+    np.testing.assert_allclose(O.z_loss_terms(s), (0.7 + math.log(E)) ** 2, rtol=1e-14)
+    s = np.zeros((3, E)); s[:, 2] = 900.0          # one dominant score: lse = that score
+    np.testing.assert_allclose(O.z_loss_terms(s), 900.0 ** 2, rtol=1e-12)
+    rng = np.random.default_rng(33)
+    s = rng.standard_normal((40, 5)) * 10
+    np.testing.assert_allclose(O.z_loss_terms(s), scipy.special.logsumexp(s, axis=1) ** 2, rtol=1e-13)
+    assert O.z_loss(s, 1e-3) == pytest.approx(1e-3 * np.mean(scipy.special.logsumexp(s, axis=1) ** 2), rel=1e-13)
+    assert O.z_loss(np.zeros((0, 5)), 1.0) == 0.0
