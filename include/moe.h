@@ -87,6 +87,22 @@ int moe_router_topk(const void* x, const void* w_gate, const float* bias,
                     uint32_t flags, int32_t* topk_idx, float* topk_w, float* probs,
                     hipStream_t stream);
 
+/* The router with the pages' balancing knobs for hot experts (SP/EP page,
+ * EP section: adjust the routing temperature, add a random perturbation;
+ * ETP page: a routing z-loss spreads the gate's choices). Same as
+ * moe_router_topk, with softmax and top-k taken over the scores
+ *   s[t, e] = (l[t, e] + noise[t, e]) / temperature
+ *   noise       [T, E] f32 in, nullable (0): a perturbation the caller draws
+ *   temperature  finite, > 0 (1: the plain router)
+ *   zsq         [T] f32 out, nullable: (log sum_e exp s[t, e])^2, the
+ *               per-token term of the router z-loss (see moe_z_loss)
+ * moe_router_topk == moe_router_topk_ex(noise NULL, temperature 1, zsq NULL). */
+int moe_router_topk_ex(const void* x, const void* w_gate, const float* bias,
+                       const float* noise, int64_t T, int64_t d, int32_t E, int32_t k,
+                       int32_t dtype, uint32_t flags, float temperature,
+                       int32_t* topk_idx, float* topk_w, float* probs, float* zsq,
+                       hipStream_t stream);
+
 /* Bytes of device workspace moe_dispatch needs (0 when T == 0). */
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E);
 
@@ -202,6 +218,14 @@ int moe_aux_loss(const float* probs, const int32_t* counts, int64_t T, int32_t E
                  size_t workspace_bytes, hipStream_t stream);
 
 /* Text describing the last non-OK status returned on the calling thread. */
+/* Router z-loss (ETP page names it; no formula there -- read as the usual
+ * one): *loss = coeff * (1/T) * sum_t zsq[t], zsq from moe_router_topk_ex.
+ * Summed in double in a fixed order (deterministic); T == 0 gives 0.
+ * workspace: moe_z_loss_workspace_bytes(T) bytes, 8-byte aligned. */
+size_t moe_z_loss_workspace_bytes(int64_t T);
+int moe_z_loss(const float* zsq, int64_t T, float coeff, float* loss, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
 const char* moe_last_error(void);
 
 #ifdef __cplusplus

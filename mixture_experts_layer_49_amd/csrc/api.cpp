@@ -137,14 +137,17 @@ int64_t moe_rows_max(int64_t T, int32_t k, int32_t E, int64_t capacity) {
   return tk < ec ? tk : ec;
 }
 
-int moe_router_topk(const void* x, const void* w_gate, const float* bias, int64_t T, int64_t d,
-                    int32_t E, int32_t k, int32_t dtype, uint32_t flags, int32_t* topk_idx,
-                    float* topk_w, float* probs, hipStream_t stream) {
+int moe_router_topk_ex(const void* x, const void* w_gate, const float* bias, const float* noise,
+                       int64_t T, int64_t d, int32_t E, int32_t k, int32_t dtype, uint32_t flags,
+                       float temperature, int32_t* topk_idx, float* topk_w, float* probs,
+                       float* zsq, hipStream_t stream) {
   MOE_TRY(check_dtype(dtype));
   MOE_TRY(check_experts(E, k));
   if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
   if (T > (1LL << 31) / MOE_MAX_K) return fail(MOE_ERR_SHAPE, "T too large");
   if (flags & ~MOE_RENORM) return fail(MOE_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (!(temperature > 0.0f) || !std::isfinite(temperature))
+    return fail(MOE_ERR_ARG, "temperature must be finite and > 0");
   MOE_TRY(check_row("d", d, dtype));
   if (T == 0) return MOE_OK;
   MOE_NONNULL(x);
@@ -153,9 +156,30 @@ int moe_router_topk(const void* x, const void* w_gate, const float* bias, int64_
   MOE_NONNULL(topk_w);
   MOE_TRY(check_ptr16("x", x));
   MOE_TRY(check_ptr16("w_gate", w_gate));
-  return hip_status(moe::launch_router(x, w_gate, bias, T, d, E, k, dtype, flags, topk_idx, topk_w,
-                                       probs, stream),
-                    "moe_router_topk launch");
+  moe::RouterArgs a;
+  a.x = x;
+  a.wg = w_gate;
+  a.bias = bias;
+  a.noise = noise;
+  a.temperature = temperature;
+  a.T = T;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.dtype = dtype;
+  a.flags = flags;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.probs = probs;
+  a.zsq = zsq;
+  return hip_status(moe::launch_router(a, stream), "moe_router_topk launch");
+}
+
+int moe_router_topk(const void* x, const void* w_gate, const float* bias, int64_t T, int64_t d,
+                    int32_t E, int32_t k, int32_t dtype, uint32_t flags, int32_t* topk_idx,
+                    float* topk_w, float* probs, hipStream_t stream) {
+  return moe_router_topk_ex(x, w_gate, bias, nullptr, T, d, E, k, dtype, flags, 1.0f, topk_idx,
+                            topk_w, probs, nullptr, stream);
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
@@ -325,6 +349,26 @@ int moe_aux_loss(const float* probs, const int32_t* counts, int64_t T, int32_t E
   return hip_status(moe::launch_aux_loss(probs, counts, T, E, k, alpha, loss,
                                          static_cast<double*>(workspace), stream),
                     "moe_aux_loss launch");
+}
+
+size_t moe_z_loss_workspace_bytes(int64_t T) {
+  if (T < 0) return 0;
+  return moe::z_ws_doubles(T) * sizeof(double);
+}
+
+int moe_z_loss(const float* zsq, int64_t T, float coeff, float* loss, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
+  MOE_NONNULL(loss);
+  if (T > 0) MOE_NONNULL(zsq);
+  const size_t need = moe_z_loss_workspace_bytes(T);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+    return fail(MOE_ERR_ALIGN, "workspace is not 8-byte aligned");
+  return hip_status(moe::launch_z_loss(zsq, T, coeff, loss, static_cast<double*>(workspace), stream),
+                    "moe_z_loss launch");
 }
 
 const char* moe_last_error(void) { return g_err; }

@@ -135,6 +135,24 @@ __global__ __launch_bounds__(kMaxE) void aux_final_kernel(const double* __restri
   if (e == 0) loss[0] = static_cast<float>(static_cast<double>(alpha) * E * s[0]);
 }
 
+// Router z-loss: the per-block partial sums of zsq come from
+// aux_partial_kernel with E = 1; this adds them in block order.
+__global__ __launch_bounds__(kMaxE) void z_final_kernel(const double* __restrict__ part,
+                                                        int nblocks, int64_t T, float coeff,
+                                                        float* __restrict__ loss) {
+  __shared__ double s[kMaxE];
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+  for (int b = tid; b < nblocks; b += kMaxE) acc += part[b];   // b = tid, tid + 256, ...
+  s[tid] = acc;
+  __syncthreads();
+  for (int o = kMaxE / 2; o > 0; o >>= 1) {
+    if (tid < o) s[tid] += s[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) loss[0] = T > 0 ? static_cast<float>(static_cast<double>(coeff) * s[0] / static_cast<double>(T)) : 0.f;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w, int64_t T,
@@ -168,6 +186,24 @@ hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T,
   }
   hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(kMaxE), 0, s, ws, nblocks, counts, T, E, k,
                      alpha, loss);
+  return hipGetLastError();
+}
+
+size_t z_ws_doubles(int64_t T) {
+  (void)T;
+  return static_cast<size_t>(kAuxBlocks);
+}
+
+hipError_t launch_z_loss(const float* zsq, int64_t T, float coeff, float* loss, double* ws,
+                         hipStream_t s) {
+  int nblocks = 0;
+  if (T > 0) {
+    const int64_t chunk = (T + kAuxBlocks - 1) / kAuxBlocks;
+    nblocks = static_cast<int>((T + chunk - 1) / chunk);
+    hipLaunchKernelGGL(aux_partial_kernel, dim3(nblocks), dim3(kAuxThreads), 0, s, zsq, T, 1,
+                       chunk, ws);
+  }
+  hipLaunchKernelGGL(z_final_kernel, dim3(1), dim3(kMaxE), 0, s, ws, nblocks, T, coeff, loss);
   return hipGetLastError();
 }
 

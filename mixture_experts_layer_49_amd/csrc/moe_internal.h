@@ -30,9 +30,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Launchers (host). Arguments are validated by the C-ABI layer before these
 // run; each enqueues on `s` and returns the launch status.
-hipError_t launch_router(const void* x, const void* wg, const float* bias, int64_t T,
-                         int64_t d, int E, int k, int dtype, uint32_t flags,
-                         int32_t* topk_idx, float* topk_w, float* probs, hipStream_t s);
+// Router arguments (validated by the C-ABI layer).
+struct RouterArgs {
+  const void* x;
+  const void* wg;
+  const float* bias;    // nullable [E]
+  const float* noise;   // nullable [T, E], added to the logits
+  float temperature;    // > 0; scores = (logits + noise) / temperature
+  int64_t T, d;
+  int E, k, dtype;
+  uint32_t flags;
+  int32_t* topk_idx;
+  float* topk_w;
+  float* probs;         // nullable [T, E]
+  float* zsq;           // nullable [T]: (log sum_e exp(score))^2
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
 hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
                                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
@@ -62,6 +75,11 @@ size_t ffn_mfma_workspace_bytes();
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                           int64_t T, int k, int64_t d, void* y, int out_dtype, hipStream_t s);
+
+// Router z-loss: loss = coeff * mean_t zsq[t]; ws as for the aux loss.
+hipError_t launch_z_loss(const float* zsq, int64_t T, float coeff, float* loss, double* ws,
+                         hipStream_t s);
+size_t z_ws_doubles(int64_t T);
 
 hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T, int E, int k,
                            float alpha, float* loss, double* ws, hipStream_t s);

@@ -9,6 +9,10 @@
 // the four partial tiles meet in LDS and are summed in a fixed order. Softmax
 // and top-k then run with 16 lanes per token, each lane owning experts
 // e = lane%16 + 16*i, so a token's E logits never leave registers.
+// Balancing knobs (SP/EP page, EP section: routing temperature and a random
+// perturbation; ETP page: routing z-loss): softmax and top-k see the scores
+// s = (l + noise) / temperature, and the per-token z-loss term
+// (log sum_e exp s)^2 falls out of the softmax's max and sum.
 #include "moe_internal.h"
 
 namespace moe {
@@ -22,7 +26,8 @@ constexpr int kChunk = 128;   // d-elements one wave consumes per step
 // e = q + 16*i (i < NT). Invalid experts (e >= E) carry -inf and are skipped.
 template <int NT>
 __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int64_t t,
-                            int q, int32_t* topk_idx, float* topk_w, float* probs) {
+                            int q, int32_t* topk_idx, float* topk_w, float* probs,
+                            float* zsq) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NT; ++i) m = fmaxf(m, lg[i]);
@@ -39,6 +44,10 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
   const float inv_s = 1.0f / s;
+  if (zsq != nullptr && q == 0) {
+    const float lse = m + logf(s);
+    zsq[t] = lse * lse;
+  }
   if (probs) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -100,8 +109,9 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
 template <int NT>
 __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
-    const float* __restrict__ bias, int64_t T, int64_t d, int E, int k, uint32_t flags,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ probs) {
+    const float* __restrict__ bias, const float* __restrict__ noise, float temperature,
+    int64_t T, int64_t d, int E, int k, uint32_t flags, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ probs, float* __restrict__ zsq) {
   __shared__ float red[4][kTok][NT * 16];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -161,17 +171,19 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     const int e = q + 16 * i;
     float v = red[0][tok][e] + red[1][tok][e] + red[2][tok][e] + red[3][tok][e];
     if (bias != nullptr && e < E) v += bias[e];
-    lg[i] = (e < E) ? v : -INFINITY;
+    if (noise != nullptr && e < E && t < T) v += noise[t * E + e];
+    lg[i] = (e < E) ? v / temperature : -INFINITY;
   }
-  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs);
+  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, zsq);
 }
 
 // f32: plain FMA dot products, one (token, expert) pair per lane and step.
 template <int NT>
 __global__ __launch_bounds__(kThreads) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
-    int64_t T, int64_t d, int E, int k, uint32_t flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ probs) {
+    const float* __restrict__ noise, float temperature, int64_t T, int64_t d, int E, int k,
+    uint32_t flags, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ probs, float* __restrict__ zsq) {
   const int tid = threadIdx.x;
   const int tok = tid >> 4, q = tid & 15;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + tok;
@@ -185,41 +197,40 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(
       float v = 0.f;
       for (int64_t c = 0; c < d; ++c) v = fmaf(xr[c], wr[c], v);
       if (bias != nullptr) v += bias[e];
-      lg[i] = v;
+      if (noise != nullptr && t < T) v += noise[t * E + e];
+      lg[i] = v / temperature;
     } else {
       lg[i] = -INFINITY;
     }
   }
-  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs);
+  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, zsq);
 }
 
 template <int NT>
-hipError_t launch_nt(const void* x, const void* wg, const float* bias, int64_t T, int64_t d,
-                     int E, int k, int dtype, uint32_t flags, int32_t* idx, float* w,
-                     float* probs, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok)), block(kThreads);
-  if (dtype == 1)
+hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.T + kTok - 1) / kTok)), block(kThreads);
+  if (a.dtype == 1)
     hipLaunchKernelGGL(router_bf16_kernel<NT>, grid, block, 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias,
-                       T, d, E, k, flags, idx, w, probs);
+                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,
+                       a.noise, a.temperature, a.T, a.d, a.E, a.k, a.flags, a.topk_idx, a.topk_w,
+                       a.probs, a.zsq);
   else
-    hipLaunchKernelGGL(router_f32_kernel<NT>, grid, block, 0, s, static_cast<const float*>(x),
-                       static_cast<const float*>(wg), bias, T, d, E, k, flags, idx, w, probs);
+    hipLaunchKernelGGL(router_f32_kernel<NT>, grid, block, 0, s, static_cast<const float*>(a.x),
+                       static_cast<const float*>(a.wg), a.bias, a.noise, a.temperature, a.T, a.d,
+                       a.E, a.k, a.flags, a.topk_idx, a.topk_w, a.probs, a.zsq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router(const void* x, const void* wg, const float* bias, int64_t T, int64_t d,
-                         int E, int k, int dtype, uint32_t flags, int32_t* topk_idx,
-                         float* topk_w, float* probs, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const int nt = (E + 15) / 16;
-  if (nt <= 1) return launch_nt<1>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
-  if (nt <= 2) return launch_nt<2>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
-  if (nt <= 4) return launch_nt<4>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
-  if (nt <= 8) return launch_nt<8>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
-  return launch_nt<16>(x, wg, bias, T, d, E, k, dtype, flags, topk_idx, topk_w, probs, s);
+hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const int nt = (a.E + 15) / 16;
+  if (nt <= 1) return launch_nt<1>(a, s);
+  if (nt <= 2) return launch_nt<2>(a, s);
+  if (nt <= 4) return launch_nt<4>(a, s);
+  if (nt <= 8) return launch_nt<8>(a, s);
+  return launch_nt<16>(a, s);
 }
 
 }  // namespace moe

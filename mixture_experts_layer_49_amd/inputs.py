@@ -119,6 +119,13 @@ def _normal(rng, shape, std, dtype):
     return a if dtype == F32 else to_bf16_bits(a)
 
 
+def routing_noise(T: int, E: int, scale: float, seed: int) -> np.ndarray:
+    """A caller-drawn routing perturbation [T, E] f32: N(0, scale^2), its own
+    PCG64 stream (seed), independent of the layer inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal(size=(T, E), dtype=np.float32) * np.float32(scale)).astype(np.float32)
+
+
 def zipf_counts(n: int, E: int, s: float) -> np.ndarray:
     """Per-expert counts of n rows following Zipf(s) over experts 0..E-1,
     rounded to integers by largest remainder (ties: lower expert first)."""

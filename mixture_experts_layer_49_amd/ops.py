@@ -22,9 +22,10 @@ MOE_MAX_E, MOE_MAX_K = 256, 8
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
-EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_dispatch_workspace_bytes",
+EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
-           "moe_ffn_workspace_bytes", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_last_error"]
+           "moe_ffn_workspace_bytes", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
+           "moe_z_loss", "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -52,6 +53,10 @@ def lib() -> ctypes.CDLL:
         "moe_capacity": (I64, [I64, I32, F64]),
         "moe_rows_max": (I64, [I64, I32, I32, I64]),
         "moe_router_topk": (ctypes.c_int, [P, P, P, I64, I64, I32, I32, I32, U32, P, P, P, P]),
+        "moe_router_topk_ex": (ctypes.c_int, [P, P, P, P, I64, I64, I32, I32, I32, U32, F32, P, P, P,
+                                              P, P]),
+        "moe_z_loss_workspace_bytes": (SZ, [I64]),
+        "moe_z_loss": (ctypes.c_int, [P, I64, F32, P, P, SZ, P]),
         "moe_dispatch_workspace_bytes": (SZ, [I64, I32, I32]),
         "moe_dispatch": (ctypes.c_int, [P, I64, I32, I32, I64, P, I64, I32, P, P, P, P, P, P, SZ, P]),
         "moe_dispatch_plan": (ctypes.c_int, [P, I64, I32, I32, I64, P, P, P, P, P, SZ, P]),
@@ -125,6 +130,39 @@ def moe_router_topk(x, w_gate, bias, k: int, flags: int = 0, want_probs: bool = 
                                  dtype_code(x.dtype), flags, _ptr(topk_idx), _ptr(topk_w),
                                  _ptr(probs), _stream(stream)))
     return topk_idx, topk_w, probs
+
+
+def moe_router_topk_ex(x, w_gate, bias, k: int, flags: int = 0, temperature: float = 1.0,
+                       noise=None, want_probs: bool = True, want_zsq: bool = True,
+                       topk_idx=None, topk_w=None, probs=None, zsq=None, stream=None):
+    """Router with temperature, a caller-drawn perturbation `noise` [T, E] f32
+    and the per-token z-loss terms `zsq` [T] (see include/moe.h)."""
+    T, d = x.shape
+    E = w_gate.shape[0]
+    topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+    topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    if want_probs and probs is None:
+        probs = _empty((T, E), torch.float32, x)
+    if want_zsq and zsq is None:
+        zsq = _empty((max(T, 1),), torch.float32, x)
+    _check(lib().moe_router_topk_ex(_ptr(x), _ptr(w_gate), _ptr(bias), _ptr(noise), T, d, E, k,
+                                    dtype_code(x.dtype), flags, float(temperature),
+                                    _ptr(topk_idx), _ptr(topk_w), _ptr(probs), _ptr(zsq),
+                                    _stream(stream)))
+    return topk_idx, topk_w, probs, zsq
+
+
+def moe_z_loss_workspace_bytes(T: int) -> int:
+    return int(lib().moe_z_loss_workspace_bytes(T))
+
+
+def moe_z_loss(zsq, T: int, coeff: float, loss=None, workspace=None, stream=None):
+    loss = _empty((1,), torch.float32, zsq) if loss is None else loss
+    if workspace is None:
+        workspace = _empty((max(moe_z_loss_workspace_bytes(T), 8),), torch.uint8, zsq)
+    _check(lib().moe_z_loss(_ptr(zsq), T, float(coeff), _ptr(loss), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return loss
 
 
 def moe_dispatch_workspace_bytes(T: int, k: int, E: int) -> int:

@@ -105,6 +105,31 @@ def test_dispatch_argument_errors():
     assert L.moe_dispatch(*a) == -1
 
 
+def test_router_ex_and_z_loss_argument_errors():
+    L = ops.lib()
+    base = [FAKE, FAKE, None, None, 100, 64, 8, 2, 1, 0, 1.0, FAKE, FAKE, None, None, None]
+
+    def call(i, v):
+        a = list(base); a[i] = v
+        return L.moe_router_topk_ex(*a)
+    assert call(10, 0.0) == -1                    # temperature must be > 0
+    assert call(10, -2.0) == -1
+    assert call(10, float("nan")) == -1
+    assert call(10, float("inf")) == -1
+    assert call(9, 0x4) == -1                     # unknown flag
+    assert call(7, 9) == -3                       # k > E
+    assert call(5, 60) == -6                      # bf16 d % 8
+    assert call(0, None) == -1
+    # moe_z_loss(zsq, T, coeff, loss, ws, ws_bytes, stream)
+    need = L.moe_z_loss_workspace_bytes(100)
+    assert need > 0
+    assert L.moe_z_loss(FAKE, -1, 1.0, FAKE, FAKE, need, None) == -1
+    assert L.moe_z_loss(FAKE, 100, 1.0, None, FAKE, need, None) == -1
+    assert L.moe_z_loss(None, 100, 1.0, FAKE, FAKE, need, None) == -1
+    assert L.moe_z_loss(FAKE, 100, 1.0, FAKE, FAKE, need - 1, None) == -4
+    assert L.moe_z_loss(FAKE, 100, 1.0, FAKE, ctypes.c_void_p((1 << 20) + 4), need, None) == -6
+
+
 def test_plan_and_permute_argument_errors():
     L = ops.lib()
     need = L.moe_dispatch_workspace_bytes(100, 2, 8)

@@ -104,6 +104,56 @@ def check_routing(inp, cfg, flags=0):
     return ref, idx
 
 
+def check_routing_ex(inp, cfg, temperature, noise_scale, coeff=1e-3):
+    """Router with temperature, perturbation and z-loss terms vs the oracle."""
+    noise = None if noise_scale == 0 else I.routing_noise(cfg.T, cfg.E, noise_scale, 900 + cfg.seed)
+    ref = O.route(inp["x"], inp["w_gate"], inp["bias"], cfg.dtype, cfg.k, temperature=temperature,
+                  noise=noise)
+    t = gpu_tensors(inp, cfg)
+    nz = None if noise is None else dev(noise, "f32")
+    idx, w, probs, zsq = ops.moe_router_topk_ex(t["x"], t["w_gate"], t["bias"], cfg.k,
+                                                temperature=temperature, noise=nz)
+    zl = ops.moe_z_loss(zsq, cfg.T, coeff)
+    torch.cuda.synchronize()
+    idx, w, probs, zsq, zl = host(idx), host(w), host(probs), host(zsq), float(host(zl)[0])
+    gap = topk_gap(ref["logits"], cfg.k)
+    firm = gap >= GAP
+    mism = (idx != ref["topk_idx"]).any(axis=1)
+    say("  %s tau=%g noise=%g: %d below the gap, %d of those differ" % (
+        cfg.name, temperature, noise_scale, int((~firm).sum()), int((mism & ~firm).sum())))
+    assert not (mism & firm).any()
+    tol = 1e-4 if cfg.dtype == "bf16" else 1e-5
+    np.testing.assert_allclose(probs, ref["probs"], rtol=tol, atol=1e-7)
+    np.testing.assert_allclose(w[~mism], ref["topk_w"][~mism], rtol=tol, atol=1e-7)
+    # z-loss terms: (log-sum-exp)^2 of the scores, relative to their own size
+    np.testing.assert_allclose(zsq, ref["zsq"], rtol=10 * tol, atol=1e-6)
+    # the reduction: coeff * mean of the GPU's own terms, summed in double
+    assert abs(zl - coeff * float(np.mean(zsq.astype(np.float64)))) <= 1e-6 * abs(zl) + 1e-12
+    assert abs(zl - O.z_loss(ref["logits"], coeff)) <= 10 * tol * abs(zl) + 1e-9
+
+
+@pytest.mark.parametrize("cfg", [c for c in SMALL if c.name in ("small-bf16", "small-f32", "zipf-bias", "max-experts", "single-token")],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("tau,noise", [(1.0, 0.0), (0.5, 0.0), (2.0, 0.5)])
+def test_router_temperature_noise_zloss_small(cfg, tau, noise):
+    check_routing_ex(I.make_inputs(cfg), cfg, tau, noise)
+
+
+def test_router_temperature_noise_zloss_full():
+    cfg = FULL[1]   # 16 experts, Zipf-biased gate
+    check_routing_ex(cached_inputs(cfg), cfg, 1.7, 0.3)
+
+
+def test_router_ex_at_defaults_is_the_plain_router():
+    cfg = I.small("ex-defaults", T=513, d=256, d_ff=64, E=12, k=3, seed=71)
+    t = gpu_tensors(I.make_inputs(cfg), cfg)
+    a = ops.moe_router_topk(t["x"], t["w_gate"], t["bias"], cfg.k)
+    b = ops.moe_router_topk_ex(t["x"], t["w_gate"], t["bias"], cfg.k)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b[:3]):
+        assert torch.equal(u, v)
+
+
 @pytest.mark.parametrize("cfg", [c for c in SMALL if c.routed], ids=ids([c for c in SMALL if c.routed]))
 def test_router_small(cfg):
     check_routing(I.make_inputs(cfg), cfg)
