@@ -237,3 +237,82 @@ def forward(inp: dict, dtype: str, k: int, cf: float, alpha: float = 0.01,
     out["y_perm_rows"] = rows
     out["y"] = combine(y_perm, need, out["topk_w"][toks], toks.size)
     return out
+
+
+# ----------------------------------------------------------------- backward --
+# The layer's backward (EP tutorial section 5.1: the aux loss exists for its
+# gradient; the pages' reverse path runs combine, expert FFN, dispatch and the
+# gate in reverse). Reading: the routing choice (top-k indices, capacity
+# drops) and the counts in f_i are constants; gradients flow through the
+# chosen experts' probabilities, the FFN and the gate.
+
+def gelu_tanh_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of gelu_tanh: 0.5 (1 + tanh u) + 0.5 z (1 - tanh^2 u) u',
+    u = sqrt(2/pi)(z + 0.044715 z^3), u' = sqrt(2/pi)(1 + 3 * 0.044715 z^2)."""
+    c = np.sqrt(2.0 / np.pi)
+    u = c * (z + 0.044715 * z ** 3)
+    th = np.tanh(u)
+    return 0.5 * (1.0 + th) + 0.5 * z * (1.0 - th * th) * c * (1.0 + 3.0 * 0.044715 * z * z)
+
+
+def backward(inp: dict, fwd: dict, dy: np.ndarray, dtype: str, k: int, alpha: float = 0.01,
+             aux_scale: float = 1.0) -> dict:
+    """Gradients of L = sum(dy * y) + aux_scale * L_aux with respect to x, the
+    gate weight and bias, W1 and W2, given the forward's routing and dispatch
+    (`fwd`: topk_idx, topk_w, probs, counts, offsets, dest, src).
+
+    Expert part, for each kept row r (token t = src[r], slot j, weight w):
+      do_r = w dy_t;  dw_tj = dy_t . o_r;  dh_r = W2^T do_r;
+      dz_r = dh_r * gelu'(z_r);  dW2 += do_r h_r^T;  dW1 += dz_r x_t^T;
+      dx_t += W1^T dz_r.
+    Gate: dp[t, idx_tj] += dw_tj; dp[t, i] += aux_scale * alpha * E * f_i / T;
+      dl = p * (dp - sum_e p_e dp_e) (softmax backward);
+      dWg = dl^T x;  db = sum_t dl_t;  dx += dl Wg."""
+    x = decode(inp["x"], dtype)
+    w1 = decode(inp["w1"], dtype)
+    w2 = decode(inp["w2"], dtype)
+    T, d = x.shape
+    E = w1.shape[0]
+    dy = np.asarray(dy, dtype=np.float64)
+    dest, src, offsets = fwd["dest"], fwd["src"], fwd["offsets"]
+    idx, tw = fwd["topk_idx"], np.asarray(fwd["topk_w"], dtype=np.float64)
+    R = int(offsets[-1])
+    slot_of_row = np.empty((R, 2), dtype=np.int64)        # (t, j) of each kept row
+    for t in range(T):
+        for j in range(dest.shape[1]):
+            if dest[t, j] >= 0:
+                slot_of_row[dest[t, j]] = (t, j)
+    dx = np.zeros((T, d))
+    dw = np.zeros_like(tw)
+    dw1 = np.zeros_like(w1)
+    dw2 = np.zeros_like(w2)
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if rows.size == 0:
+            continue
+        t_r, j_r = slot_of_row[rows, 0], slot_of_row[rows, 1]
+        xr = x[t_r]
+        z = xr @ w1[e].T
+        h = gelu_tanh(z)
+        o = h @ w2[e].T
+        do = tw[t_r, j_r][:, None] * dy[t_r]
+        dw[t_r, j_r] = np.sum(dy[t_r] * o, axis=1)
+        dh = do @ w2[e]
+        dz = dh * gelu_tanh_grad(z)
+        dw2[e] = do.T @ h
+        dw1[e] = dz.T @ xr
+        np.add.at(dx, t_r, dz @ w1[e])
+    out = {"dx_experts": dx.copy(), "dw1": dw1, "dw2": dw2, "dw": dw}
+    if inp.get("w_gate") is not None:
+        wg = decode(inp["w_gate"], dtype)
+        p = np.asarray(fwd["probs"], dtype=np.float64)
+        dp = np.zeros((T, E))
+        for j in range(idx.shape[1]):
+            np.add.at(dp, (np.arange(T), idx[:, j]), dw[:, j])
+        f = np.asarray(fwd["counts"], dtype=np.float64) / float(T * k)
+        dp += aux_scale * alpha * E * f[None, :] / T
+        dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        out.update(dl=dl, dwg=dl.T @ x, db=dl.sum(axis=0))
+        dx += dl @ wg
+    out["dx"] = dx
+    return out

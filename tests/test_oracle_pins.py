@@ -374,3 +374,66 @@ def test_router_z_loss_closed_forms():
     np.testing.assert_allclose(O.z_loss_terms(s), scipy.special.logsumexp(s, axis=1) ** 2, rtol=1e-13)
     assert O.z_loss(s, 1e-3) == pytest.approx(1e-3 * np.mean(scipy.special.logsumexp(s, axis=1) ** 2), rel=1e-13)
     assert O.z_loss(np.zeros((0, 5)), 1.0) == 0.0
+
+
+def _torch_layer(inp, idx, dest, T, E, k):
+    """The forward written with torch ops (float64) for autograd: routing
+    choices and drops fixed, as the backward's reading says."""
+    x = torch.tensor(inp["x"], dtype=torch.float64, requires_grad=True)
+    wg = torch.tensor(inp["w_gate"], dtype=torch.float64, requires_grad=True)
+    b = torch.tensor(inp["bias"], dtype=torch.float64, requires_grad=True)
+    w1 = torch.tensor(inp["w1"], dtype=torch.float64, requires_grad=True)
+    w2 = torch.tensor(inp["w2"], dtype=torch.float64, requires_grad=True)
+    p = torch.softmax(x @ wg.T + b, dim=1)
+    y = torch.zeros(T, x.shape[1], dtype=torch.float64)
+    for t in range(T):
+        for j in range(k):
+            if dest[t, j] >= 0:
+                e = int(idx[t, j])
+                hid = torch.nn.functional.gelu(w1[e] @ x[t], approximate="tanh")
+                y[t] = y[t] + p[t, e] * (w2[e] @ hid)
+    return (x, wg, b, w1, w2), p, y
+
+
+def test_backward_vs_torch_autograd():
+    rng = np.random.default_rng(41)
+    T, d, dff, E, k, alpha, s = 23, 6, 10, 4, 2, 0.05, 0.7
+    inp = {"x": rng.standard_normal((T, d)), "w_gate": rng.standard_normal((E, d)) * 0.7,
+           "bias": rng.standard_normal(E) * 0.3, "w1": rng.standard_normal((E, dff, d)) * 0.5,
+           "w2": rng.standard_normal((E, d, dff)) * 0.5}
+    fwd = O.forward(inp, "f32", k=k, cf=1.0, alpha=alpha)      # C = 6 < some counts: drops happen
+    assert (fwd["dest"] < 0).any()
+    dy = rng.standard_normal((T, d))
+    g = O.backward(inp, fwd, dy, "f32", k, alpha=alpha, aux_scale=s)
+    params, p, y = _torch_layer(inp, fwd["topk_idx"], fwd["dest"], T, E, k)
+    np.testing.assert_allclose(y.detach().numpy(), fwd["y"], rtol=1e-12, atol=1e-12)
+    f = torch.tensor(fwd["counts"] / (T * k))
+    loss = (y * torch.tensor(dy)).sum() + s * alpha * E * (f * p.mean(dim=0)).sum()
+    loss.backward()
+    x, wg, b, w1, w2 = params
+    for name, t_ in (("dx", x), ("dwg", wg), ("db", b), ("dw1", w1), ("dw2", w2)):
+        np.testing.assert_allclose(g[name], t_.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_backward_finite_differences_and_gelu_grad():
+    rng = np.random.default_rng(43)
+    z = rng.standard_normal(50) * 3
+    h = 1e-6
+    np.testing.assert_allclose(O.gelu_tanh_grad(z), (O.gelu_tanh(z + h) - O.gelu_tanh(z - h)) / (2 * h),
+                               rtol=1e-7, atol=1e-9)
+    T, d, dff, E, k = 9, 4, 5, 3, 2
+    inp = {"x": rng.standard_normal((T, d)), "w_gate": rng.standard_normal((E, d)),
+           "bias": np.zeros(E), "w1": rng.standard_normal((E, dff, d)),
+           "w2": rng.standard_normal((E, d, dff))}
+    fwd = O.forward(inp, "f32", k=k, cf=-1)
+    dy = rng.standard_normal((T, d))
+    g = O.backward(inp, fwd, dy, "f32", k, alpha=0.0)
+
+    def loss_w1(w1):                       # routing does not depend on W1: exact check
+        q = dict(inp, w1=w1)
+        return float(np.sum(O.forward(q, "f32", k=k, cf=-1, alpha=0.0)["y"] * dy))
+    for (e, a, c) in [(0, 1, 2), (2, 4, 0), (1, 0, 3)]:
+        wp, wm = inp["w1"].copy(), inp["w1"].copy()
+        wp[e, a, c] += h
+        wm[e, a, c] -= h
+        assert (loss_w1(wp) - loss_w1(wm)) / (2 * h) == pytest.approx(g["dw1"][e, a, c], rel=1e-6, abs=1e-8)
