@@ -43,6 +43,9 @@ Readings where the pages are silent (each also listed in the design notes):
     s = (l + noise) / temperature replace the logits in softmax and top-k
     (the caller draws the noise), and the z-loss is the mean over tokens of
     (log sum_e exp(s[t, e]))^2, the usual router z-loss.
+  * backward (the pages train the layer and give the aux loss for its
+    gradient, no formulas): the routing choice and the counts in f_i are
+    constants; the caller's noise is an input.
 """
 from __future__ import annotations
 
@@ -172,12 +175,16 @@ def balance_scores(logits: np.ndarray, temperature: float = 1.0, noise=None) -> 
     return s / float(temperature)
 
 
+def log_sum_exp(scores: np.ndarray) -> np.ndarray:
+    """log sum_e exp(s[t, e]) per token, max-subtracted."""
+    m = scores.max(axis=1)
+    return m + np.log(np.exp(scores - m[:, None]).sum(axis=1))
+
+
 def z_loss_terms(scores: np.ndarray) -> np.ndarray:
     """Per-token term of the router z-loss (ETP page: routing z-loss spreads
-    the gate's attention): (log sum_e exp(s[t, e]))^2, max-subtracted."""
-    m = scores.max(axis=1)
-    lse = m + np.log(np.exp(scores - m[:, None]).sum(axis=1))
-    return lse ** 2
+    the gate's attention): (log sum_e exp(s[t, e]))^2."""
+    return log_sum_exp(scores) ** 2
 
 
 def z_loss(scores: np.ndarray, coeff: float) -> float:
@@ -195,11 +202,13 @@ def route(x, w_gate, bias, dtype: str, k: int, renorm: bool = False, temperature
     s = balance_scores(l, temperature, noise)
     p = softmax(s)
     idx, w = topk(s, p, k, renorm)
-    return {"logits": s, "probs": p, "topk_idx": idx, "topk_w": w, "zsq": z_loss_terms(s)}
+    lse = log_sum_exp(s)
+    return {"logits": s, "probs": p, "topk_idx": idx, "topk_w": w, "lse": lse, "zsq": lse ** 2}
 
 
 def forward(inp: dict, dtype: str, k: int, cf: float, alpha: float = 0.01,
-            renorm: bool = False, sample_tokens=None) -> dict:
+            renorm: bool = False, sample_tokens=None, temperature: float = 1.0,
+            noise=None) -> dict:
     """The whole layer: route (unless `inp` carries topk_idx/topk_w), dispatch,
     expert FFN, combine, aux loss.
 
@@ -211,7 +220,7 @@ def forward(inp: dict, dtype: str, k: int, cf: float, alpha: float = 0.01,
     E = inp["w1"].shape[0]
     out = {}
     if inp.get("w_gate") is not None:
-        out.update(route(x, inp["w_gate"], inp.get("bias"), dtype, k, renorm))
+        out.update(route(x, inp["w_gate"], inp.get("bias"), dtype, k, renorm, temperature, noise))
     else:
         out["topk_idx"] = np.asarray(inp["topk_idx"], dtype=np.int64)
         out["topk_w"] = np.asarray(inp["topk_w"], dtype=np.float64)
@@ -242,9 +251,10 @@ def forward(inp: dict, dtype: str, k: int, cf: float, alpha: float = 0.01,
 # ----------------------------------------------------------------- backward --
 # The layer's backward (EP tutorial section 5.1: the aux loss exists for its
 # gradient; the pages' reverse path runs combine, expert FFN, dispatch and the
-# gate in reverse). Reading: the routing choice (top-k indices, capacity
+# gate in reverse). Readings: the routing choice (top-k indices, capacity
 # drops) and the counts in f_i are constants; gradients flow through the
-# chosen experts' probabilities, the FFN and the gate.
+# chosen experts' weights, the FFN, the softmax and the gate; the noise is
+# an input, so only 1/temperature scales the gate gradient.
 
 def gelu_tanh_grad(z: np.ndarray) -> np.ndarray:
     """d/dz of gelu_tanh: 0.5 (1 + tanh u) + 0.5 z (1 - tanh^2 u) u',
@@ -255,63 +265,110 @@ def gelu_tanh_grad(z: np.ndarray) -> np.ndarray:
     return 0.5 * (1.0 + th) + 0.5 * z * (1.0 - th * th) * c * (1.0 + 3.0 * 0.044715 * z * z)
 
 
-def backward(inp: dict, fwd: dict, dy: np.ndarray, dtype: str, k: int, alpha: float = 0.01,
-             aux_scale: float = 1.0) -> dict:
-    """Gradients of L = sum(dy * y) + aux_scale * L_aux with respect to x, the
-    gate weight and bias, W1 and W2, given the forward's routing and dispatch
-    (`fwd`: topk_idx, topk_w, probs, counts, offsets, dest, src).
+def combine_backward(dy: np.ndarray, y_perm: np.ndarray, dest: np.ndarray, topk_w: np.ndarray,
+                     R: int):
+    """Transpose of the weighted combine y[t] = sum_j w[t,j] o[dest[t,j]]:
+    d_out[dest[t,j]] = w[t,j] dy[t] and dw[t,j] = dy[t] . o[dest[t,j]];
+    a dropped slot gets dw = 0."""
+    T, k = dest.shape
+    d = dy.shape[1]
+    d_out = np.zeros((R, d))
+    dw = np.zeros((T, k))
+    for j in range(k):
+        keep = dest[:, j] >= 0
+        r = dest[keep, j]
+        d_out[r] = topk_w[keep, j][:, None] * dy[keep]
+        dw[keep, j] = np.sum(dy[keep] * y_perm[r], axis=1)
+    return d_out, dw
 
-    Expert part, for each kept row r (token t = src[r], slot j, weight w):
-      do_r = w dy_t;  dw_tj = dy_t . o_r;  dh_r = W2^T do_r;
-      dz_r = dh_r * gelu'(z_r);  dW2 += do_r h_r^T;  dW1 += dz_r x_t^T;
-      dx_t += W1^T dz_r.
-    Gate: dp[t, idx_tj] += dw_tj; dp[t, i] += aux_scale * alpha * E * f_i / T;
-      dl = p * (dp - sum_e p_e dp_e) (softmax backward);
-      dWg = dl^T x;  db = sum_t dl_t;  dx += dl Wg."""
+
+def gate_backward(dw: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, probs: np.ndarray,
+                  counts: np.ndarray, k: int, alpha: float, aux_grad: float, renorm: bool = False,
+                  temperature: float = 1.0, lse=None, z_coeff: float = 0.0) -> np.ndarray:
+    """Gradient of the gate's linear output (the logits before the routing
+    knobs) from: the combine weights' gradient dw, aux_grad times the aux
+    loss (EP tutorial 5.1), and z_coeff times the mean over tokens of lse^2.
+
+    p = softmax(s), s = (l + noise) / temperature. Chosen weight w_j = p_j,
+    or p_j / S with S = sum over the chosen p when renormalised, whose
+    gradient with respect to a chosen p_m is (dw_m - sum_j dw_j w_j) / S.
+    dL_aux/dp[t, i] = alpha E f_i / T with f_i = counts_i / (T k).
+    Softmax: ds = p (dp - sum_e p dp); z-loss: ds += z_coeff 2 lse p / T;
+    dl = ds / temperature."""
+    T, E = probs.shape
+    p = np.asarray(probs, dtype=np.float64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    g = np.asarray(dw, dtype=np.float64).copy()
+    if renorm:
+        S = np.take_along_axis(p, topk_idx, axis=1).sum(axis=1, keepdims=True)
+        g = (g - np.sum(g * w, axis=1, keepdims=True)) / S
+    dp = np.zeros((T, E))
+    for j in range(topk_idx.shape[1]):
+        np.add.at(dp, (np.arange(T), topk_idx[:, j]), g[:, j])
+    if T > 0:
+        f = np.asarray(counts, dtype=np.float64) / float(T * k)
+        dp += aux_grad * alpha * E * f[None, :] / T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    if z_coeff != 0.0 and T > 0:
+        ds += z_coeff * 2.0 * np.asarray(lse, dtype=np.float64)[:, None] * p / T
+    return ds / float(temperature)
+
+
+def backward(inp: dict, fwd: dict, dy: np.ndarray, dtype: str, k: int, alpha: float = 0.01,
+             aux_scale: float = 1.0, renorm: bool = False, temperature: float = 1.0,
+             z_coeff: float = 0.0) -> dict:
+    """Gradients of L = sum(dy * y) + aux_scale * L_aux + z_coeff * mean(lse^2)
+    with respect to x, the gate weight and bias, W1 and W2, given the
+    forward's routing and dispatch (`fwd`: topk_idx, topk_w, probs, counts,
+    offsets, dest, src, y_perm, lse).
+
+    Expert part, for each kept row r (token t = src[r]):
+      d_out_r, dw from combine_backward;  z_r = W1 x_t;  h_r = gelu(z_r);
+      dz_r = (W2^T d_out_r) * gelu'(z_r);  dW2 += d_out_r h_r^T;
+      dW1 += dz_r x_t^T;  dx_perm_r = W1^T dz_r;  dx_t += dx_perm_r.
+    Gate: dl from gate_backward; dWg = dl^T x; db = sum_t dl_t; dx += dl Wg.
+    Also returns the per-row intermediates (z_perm, h_perm, d_out_perm,
+    dz_perm, dx_perm)."""
     x = decode(inp["x"], dtype)
     w1 = decode(inp["w1"], dtype)
     w2 = decode(inp["w2"], dtype)
     T, d = x.shape
-    E = w1.shape[0]
+    E, dff = w1.shape[0], w1.shape[1]
     dy = np.asarray(dy, dtype=np.float64)
     dest, src, offsets = fwd["dest"], fwd["src"], fwd["offsets"]
-    idx, tw = fwd["topk_idx"], np.asarray(fwd["topk_w"], dtype=np.float64)
+    tw = np.asarray(fwd["topk_w"], dtype=np.float64)
     R = int(offsets[-1])
-    slot_of_row = np.empty((R, 2), dtype=np.int64)        # (t, j) of each kept row
-    for t in range(T):
-        for j in range(dest.shape[1]):
-            if dest[t, j] >= 0:
-                slot_of_row[dest[t, j]] = (t, j)
-    dx = np.zeros((T, d))
-    dw = np.zeros_like(tw)
+    xp = x[src]
+    z = np.zeros((R, dff))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        z[a:b] = xp[a:b] @ w1[e].T
+    h = gelu_tanh(z)
+    y_perm = np.zeros((R, d))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        y_perm[a:b] = h[a:b] @ w2[e].T
+    d_out, dw = combine_backward(dy, y_perm, dest, tw, R)
+    dz = np.zeros((R, dff))
+    dx_perm = np.zeros((R, d))
     dw1 = np.zeros_like(w1)
     dw2 = np.zeros_like(w2)
     for e in range(E):
-        rows = np.arange(offsets[e], offsets[e + 1])
-        if rows.size == 0:
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
             continue
-        t_r, j_r = slot_of_row[rows, 0], slot_of_row[rows, 1]
-        xr = x[t_r]
-        z = xr @ w1[e].T
-        h = gelu_tanh(z)
-        o = h @ w2[e].T
-        do = tw[t_r, j_r][:, None] * dy[t_r]
-        dw[t_r, j_r] = np.sum(dy[t_r] * o, axis=1)
-        dh = do @ w2[e]
-        dz = dh * gelu_tanh_grad(z)
-        dw2[e] = do.T @ h
-        dw1[e] = dz.T @ xr
-        np.add.at(dx, t_r, dz @ w1[e])
-    out = {"dx_experts": dx.copy(), "dw1": dw1, "dw2": dw2, "dw": dw}
+        dz[a:b] = (d_out[a:b] @ w2[e]) * gelu_tanh_grad(z[a:b])
+        dw2[e] = d_out[a:b].T @ h[a:b]
+        dw1[e] = dz[a:b].T @ xp[a:b]
+        dx_perm[a:b] = dz[a:b] @ w1[e]
+    dx = np.zeros((T, d))
+    np.add.at(dx, src, dx_perm)
+    out = {"dx_experts": dx.copy(), "dw1": dw1, "dw2": dw2, "dw": dw, "z_perm": z, "h_perm": h,
+           "d_out_perm": d_out, "dz_perm": dz, "dx_perm": dx_perm}
     if inp.get("w_gate") is not None:
         wg = decode(inp["w_gate"], dtype)
-        p = np.asarray(fwd["probs"], dtype=np.float64)
-        dp = np.zeros((T, E))
-        for j in range(idx.shape[1]):
-            np.add.at(dp, (np.arange(T), idx[:, j]), dw[:, j])
-        f = np.asarray(fwd["counts"], dtype=np.float64) / float(T * k)
-        dp += aux_scale * alpha * E * f[None, :] / T
-        dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        dl = gate_backward(dw, fwd["topk_idx"], tw, fwd["probs"], fwd["counts"], k, alpha,
+                           aux_scale, renorm, temperature, fwd.get("lse"), z_coeff)
         out.update(dl=dl, dwg=dl.T @ x, db=dl.sum(axis=0))
         dx += dl @ wg
     out["dx"] = dx

@@ -376,7 +376,7 @@ def test_router_z_loss_closed_forms():
     assert O.z_loss(np.zeros((0, 5)), 1.0) == 0.0
 
 
-def _torch_layer(inp, idx, dest, T, E, k):
+def _torch_layer(inp, idx, dest, T, E, k, renorm=False, temperature=1.0, noise=None):
     """The forward written with torch ops (float64) for autograd: routing
     choices and drops fixed, as the backward's reading says."""
     x = torch.tensor(inp["x"], dtype=torch.float64, requires_grad=True)
@@ -384,31 +384,47 @@ def _torch_layer(inp, idx, dest, T, E, k):
     b = torch.tensor(inp["bias"], dtype=torch.float64, requires_grad=True)
     w1 = torch.tensor(inp["w1"], dtype=torch.float64, requires_grad=True)
     w2 = torch.tensor(inp["w2"], dtype=torch.float64, requires_grad=True)
-    p = torch.softmax(x @ wg.T + b, dim=1)
+    s = x @ wg.T + b
+    if noise is not None:
+        s = s + torch.tensor(noise)
+    s = s / temperature
+    p = torch.softmax(s, dim=1)
     y = torch.zeros(T, x.shape[1], dtype=torch.float64)
     for t in range(T):
+        tot = sum(p[t, int(idx[t, j])] for j in range(k)) if renorm else 1.0
         for j in range(k):
             if dest[t, j] >= 0:
                 e = int(idx[t, j])
                 hid = torch.nn.functional.gelu(w1[e] @ x[t], approximate="tanh")
-                y[t] = y[t] + p[t, e] * (w2[e] @ hid)
-    return (x, wg, b, w1, w2), p, y
+                y[t] = y[t] + p[t, e] / tot * (w2[e] @ hid)
+    return (x, wg, b, w1, w2), s, p, y
 
 
-def test_backward_vs_torch_autograd():
+@pytest.mark.parametrize("variant", ["plain", "renorm-temp-noise-zloss"])
+def test_backward_vs_torch_autograd(variant):
     rng = np.random.default_rng(41)
-    T, d, dff, E, k, alpha, s = 23, 6, 10, 4, 2, 0.05, 0.7
+    T, d, dff, E, k, alpha, a_s = 23, 6, 10, 4, 2, 0.05, 0.7
     inp = {"x": rng.standard_normal((T, d)), "w_gate": rng.standard_normal((E, d)) * 0.7,
            "bias": rng.standard_normal(E) * 0.3, "w1": rng.standard_normal((E, dff, d)) * 0.5,
            "w2": rng.standard_normal((E, d, dff)) * 0.5}
-    fwd = O.forward(inp, "f32", k=k, cf=1.0, alpha=alpha)      # C = 6 < some counts: drops happen
+    kw = {}
+    bw = {}
+    if variant != "plain":
+        noise = rng.standard_normal((T, E)) * 0.2
+        kw = dict(renorm=True, temperature=1.7, noise=noise)
+        bw = dict(renorm=True, temperature=1.7, z_coeff=0.3)
+    fwd = O.forward(inp, "f32", k=k, cf=1.0, alpha=alpha, **kw)   # C = 6 < some counts: drops
     assert (fwd["dest"] < 0).any()
     dy = rng.standard_normal((T, d))
-    g = O.backward(inp, fwd, dy, "f32", k, alpha=alpha, aux_scale=s)
-    params, p, y = _torch_layer(inp, fwd["topk_idx"], fwd["dest"], T, E, k)
+    g = O.backward(inp, fwd, dy, "f32", k, alpha=alpha, aux_scale=a_s, **bw)
+    params, s, p, y = _torch_layer(inp, fwd["topk_idx"], fwd["dest"], T, E, k,
+                                   kw.get("renorm", False), kw.get("temperature", 1.0),
+                                   kw.get("noise"))
     np.testing.assert_allclose(y.detach().numpy(), fwd["y"], rtol=1e-12, atol=1e-12)
     f = torch.tensor(fwd["counts"] / (T * k))
-    loss = (y * torch.tensor(dy)).sum() + s * alpha * E * (f * p.mean(dim=0)).sum()
+    loss = (y * torch.tensor(dy)).sum() + a_s * alpha * E * (f * p.mean(dim=0)).sum()
+    if bw.get("z_coeff"):
+        loss = loss + bw["z_coeff"] * (torch.logsumexp(s, dim=1) ** 2).mean()
     loss.backward()
     x, wg, b, w1, w2 = params
     for name, t_ in (("dx", x), ("dwg", wg), ("db", b), ("dw1", w1), ("dw2", w2)):
