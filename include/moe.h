@@ -1,6 +1,6 @@
 /*
- * moe.h -- C ABI of the single-GPU Mixture-of-Experts layer forward
- *          (gfx950 / CDNA4, HIP).
+ * moe.h -- C ABI of the single-GPU Mixture-of-Experts layer, forward and
+ *          backward (gfx950 / CDNA4, HIP).
  *
  * The layer replaces a Transformer FFN with a gate, a set of expert FFNs and
  * sparse top-K activation (EP tutorial "专家并行：混合专家模型的分布式训练方案",
@@ -13,6 +13,11 @@
  *                    the w1 / w2 up- and down-projection example; tutorial 2.1 step 4)
  *   moe_combine      weighted return to token order            (tutorial 2.1 step 5)
  *   moe_aux_loss     L_aux = alpha * E * sum_i f_i * P_i       (tutorial 5.1)
+ *
+ * The backward (see the section near the end) runs the same path in reverse:
+ * moe_combine_backward, moe_expert_down_backward, moe_expert_up_backward,
+ * moe_expert_weight_grads, moe_gate_backward, moe_gate_weight_grads,
+ * moe_dispatch_backward.
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers, row-major, densely packed, owned
@@ -94,13 +99,14 @@ int moe_router_topk(const void* x, const void* w_gate, const float* bias,
  *   s[t, e] = (l[t, e] + noise[t, e]) / temperature
  *   noise       [T, E] f32 in, nullable (0): a perturbation the caller draws
  *   temperature  finite, > 0 (1: the plain router)
- *   zsq         [T] f32 out, nullable: (log sum_e exp s[t, e])^2, the
- *               per-token term of the router z-loss (see moe_z_loss)
- * moe_router_topk == moe_router_topk_ex(noise NULL, temperature 1, zsq NULL). */
+ *   lse         [T] f32 out, nullable: log sum_e exp s[t, e], whose square
+ *               is the per-token term of the router z-loss (see moe_z_loss)
+ *               and which the z-loss gradient needs (moe_gate_backward)
+ * moe_router_topk == moe_router_topk_ex(noise NULL, temperature 1, lse NULL). */
 int moe_router_topk_ex(const void* x, const void* w_gate, const float* bias,
                        const float* noise, int64_t T, int64_t d, int32_t E, int32_t k,
                        int32_t dtype, uint32_t flags, float temperature,
-                       int32_t* topk_idx, float* topk_w, float* probs, float* zsq,
+                       int32_t* topk_idx, float* topk_w, float* probs, float* lse,
                        hipStream_t stream);
 
 /* Bytes of device workspace moe_dispatch needs (0 when T == 0). */
@@ -217,15 +223,108 @@ int moe_aux_loss(const float* probs, const int32_t* counts, int64_t T, int32_t E
                  int32_t k, float alpha, float* loss, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
-/* Text describing the last non-OK status returned on the calling thread. */
 /* Router z-loss (ETP page names it; no formula there -- read as the usual
- * one): *loss = coeff * (1/T) * sum_t zsq[t], zsq from moe_router_topk_ex.
+ * one): *loss = coeff * (1/T) * sum_t lse[t]^2, lse from moe_router_topk_ex.
  * Summed in double in a fixed order (deterministic); T == 0 gives 0.
  * workspace: moe_z_loss_workspace_bytes(T) bytes, 8-byte aligned. */
 size_t moe_z_loss_workspace_bytes(int64_t T);
-int moe_z_loss(const float* zsq, int64_t T, float coeff, float* loss, void* workspace,
+int moe_z_loss(const float* lse, int64_t T, float coeff, float* loss, void* workspace,
                size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------- backward --
+ * The layer's backward on one GPU. The pages train the layer end to end and
+ * keep the aux loss for its gradient on the gate (EP tutorial 5.1); the
+ * reverse path runs combine, the expert FFN, dispatch and the gate in turn.
+ * Readings: the routing choice (top-k indices, capacity drops) and the counts
+ * in f_i are constants of the backward; a caller-drawn noise is an input.
+ * Gradient storage of a layer: bf16 (RNE) when dtype is MOE_BF16, f32 when
+ * MOE_F32; dx_perm, dx and every weight gradient are f32. The bf16 GEMMs
+ * accumulate in f32 on the MFMA units.
+ * Limits on top of the forward's for MOE_BF16: d * d_ff < 2^30 and
+ * rows_max * max(d, d_ff) < 2^30. */
+
+/* moe_expert_up_gelu that also stores the pre-activation
+ *   z[r] = W1[e] . x_perm[r]       z [rows_max, d_ff] in the hidden storage
+ * (fp16 for MOE_BF16, f32 for MOE_F32), which moe_expert_down_backward needs. */
+int moe_expert_up_gelu_z(const void* x_perm, const int32_t* offsets, int32_t E,
+                         int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                         int32_t dtype, void* h, void* z, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Transpose of moe_combine. For every slot (t, j) with r = dest[t,j] >= 0:
+ *   d_out_perm[r] = topk_w[t,j] * dy[t]       (gradient storage, [rows, d])
+ *   d_topk_w[t,j] = dy[t] . y_perm[r]          (f32 [T, k]; 0 when dropped)
+ * dy [T, d] f32, y_perm [rows, d] f32 (the expert outputs of the forward).
+ * Rows of d_out_perm that no slot names are not written. Dot products are
+ * summed in a fixed order (deterministic). */
+int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                         const float* topk_w, int64_t T, int32_t k, int64_t d,
+                         int32_t dtype, void* d_out_perm, float* d_topk_w,
+                         hipStream_t stream);
+
+/* Backward of the down-projection and the GELU, per expert segment:
+ *   dz[r] = (W2[e]^T d_out_perm[r]) * gelu_tanh'(z[r])    [rows_max, d_ff]
+ * d_out_perm [rows_max, d] and dz in gradient storage, z from
+ * moe_expert_up_gelu_z, w2 [E, d, d_ff] as in the forward. workspace as for
+ * moe_grouped_ffn (optional split tiles, deterministic). */
+int moe_expert_down_backward(const void* d_out_perm, const int32_t* offsets, int32_t E,
+                             int64_t rows_max, int64_t d, int64_t d_ff, const void* w2,
+                             const void* z, int32_t dtype, void* dz, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of the up-projection to the grouped rows:
+ *   dx_perm[r] = W1[e]^T dz[r]         f32 [rows_max, d]
+ * w1 [E, d_ff, d] as in the forward; workspace as for moe_grouped_ffn. */
+int moe_expert_up_backward(const void* dz, const int32_t* offsets, int32_t E,
+                           int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                           int32_t dtype, float* dx_perm, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Expert weight gradients, summed over each expert's kept rows:
+ *   dw1[e] = sum_r dz[r]^T x_perm[r]          f32 [E, d_ff, d]   (NULL: skip)
+ *   dw2[e] = sum_r d_out_perm[r]^T h[r]       f32 [E, d, d_ff]   (NULL: skip)
+ * Every expert's block is written (zeros for an expert with no rows). For
+ * MOE_BF16, h (fp16) is rounded to bf16 on its way into the product. */
+int moe_expert_weight_grads(const void* x_perm, const void* h, const void* d_out_perm,
+                            const void* dz, const int32_t* offsets, int32_t E,
+                            int64_t rows_max, int64_t d, int64_t d_ff, int32_t dtype,
+                            float* dw1, float* dw2, hipStream_t stream);
+
+/* Gradient of the gate's linear output l = x Wg^T + b, [T, E] f32, for
+ *   L = <dy, y> + aux_grad * L_aux + z_coeff * (1/T) sum_t lse[t]^2.
+ * With s = (l + noise) / temperature and p = softmax(s) (moe_router_topk_ex):
+ *   g[t,j] = d_topk_w[t,j], or, with flags & MOE_RENORM (w = p / S, S the
+ *            sum of the chosen p), (d_topk_w[t,j] - sum_i d_topk_w[t,i] w[t,i]) / S;
+ *   dp[t,e] = sum over slots j choosing e of g[t,j]
+ *             + aux_grad * alpha * E * counts[e] / (T k) / T   (EP tutorial 5.1);
+ *   ds = p (dp - sum_e p dp) + z_coeff * 2 lse[t] p / T;  d_logits = ds / temperature.
+ * topk_w may be NULL without MOE_RENORM; lse may be NULL when z_coeff == 0. */
+int moe_gate_backward(const float* d_topk_w, const int32_t* topk_idx, const float* topk_w,
+                      const float* probs, const int32_t* counts, const float* lse,
+                      int64_t T, int32_t E, int32_t k, uint32_t flags, float temperature,
+                      float alpha, float aux_grad, float z_coeff, float* d_logits,
+                      hipStream_t stream);
+
+/* Gate weight gradients: d_w_gate = d_logits^T x  (f32 [E, d]) and
+ * d_bias = column sums of d_logits (f32 [E], nullable). x [T, d] in dtype.
+ * Partial sums over token chunks are added in chunk order (deterministic).
+ * workspace: moe_gate_weight_grads_workspace_bytes(T, d, E) bytes, 16-byte
+ * aligned. */
+size_t moe_gate_weight_grads_workspace_bytes(int64_t T, int64_t d, int32_t E);
+int moe_gate_weight_grads(const float* d_logits, const void* x, int64_t T, int64_t d,
+                          int32_t E, int32_t dtype, float* d_w_gate, float* d_bias,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Transpose of dispatch plus the gate's input gradient:
+ *   dx[t] = sum over kept slots j (in slot order) of dx_perm[dest[t,j]]
+ *           + sum_e d_logits[t,e] * w_gate[e]          f32 [T, d]
+ * d_logits and w_gate ([E, d] in dtype) are both given or both NULL (a layer
+ * with caller-given routing). */
+int moe_dispatch_backward(const float* dx_perm, const int32_t* dest, const float* d_logits,
+                          const void* w_gate, int64_t T, int32_t k, int64_t d, int32_t E,
+                          int32_t dtype, float* dx, hipStream_t stream);
+
+/* Text describing the last non-OK status returned on the calling thread. */
 const char* moe_last_error(void);
 
 #ifdef __cplusplus

@@ -1,4 +1,4 @@
-// C ABI of the MoE layer forward: argument validation, capacity arithmetic,
+// C ABI of the MoE layer forward and backward: argument validation, capacity arithmetic,
 // workspace sizing and kernel launches. Every check runs on the host before
 // anything is enqueued; see include/moe.h for the contract of each call.
 #include "moe.h"
@@ -140,7 +140,7 @@ int64_t moe_rows_max(int64_t T, int32_t k, int32_t E, int64_t capacity) {
 int moe_router_topk_ex(const void* x, const void* w_gate, const float* bias, const float* noise,
                        int64_t T, int64_t d, int32_t E, int32_t k, int32_t dtype, uint32_t flags,
                        float temperature, int32_t* topk_idx, float* topk_w, float* probs,
-                       float* zsq, hipStream_t stream) {
+                       float* lse, hipStream_t stream) {
   MOE_TRY(check_dtype(dtype));
   MOE_TRY(check_experts(E, k));
   if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
@@ -171,7 +171,7 @@ int moe_router_topk_ex(const void* x, const void* w_gate, const float* bias, con
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.probs = probs;
-  a.zsq = zsq;
+  a.lse = lse;
   return hip_status(moe::launch_router(a, stream), "moe_router_topk launch");
 }
 
@@ -273,7 +273,7 @@ int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E, in
   MOE_TRY(check_ffn(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h));
   MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
   return hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h,
-                                        workspace, stream),
+                                        nullptr, workspace, stream),
                     "moe_expert_up_gelu launch");
 }
 
@@ -295,7 +295,7 @@ int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E, int64
   MOE_TRY(check_ffn(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm));
   MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
   MOE_TRY(hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h,
-                                         workspace, stream),
+                                         nullptr, workspace, stream),
                      "moe_grouped_ffn up-projection launch"));
   return hip_status(moe::launch_down(h, offsets, E, rows_max, d, d_ff, w2, dtype, y_perm,
                                      workspace, stream),
@@ -356,19 +356,209 @@ size_t moe_z_loss_workspace_bytes(int64_t T) {
   return moe::z_ws_doubles(T) * sizeof(double);
 }
 
-int moe_z_loss(const float* zsq, int64_t T, float coeff, float* loss, void* workspace,
+int moe_z_loss(const float* lse, int64_t T, float coeff, float* loss, void* workspace,
                size_t workspace_bytes, hipStream_t stream) {
   if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
   MOE_NONNULL(loss);
-  if (T > 0) MOE_NONNULL(zsq);
+  if (T > 0) MOE_NONNULL(lse);
   const size_t need = moe_z_loss_workspace_bytes(T);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
                 workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
     return fail(MOE_ERR_ALIGN, "workspace is not 8-byte aligned");
-  return hip_status(moe::launch_z_loss(zsq, T, coeff, loss, static_cast<double*>(workspace), stream),
+  return hip_status(moe::launch_z_loss(lse, T, coeff, loss, static_cast<double*>(workspace), stream),
                     "moe_z_loss launch");
+}
+
+// ------------------------------------------------------------------ backward
+
+namespace {
+
+// The bf16 backward GEMMs address a weight matrix of one expert, and the rows
+// of one expert's activations, through 32-bit buffer ranges.
+int check_bwd_limits(int64_t rows_max, int64_t d, int64_t d_ff, int32_t dtype) {
+  if (dtype != MOE_BF16) return MOE_OK;
+  const int64_t wide = d > d_ff ? d : d_ff;
+  if (d * d_ff >= (1LL << 30) || rows_max * wide >= (1LL << 30))
+    return fail(MOE_ERR_SHAPE, "backward needs d * d_ff < 2^30 and rows_max * max(d, d_ff) < 2^30");
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_expert_up_gelu_z(const void* x_perm, const int32_t* offsets, int32_t E, int64_t rows_max,
+                         int64_t d, int64_t d_ff, const void* w1, int32_t dtype, void* h, void* z,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_ffn(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h));
+  MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
+  if (rows_max > 0) {
+    MOE_NONNULL(z);
+    MOE_TRY(check_ptr16("z", z));
+  }
+  return hip_status(moe::launch_up_gelu(x_perm, offsets, E, rows_max, d, d_ff, w1, dtype, h, z,
+                                        workspace, stream),
+                    "moe_expert_up_gelu_z launch");
+}
+
+int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                         const float* topk_w, int64_t T, int32_t k, int64_t d, int32_t dtype,
+                         void* d_out_perm, float* d_topk_w, hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  if (T < 0 || d <= 0 || k < 1 || k > MOE_MAX_K)
+    return fail(MOE_ERR_ARG, "need T >= 0, d > 0, 1 <= k <= %d", MOE_MAX_K);
+  MOE_TRY(check_row("d", d, dtype));
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(dy);
+  MOE_NONNULL(y_perm);
+  MOE_NONNULL(dest);
+  MOE_NONNULL(topk_w);
+  MOE_NONNULL(d_out_perm);
+  MOE_NONNULL(d_topk_w);
+  MOE_TRY(check_ptr16("dy", dy));
+  MOE_TRY(check_ptr16("y_perm", y_perm));
+  MOE_TRY(check_ptr16("d_out_perm", d_out_perm));
+  return hip_status(moe::launch_combine_backward(dy, y_perm, dest, topk_w, T, k, d, dtype,
+                                                 d_out_perm, d_topk_w, stream),
+                    "moe_combine_backward launch");
+}
+
+int moe_expert_down_backward(const void* d_out_perm, const int32_t* offsets, int32_t E,
+                             int64_t rows_max, int64_t d, int64_t d_ff, const void* w2,
+                             const void* z, int32_t dtype, void* dz, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_ffn(d_out_perm, offsets, E, rows_max, d, d_ff, w2, dtype, dz));
+  MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
+  MOE_TRY(check_bwd_limits(rows_max, d, d_ff, dtype));
+  if (rows_max == 0) return MOE_OK;
+  MOE_NONNULL(z);
+  MOE_TRY(check_ptr16("z", z));
+  return hip_status(moe::launch_down_backward(d_out_perm, offsets, E, rows_max, d, d_ff, w2, z,
+                                              dtype, dz, workspace, stream),
+                    "moe_expert_down_backward launch");
+}
+
+int moe_expert_up_backward(const void* dz, const int32_t* offsets, int32_t E, int64_t rows_max,
+                           int64_t d, int64_t d_ff, const void* w1, int32_t dtype, float* dx_perm,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_ffn(dz, offsets, E, rows_max, d, d_ff, w1, dtype, dx_perm));
+  MOE_TRY(check_ffn_ws(dtype, workspace, workspace_bytes));
+  MOE_TRY(check_bwd_limits(rows_max, d, d_ff, dtype));
+  return hip_status(moe::launch_up_backward(dz, offsets, E, rows_max, d, d_ff, w1, dtype, dx_perm,
+                                            workspace, stream),
+                    "moe_expert_up_backward launch");
+}
+
+int moe_expert_weight_grads(const void* x_perm, const void* h, const void* d_out_perm,
+                            const void* dz, const int32_t* offsets, int32_t E, int64_t rows_max,
+                            int64_t d, int64_t d_ff, int32_t dtype, float* dw1, float* dw2,
+                            hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, MOE_MAX_E);
+  if (rows_max < 0 || d <= 0 || d_ff <= 0)
+    return fail(MOE_ERR_ARG, "need rows_max >= 0, d > 0, d_ff > 0");
+  if (d > (1 << 22) || d_ff > (1 << 22) || rows_max > 0x7fffffffLL)
+    return fail(MOE_ERR_SHAPE, "d and d_ff must be <= 2^22 and rows_max < 2^31");
+  MOE_TRY(check_row("d", d, dtype));
+  MOE_TRY(check_row("d_ff", d_ff, dtype));
+  MOE_TRY(check_bwd_limits(rows_max, d, d_ff, dtype));
+  MOE_NONNULL(offsets);
+  if (dw1 != nullptr) {
+    MOE_NONNULL(dz);
+    MOE_NONNULL(x_perm);
+    MOE_TRY(check_ptr16("dz", dz));
+    MOE_TRY(check_ptr16("x_perm", x_perm));
+    MOE_TRY(check_ptr16("dw1", dw1));
+  }
+  if (dw2 != nullptr) {
+    MOE_NONNULL(d_out_perm);
+    MOE_NONNULL(h);
+    MOE_TRY(check_ptr16("d_out_perm", d_out_perm));
+    MOE_TRY(check_ptr16("h", h));
+    MOE_TRY(check_ptr16("dw2", dw2));
+  }
+  if (dw2 != nullptr)
+    MOE_TRY(hip_status(moe::launch_expert_dw2(d_out_perm, h, offsets, E, d, d_ff, dtype, dw2, stream),
+                       "moe_expert_weight_grads dW2 launch"));
+  if (dw1 != nullptr)
+    MOE_TRY(hip_status(moe::launch_expert_dw1(dz, x_perm, offsets, E, d, d_ff, dtype, dw1, stream),
+                       "moe_expert_weight_grads dW1 launch"));
+  return MOE_OK;
+}
+
+int moe_gate_backward(const float* d_topk_w, const int32_t* topk_idx, const float* topk_w,
+                      const float* probs, const int32_t* counts, const float* lse, int64_t T,
+                      int32_t E, int32_t k, uint32_t flags, float temperature, float alpha,
+                      float aux_grad, float z_coeff, float* d_logits, hipStream_t stream) {
+  MOE_TRY(check_experts(E, k));
+  if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
+  if (!(temperature > 0.0f) || !std::isfinite(temperature))
+    return fail(MOE_ERR_ARG, "temperature must be finite and > 0");
+  if (!std::isfinite(alpha) || !std::isfinite(aux_grad) || !std::isfinite(z_coeff))
+    return fail(MOE_ERR_ARG, "alpha, aux_grad and z_coeff must be finite");
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(d_topk_w);
+  MOE_NONNULL(topk_idx);
+  MOE_NONNULL(probs);
+  MOE_NONNULL(counts);
+  MOE_NONNULL(d_logits);
+  if (flags & MOE_RENORM) MOE_NONNULL(topk_w);
+  if (z_coeff != 0.0f) MOE_NONNULL(lse);
+  return hip_status(moe::launch_gate_backward(d_topk_w, topk_idx, topk_w, probs, counts, lse, T,
+                                              E, k, (flags & MOE_RENORM) != 0, temperature, alpha,
+                                              aux_grad, z_coeff, d_logits, stream),
+                    "moe_gate_backward launch");
+}
+
+size_t moe_gate_weight_grads_workspace_bytes(int64_t T, int64_t d, int32_t E) {
+  if (T < 0 || d <= 0 || E < 1) return 0;
+  return moe::gate_wgrad_ws_floats(T, d, E) * sizeof(float);
+}
+
+int moe_gate_weight_grads(const float* d_logits, const void* x, int64_t T, int64_t d, int32_t E,
+                          int32_t dtype, float* d_w_gate, float* d_bias, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, MOE_MAX_E);
+  if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
+  MOE_TRY(check_row("d", d, dtype));
+  MOE_NONNULL(d_w_gate);
+  MOE_TRY(check_ptr16("d_w_gate", d_w_gate));
+  if (T > 0) {
+    MOE_NONNULL(d_logits);
+    MOE_NONNULL(x);
+    MOE_TRY(check_ptr16("x", x));
+  }
+  const size_t need = moe_gate_weight_grads_workspace_bytes(T, d, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+  MOE_TRY(check_ptr16("workspace", workspace));
+  return hip_status(moe::launch_gate_wgrad(d_logits, x, T, d, E, dtype, d_w_gate, d_bias,
+                                           static_cast<float*>(workspace), stream),
+                    "moe_gate_weight_grads launch");
+}
+
+int moe_dispatch_backward(const float* dx_perm, const int32_t* dest, const float* d_logits,
+                          const void* w_gate, int64_t T, int32_t k, int64_t d, int32_t E,
+                          int32_t dtype, float* dx, hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  if (T < 0 || d <= 0 || k < 1 || k > MOE_MAX_K)
+    return fail(MOE_ERR_ARG, "need T >= 0, d > 0, 1 <= k <= %d", MOE_MAX_K);
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, MOE_MAX_E);
+  MOE_TRY(check_row("d", d, dtype));
+  if ((d_logits == nullptr) != (w_gate == nullptr))
+    return fail(MOE_ERR_ARG, "d_logits and w_gate are both given or both NULL");
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(dx_perm);
+  MOE_NONNULL(dest);
+  MOE_NONNULL(dx);
+  MOE_TRY(check_ptr16("dx_perm", dx_perm));
+  MOE_TRY(check_ptr16("dx", dx));
+  if (w_gate != nullptr) MOE_TRY(check_ptr16("w_gate", w_gate));
+  return hip_status(moe::launch_dispatch_backward(dx_perm, dest, d_logits, w_gate, T, k, d, E,
+                                                  dtype, dx, stream),
+                    "moe_dispatch_backward launch");
 }
 
 const char* moe_last_error(void) { return g_err; }

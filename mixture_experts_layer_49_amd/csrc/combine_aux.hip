@@ -78,6 +78,8 @@ constexpr int kAuxThreads = 256;
 // Partial column sums: workgroup b takes tokens [b*chunk, (b+1)*chunk); thread
 // (e = tid % E, g = tid / E) sums tokens t = g, g + G, ... of the chunk; the
 // G per-thread sums are then added in g order. Fixed order -> deterministic.
+// SQUARE: sums of squares (the z-loss).
+template <bool SQUARE>
 __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float* __restrict__ probs,
                                                                   int64_t T, int E, int64_t chunk,
                                                                   double* __restrict__ part) {
@@ -89,7 +91,10 @@ __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float* _
   const int64_t t1 = min(t0 + chunk, T);
   double acc = 0.0;
   if (g < G)
-    for (int64_t t = t0 + g; t < t1; t += G) acc += static_cast<double>(probs[t * E + e]);
+    for (int64_t t = t0 + g; t < t1; t += G) {
+      const double v = static_cast<double>(probs[t * E + e]);
+      acc += SQUARE ? v * v : v;
+    }
   s[tid] = acc;
   __syncthreads();
   if (tid < E) {
@@ -135,8 +140,8 @@ __global__ __launch_bounds__(kMaxE) void aux_final_kernel(const double* __restri
   if (e == 0) loss[0] = static_cast<float>(static_cast<double>(alpha) * E * s[0]);
 }
 
-// Router z-loss: the per-block partial sums of zsq come from
-// aux_partial_kernel with E = 1; this adds them in block order.
+// Router z-loss: the per-block partial sums of lse^2 come from
+// aux_partial_kernel<true> with E = 1; this adds them in block order.
 __global__ __launch_bounds__(kMaxE) void z_final_kernel(const double* __restrict__ part,
                                                         int nblocks, int64_t T, float coeff,
                                                         float* __restrict__ loss) {
@@ -181,7 +186,7 @@ hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T,
   if (T > 0) {
     const int64_t chunk = (T + kAuxBlocks - 1) / kAuxBlocks;
     nblocks = static_cast<int>((T + chunk - 1) / chunk);
-    hipLaunchKernelGGL(aux_partial_kernel, dim3(nblocks), dim3(kAuxThreads), 0, s, probs, T, E,
+    hipLaunchKernelGGL(aux_partial_kernel<false>, dim3(nblocks), dim3(kAuxThreads), 0, s, probs, T, E,
                        chunk, ws);
   }
   hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(kMaxE), 0, s, ws, nblocks, counts, T, E, k,
@@ -194,13 +199,13 @@ size_t z_ws_doubles(int64_t T) {
   return static_cast<size_t>(kAuxBlocks);
 }
 
-hipError_t launch_z_loss(const float* zsq, int64_t T, float coeff, float* loss, double* ws,
+hipError_t launch_z_loss(const float* lse, int64_t T, float coeff, float* loss, double* ws,
                          hipStream_t s) {
   int nblocks = 0;
   if (T > 0) {
     const int64_t chunk = (T + kAuxBlocks - 1) / kAuxBlocks;
     nblocks = static_cast<int>((T + chunk - 1) / chunk);
-    hipLaunchKernelGGL(aux_partial_kernel, dim3(nblocks), dim3(kAuxThreads), 0, s, zsq, T, 1,
+    hipLaunchKernelGGL(aux_partial_kernel<true>, dim3(nblocks), dim3(kAuxThreads), 0, s, lse, T, 1,
                        chunk, ws);
   }
   hipLaunchKernelGGL(z_final_kernel, dim3(1), dim3(kMaxE), 0, s, ws, nblocks, T, coeff, loss);

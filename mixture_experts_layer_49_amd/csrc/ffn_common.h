@@ -65,11 +65,30 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z / (1.0f + __expf(-2.0f * u));
 }
 
+// d/dz gelu_tanh(z) = s (1 + 2 z (1 - s) u'), s = sigmoid(2u) = (1 + tanh u) / 2,
+// u' = sqrt(2/pi)(1 + 3 * 0.044715 z^2).
+__device__ __forceinline__ float gelu_tanh_grad(float z) {
+  const float c = 0.7978845608028654f;
+  const float u = c * fmaf(0.044715f * z, z * z, z);
+  const float s = 1.0f / (1.0f + __expf(-2.0f * u));
+  const float du = c * fmaf(3.0f * 0.044715f * z, z, 1.0f);
+  return s * fmaf(2.0f * z * (1.0f - s), du, 1.0f);
+}
+
 // The same function with hardware exp2 and reciprocal (about 1e-6 relative
 // error), for results that are rounded to 16-bit floats anyway.
 __device__ __forceinline__ float gelu_tanh_fast(float z) {
   const float u = 0.7978845608028654f * fmaf(0.044715f * z, z * z, z);
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+}
+
+// gelu_tanh_grad with hardware exp2 and reciprocal.
+__device__ __forceinline__ float gelu_tanh_grad_fast(float z) {
+  const float c = 0.7978845608028654f;
+  const float u = c * fmaf(0.044715f * z, z * z, z);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+  const float du = c * fmaf(3.0f * 0.044715f * z, z, 1.0f);
+  return s * fmaf(2.0f * z * (1.0f - s), du, 1.0f);
 }
 
 // Two bf16 values (one 32-bit word) -> two IEEE fp16 values, round to nearest
@@ -83,6 +102,19 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
   return uint4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
                bf16x2_to_f16x2(v.w)};
+}
+
+// Two fp16 values -> two bf16 values, round to nearest even.
+__device__ __forceinline__ uint32_t f16x2_to_bf16x2(uint32_t v) {
+  const f16x2 h = __builtin_bit_cast(f16x2, v);
+  const bf16x2 b = {static_cast<__bf16>(static_cast<float>(h[0])),
+                    static_cast<__bf16>(static_cast<float>(h[1]))};
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ uint4 f16x8_to_bf16x8(uint4 v) {
+  return uint4{f16x2_to_bf16x2(v.x), f16x2_to_bf16x2(v.y), f16x2_to_bf16x2(v.z),
+               f16x2_to_bf16x2(v.w)};
 }
 
 }  // namespace ffn

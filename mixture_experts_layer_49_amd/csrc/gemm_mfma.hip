@@ -1,22 +1,30 @@
-// Segmented bf16/fp16 MFMA GEMM for the grouped expert FFN on gfx950.
+// Segmented bf16/fp16 MFMA GEMM for the grouped expert FFN on gfx950, forward
+// and backward.
 //
-// C[m, n] = sum_k A[m, k] B[n, k] over the expert-major row segments given by
-// offsets[] (A and B K-contiguous):
-//   up:   A = x_perm [R, d] bf16, B = W1[e] [d_ff, d] bf16 -> h = fp16(gelu_tanh(C))
+// Row-segmented kinds: C[m, n] = sum_k A[m, k] B_e(n, k) over the expert-major
+// row segments given by offsets[] (A K-contiguous):
+//   up:   A = x_perm [R, d] bf16, B = W1[e] [d_ff, d] bf16 -> h = fp16(gelu_tanh(C)),
+//         optionally also the pre-activation z = fp16(C) for the backward
 //   down: A = h [R, d_ff] fp16,   B = W2[e] [d, d_ff] bf16 (-> fp16) -> y_perm = C (f32)
+//   dh:   A = do [R, d] bf16,     B = W2[e] read as [d][d_ff] (k-major) -> dz = bf16(C gelu'(z))
+//   dx:   A = dz [R, d_ff] bf16,  B = W1[e] read as [d_ff][d] (k-major) -> dx_perm = C (f32)
+// K-segmented kinds (weight gradients): C_e[m, n] = sum over the rows r of
+// expert e of A[r, m] B[r, n], both operands k-major:
+//   dW2:  A = do [R, d] bf16, B = h [R, d_ff] fp16 (-> bf16) -> dW2 [E, d, d_ff] f32
+//   dW1:  A = dz [R, d_ff] bf16, B = x_perm [R, d] bf16      -> dW1 [E, d_ff, d] f32
 // (ETP page "ETP专家并行加速MoE模型": up-projection w1, down-projection w2;
-// EP tutorial "专家并行：混合专家模型的分布式训练方案", 2.1 step 4.)
+// EP tutorial "专家并行：混合专家模型的分布式训练方案", 2.1 step 4; the
+// backward is the same chain taken in reverse.)
 //
 // Shape of the work: 256x256 output tiles, 4 waves in a 2x2 grid, each wave
 // 128x128 = 4x4 v_mfma_f32_32x32x16_{bf16,f16} tiles with its 256
 // accumulators in AGPRs. K advances 64 at a time through two 64 KiB LDS
 // stages:
 //   * stages are fetched with buffer_load_dwordx4 ... lds: the data goes
-//     HBM/L2 -> LDS without touching VGPRs, and every row of a stage is one
-//     whole 128-byte line (half-line rows would double the L2 -> CU traffic).
-//     In the down-projection W2 lands in LDS as bf16 and each wave converts
-//     its B fragments to fp16 (exactly) in registers, interleaved with the
-//     MFMAs of the previous k-slice;
+//     HBM/L2 -> LDS without touching VGPRs, and every row of a stage is whole
+//     128-byte lines (half-line rows would double the L2 -> CU traffic). A
+//     16-bit operand of the other float format is converted in registers,
+//     interleaved with the MFMAs of the previous k-slice;
 //   * the two stages are two separate LDS variables, addressed with
 //     compile-time slot numbers (the stage loop is unrolled by two), so the
 //     compiler can see that reading one stage never aliases the DMA still
@@ -26,21 +34,31 @@
 //     then the next stage has landed and every wave holds the last slice's
 //     fragments, so the stage two ahead is issued into the freed slot and the
 //     next stage's first fragments are read while the fourth slice's MFMAs run;
-//   * LDS layout: a tile row is 8 chunks of 16 B; logical chunk c of row r
-//     sits at chunk c ^ ((r >> 1) & 7). A fragment read touches 16 consecutive
-//     rows at one logical chunk per LDS cycle, which this spreads over all 64
-//     banks.
+//   * K-contiguous operand in LDS: a tile row is 8 chunks of 16 B; logical
+//     chunk c of row r sits at chunk c ^ ((r >> 1) & 7). A fragment read
+//     touches 16 consecutive rows at one logical chunk per LDS cycle, which
+//     this spreads over all 64 banks;
+//   * k-major operand (stored [K][M or N]) in LDS: 64 k-rows of 256 values;
+//     each wave-wide DMA load fills 1 KiB = two k-rows, in which the 16-B
+//     chunk (row bit rb, column half h, 32-column block ib, chunk j) sits at
+//     slot 16 ib + 4 ((2 h + rb) ^ 2 p) + j, p = bit 1 of the row. Fragments
+//     come out with ds_read_b64_tr_b16, which hands each lane four k-values
+//     of one column: one read covers four k-rows, which this layout puts on
+//     distinct banks, and the 32-column blocks sit 256 B apart, so every read
+//     of a slice is one lane address plus a constant.
 // Epilogue: accumulators go through the freed LDS stage so that the outputs
 // leave in whole rows, 16 B per lane, while the next tile's first stage
 // streams into the other one.
 // Persistent: one workgroup per CU walks the tile list that it derives on the
-// device from offsets[] (no host read-back). The list (expert, n-panel,
-// m-tile order) is cut into eight contiguous ranges, one per XCD, so an XCD
-// owns one or a few experts: their weights and rows come from HBM about once
-// and are reused from that XCD's L2, and within the XCD the workgroups take
-// consecutive tiles, i.e. the m-tiles of the same weight panel. When the last
-// round of an XCD has fewer tiles than workgroups, those tiles are split
-// along K over the idle workgroups (needs the workspace; see the epilogue).
+// device from offsets[] (no host read-back). The list is cut into eight
+// contiguous ranges, one per XCD, so an XCD owns one or a few experts: their
+// weights and rows come from HBM about once and are reused from that XCD's
+// L2, and within the XCD the workgroups take consecutive tiles. Row-segmented
+// lists run expert, n-panel, m-tile and are cut into equal tile counts; when
+// the last round of an XCD has fewer tiles than workgroups, those tiles are
+// split along K over the idle workgroups (needs the workspace; see the
+// epilogue). K-segmented lists run expert, m-tile, n-tile and are cut into
+// equal shares of k-steps, since an expert's tiles cost its row count.
 #include "ffn_common.h"
 
 namespace moe {
@@ -49,6 +67,8 @@ namespace {
 using namespace ffn;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int BM = 256, BN = 256, BK = 64, NS = 2;
 constexpr int kThreads = 256;
@@ -60,9 +80,12 @@ constexpr int kRowsPerLoad = kWave / kCpr;              // rows per wave-wide 16
 constexpr int kLoadsA = BM / kRowsPerLoad / kWaves;     // LDS-DMA loads per wave per stage (8)
 constexpr int kLoadsB = BN / kRowsPerLoad / kWaves;
 constexpr int kStage = (BM + BN) * kCpr;                // uint4 per stage (64 KiB)
+constexpr uint32_t kBRegion = BM * kCpr * 16;           // byte offset of the B half of a stage
 static_assert(NS == 2 && BK == 64 && kWaves % 2 == 0, "the pipeline below assumes these");
+static_assert(BM == 256 && BN == 256, "the k-major LDS layout assumes 256-wide tiles");
 constexpr size_t kPartBytes = static_cast<size_t>(BM) * BN * sizeof(float);   // one split partial
 constexpr int kMaxSplit = 8;
+constexpr int kEpiCost = 4;   // epilogue of a tile, in k-steps (K-segmented load balance)
 
 #define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 #define MOE_BARRIER()                                       \
@@ -72,46 +95,144 @@ constexpr int kMaxSplit = 8;
     asm volatile("" ::: "memory");                          \
   } while (0)
 
+enum Cvt { kCvtNone, kCvtBf16ToF16, kCvtF16ToBf16 };
+enum Epi { kEpiGelu, kEpiF32, kEpiDGelu };
+
+// One kind of product: operand layouts (k-major = stored [K][M or N]), the
+// tile list (row- or K-segmented), the MFMA input type, the conversion of B
+// and the epilogue.
+template <bool A_KM, bool B_KM, bool SEG_K, bool F16, int CVT_B, int EPI, bool SAVE_Z>
+struct GemmOp {
+  static constexpr bool kAKM = A_KM, kBKM = B_KM, kSegK = SEG_K, kF16 = F16, kSaveZ = SAVE_Z;
+  static constexpr int kCvt = CVT_B, kEpi = EPI;
+};
+using OpUp = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, false>;
+using OpUpZ = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, true>;
+using OpDown = GemmOp<false, false, false, true, kCvtBf16ToF16, kEpiF32, false>;
+using OpDh = GemmOp<false, true, false, false, kCvtNone, kEpiDGelu, false>;
+using OpDx = GemmOp<false, true, false, false, kCvtNone, kEpiF32, false>;
+using OpDw2 = GemmOp<true, true, true, false, kCvtF16ToBf16, kEpiF32, false>;
+using OpDw1 = GemmOp<true, true, true, false, kCvtNone, kEpiF32, false>;
+
 struct Ctx {
   __amdgpu_buffer_rsrc_t a, b;
-  int m0, n0, seg1;
+  int m0, n0, seg1, e;
 };
 
-template <bool UP>
+// Four consecutive k-values of one column from the k-major LDS tile (see the
+// layout above); `p` is this lane's address.
+__device__ __forceinline__ uint2 ds_read_tr(const char* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Byte offset, within a k-major operand's half of a stage, of the 8 bytes
+// this lane gives to ds_read_b64_tr_b16 for k-slice 0, first k-quad, column
+// block 0 of column half `hx`. Lane l = 16 g + s reads k-row
+// 8 (g >> 1) + (s >> 2) at columns 128 hx + 16 (g & 1) + 4 (s & 3) .. +3, so
+// that after the transpose lane l holds column l % 32 at k-rows
+// 8 (l / 32) .. +3, the MFMA operand layout. Slice kk, quad h2 and block ib
+// add 8192 kk + 2048 h2 + 256 ib.
+__device__ __forceinline__ uint32_t kmajor_lane_offset(int lane, int hx) {
+  const int g = lane >> 4, s = lane & 15;
+  const int blk = 4 * (g >> 1) + (s >> 3);
+  const int rb = (s >> 2) & 1, p = (s >> 3) & 1;
+  const int slot = 4 * ((2 * hx + rb) ^ (2 * p)) + 2 * (g & 1) + ((s & 3) >> 1);
+  return static_cast<uint32_t>(blk * 1024 + slot * 16 + (s & 1) * 8);
+}
+
+// Per-lane global byte offset of a wave-wide LDS-DMA load of a k-major
+// operand: lane L lands at slot L of the 1 KiB block, i.e. k-row rb of the
+// block's two, logical chunk 16 h + 4 ib + j (see the layout above); p is bit
+// 1 of the block's first k-row, the parity of the block index.
+__device__ __forceinline__ uint32_t kmajor_dma_offset(int lane, int p, uint32_t row_bytes) {
+  const int ib = lane >> 4, f = (lane >> 2) & 3, j = lane & 3;
+  const int g2 = f ^ (2 * p);
+  const int h = g2 >> 1, rb = g2 & 1;
+  return static_cast<uint32_t>(rb) * row_bytes + static_cast<uint32_t>(16 * h + 4 * ib + j) * 16u;
+}
+
+// K-segmented lists: k-steps of expert e, rounded up to the even count the
+// stage pairs need (two all-zero stages for an expert with no rows).
+__device__ __forceinline__ int seg_k_steps(const int* s_off, int e) {
+  const int nk = (s_off[e + 1] - s_off[e] + BK - 1) / BK;
+  return max(2, (nk + 1) & ~1);
+}
+
+template <class Op>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int N, int K,
-    const uint16_t* __restrict__ B, void* __restrict__ Cout, float* __restrict__ part,
-    int* __restrict__ cnt, int max_split) {
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int M, int N,
+    int K, const uint16_t* __restrict__ B, void* __restrict__ Cout, uint16_t* __restrict__ Z,
+    float* __restrict__ part, int* __restrict__ cnt, int max_split) {
+  constexpr bool AKM = Op::kAKM, BKM = Op::kBKM, SEGK = Op::kSegK, F16 = Op::kF16;
+  constexpr int CVT = Op::kCvt, EPI = Op::kEpi;
+  // Both operands K-contiguous: chunks past K hold the next row's values and
+  // are zeroed; a k-major operand reads zeros past K (the buffer ends there),
+  // which cancels whatever finite values the other operand holds.
+  constexpr bool ZERO_TAIL = !AKM && !BKM;
   __shared__ uint4 st0[kStage];
   __shared__ uint4 st1[kStage];
   __shared__ int s_pref[kMaxE + 1];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_tmp[kMaxE];
+  __shared__ long long s_cost[SEGK ? kMaxE + 1 : 1];
   __shared__ int s_ticket;
   uint4* const L[NS] = {st0, st1};
+  const int tid = threadIdx.x;
 
-  for (int e = threadIdx.x; e <= E; e += kThreads) s_off[e] = offsets[e];
-  build_tile_prefix(offsets, E, BM, s_pref, s_tmp);
+  for (int e = tid; e <= E; e += kThreads) s_off[e] = offsets[e];
+  if constexpr (!SEGK) build_tile_prefix(offsets, E, BM, s_pref, s_tmp);
   const int tiles_n = (N + BN - 1) / BN;
-  const int nk = (K + BK - 1) / BK;
+  const int tiles_m = SEGK ? (M + BM - 1) / BM : 0;
+  const int tpe = tiles_m * tiles_n;   // K-segmented: tiles per expert
+  const int nk = SEGK ? 0 : (K + BK - 1) / BK;
   const int nk2 = (nk + 1) & ~1;     // stages run in pairs; a padding stage is all zeros
-  const int kz = K / BK;             // first stage with columns past K
-  // The tile list is cut into 8 equal contiguous ranges, one per XCD
-  // (workgroup b runs on XCD b % 8); the XCD's P workgroups take the range's
-  // tiles round-robin. A range covers one or a few experts, so each XCD
-  // streams its experts' weights and rows from HBM about once and reuses them
-  // in its own L2. When the last round has fewer tiles than workgroups
-  // (rem < P), each of those tiles is split into S k-ranges so the round
-  // keeps every workgroup busy; the split partial sums meet in `part`.
-  const int64_t total =
-      static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pref[E])) * tiles_n;
+  const int kz = ZERO_TAIL ? K / BK : 0x7fffffff;   // first stage with columns past K
   const int P = gridDim.x >> 3;   // the grid is a multiple of 8
   const int xcd = blockIdx.x & 7, w = blockIdx.x >> 3;
-  const int64_t r_beg = total * xcd / 8, n_x = total * (xcd + 1) / 8 - r_beg;
+  // Row-segmented: the tile list is cut into 8 equal contiguous ranges, one
+  // per XCD (workgroup b runs on XCD b % 8); the XCD's P workgroups take the
+  // range's tiles round-robin. When the last round has fewer tiles than
+  // workgroups (rem < P), each of those tiles is split into S k-ranges so the
+  // round keeps every workgroup busy; the split partial sums meet in `part`.
+  // K-segmented: the 8 ranges hold equal shares of k-steps.
+  int64_t r_beg, n_x;
+  if constexpr (SEGK) {
+    __syncthreads();
+    if (tid == 0) {
+      long long c = 0;
+      for (int e = 0; e < E; ++e) {
+        s_cost[e] = c;
+        c += static_cast<long long>(tpe) * (seg_k_steps(s_off, e) + kEpiCost);
+      }
+      s_cost[E] = c;
+    }
+    __syncthreads();
+    const long long tot = s_cost[E];
+    // First tile whose cumulative cost reaches c.
+    auto tile_at = [&](long long c) -> int64_t {
+      if (c >= tot) return static_cast<int64_t>(E) * tpe;
+      int lo = 0, hi = E;   // largest e with s_cost[e] <= c
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_cost[mid] <= c) lo = mid;
+        else hi = mid;
+      }
+      const long long per = seg_k_steps(s_off, lo) + kEpiCost;
+      return static_cast<int64_t>(lo) * tpe + (c - s_cost[lo] + per - 1) / per;
+    };
+    r_beg = tile_at(tot * xcd / 8);
+    n_x = tile_at(tot * (xcd + 1) / 8) - r_beg;
+  } else {
+    const int64_t total =
+        static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pref[E])) * tiles_n;
+    r_beg = total * xcd / 8;
+    n_x = total * (xcd + 1) / 8 - r_beg;
+  }
   const int64_t full = n_x / P;
   const int rem = static_cast<int>(n_x - full * P);
   int S = 1;
-  if (rem > 0 && max_split > 1) S = max(1, min(min(P / rem, max_split), nk2 / 8));
+  if (!SEGK && rem > 0 && max_split > 1) S = max(1, min(min(P / rem, max_split), nk2 / 8));
   const int64_t n_units = full + (w < rem * S ? 1 : 0);
   if (n_units == 0) return;
   // Unit q of this workgroup: a whole tile of round q, or (q == full) its
@@ -125,7 +246,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     if (q < full || S == 1) {
       u.tile = r_beg + w + q * P;
       u.klo = 0;
-      u.khi = nk2;
+      if constexpr (SEGK)
+        u.khi = seg_k_steps(s_off, __builtin_amdgcn_readfirstlane(static_cast<int>(u.tile / tpe)));
+      else
+        u.khi = nk2;
       u.tail = -1;
     } else {
       const int tr = w % rem, si = w / rem, np = nk2 / 2;
@@ -137,50 +261,89 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     return u;
   };
 
-  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hl = lane >> 5;
-  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
+  // Row pitch of each operand in global memory.
+  const uint32_t a_rb = static_cast<uint32_t>(AKM ? M : K) * 2u;
+  const uint32_t b_rb = static_cast<uint32_t>(BKM ? N : K) * 2u;
 
-  // LDS-DMA: wave-wide load j of wave w fills the 8 rows from 8 (4j + w); lane
-  // l lands in row + l/8 at physical chunk l%8 and fetches logical chunk
-  // (l%8) ^ ((row >> 1) & 7) = (l%8) ^ (4 (w & 1) + l/16).
-  const uint32_t ld_voff = (lane >> 3) * row_bytes + (((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16u);
+  // LDS-DMA, K-contiguous operand: wave-wide load j of wave w fills the 8 rows
+  // from 8 (4j + w); lane l lands in row + l/8 at physical chunk l%8 and
+  // fetches logical chunk (l%8) ^ ((row >> 1) & 7) = (l%8) ^ (4 (w & 1) + l/16).
+  // k-major operand: load j of wave w fills k-rows 2 (4j + w) and the next.
+  auto dma_voff = [&](bool kmaj, uint32_t rb) -> uint32_t {
+    if (kmaj) return kmajor_dma_offset(lane, wave & 1, rb);
+    return (lane >> 3) * rb + (((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16u);
+  };
+  const uint32_t ld_voff_a = dma_voff(AKM, a_rb);
+  const uint32_t ld_voff_b = dma_voff(BKM, b_rb);
   const int fr_a = (wm * (BM / WM) + l32) * kCpr;
   const int fr_b = BM * kCpr + (wn * (BN / WN) + l32) * kCpr;
   const int fr_x = hl ^ ((l32 >> 1) & 7);   // chunk (2 kk + hl) sits at (2 kk) ^ fr_x
+  const uint32_t tr_a = kmajor_lane_offset(lane, wm);
+  const uint32_t tr_b = kBRegion + kmajor_lane_offset(lane, wn);
 
   auto make_ctx = [&](int64_t tile_id, Ctx& c) {
     // Every lane computes the same tile; readfirstlane makes that visible to
     // the compiler, so the buffer resources live in SGPRs (a resource in VGPRs
     // would turn each LDS-DMA load into a waterfall loop).
-    const Tile tl = find_tile(s_pref, E, tiles_n, tile_id);
-    const int te = __builtin_amdgcn_readfirstlane(tl.e);
-    c.seg1 = __builtin_amdgcn_readfirstlane(s_off[te + 1]);
-    c.m0 = __builtin_amdgcn_readfirstlane(s_off[te] + tl.mi * BM);
-    c.n0 = __builtin_amdgcn_readfirstlane(tl.nt * BN);
-    const int a_rows = min(c.seg1 - c.m0, BM), b_rows = min(N - c.n0, BN);
-    c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A + static_cast<int64_t>(c.m0) * K),
-                                            0, static_cast<int>(a_rows * row_bytes), 0x00020000);
-    c.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B + (static_cast<int64_t>(te) * N + c.n0) * K), 0,
-                                            static_cast<int>(b_rows * row_bytes), 0x00020000);
+    if constexpr (SEGK) {
+      const int te = __builtin_amdgcn_readfirstlane(static_cast<int>(tile_id / tpe));
+      const int local = static_cast<int>(tile_id - static_cast<int64_t>(te) * tpe);
+      const int r0 = __builtin_amdgcn_readfirstlane(s_off[te]);
+      const int rows = __builtin_amdgcn_readfirstlane(s_off[te + 1]) - r0;
+      c.e = te;
+      c.seg1 = M;
+      c.m0 = __builtin_amdgcn_readfirstlane((local / tiles_n) * BM);
+      c.n0 = __builtin_amdgcn_readfirstlane((local % tiles_n) * BN);
+      const int64_t na = max<int64_t>(0, static_cast<int64_t>(rows) * M - c.m0);
+      const int64_t nb = max<int64_t>(0, static_cast<int64_t>(rows) * N - c.n0);
+      c.a = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(A + static_cast<int64_t>(r0) * M + c.m0), 0, static_cast<int>(na * 2), 0x00020000);
+      c.b = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(B + static_cast<int64_t>(r0) * N + c.n0), 0, static_cast<int>(nb * 2), 0x00020000);
+    } else {
+      const Tile tl = find_tile(s_pref, E, tiles_n, tile_id);
+      const int te = __builtin_amdgcn_readfirstlane(tl.e);
+      c.e = te;
+      c.seg1 = __builtin_amdgcn_readfirstlane(s_off[te + 1]);
+      c.m0 = __builtin_amdgcn_readfirstlane(s_off[te] + tl.mi * BM);
+      c.n0 = __builtin_amdgcn_readfirstlane(tl.nt * BN);
+      const int a_rows = min(c.seg1 - c.m0, BM);
+      c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A + static_cast<int64_t>(c.m0) * K),
+                                              0, static_cast<int>(a_rows * a_rb), 0x00020000);
+      if constexpr (BKM) {
+        // B_e is [K][N]: the tile's columns start at n0 of every k-row; the
+        // buffer ends after k-row K - 1.
+        const int64_t nb = static_cast<int64_t>(K) * N - c.n0;
+        c.b = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(B + static_cast<int64_t>(te) * K * N + c.n0), 0, static_cast<int>(nb * 2), 0x00020000);
+      } else {
+        const int b_rows = min(N - c.n0, BN);
+        c.b = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(B + (static_cast<int64_t>(te) * N + c.n0) * K), 0,
+            static_cast<int>(b_rows * b_rb), 0x00020000);
+      }
+    }
   };
 
   auto issue = [&](const Ctx& c, int kt, int S) {
     uint4* const dst = L[S];
-    const uint32_t kb = static_cast<uint32_t>(kt) * BK * 2u;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
       const int blk = j * kWaves + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16, ld_voff,
-                                               blk * kRowsPerLoad * row_bytes + kb, 0, 0);
+      const uint32_t so = AKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * a_rb)
+                              : (blk * kRowsPerLoad * a_rb + static_cast<uint32_t>(kt) * BK * 2u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16, ld_voff_a, so, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
       const int blk = j * kWaves + wave;
+      const uint32_t so = BKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * b_rb)
+                              : (blk * kRowsPerLoad * b_rb + static_cast<uint32_t>(kt) * BK * 2u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(dst + BM * kCpr + blk * kWave), 16,
-                                               ld_voff, blk * kRowsPerLoad * row_bytes + kb, 0, 0);
+                                               ld_voff_b, so, 0, 0);
     }
   };
   // Zero the chunks of stage kt (slot S) that lie past K.
@@ -193,21 +356,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
 
   uint4 fa[2][MI], fb[2][NI];
   auto read_frags = [&](int S, int kk, int fs) {
-    // The lane term is made opaque here so that the bases are recomputed
-    // (three adds) rather than eight of them held across the loop.
+    // The lane terms are made opaque here so that the bases are recomputed
+    // (a few adds) rather than eight of them held across the loop.
     int x = fr_x;
     asm volatile("" : "+v"(x));
     const int c = x ^ (kk * 2);
     const int ab = fr_a + c, bb = fr_b + c;
+    const char* const base = reinterpret_cast<const char*>(L[S]);
+    if constexpr (AKM) {
+      uint32_t t = tr_a;
+      asm volatile("" : "+v"(t));
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[fs][i] = L[S][ab + i * 32 * kCpr];
+      for (int i = 0; i < MI; ++i) {
+        const char* p = base + t + kk * 8192 + i * 256;
+        const uint2 lo = ds_read_tr(p), hi = ds_read_tr(p + 2048);
+        fa[fs][i] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) fb[fs][j] = L[S][bb + j * 32 * kCpr];
+      for (int i = 0; i < MI; ++i) fa[fs][i] = L[S][ab + i * 32 * kCpr];
+    }
+    if constexpr (BKM) {
+      uint32_t t = tr_b;
+      asm volatile("" : "+v"(t));
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const char* p = base + t + kk * 8192 + j * 256;
+        const uint2 lo = ds_read_tr(p), hi = ds_read_tr(p + 2048);
+        fb[fs][j] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) fb[fs][j] = L[S][bb + j * 32 * kCpr];
+    }
   };
   auto conv_fb = [&](int fs) {
-    if (!UP) {
+    if constexpr (CVT == kCvtBf16ToF16) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) fb[fs][j] = bf16x8_to_f16x8(fb[fs][j]);
+    } else if constexpr (CVT == kCvtF16ToBf16) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) fb[fs][j] = f16x8_to_bf16x8(fb[fs][j]);
     }
   };
 
@@ -217,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        if (UP)
+        if constexpr (!F16)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, fa[fs][i]), __builtin_bit_cast(bf16x8, fb[fs][j]),
               acc[i][j], 0, 0, 0);
@@ -226,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
               __builtin_bit_cast(f16x8, fa[fs][i]), __builtin_bit_cast(f16x8, fb[fs][j]),
               acc[i][j], 0, 0, 0);
       }
-    if (!UP) {
+    if constexpr (CVT != kCvtNone) {
       conv_fb(cs);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
@@ -283,24 +472,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
 
   // Output of VPC consecutive values (row, col .. col+VPC-1) of the tile, given
-  // as floats: up-projection GELU -> fp16, down-projection f32; 16 B per store.
-  constexpr int VPC = UP ? 8 : 4;
-  auto emit = [&](int grow, int gcol, const float4& a, const float4& b) {
-    uint4 out;
-    if (UP) {
+  // as floats; 16 B per store. GELU -> fp16 (and the fp16 pre-activation);
+  // f32; or the GELU backward: bf16(value * gelu'(z)) with z read from Z.
+  constexpr int VPC = EPI == kEpiF32 ? 4 : 8;
+  auto emit = [&](int c_e, int grow, int gcol, const float4& a, const float4& b) {
+    const int64_t at = (SEGK ? static_cast<int64_t>(c_e) * M + grow : static_cast<int64_t>(grow)) * N + gcol;
+    if constexpr (EPI == kEpiGelu) {
       const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
       const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
       const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
       const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
-      out = uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                  __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Cout) + at) =
+          uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+      if constexpr (Op::kSaveZ) {
+        const f16x2 z0 = {static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)};
+        const f16x2 z1 = {static_cast<_Float16>(a.z), static_cast<_Float16>(a.w)};
+        const f16x2 z2 = {static_cast<_Float16>(b.x), static_cast<_Float16>(b.y)};
+        const f16x2 z3 = {static_cast<_Float16>(b.z), static_cast<_Float16>(b.w)};
+        *reinterpret_cast<uint4*>(Z + at) =
+            uint4{__builtin_bit_cast(uint32_t, z0), __builtin_bit_cast(uint32_t, z1),
+                  __builtin_bit_cast(uint32_t, z2), __builtin_bit_cast(uint32_t, z3)};
+      }
+    } else if constexpr (EPI == kEpiDGelu) {
+      const uint4 zr = *reinterpret_cast<const uint4*>(Z + at);
+      const f16x2 z0 = __builtin_bit_cast(f16x2, zr.x), z1 = __builtin_bit_cast(f16x2, zr.y);
+      const f16x2 z2 = __builtin_bit_cast(f16x2, zr.z), z3 = __builtin_bit_cast(f16x2, zr.w);
+      const bf16x2 q0 = {static_cast<__bf16>(a.x * gelu_tanh_grad_fast(static_cast<float>(z0[0]))),
+                         static_cast<__bf16>(a.y * gelu_tanh_grad_fast(static_cast<float>(z0[1])))};
+      const bf16x2 q1 = {static_cast<__bf16>(a.z * gelu_tanh_grad_fast(static_cast<float>(z1[0]))),
+                         static_cast<__bf16>(a.w * gelu_tanh_grad_fast(static_cast<float>(z1[1])))};
+      const bf16x2 q2 = {static_cast<__bf16>(b.x * gelu_tanh_grad_fast(static_cast<float>(z2[0]))),
+                         static_cast<__bf16>(b.y * gelu_tanh_grad_fast(static_cast<float>(z2[1])))};
+      const bf16x2 q3 = {static_cast<__bf16>(b.z * gelu_tanh_grad_fast(static_cast<float>(z3[0]))),
+                         static_cast<__bf16>(b.w * gelu_tanh_grad_fast(static_cast<float>(z3[1])))};
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Cout) + at) =
+          uint4{__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+                __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)};
     } else {
-      out = __builtin_bit_cast(uint4, a);
+      *reinterpret_cast<float4*>(static_cast<float*>(Cout) + at) = a;
     }
-    char* dst = static_cast<char*>(Cout) + (static_cast<int64_t>(grow) * N + gcol) * (UP ? 2 : 4);
-    *reinterpret_cast<uint4*>(dst) = out;
   };
-
   // Epilogue through LDS slot 1 in four passes of 64 rows: a pass first copies
   // the raw f32 accumulators of its rows into LDS (no arithmetic, so the 256
   // accumulators need no extra registers), then a compact loop reads them back
@@ -312,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   // A split tile then takes a ticket; the last of its S splits to arrive adds
   // the S partials up in split order (the sum does not depend on who arrives
   // last) and emits the tile.
-  auto epilogue = [&](int c_m0, int c_n0, int c_seg1, int tail) {
+  auto epilogue = [&](int c_m0, int c_n0, int c_seg1, int c_e, int tail) {
     float* const h0 = reinterpret_cast<float*>(st1);
     float* const h1 = reinterpret_cast<float*>(st1 + kStage / 2);
     float* const hw = wn == 0 ? h0 : h1;   // this wave's 128-column half
@@ -345,8 +557,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
           if (grow >= c_seg1 || gcol >= N) continue;
           const float* src = (col < 128 ? h0 : h1) + row * 128 + ((col & 127) ^ (((row >> 2) & 1) * 32));
           const float4 a = *reinterpret_cast<const float4*>(src);
-          const float4 b = UP ? *reinterpret_cast<const float4*>(src + 4) : a;
-          emit(grow, gcol, a, b);
+          const float4 b = VPC == 8 ? *reinterpret_cast<const float4*>(src + 4) : a;
+          emit(c_e, grow, gcol, a, b);
         }
       } else {
 #pragma unroll 1
@@ -377,18 +589,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       if (grow >= c_seg1 || gcol >= N) continue;
       const float* src = first + row * BN + col;
       float4 a = *reinterpret_cast<const float4*>(src);
-      float4 b = UP ? *reinterpret_cast<const float4*>(src + 4) : a;
+      float4 b = VPC == 8 ? *reinterpret_cast<const float4*>(src + 4) : a;
 #pragma unroll 1
       for (int si = 1; si < S; ++si) {
         src += step;
         const float4 a2 = *reinterpret_cast<const float4*>(src);
         a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-        if (UP) {
+        if (VPC == 8) {
           const float4 b2 = *reinterpret_cast<const float4*>(src + 4);
           b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
         }
       }
-      emit(grow, gcol, a, b);
+      emit(c_e, grow, gcol, a, b);
     }
   };
 
@@ -426,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
     // The last two stages (slots 0 and 1); slot 0, once free, takes the next
     // unit's first stage, slot 1 then stages this unit's outputs.
-    const int m0 = cur.m0, n0 = cur.n0, seg1 = cur.seg1, tail = u.tail;
+    const int m0 = cur.m0, n0 = cur.n0, seg1 = cur.seg1, te = cur.e, tail = u.tail;
     const bool has_next = q + 1 < n_units;
     slices012(0);
     MOE_WAIT_VM(0);
@@ -446,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     slice3();
 
     MOE_BARRIER();   // every wave is done reading slot 1
-    epilogue(m0, n0, seg1, tail);
+    epilogue(m0, n0, seg1, te, tail);
     if (!has_next) break;
     issue(cur, u.klo + 1, 1);
   }
@@ -460,6 +672,14 @@ __global__ void zero_ints_kernel(int* p, int n) {
 // One workgroup per CU, a multiple of 8 (one group per XCD).
 int ffn_mfma_grid() { return (device_cu_count() + 7) / 8 * 8; }
 
+template <class Op>
+void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int E, int M, int N,
+               int K, const void* B, void* C, void* Z, float* part, int* cnt, int max_split) {
+  hipLaunchKernelGGL(gemm_mfma_kernel<Op>, g, dim3(kThreads), 0, s, static_cast<const uint16_t*>(A),
+                     offsets, E, M, N, K, static_cast<const uint16_t*>(B), C,
+                     static_cast<uint16_t*>(Z), part, cnt, max_split);
+}
+
 }  // namespace
 
 size_t ffn_mfma_workspace_bytes() {
@@ -467,35 +687,48 @@ size_t ffn_mfma_workspace_bytes() {
   return g * kPartBytes + g * sizeof(int);
 }
 
-hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets, int E, int64_t rows_max,
-                           int N, int K, const void* B, void* C, void* ws, hipStream_t s) {
-  if (rows_max == 0) return hipSuccess;
-  const int64_t tiles_n = (N + BN - 1) / BN;
-  const int64_t upper = (rows_max / BM + E) * tiles_n;   // >= sum_e ceil(kept_e / BM) * tiles_n
+hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
+                            int64_t rows_max, int M, int N, int K, const void* B, void* C,
+                            void* Z, void* ws, hipStream_t s) {
+  const bool seg_k = kind == GemmKind::kDw2 || kind == GemmKind::kDw1;
   const int grid_max = ffn_mfma_grid();
-  // Split tiles need the workspace: G partial tiles, then one counter per
-  // workgroup slot, zeroed here (by a kernel, so the call can be captured).
+  int64_t g = grid_max;
   float* part = nullptr;
   int* cnt = nullptr;
   int max_split = 1;
-  if (ws != nullptr) {
-    part = static_cast<float*>(ws);
-    cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + static_cast<size_t>(grid_max) * kPartBytes);
-    max_split = kMaxSplit;
-    hipLaunchKernelGGL(zero_ints_kernel, dim3((grid_max + 255) / 256), dim3(256), 0, s, cnt, grid_max);
+  if (seg_k) {
+    // Every expert's M x N block is written, zeros for an expert with no rows.
+    const int64_t tiles = static_cast<int64_t>(E) * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles == 0) return hipSuccess;
+    if (tiles < g) g = (tiles + 7) / 8 * 8;
+  } else {
+    if (rows_max == 0) return hipSuccess;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t upper = (rows_max / BM + E) * tiles_n;   // >= sum_e ceil(kept_e / BM) * tiles_n
+    // Split tiles need the workspace: G partial tiles, then one counter per
+    // workgroup slot, zeroed here (by a kernel, so the call can be captured).
+    if (ws != nullptr) {
+      part = static_cast<float*>(ws);
+      cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + static_cast<size_t>(grid_max) * kPartBytes);
+      max_split = kMaxSplit;
+      hipLaunchKernelGGL(zero_ints_kernel, dim3((grid_max + 255) / 256), dim3(256), 0, s, cnt, grid_max);
+    }
+    // Without splitting, workgroups beyond the tile count would find no work;
+    // with it, a short list still spreads over every XCD's workgroups.
+    if (max_split == 1 && upper < g) g = (upper + 7) / 8 * 8;
   }
-  // Without splitting, workgroups beyond the tile count would find no work;
-  // with it, a short list still spreads over every XCD's workgroups.
-  int64_t g = grid_max;
-  if (max_split == 1 && upper < g) g = (upper + 7) / 8 * 8;
-  if (up)
-    hipLaunchKernelGGL(gemm_mfma_kernel<true>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
-                       s, static_cast<const uint16_t*>(A), offsets, E, N, K,
-                       static_cast<const uint16_t*>(B), C, part, cnt, max_split);
-  else
-    hipLaunchKernelGGL(gemm_mfma_kernel<false>, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0,
-                       s, static_cast<const uint16_t*>(A), offsets, E, N, K,
-                       static_cast<const uint16_t*>(B), C, part, cnt, max_split);
+  const dim3 grid(static_cast<unsigned>(g));
+  switch (kind) {
+    case GemmKind::kUp:
+      if (Z != nullptr) launch_op<OpUpZ>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split);
+      else launch_op<OpUp>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split);
+      break;
+    case GemmKind::kDown: launch_op<OpDown>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split); break;
+    case GemmKind::kDh: launch_op<OpDh>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split); break;
+    case GemmKind::kDx: launch_op<OpDx>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split); break;
+    case GemmKind::kDw2: launch_op<OpDw2>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, 1); break;
+    case GemmKind::kDw1: launch_op<OpDw1>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, 1); break;
+  }
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
                                                         const int32_t* __restrict__ offsets,
                                                         int E, int N, int K,
                                                         const float* __restrict__ B,
-                                                        float* __restrict__ C) {
+                                                        float* __restrict__ C,
+                                                        float* __restrict__ Z) {
   __shared__ float As[FK][FM + 4];
   __shared__ float Bs[FK][FN + 4];
   __shared__ int s_pref[kMaxE + 1];
@@ -78,7 +79,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = n0 + tx * 4 + j;
-        if (col < N) C[static_cast<int64_t>(row) * N + col] = UP ? gelu_tanh(acc[i][j]) : acc[i][j];
+        if (col >= N) continue;
+        C[static_cast<int64_t>(row) * N + col] = UP ? gelu_tanh(acc[i][j]) : acc[i][j];
+        if (UP && Z != nullptr) Z[static_cast<int64_t>(row) * N + col] = acc[i][j];
       }
     }
     __syncthreads();
@@ -87,32 +90,34 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
 
 template <bool UP>
 hipError_t launch_gemm(const void* A, const int32_t* offsets, int E, int64_t rows_max, int N,
-                       int K, const void* B, int dtype, void* C, void* ws, hipStream_t s) {
+                       int K, const void* B, int dtype, void* C, void* Z, void* ws, hipStream_t s) {
   if (rows_max == 0) return hipSuccess;
-  if (dtype == 1) return launch_ffn_mfma(UP, A, offsets, E, rows_max, N, K, B, C, ws, s);
+  if (dtype == 1)
+    return launch_gemm_mfma(UP ? GemmKind::kUp : GemmKind::kDown, A, offsets, E, rows_max, 0, N,
+                            K, B, C, Z, ws, s);
   const int64_t tiles_n = (N + FN - 1) / FN;
   int64_t g = (rows_max / FM + E) * tiles_n;
   if (g > 65535) g = 65535;
   hipLaunchKernelGGL(grouped_gemm_f32<UP>, dim3(static_cast<unsigned>(g)), dim3(256), 0, s,
                      static_cast<const float*>(A), offsets, E, N, K, static_cast<const float*>(B),
-                     static_cast<float*>(C));
+                     static_cast<float*>(C), static_cast<float*>(Z));
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,
-                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* ws,
-                          hipStream_t s) {
+                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* z,
+                          void* ws, hipStream_t s) {
   return launch_gemm<true>(x_perm, offsets, E, rows_max, static_cast<int>(d_ff),
-                           static_cast<int>(d), w1, dtype, h, ws, s);
+                           static_cast<int>(d), w1, dtype, h, z, ws, s);
 }
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
                        int64_t d_ff, const void* w2, int dtype, float* y_perm, void* ws,
                        hipStream_t s) {
   return launch_gemm<false>(h, offsets, E, rows_max, static_cast<int>(d), static_cast<int>(d_ff),
-                            w2, dtype, y_perm, ws, s);
+                            w2, dtype, y_perm, nullptr, ws, s);
 }
 
 size_t ffn_workspace_bytes(int dtype) { return dtype == 1 ? ffn_mfma_workspace_bytes() : 0; }

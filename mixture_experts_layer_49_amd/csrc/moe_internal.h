@@ -10,6 +10,7 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -43,7 +44,7 @@ struct RouterArgs {
   int32_t* topk_idx;
   float* topk_w;
   float* probs;         // nullable [T, E]
-  float* zsq;           // nullable [T]: (log sum_e exp(score))^2
+  float* lse;           // nullable [T]: log sum_e exp(score)
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
@@ -56,18 +57,37 @@ hipError_t launch_permute(const void* x, int64_t d, int elem_bytes, const int32_
                           hipStream_t s);
 
 // ws: the expert-FFN workspace (ffn_workspace_bytes(dtype) bytes) or null.
+// z: nullable; receives the pre-activation in the hidden storage type.
 hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,
-                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* ws,
-                          hipStream_t s);
+                          int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* z,
+                          void* ws, hipStream_t s);
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max,
                        int64_t d, int64_t d_ff, const void* w2, int dtype, float* y_perm,
                        void* ws, hipStream_t s);
 
-// bf16 layers: the segmented MFMA GEMM (up: GELU -> fp16 h; down: f32 out).
-// With a workspace, output tiles of a short last round are split along K.
-hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets, int E, int64_t rows_max,
-                           int N, int K, const void* B, void* C, void* ws, hipStream_t s);
+// bf16 layers: the segmented MFMA GEMM. Row-segmented kinds (rows of A and C
+// grouped by expert, K fixed):
+//   kUp:   A [R, K] bf16,  B = W1 [E, N, K] bf16 -> C = fp16 gelu(A B^T)
+//          (and, with Z, the fp16 pre-activation A B^T in Z [R, N])
+//   kDown: A [R, K] fp16,  B = W2 [E, N, K] bf16 -> C = A B^T f32
+//   kDh:   A [R, K] bf16,  B = W2 [E, K, N] bf16 -> C = bf16((A B) * gelu'(Z)), Z [R, N] fp16
+//   kDx:   A [R, K] bf16,  B = W1 [E, K, N] bf16 -> C = A B f32
+// K-segmented kinds (the contraction runs over each expert's rows):
+//   kDw2:  A [R, M] bf16,  B [R, N] fp16 -> C[e] = A_e^T B_e f32 [E, M, N]
+//   kDw1:  A [R, M] bf16,  B [R, N] bf16 -> C[e] = A_e^T B_e f32 [E, M, N]
+// With a workspace, output tiles of a short last round of a row-segmented
+// kind are split along K.
+enum class GemmKind { kUp, kDown, kDh, kDx, kDw2, kDw1 };
+hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
+                            int64_t rows_max, int M, int N, int K, const void* B, void* C,
+                            void* Z, void* ws, hipStream_t s);
+inline hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets, int E,
+                                  int64_t rows_max, int N, int K, const void* B, void* C,
+                                  void* ws, hipStream_t s) {
+  return launch_gemm_mfma(up ? GemmKind::kUp : GemmKind::kDown, A, offsets, E, rows_max, 0, N, K,
+                          B, C, nullptr, ws, s);
+}
 
 // Workspace bytes of the expert FFN on the current device (0 for f32 layers).
 size_t ffn_workspace_bytes(int dtype);
@@ -76,8 +96,8 @@ size_t ffn_mfma_workspace_bytes();
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                           int64_t T, int k, int64_t d, void* y, int out_dtype, hipStream_t s);
 
-// Router z-loss: loss = coeff * mean_t zsq[t]; ws as for the aux loss.
-hipError_t launch_z_loss(const float* zsq, int64_t T, float coeff, float* loss, double* ws,
+// Router z-loss: loss = coeff * mean_t lse[t]^2; ws as for the aux loss.
+hipError_t launch_z_loss(const float* lse, int64_t T, float coeff, float* loss, double* ws,
                          hipStream_t s);
 size_t z_ws_doubles(int64_t T);
 
@@ -86,6 +106,33 @@ hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T,
 
 size_t dispatch_ws_ints(int64_t T, int E);
 size_t aux_ws_doubles(int64_t T, int E);
+
+// Backward (backward.hip). Gradient storage of a layer: bf16 for dtype 1, f32
+// for dtype 0; dx_perm, dW1, dW2, dWg and db are f32.
+hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                                   const float* topk_w, int64_t T, int k, int64_t d, int dtype,
+                                   void* d_out, float* dw, hipStream_t s);
+hipError_t launch_gate_backward(const float* dw, const int32_t* topk_idx, const float* topk_w,
+                                const float* probs, const int32_t* counts, const float* lse,
+                                int64_t T, int E, int k, bool renorm, float temperature,
+                                float alpha, float aux_grad, float z_coeff, float* dl,
+                                hipStream_t s);
+size_t gate_wgrad_ws_floats(int64_t T, int64_t d, int E);
+hipError_t launch_gate_wgrad(const float* dl, const void* x, int64_t T, int64_t d, int E,
+                             int dtype, float* dwg, float* db, float* ws, hipStream_t s);
+hipError_t launch_dispatch_backward(const float* dx_perm, const int32_t* dest, const float* dl,
+                                    const void* wg, int64_t T, int k, int64_t d, int E, int dtype,
+                                    float* dx, hipStream_t s);
+hipError_t launch_down_backward(const void* d_out, const int32_t* offsets, int E, int64_t rows_max,
+                                int64_t d, int64_t d_ff, const void* w2, const void* z, int dtype,
+                                void* dz, void* ws, hipStream_t s);
+hipError_t launch_up_backward(const void* dz, const int32_t* offsets, int E, int64_t rows_max,
+                              int64_t d, int64_t d_ff, const void* w1, int dtype, float* dx_perm,
+                              void* ws, hipStream_t s);
+hipError_t launch_expert_dw2(const void* d_out, const void* h, const int32_t* offsets, int E,
+                             int64_t d, int64_t d_ff, int dtype, float* dw2, hipStream_t s);
+hipError_t launch_expert_dw1(const void* dz, const void* x_perm, const int32_t* offsets, int E,
+                             int64_t d, int64_t d_ff, int dtype, float* dw1, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -11,8 +11,9 @@
 // e = lane%16 + 16*i, so a token's E logits never leave registers.
 // Balancing knobs (SP/EP page, EP section: routing temperature and a random
 // perturbation; ETP page: routing z-loss): softmax and top-k see the scores
-// s = (l + noise) / temperature, and the per-token z-loss term
-// (log sum_e exp s)^2 falls out of the softmax's max and sum.
+// s = (l + noise) / temperature, and the per-token log sum_e exp s that the
+// z-loss squares (and its gradient needs) falls out of the softmax's max and
+// sum.
 #include "moe_internal.h"
 
 namespace moe {
@@ -27,7 +28,7 @@ constexpr int kChunk = 128;   // d-elements one wave consumes per step
 template <int NT>
 __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int64_t t,
                             int q, int32_t* topk_idx, float* topk_w, float* probs,
-                            float* zsq) {
+                            float* lse) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NT; ++i) m = fmaxf(m, lg[i]);
@@ -44,10 +45,7 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
   const float inv_s = 1.0f / s;
-  if (zsq != nullptr && q == 0) {
-    const float lse = m + logf(s);
-    zsq[t] = lse * lse;
-  }
+  if (lse != nullptr && q == 0) lse[t] = m + logf(s);
   if (probs) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -111,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, const float* __restrict__ noise, float temperature,
     int64_t T, int64_t d, int E, int k, uint32_t flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ probs, float* __restrict__ zsq) {
+    float* __restrict__ topk_w, float* __restrict__ probs, float* __restrict__ lse) {
   __shared__ float red[4][kTok][NT * 16];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -174,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     if (noise != nullptr && e < E && t < T) v += noise[t * E + e];
     lg[i] = (e < E) ? v / temperature : -INFINITY;
   }
-  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, zsq);
+  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, lse);
 }
 
 // f32: plain FMA dot products, one (token, expert) pair per lane and step.
@@ -183,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     const float* __restrict__ noise, float temperature, int64_t T, int64_t d, int E, int k,
     uint32_t flags, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ probs, float* __restrict__ zsq) {
+    float* __restrict__ probs, float* __restrict__ lse) {
   const int tid = threadIdx.x;
   const int tok = tid >> 4, q = tid & 15;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + tok;
@@ -203,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(
       lg[i] = -INFINITY;
     }
   }
-  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, zsq);
+  if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, lse);
 }
 
 template <int NT>
@@ -213,11 +211,11 @@ hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(router_bf16_kernel<NT>, grid, block, 0, s,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,
                        a.noise, a.temperature, a.T, a.d, a.E, a.k, a.flags, a.topk_idx, a.topk_w,
-                       a.probs, a.zsq);
+                       a.probs, a.lse);
   else
     hipLaunchKernelGGL(router_f32_kernel<NT>, grid, block, 0, s, static_cast<const float*>(a.x),
                        static_cast<const float*>(a.wg), a.bias, a.noise, a.temperature, a.T, a.d,
-                       a.E, a.k, a.flags, a.topk_idx, a.topk_w, a.probs, a.zsq);
+                       a.E, a.k, a.flags, a.topk_idx, a.topk_w, a.probs, a.lse);
   return hipGetLastError();
 }
 

@@ -183,3 +183,10 @@ def make_inputs(cfg: MoEConfig, seed: int | None = None) -> dict:
         out["topk_idx"] = np.ascontiguousarray(labels.reshape(T, 1), dtype=np.int32)
         out["topk_w"] = rng.uniform(0.0, 1.0, size=(T, 1)).astype(np.float32)
     return out
+
+
+def upstream_grad(T: int, d: int, seed: int) -> np.ndarray:
+    """Seeded gradient of the loss with respect to the layer output, [T, d]
+    f32, standard normal (what a next layer would hand back)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.standard_normal((T, d), dtype=np.float32)

@@ -25,7 +25,10 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
-           "moe_z_loss", "moe_last_error"]
+           "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
+           "moe_expert_up_backward", "moe_expert_weight_grads", "moe_gate_backward",
+           "moe_gate_weight_grads_workspace_bytes", "moe_gate_weight_grads", "moe_dispatch_backward",
+           "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -68,6 +71,16 @@ def lib() -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [P, P, P, I64, I32, I64, P, I32, P]),
         "moe_aux_loss_workspace_bytes": (SZ, [I64, I32]),
         "moe_aux_loss": (ctypes.c_int, [P, P, I64, I32, I32, F32, P, P, SZ, P]),
+        "moe_expert_up_gelu_z": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, P, SZ, P]),
+        "moe_combine_backward": (ctypes.c_int, [P, P, P, P, I64, I32, I64, I32, P, P, P]),
+        "moe_expert_down_backward": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, SZ, P]),
+        "moe_expert_up_backward": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
+        "moe_expert_weight_grads": (ctypes.c_int, [P, P, P, P, P, I32, I64, I64, I64, I32, P, P, P]),
+        "moe_gate_backward": (ctypes.c_int, [P, P, P, P, P, P, I64, I32, I32, U32, F32, F32, F32, F32,
+                                             P, P]),
+        "moe_gate_weight_grads_workspace_bytes": (SZ, [I64, I64, I32]),
+        "moe_gate_weight_grads": (ctypes.c_int, [P, P, I64, I64, I32, I32, P, P, P, SZ, P]),
+        "moe_dispatch_backward": (ctypes.c_int, [P, P, P, P, I64, I32, I64, I32, I32, P, P]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -109,6 +122,12 @@ def hidden_dtype(dt: torch.dtype) -> torch.dtype:
     return torch.float32 if dt == torch.float32 else torch.float16
 
 
+def grad_dtype(dt: torch.dtype) -> torch.dtype:
+    """Storage of the backward's per-row gradients (d_out_perm, dz): bf16 for
+    bf16 layers, f32 for f32 layers (see the backward section of include/moe.h)."""
+    return dt
+
+
 # ------------------------------------------------------------------ calls --
 def moe_capacity(n_tokens: int, n_experts: int, capacity_factor: float) -> int:
     return int(lib().moe_capacity(n_tokens, n_experts, capacity_factor))
@@ -133,34 +152,35 @@ def moe_router_topk(x, w_gate, bias, k: int, flags: int = 0, want_probs: bool = 
 
 
 def moe_router_topk_ex(x, w_gate, bias, k: int, flags: int = 0, temperature: float = 1.0,
-                       noise=None, want_probs: bool = True, want_zsq: bool = True,
-                       topk_idx=None, topk_w=None, probs=None, zsq=None, stream=None):
+                       noise=None, want_probs: bool = True, want_lse: bool = True,
+                       topk_idx=None, topk_w=None, probs=None, lse=None, stream=None):
     """Router with temperature, a caller-drawn perturbation `noise` [T, E] f32
-    and the per-token z-loss terms `zsq` [T] (see include/moe.h)."""
+    and the per-token log-sum-exp `lse` [T] of the scores (see include/moe.h)."""
     T, d = x.shape
     E = w_gate.shape[0]
     topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
     topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
     if want_probs and probs is None:
         probs = _empty((T, E), torch.float32, x)
-    if want_zsq and zsq is None:
-        zsq = _empty((max(T, 1),), torch.float32, x)
+    if want_lse and lse is None:
+        lse = _empty((max(T, 1),), torch.float32, x)
     _check(lib().moe_router_topk_ex(_ptr(x), _ptr(w_gate), _ptr(bias), _ptr(noise), T, d, E, k,
                                     dtype_code(x.dtype), flags, float(temperature),
-                                    _ptr(topk_idx), _ptr(topk_w), _ptr(probs), _ptr(zsq),
+                                    _ptr(topk_idx), _ptr(topk_w), _ptr(probs), _ptr(lse),
                                     _stream(stream)))
-    return topk_idx, topk_w, probs, zsq
+    return topk_idx, topk_w, probs, lse
 
 
 def moe_z_loss_workspace_bytes(T: int) -> int:
     return int(lib().moe_z_loss_workspace_bytes(T))
 
 
-def moe_z_loss(zsq, T: int, coeff: float, loss=None, workspace=None, stream=None):
-    loss = _empty((1,), torch.float32, zsq) if loss is None else loss
+def moe_z_loss(lse, T: int, coeff: float, loss=None, workspace=None, stream=None):
+    """coeff * mean over tokens of lse^2."""
+    loss = _empty((1,), torch.float32, lse) if loss is None else loss
     if workspace is None:
-        workspace = _empty((max(moe_z_loss_workspace_bytes(T), 8),), torch.uint8, zsq)
-    _check(lib().moe_z_loss(_ptr(zsq), T, float(coeff), _ptr(loss), _ptr(workspace),
+        workspace = _empty((max(moe_z_loss_workspace_bytes(T), 8),), torch.uint8, lse)
+    _check(lib().moe_z_loss(_ptr(lse), T, float(coeff), _ptr(loss), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
     return loss
 
@@ -275,12 +295,116 @@ def moe_aux_loss(probs, counts, k: int, alpha: float, loss=None, workspace=None,
     return loss
 
 
+# --------------------------------------------------------------- backward --
+def moe_expert_up_gelu_z(x_perm, offsets, w1, rows_max: int, h=None, z=None, workspace=None,
+                         stream=None):
+    """Up-projection + GELU that also keeps the pre-activation z."""
+    E, d_ff, d = w1.shape
+    hd = hidden_dtype(x_perm.dtype)
+    h = _empty((max(rows_max, 1), d_ff), hd, x_perm) if h is None else h
+    z = _empty((max(rows_max, 1), d_ff), hd, x_perm) if z is None else z
+    _check(lib().moe_expert_up_gelu_z(_ptr(x_perm), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
+                                      dtype_code(x_perm.dtype), _ptr(h), _ptr(z), _ptr(workspace),
+                                      _ws_size(workspace), _stream(stream)))
+    return h, z
+
+
+def moe_combine_backward(dy, y_perm, dest, topk_w, dtype, rows_max: int, d_out_perm=None,
+                         d_topk_w=None, stream=None):
+    """d_out_perm [rows, d] in the gradient storage of `dtype`, d_topk_w [T, k] f32."""
+    T, k = dest.shape
+    d = dy.shape[1]
+    d_out_perm = (_empty((max(rows_max, 1), d), grad_dtype(dtype), dy) if d_out_perm is None
+                  else d_out_perm)
+    d_topk_w = _empty((T, k), torch.float32, dy) if d_topk_w is None else d_topk_w
+    _check(lib().moe_combine_backward(_ptr(dy), _ptr(y_perm), _ptr(dest), _ptr(topk_w), T, k, d,
+                                      dtype_code(dtype), _ptr(d_out_perm), _ptr(d_topk_w),
+                                      _stream(stream)))
+    return d_out_perm, d_topk_w
+
+
+def moe_expert_down_backward(d_out_perm, offsets, w2, z, rows_max: int, dz=None, workspace=None,
+                             stream=None):
+    E, d, d_ff = w2.shape
+    dz = _empty((max(rows_max, 1), d_ff), d_out_perm.dtype, d_out_perm) if dz is None else dz
+    _check(lib().moe_expert_down_backward(_ptr(d_out_perm), _ptr(offsets), E, rows_max, d, d_ff,
+                                          _ptr(w2), _ptr(z), dtype_code(w2.dtype), _ptr(dz),
+                                          _ptr(workspace), _ws_size(workspace), _stream(stream)))
+    return dz
+
+
+def moe_expert_up_backward(dz, offsets, w1, rows_max: int, dx_perm=None, workspace=None,
+                           stream=None):
+    E, d_ff, d = w1.shape
+    dx_perm = _empty((max(rows_max, 1), d), torch.float32, dz) if dx_perm is None else dx_perm
+    _check(lib().moe_expert_up_backward(_ptr(dz), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
+                                        dtype_code(w1.dtype), _ptr(dx_perm), _ptr(workspace),
+                                        _ws_size(workspace), _stream(stream)))
+    return dx_perm
+
+
+def moe_expert_weight_grads(x_perm, h, d_out_perm, dz, offsets, E: int, rows_max: int, d: int,
+                            d_ff: int, dtype, dw1=None, dw2=None, want_dw1=True, want_dw2=True,
+                            stream=None):
+    like = x_perm if x_perm is not None else d_out_perm
+    if want_dw1 and dw1 is None:
+        dw1 = _empty((E, d_ff, d), torch.float32, like)
+    if want_dw2 and dw2 is None:
+        dw2 = _empty((E, d, d_ff), torch.float32, like)
+    _check(lib().moe_expert_weight_grads(_ptr(x_perm), _ptr(h), _ptr(d_out_perm), _ptr(dz),
+                                         _ptr(offsets), E, rows_max, d, d_ff, dtype_code(dtype),
+                                         _ptr(dw1 if want_dw1 else None),
+                                         _ptr(dw2 if want_dw2 else None), _stream(stream)))
+    return dw1, dw2
+
+
+def moe_gate_backward(d_topk_w, topk_idx, topk_w, probs, counts, k: int, alpha: float,
+                      aux_grad: float = 1.0, flags: int = 0, temperature: float = 1.0,
+                      lse=None, z_coeff: float = 0.0, d_logits=None, stream=None):
+    T, E = probs.shape
+    d_logits = _empty((T, E), torch.float32, probs) if d_logits is None else d_logits
+    _check(lib().moe_gate_backward(_ptr(d_topk_w), _ptr(topk_idx), _ptr(topk_w), _ptr(probs),
+                                   _ptr(counts), _ptr(lse), T, E, k, flags, float(temperature),
+                                   float(alpha), float(aux_grad), float(z_coeff), _ptr(d_logits),
+                                   _stream(stream)))
+    return d_logits
+
+
+def moe_gate_weight_grads_workspace_bytes(T: int, d: int, E: int) -> int:
+    return int(lib().moe_gate_weight_grads_workspace_bytes(T, d, E))
+
+
+def moe_gate_weight_grads(d_logits, x, E: int, d_w_gate=None, d_bias=None, want_bias=True,
+                          workspace=None, stream=None):
+    T, d = x.shape
+    d_w_gate = _empty((E, d), torch.float32, x) if d_w_gate is None else d_w_gate
+    if want_bias and d_bias is None:
+        d_bias = _empty((E,), torch.float32, x)
+    if workspace is None:
+        workspace = _empty((max(moe_gate_weight_grads_workspace_bytes(T, d, E), 16),), torch.uint8, x)
+    _check(lib().moe_gate_weight_grads(_ptr(d_logits), _ptr(x), T, d, E, dtype_code(x.dtype),
+                                       _ptr(d_w_gate), _ptr(d_bias if want_bias else None),
+                                       _ptr(workspace), _ws_size(workspace), _stream(stream)))
+    return d_w_gate, d_bias
+
+
+def moe_dispatch_backward(dx_perm, dest, d, dtype, d_logits=None, w_gate=None, dx=None,
+                          stream=None):
+    T, k = dest.shape
+    E = w_gate.shape[0] if w_gate is not None else 1
+    dx = _empty((T, d), torch.float32, dest) if dx is None else dx
+    _check(lib().moe_dispatch_backward(_ptr(dx_perm), _ptr(dest), _ptr(d_logits), _ptr(w_gate), T,
+                                       k, d, E, dtype_code(dtype), _ptr(dx), _stream(stream)))
+    return dx
+
+
 # ------------------------------------------------------------ whole layer --
 class MoEBuffers:
     """Every intermediate of one layer forward, allocated once for a shape so
     repeated forwards allocate nothing."""
 
-    def __init__(self, T, d, d_ff, E, k, capacity, dtype, device, routed=True, want_probs=True):
+    def __init__(self, T, d, d_ff, E, k, capacity, dtype, device, routed=True, want_probs=True,
+                 save_for_backward=False):
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
         self.T, self.d, self.d_ff, self.E, self.k, self.capacity = T, d, d_ff, E, k, capacity
         self.rows_max = moe_rows_max(T, k, E, capacity)
@@ -294,37 +418,109 @@ class MoEBuffers:
         self.src = z((R,), torch.int32)
         self.x_perm = z((R, d), dtype)
         self.h = z((R, d_ff), hidden_dtype(dtype))
+        # the pre-activation, kept for the backward
+        self.z = z((R, d_ff), hidden_dtype(dtype)) if save_for_backward else None
+        self.lse = z((max(T, 1),), torch.float32) if (routed and save_for_backward) else None
         self.y_perm = z((R, d), torch.float32)
         self.y = z((T, d), torch.float32)
         self.loss = z((1,), torch.float32)
         self.ws_dispatch = z((max(moe_dispatch_workspace_bytes(T, k, E), 4),), torch.uint8)
         self.ws_aux = z((max(moe_aux_loss_workspace_bytes(T, E), 8),), torch.uint8)
+        self.used_idx, self.used_w = self.topk_idx, self.topk_w
         nb = moe_ffn_workspace_bytes(dtype)
         self.ws_ffn = z((nb,), torch.uint8) if nb > 0 else None
 
 
 def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_idx=None,
                 topk_w=None, alpha: float = 0.01, flags: int = 0, bufs: MoEBuffers = None,
-                stream=None) -> MoEBuffers:
+                stream=None, save_for_backward: bool = False, temperature: float = 1.0,
+                noise=None) -> MoEBuffers:
     """router -> dispatch -> grouped FFN -> combine -> aux loss, all on one
     stream. With `w_gate` None, `topk_idx`/`topk_w` are taken as given (a
-    receiver's share: the rows it got and their weights)."""
+    receiver's share: the rows it got and their weights). With
+    `save_for_backward` the up-projection also keeps the pre-activation and
+    the router its log-sum-exp (what moe_backward needs)."""
     T, d = x.shape
     E, d_ff, _ = w1.shape
     routed = w_gate is not None
     if bufs is None:
-        bufs = MoEBuffers(T, d, d_ff, E, k, capacity, x.dtype, x.device, routed)
+        bufs = MoEBuffers(T, d, d_ff, E, k, capacity, x.dtype, x.device, routed,
+                          save_for_backward=save_for_backward)
     if routed:
-        moe_router_topk(x, w_gate, bias, k, flags, bufs.probs is not None, bufs.topk_idx,
-                        bufs.topk_w, bufs.probs, stream)
+        if temperature != 1.0 or noise is not None or bufs.lse is not None:
+            moe_router_topk_ex(x, w_gate, bias, k, flags, temperature, noise,
+                               bufs.probs is not None, bufs.lse is not None, bufs.topk_idx,
+                               bufs.topk_w, bufs.probs, bufs.lse, stream)
+        else:
+            moe_router_topk(x, w_gate, bias, k, flags, bufs.probs is not None, bufs.topk_idx,
+                            bufs.topk_w, bufs.probs, stream)
         idx, w = bufs.topk_idx, bufs.topk_w
     else:
         idx, w = topk_idx, topk_w
+    bufs.used_idx, bufs.used_w = idx, w   # the routing the layer ran with (given or computed)
     moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                  bufs.x_perm, bufs.ws_dispatch, stream)
-    moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
-                    bufs.ws_ffn, stream)
+    if bufs.z is not None:
+        moe_expert_up_gelu_z(bufs.x_perm, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.z,
+                             bufs.ws_ffn, stream)
+        moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn, stream)
+    else:
+        moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
+                        bufs.ws_ffn, stream)
     moe_combine(bufs.y_perm, bufs.dest, w, d, torch.float32, bufs.y, stream)
     if routed and bufs.probs is not None:
         moe_aux_loss(bufs.probs, bufs.counts, k, alpha, bufs.loss, bufs.ws_aux, stream)
     return bufs
+
+
+class MoEGrads:
+    """Every intermediate and result of one layer backward, allocated once."""
+
+    def __init__(self, T, d, d_ff, E, k, rows_max, dtype, device, routed=True):
+        z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
+        R = max(rows_max, 1)
+        self.d_out_perm = z((R, d), grad_dtype(dtype))
+        self.d_topk_w = z((T, k), torch.float32)
+        self.dz = z((R, d_ff), grad_dtype(dtype))
+        self.dx_perm = z((R, d), torch.float32)
+        self.dw1 = z((E, d_ff, d), torch.float32)
+        self.dw2 = z((E, d, d_ff), torch.float32)
+        self.dx = z((T, d), torch.float32)
+        self.d_logits = z((T, E), torch.float32) if routed else None
+        self.dw_gate = z((E, d), torch.float32) if routed else None
+        self.d_bias = z((E,), torch.float32) if routed else None
+        self.ws_gate = (z((max(moe_gate_weight_grads_workspace_bytes(T, d, E), 16),), torch.uint8)
+                        if routed else None)
+
+
+def moe_backward(x, w1, w2, k: int, bufs: MoEBuffers, dy, w_gate=None, alpha: float = 0.01,
+                 aux_grad: float = 1.0, flags: int = 0, temperature: float = 1.0,
+                 z_coeff: float = 0.0, grads: MoEGrads = None, stream=None) -> MoEGrads:
+    """Gradients of <dy, y> + aux_grad * L_aux + z_coeff * mean(lse^2) for a
+    forward run with save_for_backward: combine^T, down-projection and GELU
+    backward, up-projection backward, expert weight gradients, gate backward,
+    gate weight gradients, dispatch^T; all on one stream."""
+    T, d = x.shape
+    E, d_ff, _ = w1.shape
+    routed = w_gate is not None
+    if bufs.z is None:
+        raise MoEError(-1, "the forward did not keep the pre-activation (save_for_backward)")
+    if grads is None:
+        grads = MoEGrads(T, d, d_ff, E, k, bufs.rows_max, x.dtype, x.device, routed)
+    R = bufs.rows_max
+    moe_combine_backward(dy, bufs.y_perm, bufs.dest, bufs.used_w, x.dtype, R, grads.d_out_perm,
+                         grads.d_topk_w, stream)
+    moe_expert_down_backward(grads.d_out_perm, bufs.offsets, w2, bufs.z, R, grads.dz, bufs.ws_ffn,
+                             stream)
+    moe_expert_up_backward(grads.dz, bufs.offsets, w1, R, grads.dx_perm, bufs.ws_ffn, stream)
+    moe_expert_weight_grads(bufs.x_perm, bufs.h, grads.d_out_perm, grads.dz, bufs.offsets, E, R, d,
+                            d_ff, x.dtype, grads.dw1, grads.dw2, stream=stream)
+    if routed:
+        moe_gate_backward(grads.d_topk_w, bufs.topk_idx, bufs.topk_w, bufs.probs, bufs.counts, k,
+                          alpha, aux_grad, flags, temperature, bufs.lse, z_coeff, grads.d_logits,
+                          stream)
+        moe_gate_weight_grads(grads.d_logits, x, E, grads.dw_gate, grads.d_bias, True,
+                              grads.ws_gate, stream)
+    moe_dispatch_backward(grads.dx_perm, bufs.dest, d, x.dtype, grads.d_logits if routed else None,
+                          w_gate, grads.dx, stream)
+    return grads

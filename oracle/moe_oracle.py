@@ -284,7 +284,8 @@ def combine_backward(dy: np.ndarray, y_perm: np.ndarray, dest: np.ndarray, topk_
 
 def gate_backward(dw: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, probs: np.ndarray,
                   counts: np.ndarray, k: int, alpha: float, aux_grad: float, renorm: bool = False,
-                  temperature: float = 1.0, lse=None, z_coeff: float = 0.0) -> np.ndarray:
+                  temperature: float = 1.0, lse=None, z_coeff: float = 0.0,
+                  n_tokens=None) -> np.ndarray:
     """Gradient of the gate's linear output (the logits before the routing
     knobs) from: the combine weights' gradient dw, aux_grad times the aux
     loss (EP tutorial 5.1), and z_coeff times the mean over tokens of lse^2.
@@ -294,17 +295,20 @@ def gate_backward(dw: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, prob
     gradient with respect to a chosen p_m is (dw_m - sum_j dw_j w_j) / S.
     dL_aux/dp[t, i] = alpha E f_i / T with f_i = counts_i / (T k).
     Softmax: ds = p (dp - sum_e p dp); z-loss: ds += z_coeff 2 lse p / T;
-    dl = ds / temperature."""
-    T, E = probs.shape
+    dl = ds / temperature. The rows may be a sample of the layer's tokens:
+    `n_tokens` is then the layer's T."""
+    E = probs.shape[1]
+    T = probs.shape[0] if n_tokens is None else int(n_tokens)
     p = np.asarray(probs, dtype=np.float64)
     w = np.asarray(topk_w, dtype=np.float64)
     g = np.asarray(dw, dtype=np.float64).copy()
     if renorm:
         S = np.take_along_axis(p, topk_idx, axis=1).sum(axis=1, keepdims=True)
         g = (g - np.sum(g * w, axis=1, keepdims=True)) / S
-    dp = np.zeros((T, E))
+    n = probs.shape[0]
+    dp = np.zeros((n, E))
     for j in range(topk_idx.shape[1]):
-        np.add.at(dp, (np.arange(T), topk_idx[:, j]), g[:, j])
+        np.add.at(dp, (np.arange(n), topk_idx[:, j]), g[:, j])
     if T > 0:
         f = np.asarray(counts, dtype=np.float64) / float(T * k)
         dp += aux_grad * alpha * E * f[None, :] / T
@@ -312,6 +316,22 @@ def gate_backward(dw: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, prob
     if z_coeff != 0.0 and T > 0:
         ds += z_coeff * 2.0 * np.asarray(lse, dtype=np.float64)[:, None] * p / T
     return ds / float(temperature)
+
+
+def expert_backward(x_rows: np.ndarray, d_out_rows: np.ndarray, w1_e: np.ndarray,
+                    w2_e: np.ndarray, fcols=None) -> dict:
+    """One expert's FFN backward on a block of its rows (optionally only the
+    hidden units `fcols`): z = X W1^T, h = gelu(z), dz = (D W2) * gelu'(z),
+    dW1 = dz^T X, dW2 = D^T h and, over all hidden units, dx_perm = dz W1."""
+    w1s = w1_e if fcols is None else w1_e[fcols]
+    w2s = w2_e if fcols is None else w2_e[:, fcols]
+    z = x_rows @ w1s.T
+    h = gelu_tanh(z)
+    dz = (d_out_rows @ w2s) * gelu_tanh_grad(z)
+    out = {"z": z, "h": h, "dz": dz, "dw1": dz.T @ x_rows, "dw2": d_out_rows.T @ h}
+    if fcols is None:
+        out["dx_perm"] = dz @ w1_e
+    return out
 
 
 def backward(inp: dict, fwd: dict, dy: np.ndarray, dtype: str, k: int, alpha: float = 0.01,
@@ -339,16 +359,13 @@ def backward(inp: dict, fwd: dict, dy: np.ndarray, dtype: str, k: int, alpha: fl
     tw = np.asarray(fwd["topk_w"], dtype=np.float64)
     R = int(offsets[-1])
     xp = x[src]
-    z = np.zeros((R, dff))
-    for e in range(E):
-        a, b = int(offsets[e]), int(offsets[e + 1])
-        z[a:b] = xp[a:b] @ w1[e].T
-    h = gelu_tanh(z)
     y_perm = np.zeros((R, d))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
-        y_perm[a:b] = h[a:b] @ w2[e].T
+        y_perm[a:b] = gelu_tanh(xp[a:b] @ w1[e].T) @ w2[e].T
     d_out, dw = combine_backward(dy, y_perm, dest, tw, R)
+    z = np.zeros((R, dff))
+    h = np.zeros((R, dff))
     dz = np.zeros((R, dff))
     dx_perm = np.zeros((R, d))
     dw1 = np.zeros_like(w1)
@@ -357,10 +374,9 @@ def backward(inp: dict, fwd: dict, dy: np.ndarray, dtype: str, k: int, alpha: fl
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b == a:
             continue
-        dz[a:b] = (d_out[a:b] @ w2[e]) * gelu_tanh_grad(z[a:b])
-        dw2[e] = d_out[a:b].T @ h[a:b]
-        dw1[e] = dz[a:b].T @ xp[a:b]
-        dx_perm[a:b] = dz[a:b] @ w1[e]
+        g = expert_backward(xp[a:b], d_out[a:b], w1[e], w2[e])
+        z[a:b], h[a:b], dz[a:b], dx_perm[a:b] = g["z"], g["h"], g["dz"], g["dx_perm"]
+        dw1[e], dw2[e] = g["dw1"], g["dw2"]
     dx = np.zeros((T, d))
     np.add.at(dx, src, dx_perm)
     out = {"dx_experts": dx.copy(), "dw1": dw1, "dw2": dw2, "dw": dw, "z_perm": z, "h_perm": h,

@@ -120,7 +120,7 @@ def test_router_ex_and_z_loss_argument_errors():
     assert call(7, 9) == -3                       # k > E
     assert call(5, 60) == -6                      # bf16 d % 8
     assert call(0, None) == -1
-    # moe_z_loss(zsq, T, coeff, loss, ws, ws_bytes, stream)
+    # moe_z_loss(lse, T, coeff, loss, ws, ws_bytes, stream)
     need = L.moe_z_loss_workspace_bytes(100)
     assert need > 0
     assert L.moe_z_loss(FAKE, -1, 1.0, FAKE, FAKE, need, None) == -1
@@ -195,3 +195,90 @@ def test_binding_raises_typed_errors():
     with pytest.raises(ops.MoEError) as e:
         ops._check(-3)
     assert e.value.status == -3
+
+
+def test_backward_argument_errors():
+    L = ops.lib()
+    # moe_combine_backward(dy, y_perm, dest, topk_w, T, k, d, dtype, d_out, d_topk_w, stream)
+    cb = [FAKE, FAKE, FAKE, FAKE, 100, 2, 64, 1, FAKE, FAKE, None]
+
+    def comb(i, v):
+        a = list(cb); a[i] = v
+        return L.moe_combine_backward(*a)
+    assert comb(0, None) == -1
+    assert comb(9, None) == -1
+    assert comb(6, 60) == -6                      # bf16 rows: multiple of 8
+    assert comb(7, 3) == -2
+    assert comb(5, 9) == -1
+    assert comb(4, 0) == 0                        # empty batch: nothing launched
+    # moe_expert_down_backward(d_out, offsets, E, rows_max, d, d_ff, w2, z, dtype, dz, ws, wsb, s)
+    db = [FAKE, FAKE, 8, 1000, 64, 128, FAKE, FAKE, 1, FAKE, None, 0, None]
+
+    def down(i, v):
+        a = list(db); a[i] = v
+        return L.moe_expert_down_backward(*a)
+    assert down(7, None) == -1                    # the forward's pre-activation is required
+    assert down(2, 0) == -3
+    a = list(db); a[4] = 1 << 16; a[5] = 1 << 14; a[3] = 8
+    assert L.moe_expert_down_backward(*a) == -3   # d * d_ff >= 2^30
+    assert down(3, 0) == 0                        # no rows: nothing launched
+    assert down(10, FAKE) == -4                   # workspace given but too small
+    # moe_expert_up_backward(dz, offsets, E, rows_max, d, d_ff, w1, dtype, dx_perm, ws, wsb, s)
+    ub = [FAKE, FAKE, 8, 1000, 64, 128, FAKE, 1, FAKE, None, 0, None]
+    a = list(ub); a[8] = None
+    assert L.moe_expert_up_backward(*a) == -1
+    a = list(ub); a[3] = 1 << 20; a[5] = 1 << 12
+    assert L.moe_expert_up_backward(*a) == -3     # rows_max * d_ff >= 2^30
+    # moe_expert_weight_grads(x_perm, h, d_out, dz, offsets, E, rows_max, d, d_ff, dtype, dw1, dw2, s)
+    wb = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1000, 64, 128, 1, FAKE, FAKE, None]
+
+    def wgr(i, v):
+        a = list(wb); a[i] = v
+        return L.moe_expert_weight_grads(*a)
+    assert wgr(3, None) == -1                     # dW1 needs dz
+    assert wgr(1, None) == -1                     # dW2 needs h
+    assert wgr(4, None) == -1
+    assert wgr(8, 100) == -6
+    assert wgr(11, ctypes.c_void_p((1 << 20) + 4)) == -6
+    # moe_gate_backward(dw, idx, w, probs, counts, lse, T, E, k, flags, tau, alpha, aux, zc, dl, s)
+    gb = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 100, 8, 2, 0, 1.0, 0.01, 1.0, 0.0, FAKE, None]
+
+    def gate(i, v):
+        a = list(gb); a[i] = v
+        return L.moe_gate_backward(*a)
+    assert gate(10, 0.0) == -1                    # temperature
+    assert gate(10, float("nan")) == -1
+    assert gate(12, float("inf")) == -1           # aux_grad must be finite
+    assert gate(13, 0.5) == -1                    # z-loss gradient needs lse
+    assert gate(7, 0) == -3
+    assert gate(8, 9) == -3
+    assert gate(14, None) == -1
+    a = list(gb); a[2] = None; a[9] = 1           # renormalised weights need topk_w
+    assert L.moe_gate_backward(*a) == -1
+    assert gate(6, 0) == 0
+    # moe_gate_weight_grads(dl, x, T, d, E, dtype, dwg, db, ws, wsb, s)
+    need = L.moe_gate_weight_grads_workspace_bytes(8192, 4096, 8)
+    assert need >= 8 * 4096 * 4
+    assert L.moe_gate_weight_grads_workspace_bytes(100, 64, 8) < need
+    gw = [FAKE, FAKE, 8192, 4096, 8, 1, FAKE, FAKE, FAKE, need, None]
+
+    def gwg(i, v):
+        a = list(gw); a[i] = v
+        return L.moe_gate_weight_grads(*a)
+    assert gwg(9, need - 4) == -4
+    assert gwg(8, None) == -4
+    assert gwg(6, None) == -1
+    assert gwg(3, 4092) == -6
+    assert gwg(4, 300) == -3
+    # moe_dispatch_backward(dx_perm, dest, dl, w_gate, T, k, d, E, dtype, dx, s)
+    dbk = [FAKE, FAKE, FAKE, FAKE, 100, 2, 64, 8, 1, FAKE, None]
+
+    def disp(i, v):
+        a = list(dbk); a[i] = v
+        return L.moe_dispatch_backward(*a)
+    assert disp(2, None) == -1                    # d_logits and w_gate go together
+    assert disp(3, None) == -1
+    assert disp(9, None) == -1
+    assert disp(6, 12) == -6
+    assert disp(7, 0) == -3
+    assert disp(4, 0) == 0

@@ -453,3 +453,31 @@ def test_backward_finite_differences_and_gelu_grad():
         wp[e, a, c] += h
         wm[e, a, c] -= h
         assert (loss_w1(wp) - loss_w1(wm)) / (2 * h) == pytest.approx(g["dw1"][e, a, c], rel=1e-6, abs=1e-8)
+
+
+def test_backward_slices_agree_with_the_whole():
+    """The sampled forms the full-size GPU tests use (a subset of hidden units,
+    a subset of tokens) give the corresponding parts of the autograd-pinned
+    whole backward."""
+    rng = np.random.default_rng(47)
+    T, d, dff, E, k = 31, 8, 12, 3, 2
+    inp = {"x": rng.standard_normal((T, d)), "w_gate": rng.standard_normal((E, d)),
+           "bias": rng.standard_normal(E), "w1": rng.standard_normal((E, dff, d)) * 0.4,
+           "w2": rng.standard_normal((E, d, dff)) * 0.4}
+    fwd = O.forward(inp, "f32", k=k, cf=1.0, renorm=True)
+    dy = rng.standard_normal((T, d))
+    g = O.backward(inp, fwd, dy, "f32", k, alpha=0.1, aux_scale=0.5, renorm=True, z_coeff=0.2)
+    off = fwd["offsets"]
+    e = int(np.argmax(np.diff(off)))
+    a, b = int(off[e]), int(off[e + 1])
+    fcols = np.array([1, 5, 11])
+    xp = inp["x"][fwd["src"][a:b]]
+    part = O.expert_backward(xp, g["d_out_perm"][a:b], inp["w1"][e], inp["w2"][e], fcols)
+    np.testing.assert_allclose(part["dw1"], g["dw1"][e][fcols], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dw2"], g["dw2"][e][:, fcols], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dz"], g["dz_perm"][a:b][:, fcols], rtol=1e-12, atol=1e-12)
+    toks = np.array([0, 7, 30])
+    dl = O.gate_backward(g["dw"][toks], fwd["topk_idx"][toks], fwd["topk_w"][toks],
+                         fwd["probs"][toks], fwd["counts"], k, 0.1, 0.5, True, 1.0,
+                         fwd["lse"][toks], 0.2, n_tokens=T)
+    np.testing.assert_allclose(dl, g["dl"][toks], rtol=1e-12, atol=1e-14)

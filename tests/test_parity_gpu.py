@@ -111,11 +111,11 @@ def check_routing_ex(inp, cfg, temperature, noise_scale, coeff=1e-3):
                   noise=noise)
     t = gpu_tensors(inp, cfg)
     nz = None if noise is None else dev(noise, "f32")
-    idx, w, probs, zsq = ops.moe_router_topk_ex(t["x"], t["w_gate"], t["bias"], cfg.k,
+    idx, w, probs, lse = ops.moe_router_topk_ex(t["x"], t["w_gate"], t["bias"], cfg.k,
                                                 temperature=temperature, noise=nz)
-    zl = ops.moe_z_loss(zsq, cfg.T, coeff)
+    zl = ops.moe_z_loss(lse, cfg.T, coeff)
     torch.cuda.synchronize()
-    idx, w, probs, zsq, zl = host(idx), host(w), host(probs), host(zsq), float(host(zl)[0])
+    idx, w, probs, lse, zl = host(idx), host(w), host(probs), host(lse), float(host(zl)[0])
     gap = topk_gap(ref["logits"], cfg.k)
     firm = gap >= GAP
     mism = (idx != ref["topk_idx"]).any(axis=1)
@@ -125,10 +125,12 @@ def check_routing_ex(inp, cfg, temperature, noise_scale, coeff=1e-3):
     tol = 1e-4 if cfg.dtype == "bf16" else 1e-5
     np.testing.assert_allclose(probs, ref["probs"], rtol=tol, atol=1e-7)
     np.testing.assert_allclose(w[~mism], ref["topk_w"][~mism], rtol=tol, atol=1e-7)
-    # z-loss terms: (log-sum-exp)^2 of the scores, relative to their own size
-    np.testing.assert_allclose(zsq, ref["zsq"], rtol=10 * tol, atol=1e-6)
-    # the reduction: coeff * mean of the GPU's own terms, summed in double
-    assert abs(zl - coeff * float(np.mean(zsq.astype(np.float64)))) <= 1e-6 * abs(zl) + 1e-12
+    # log-sum-exp of the scores: its error follows the logits' (relative to
+    # their size, plus one unit)
+    assert np.all(np.abs(lse[:cfg.T] - ref["lse"]) <= 10 * tol * (np.abs(ref["lse"]) + 1.0))
+    # the reduction: coeff * mean of the GPU's own lse^2, summed in double
+    l64 = lse[:cfg.T].astype(np.float64)
+    assert abs(zl - coeff * float(np.mean(l64 * l64))) <= 1e-6 * abs(zl) + 1e-12
     assert abs(zl - O.z_loss(ref["logits"], coeff)) <= 10 * tol * abs(zl) + 1e-9
 
 
