@@ -1,7 +1,7 @@
 """Benchmark: one MoE layer forward per step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--backward]
 
 A step is the whole forward -- gate + softmax + top-k, dispatch (index build +
 permute), grouped expert FFN (up-projection + GELU, down-projection), weighted
@@ -12,6 +12,11 @@ d_ff=16384, E=8, top-2, capacity factor 1.25, bf16).
 Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
 kernel (timed live with HIP events on the launch stream), a per-call
 breakdown, and the CPU oracle timed on this host as a baseline.
+
+With --backward a step is one training step of the layer instead: the
+forward keeping what the backward needs, then the whole backward (combine^T,
+GELU and down-projection backward, up-projection backward, expert weight
+gradients, gate backward, gate weight gradients, dispatch^T).
 """
 from __future__ import annotations
 
@@ -43,6 +48,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large-experts-e8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step (forward + backward) instead of the forward")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps, as a "
                          "known-size reference for memory-traffic counters")
@@ -93,6 +100,165 @@ def cpu_baseline(inp, cfg):
                       % (cfg.T, dt), "seconds": dt}
 
 
+def cpu_baseline_backward(inp, cfg, n_tokens):
+    """The CPU oracle's forward + backward on the first n_tokens tokens of the
+    same workload (the whole batch would take minutes)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mixture_experts_layer_49_amd import inputs as I
+    from oracle import moe_oracle as O
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    sub = dict(inp)
+    sub["x"] = inp["x"][:n_tokens]
+    dy = I.upstream_grad(n_tokens, cfg.d, 77).astype(np.float64)
+    t0 = time.perf_counter()
+    fwd = O.forward(sub, cfg.dtype, cfg.k, cfg.cf, cfg.alpha)
+    O.backward(sub, fwd, dy, cfg.dtype, cfg.k, alpha=cfg.alpha)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "first %d of the %d tokens (capacity from the sample's own T), forward + "
+                      "backward in float64 numpy; %.1f s wall" % (n_tokens, cfg.T, dt),
+            "seconds": dt}
+
+
+def bench_backward(args, cfg, inp, ops, torch, np):
+    """One training step per timed step; prints the JSON line."""
+    from mixture_experts_layer_49_amd import inputs as I
+
+    def dev(a, bf16):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf16 else t).to("cuda:0")
+
+    bf = cfg.dtype == "bf16"
+    if not cfg.routed:
+        print("--backward runs routed workloads", file=sys.stderr)
+        return 2
+    x, w1, w2 = dev(inp["x"], bf), dev(inp["w1"], bf), dev(inp["w2"], bf)
+    wg = dev(inp["w_gate"], bf)
+    bias = dev(inp["bias"], False) if inp["bias"] is not None else None
+    dy = dev(I.upstream_grad(cfg.T, cfg.d, 77), False)
+    C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, True,
+                       save_for_backward=True)
+    g = ops.MoEGrads(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, b.rows_max, x.dtype, x.device, True)
+    stream = torch.cuda.current_stream()
+    T, d, dff, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
+    R_max = b.rows_max
+
+    names = ["router", "dispatch_plan", "permute", "up_gelu_z", "down", "combine", "aux",
+             "combine_bwd", "down_bwd", "up_bwd", "dw2", "dw1", "gate_bwd", "gate_wgrad",
+             "dispatch_bwd"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        ops.moe_router_topk_ex(x, wg, bias, k, 0, 1.0, None, True, True, b.topk_idx, b.topk_w,
+                               b.probs, b.lse)
+        rec(1)
+        ops.moe_dispatch_plan(b.topk_idx, E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
+        rec(2)
+        ops.moe_permute(x, b.src, b.offsets, R_max, b.x_perm)
+        rec(3)
+        ops.moe_expert_up_gelu_z(b.x_perm, b.offsets, w1, R_max, b.h, b.z, b.ws_ffn)
+        rec(4)
+        ops.moe_expert_down(b.h, b.offsets, w2, R_max, b.y_perm, b.ws_ffn)
+        rec(5)
+        ops.moe_combine(b.y_perm, b.dest, b.topk_w, d, torch.float32, b.y)
+        rec(6)
+        ops.moe_aux_loss(b.probs, b.counts, k, cfg.alpha, b.loss, b.ws_aux)
+        rec(7)
+        ops.moe_combine_backward(dy, b.y_perm, b.dest, b.topk_w, x.dtype, R_max, g.d_out_perm,
+                                 g.d_topk_w)
+        rec(8)
+        ops.moe_expert_down_backward(g.d_out_perm, b.offsets, w2, b.z, R_max, g.dz, b.ws_ffn)
+        rec(9)
+        ops.moe_expert_up_backward(g.dz, b.offsets, w1, R_max, g.dx_perm, b.ws_ffn)
+        rec(10)
+        ops.moe_expert_weight_grads(None, b.h, g.d_out_perm, None, b.offsets, E, R_max, d, dff,
+                                    x.dtype, None, g.dw2, want_dw1=False)
+        rec(11)
+        ops.moe_expert_weight_grads(b.x_perm, None, None, g.dz, b.offsets, E, R_max, d, dff,
+                                    x.dtype, g.dw1, None, want_dw2=False)
+        rec(12)
+        ops.moe_gate_backward(g.d_topk_w, b.topk_idx, b.topk_w, b.probs, b.counts, k, cfg.alpha,
+                              1.0, 0, 1.0, None, 0.0, g.d_logits)
+        rec(13)
+        ops.moe_gate_weight_grads(g.d_logits, x, E, g.dw_gate, g.d_bias, True, g.ws_gate)
+        rec(14)
+        ops.moe_dispatch_backward(g.dx_perm, b.dest, d, x.dtype, g.d_logits, wg, g.dx)
+        rec(15)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
+    us = dict(zip(names, (per * 1e3).tolist()))
+    R = int(b.offsets.cpu().numpy()[-1])
+    s2 = 2 if bf else 4
+    nch = ops.moe_gate_weight_grads_workspace_bytes(T, d, E) // (4 * E * (d + 1))
+    gemm_flops = 2.0 * R * d * dff
+    hbm = {
+        "combine_bwd": T * d * 4 + R * d * 4 + R * d * s2 + T * k * 16,
+        "gate_bwd": T * k * 12 + T * E * 8 + T * 4,
+        "gate_wgrad": T * E * 4 + T * d * s2 + 2 * nch * E * d * 4 + E * d * 4,
+        "dispatch_bwd": R * d * 4 + T * d * 4 + T * E * 4 + T * k * 4,
+    }
+    breakdown = {}
+    for n in names:
+        v = {"us": us[n]}
+        if n in ("down_bwd", "up_bwd", "dw2", "dw1"):
+            v["TFLOP/s"] = gemm_flops / (us[n] * 1e-6) / 1e12
+            v["mfma_frac"] = v["TFLOP/s"] / PEAK_MFMA_TFLOPS
+        if n in hbm:
+            v["bytes"] = hbm[n]
+            v["GB/s"] = hbm[n] / (us[n] * 1e-6) / 1e9
+            v["hbm_frac"] = v["GB/s"] / PEAK_HBM_GBS
+        breakdown[n] = v
+    bwd_names = names[7:]
+    bwd_us = sum(us[n] for n in bwd_names)
+    dom = max(("down_bwd", "up_bwd", "dw2", "dw1"), key=lambda n: us[n])
+    out = {
+        "metric": "MoE training step (fwd+bwd) tokens/s on 1 GPU + backward GEMM % bf16 MFMA peak",
+        "value": T * args.steps / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded; inputs and upstream gradient resident in HBM before timing)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
+                   "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "grouped_gemm_mfma<%s>" % dom, "bound": "mfma",
+                     "achieved": breakdown[dom]["TFLOP/s"], "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": breakdown[dom]["mfma_frac"], "traffic": None,
+                     "flops_per_launch": gemm_flops, "launch_us": us[dom]},
+        "backward_ms": bwd_us * 1e-3,
+        "backward_gemm_mfma_frac": 4 * gemm_flops / (sum(us[n] for n in ("down_bwd", "up_bwd", "dw2", "dw1")) * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (forward + backward) on the host ...")
+        out["cpu_baseline"] = cpu_baseline_backward(inp, cfg, 256)
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +279,8 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     inp = I.make_inputs(cfg)
     log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+    if args.backward:
+        return bench_backward(args, cfg, inp, ops, torch, np)
 
     def dev(a, bf16):
         t = torch.from_numpy(np.ascontiguousarray(a))
