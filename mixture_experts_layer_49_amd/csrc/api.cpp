@@ -78,6 +78,8 @@ int check_ffn(const void* a, const int32_t* offsets, int32_t E, int64_t rows_max
                 static_cast<long long>(d_ff));
   if (d > (1 << 22) || d_ff > (1 << 22) || rows_max > 0x7fffffffLL)
     return fail(MOE_ERR_SHAPE, "d and d_ff must be <= 2^22 and rows_max < 2^31");
+  if (dtype == MOE_BF16 && (d > (1 << 20) || d_ff > (1 << 20)))
+    return fail(MOE_ERR_SHAPE, "bf16 layers need d and d_ff <= 2^20");
   MOE_TRY(check_row("d", d, dtype));
   MOE_TRY(check_row("d_ff", d_ff, dtype));
   if (rows_max == 0) return MOE_OK;
@@ -459,6 +461,8 @@ int moe_expert_weight_grads(const void* x_perm, const void* h, const void* d_out
     return fail(MOE_ERR_ARG, "need rows_max >= 0, d > 0, d_ff > 0");
   if (d > (1 << 22) || d_ff > (1 << 22) || rows_max > 0x7fffffffLL)
     return fail(MOE_ERR_SHAPE, "d and d_ff must be <= 2^22 and rows_max < 2^31");
+  if (dtype == MOE_BF16 && (d > (1 << 20) || d_ff > (1 << 20)))
+    return fail(MOE_ERR_SHAPE, "bf16 layers need d and d_ff <= 2^20");
   MOE_TRY(check_row("d", d, dtype));
   MOE_TRY(check_row("d_ff", d_ff, dtype));
   MOE_TRY(check_bwd_limits(rows_max, d, d_ff, dtype));

@@ -86,8 +86,10 @@ static_assert(BM == 256 && BN == 256, "the k-major LDS layout assumes 256-wide t
 constexpr size_t kPartBytes = static_cast<size_t>(BM) * BN * sizeof(float);   // one split partial
 constexpr int kMaxSplit = 8;
 constexpr int kEpiCost = 4;   // epilogue of a tile, in k-steps (K-segmented load balance)
+constexpr int kEpiPitch = 136;   // floats per row of a wave's epilogue staging buffer (see epilogue_wave)
 
-#define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+// s_waitcnt with vmcnt = n (0..62; bits 3:0 and 15:14), expcnt and lgkmcnt not waited on.
+#define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 #define MOE_BARRIER()                                       \
   do {                                                      \
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      \
@@ -113,6 +115,14 @@ using OpDh = GemmOp<false, true, false, false, kCvtNone, kEpiDGelu, false>;
 using OpDx = GemmOp<false, true, false, false, kCvtNone, kEpiF32, false>;
 using OpDw2 = GemmOp<true, true, true, false, kCvtF16ToBf16, kEpiF32, false>;
 using OpDw1 = GemmOp<true, true, true, false, kCvtNone, kEpiF32, false>;
+
+typedef unsigned int u32x4v __attribute__((__vector_size__(16)));
+
+// 16-byte buffer store; a lane whose offset is past the buffer's range stores nothing.
+__device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const u32x4v x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, 0, 0);
+}
 
 struct Ctx {
   __amdgpu_buffer_rsrc_t a, b;
@@ -170,6 +180,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   // are zeroed; a k-major operand reads zeros past K (the buffer ends there),
   // which cancels whatever finite values the other operand holds.
   constexpr bool ZERO_TAIL = !AKM && !BKM;
+  // Output: VPC consecutive values per 16-byte store.
+  constexpr int VPC = EPI == kEpiF32 ? 4 : 8;
+  constexpr int OUT_BYTES = EPI == kEpiF32 ? 4 : 2;
+  constexpr int ITEMS = 8 * (BN / WN) / VPC / kWave;              // 16-B items per lane per chunk
+  constexpr int NST = MI * 4 * ITEMS * (Op::kSaveZ ? 2 : 1);      // stores per lane per tile
+  static_assert(ITEMS * VPC * kWave == 8 * (BN / WN), "a chunk is 8 rows of the quadrant");
+  constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+  // After a per-wave epilogue the memory operations in flight are, oldest
+  // first: the next unit's stage klo, its stage klo+1, then the NST stores.
+  constexpr int kWaitFirstStage = kLoadsPerStage + NST < 62 ? kLoadsPerStage + NST : 62;
+  constexpr int kWaitAfterStores = NST < 62 ? NST : 62;
   __shared__ uint4 st0[kStage];
   __shared__ uint4 st1[kStage];
   __shared__ int s_pref[kMaxE + 1];
@@ -177,7 +198,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   __shared__ int s_tmp[kMaxE];
   __shared__ long long s_cost[SEGK ? kMaxE + 1 : 1];
   __shared__ int s_ticket;
-  uint4* const L[NS] = {st0, st1};
+  __shared__ float s_epi[kWaves][8 * kEpiPitch];   // per-wave epilogue staging
+  // Stage slot S (0 or 1, a compile-time value at every use).
+  auto L = [&](int S) -> uint4* { return S ? st1 : st0; };
   const int tid = threadIdx.x;
 
   for (int e = tid; e <= E; e += kThreads) s_off[e] = offsets[e];
@@ -329,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
 
   auto issue = [&](const Ctx& c, int kt, int S) {
-    uint4* const dst = L[S];
+    uint4* const dst = L(S);
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
       const int blk = j * kWaves + wave;
@@ -350,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   auto zero_tail = [&](int kt, int S) {
     for (int p = tid; p < kStage; p += kThreads) {
       const int c = (p & 7) ^ ((p >> 4) & 7);
-      if (kt * BK + c * 8 >= K) L[S][p] = uint4{0, 0, 0, 0};
+      if (kt * BK + c * 8 >= K) L(S)[p] = uint4{0, 0, 0, 0};
     }
   };
 
@@ -362,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     asm volatile("" : "+v"(x));
     const int c = x ^ (kk * 2);
     const int ab = fr_a + c, bb = fr_b + c;
-    const char* const base = reinterpret_cast<const char*>(L[S]);
+    const char* const base = reinterpret_cast<const char*>(L(S));
     if constexpr (AKM) {
       uint32_t t = tr_a;
       asm volatile("" : "+v"(t));
@@ -374,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[fs][i] = L[S][ab + i * 32 * kCpr];
+      for (int i = 0; i < MI; ++i) fa[fs][i] = L(S)[ab + i * 32 * kCpr];
     }
     if constexpr (BKM) {
       uint32_t t = tr_b;
@@ -387,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) fb[fs][j] = L[S][bb + j * 32 * kCpr];
+      for (int j = 0; j < NI; ++j) fb[fs][j] = L(S)[bb + j * 32 * kCpr];
     }
   };
   auto conv_fb = [&](int fs) {
@@ -457,6 +480,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     read_frags(S ^ 1, 0, 0);
     slice3();
   };
+  // The first stage of a unit that follows a per-wave epilogue: stage kt+1 was
+  // issued before that epilogue's NST stores, so waiting until at most NST
+  // memory operations are in flight is enough (the stores drain meanwhile).
+  auto steady_relaxed = [&](int kt, int S) {
+    slices012(S);
+    MOE_WAIT_VM(kWaitAfterStores);
+    MOE_BARRIER();
+    issue(cur, kt + 2, S);
+    read_frags(S ^ 1, 0, 0);
+    slice3();
+  };
   // Any stage before the last two: zero-fills stage kt+1 where it passes K.
   auto stage = [&](int kt, int S) {
     slices012(S);
@@ -474,7 +508,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   // Output of VPC consecutive values (row, col .. col+VPC-1) of the tile, given
   // as floats; 16 B per store. GELU -> fp16 (and the fp16 pre-activation);
   // f32; or the GELU backward: bf16(value * gelu'(z)) with z read from Z.
-  constexpr int VPC = EPI == kEpiF32 ? 4 : 8;
   auto emit = [&](int c_e, int grow, int gcol, const float4& a, const float4& b) {
     const int64_t at = (SEGK ? static_cast<int64_t>(c_e) * M + grow : static_cast<int64_t>(grow)) * N + gcol;
     if constexpr (EPI == kEpiGelu) {
@@ -604,14 +637,120 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
   };
 
+  // Per-wave epilogue of a whole (unsplit) tile: each wave stages its
+  // 128 x 128 quadrant through its own LDS buffer, eight rows at a time (no
+  // workgroup barrier), and writes whole output rows with 16-byte buffer
+  // stores. Lanes outside the output get an offset past the buffer's range and
+  // are dropped by the hardware, so every wave issues exactly NST stores, which
+  // the next unit's first waits count on. Staged element (row, col) of a chunk
+  // sits at row * kEpiPitch + col: the half-waves of a write (rows r and r + 4)
+  // are 32 banks apart.
+  auto epilogue_wave = [&](int c_m0, int c_n0, int c_seg1, int c_e) {
+    float* const buf = s_epi[wave];
+    // An opaque copy of the lane index: the per-item offsets below are then
+    // recomputed in each epilogue instead of being hoisted out of the unit
+    // loop (dozens of them, which would spill).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int el32 = ln & 31, ehl = ln >> 5;
+    const int rows_ok = min(c_seg1 - c_m0, BM), cols_ok = min(N - c_n0, BN);
+    const int64_t base = (SEGK ? static_cast<int64_t>(c_e) * M + c_m0 : static_cast<int64_t>(c_m0)) * N + c_n0;
+    const int nrec = rows_ok * N * OUT_BYTES;
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(Cout) + base * OUT_BYTES, 0, nrec, 0x00020000);
+    __amdgpu_buffer_rsrc_t zr = out;
+    if constexpr (Op::kSaveZ || EPI == kEpiDGelu)
+      zr = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(Z) + base * 2, 0, rows_ok * N * 2, 0x00020000);
+    // Chunk k = 4 i + c: rows 32 i + 8 c .. +7 of this wave's quadrant. Item q
+    // of a lane: staged row `row`, column `col` of the chunk.
+    auto item_row = [&](int q) { const int f = ln + kWave * q; return VPC == 4 ? (f >> 5) : (f >> 4); };
+    auto item_col = [&](int q) { const int f = ln + kWave * q; return VPC == 4 ? ((f & 31) << 2) : ((f & 15) << 3); };
+    auto item_voff = [&](int k, int q) -> uint32_t {
+      const int trow = wm * (BM / WM) + 8 * k + item_row(q), tcol = wn * (BN / WN) + item_col(q);
+      return (trow < rows_ok && tcol < cols_ok) ? static_cast<uint32_t>((trow * N + tcol) * OUT_BYTES)
+                                                : 0x80000000u;
+    };
+    // GELU backward: z of chunk k is loaded two chunks ahead, so each load is
+    // issued before the stores it would otherwise wait behind.
+    constexpr int ZD = EPI == kEpiDGelu ? 2 : 0;
+    constexpr int ZN = EPI == kEpiDGelu ? MI * 4 : 1;
+    uint4 zv[ZN][ITEMS];
+    auto load_z = [&](int k) {
+      if constexpr (EPI == kEpiDGelu) {
+#pragma unroll
+        for (int q = 0; q < ITEMS; ++q)
+          zv[k][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(zr, item_voff(k, q), 0, 0));
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < ZD; ++k) load_z(k);
+#pragma unroll
+    for (int k = 0; k < MI * 4; ++k) {
+      const int i = k >> 2, c = k & 3;
+      if (k + ZD < MI * 4) load_z(k + ZD);
+      if constexpr (EPI == kEpiDGelu) __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead
+      // register 4 c + rr of block (i, j) holds row 4 hl + rr of the chunk, column 32 j + l32
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          buf[(4 * ehl + rr) * kEpiPitch + 32 * j + el32] = acc[i][j][4 * c + rr];
+#pragma unroll
+      for (int q = 0; q < ITEMS; ++q) {
+        const int row = item_row(q), col = item_col(q);
+        const float4 a = *reinterpret_cast<const float4*>(buf + row * kEpiPitch + col);
+        const float4 b = VPC == 8 ? *reinterpret_cast<const float4*>(buf + row * kEpiPitch + col + 4) : a;
+        const uint32_t voff = item_voff(k, q);
+        if constexpr (EPI == kEpiGelu) {
+          const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
+          const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
+          const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
+          const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
+          store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                        __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
+                  out, voff);
+          if constexpr (Op::kSaveZ) {
+            const f16x2 z0 = {static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)};
+            const f16x2 z1 = {static_cast<_Float16>(a.z), static_cast<_Float16>(a.w)};
+            const f16x2 z2 = {static_cast<_Float16>(b.x), static_cast<_Float16>(b.y)};
+            const f16x2 z3 = {static_cast<_Float16>(b.z), static_cast<_Float16>(b.w)};
+            store16(uint4{__builtin_bit_cast(uint32_t, z0), __builtin_bit_cast(uint32_t, z1),
+                          __builtin_bit_cast(uint32_t, z2), __builtin_bit_cast(uint32_t, z3)},
+                    zr, voff);
+          }
+        } else if constexpr (EPI == kEpiDGelu) {
+          const uint4 zq = zv[k][q];
+          const f16x2 z0 = __builtin_bit_cast(f16x2, zq.x), z1 = __builtin_bit_cast(f16x2, zq.y);
+          const f16x2 z2 = __builtin_bit_cast(f16x2, zq.z), z3 = __builtin_bit_cast(f16x2, zq.w);
+          const bf16x2 q0 = {static_cast<__bf16>(a.x * gelu_tanh_grad_fast(static_cast<float>(z0[0]))),
+                             static_cast<__bf16>(a.y * gelu_tanh_grad_fast(static_cast<float>(z0[1])))};
+          const bf16x2 q1 = {static_cast<__bf16>(a.z * gelu_tanh_grad_fast(static_cast<float>(z1[0]))),
+                             static_cast<__bf16>(a.w * gelu_tanh_grad_fast(static_cast<float>(z1[1])))};
+          const bf16x2 q2 = {static_cast<__bf16>(b.x * gelu_tanh_grad_fast(static_cast<float>(z2[0]))),
+                             static_cast<__bf16>(b.y * gelu_tanh_grad_fast(static_cast<float>(z2[1])))};
+          const bf16x2 q3 = {static_cast<__bf16>(b.z * gelu_tanh_grad_fast(static_cast<float>(z3[0]))),
+                             static_cast<__bf16>(b.w * gelu_tanh_grad_fast(static_cast<float>(z3[1])))};
+          store16(uint4{__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+                        __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)},
+                  out, voff);
+        } else {
+          store16(__builtin_bit_cast(uint4, a), out, voff);
+        }
+      }
+    }
+  };
+
   Unit u = unit(0);
   make_ctx(u.tile, cur);
   issue(cur, u.klo, 0);
   issue(cur, u.klo + 1, 1);
 
+  bool after_wave_epi = false;   // the previous unit ended with epilogue_wave
   for (int64_t q = 0;; ++q) {
-    // Stages klo and klo+1 of this unit (and the previous unit's output stores).
-    MOE_WAIT_VM(0);
+    // Stage klo of this unit has landed (after a per-wave epilogue, stage klo+1
+    // and the stores may still be in flight).
+    if (after_wave_epi) MOE_WAIT_VM(kWaitFirstStage);
+    else MOE_WAIT_VM(0);
     MOE_BARRIER();
     if (u.klo >= kz) {
       zero_tail(u.klo, 0);
@@ -628,6 +767,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
 
     const int khi = u.khi;
     int kt = u.klo;
+    if (kt + 3 < khi && kt + 2 < kz) {
+      steady_relaxed(kt, 0);
+      steady(kt + 1, 1);
+      kt += 2;
+    }
     for (; kt + 3 < khi && kt + 2 < kz; kt += 2) {
       steady(kt, 0);
       steady(kt + 1, 1);
@@ -658,9 +802,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     slice3();
 
     MOE_BARRIER();   // every wave is done reading slot 1
-    epilogue(m0, n0, seg1, te, tail);
+    // A whole tile leaves through the per-wave epilogue, after the next unit's
+    // second stage has been issued into slot 1; a split tile's partial sum
+    // stages through slot 1 first.
+    const bool wave_epi = tail < 0;
+    if (wave_epi) {
+      if (has_next) issue(cur, u.klo + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");   // the stores stay after those loads
+      epilogue_wave(m0, n0, seg1, te);
+    } else {
+      epilogue(m0, n0, seg1, te, tail);
+      if (has_next) issue(cur, u.klo + 1, 1);
+    }
     if (!has_next) break;
-    issue(cur, u.klo + 1, 1);
+    after_wave_epi = wave_epi;
   }
 }
 
