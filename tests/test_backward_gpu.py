@@ -195,3 +195,23 @@ def test_backward_full_size_sampled():
     dl = gpu["dl"].astype(np.float64)
     close(gpu["dwg"], dl.T @ x, "f32", "dWg = d_logits^T x")
     close(gpu["db"], dl.sum(axis=0), "f32", "db = sum_t d_logits")
+
+
+@pytest.mark.parametrize("T,d,E,dt", [(20000, 256, 8, "bf16"), (9000, 72, 20, "f32"), (3, 64, 5, "bf16")])
+def test_gate_weight_grads_any_batch(T, d, E, dt):
+    """dWg = d_logits^T x and db = column sums, for batches whose token chunks
+    are longer than one staging block (T > 8192), an expert count that is not a
+    multiple of 8, and a batch of three tokens; against float64."""
+    rng = np.random.default_rng(T + d + E)
+    dl = rng.standard_normal((T, E)).astype(np.float32)
+    x_np = rng.standard_normal((T, d)).astype(np.float32)
+    if dt == "bf16":
+        x_bits = (torch.from_numpy(x_np).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16))
+        x = dev(x_bits, "bf16")
+        x64 = O.decode(x_bits, "bf16")
+    else:
+        x, x64 = dev(x_np, "f32"), x_np.astype(np.float64)
+    dwg, db = ops.moe_gate_weight_grads(dev(dl, "f32"), x, E)
+    torch.cuda.synchronize()
+    close(host(dwg), dl.astype(np.float64).T @ x64, "f32", "dWg T=%d" % T)
+    close(host(db), dl.astype(np.float64).sum(axis=0), "f32", "db T=%d" % T)
