@@ -62,9 +62,10 @@ GEMM_SOURCES = ["mixture_experts_layer_49_amd/csrc/gemm_mfma.hip",
 
 
 def measured_traffic(which: str, workload: str):
-    """HBM bytes per launch of the up/down GEMM from the committed rocprofv3
-    summary (profiles/gemm_mfma_<which>_<workload>.md), or None when there is
-    none or the kernel source changed after the counters were taken."""
+    """HBM bytes per launch of one GEMM kind (up, down, dh, dx, dw2, dw1) from
+    the committed rocprofv3 summary (profiles/gemm_mfma_<which>_<workload>.md),
+    or None when there is none or the kernel source changed after the counters
+    were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "gemm_mfma_%s_%s.md" % (which, workload))
@@ -121,6 +122,24 @@ def cpu_baseline_backward(inp, cfg, n_tokens):
             "sample": "first %d of the %d tokens (capacity from the sample's own T), forward + "
                       "backward in float64 numpy; %.1f s wall" % (n_tokens, cfg.T, dt),
             "seconds": dt}
+
+
+# bench step name -> GEMM kind (the profile summaries are named after kinds)
+KIND_OF = {"down_bwd": "dh", "up_bwd": "dx", "dw2": "dw2", "dw1": "dw1"}
+
+
+def copy_probe(args, torch, device):
+    """One plain device copy of --copy-probe-mib MiB: a known-size reference for
+    the memory-traffic counters of a profiled run."""
+    if args.copy_probe_mib <= 0:
+        return
+    n = args.copy_probe_mib << 20
+    src_probe = torch.ones(n // 4, dtype=torch.float32, device=device)
+    dst_probe = torch.empty_like(src_probe)
+    torch.cuda.synchronize()
+    dst_probe.copy_(src_probe)
+    torch.cuda.synchronize()
+    del src_probe, dst_probe
 
 
 def bench_backward(args, cfg, inp, ops, torch, np):
@@ -192,6 +211,7 @@ def bench_backward(args, cfg, inp, ops, torch, np):
         ops.moe_dispatch_backward(g.dx_perm, b.dest, d, x.dtype, g.d_logits, wg, g.dx)
         rec(15)
 
+    copy_probe(args, torch, x.device)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -244,9 +264,10 @@ def bench_backward(args, cfg, inp, ops, torch, np):
         "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
                    "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "grouped_gemm_mfma<%s>" % dom, "bound": "mfma",
+        "roofline": {"kernel": "grouped_gemm_mfma<%s>" % KIND_OF[dom], "bound": "mfma",
                      "achieved": breakdown[dom]["TFLOP/s"], "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": breakdown[dom]["mfma_frac"], "traffic": None,
+                     "unit": "TFLOP/s", "frac": breakdown[dom]["mfma_frac"],
+                     "traffic": measured_traffic(KIND_OF[dom], cfg.name),
                      "flops_per_launch": gemm_flops, "launch_us": us[dom]},
         "backward_ms": bwd_us * 1e-3,
         "backward_gemm_mfma_frac": 4 * gemm_flops / (sum(us[n] for n in ("down_bwd", "up_bwd", "dw2", "dw1")) * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS,
@@ -324,14 +345,7 @@ def main(argv=None) -> int:
             ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
         rec(7)
 
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src_probe = torch.ones(n // 4, dtype=torch.float32, device=x.device)
-        dst_probe = torch.empty_like(src_probe)
-        torch.cuda.synchronize()
-        dst_probe.copy_(src_probe)
-        torch.cuda.synchronize()
-        del src_probe, dst_probe
+    copy_probe(args, torch, x.device)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -57,8 +57,10 @@
 // lists run expert, n-panel, m-tile and are cut into equal tile counts; when
 // the last round of an XCD has fewer tiles than workgroups, those tiles are
 // split along K over the idle workgroups (needs the workspace; see the
-// epilogue). K-segmented lists run expert, m-tile, n-tile and are cut into
-// equal shares of k-steps, since an expert's tiles cost its row count.
+// epilogue). K-segmented lists run expert, group of eight m-tiles, n-tile,
+// m-tile (a round of an XCD's 32 workgroups then shares eight A and four B
+// blocks; measured best against groups of 4 and 16) and are cut into equal
+// shares of k-steps, since an expert's tiles cost its row count.
 #include "ffn_common.h"
 
 namespace moe {
@@ -86,6 +88,7 @@ static_assert(BM == 256 && BN == 256, "the k-major LDS layout assumes 256-wide t
 constexpr size_t kPartBytes = static_cast<size_t>(BM) * BN * sizeof(float);   // one split partial
 constexpr int kMaxSplit = 8;
 constexpr int kEpiCost = 4;   // epilogue of a tile, in k-steps (K-segmented load balance)
+constexpr int kSegGroup = 8;  // m-tiles per group of the K-segmented tile order
 constexpr int kEpiPitch = 136;   // floats per row of a wave's epilogue staging buffer (see epilogue_wave)
 
 // s_waitcnt with vmcnt = n (0..62; bits 3:0 and 15:14), expcnt and lgkmcnt not waited on.
@@ -318,8 +321,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       const int rows = __builtin_amdgcn_readfirstlane(s_off[te + 1]) - r0;
       c.e = te;
       c.seg1 = M;
-      c.m0 = __builtin_amdgcn_readfirstlane((local / tiles_n) * BM);
-      c.n0 = __builtin_amdgcn_readfirstlane((local % tiles_n) * BN);
+      // Grouped order: kSegGroup m-tiles at a time, each group sweeping the
+      // n-tiles with its m-tiles inner, so a round of an XCD's workgroups
+      // shares a few A and B blocks and the group's A blocks stay in L2.
+      const int gm = min(kSegGroup, tiles_m - (local / (kSegGroup * tiles_n)) * kSegGroup);
+      const int gbase = (local / (kSegGroup * tiles_n)) * kSegGroup;
+      const int in_g = local - gbase * tiles_n;
+      c.m0 = __builtin_amdgcn_readfirstlane((gbase + in_g % gm) * BM);
+      c.n0 = __builtin_amdgcn_readfirstlane((in_g / gm) * BN);
       const int64_t na = max<int64_t>(0, static_cast<int64_t>(rows) * M - c.m0);
       const int64_t nb = max<int64_t>(0, static_cast<int64_t>(rows) * N - c.n0);
       c.a = __builtin_amdgcn_make_buffer_rsrc(
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
   };
 
-  auto issue = [&](const Ctx& c, int kt, int S) {
+  auto issue = [&](const Ctx& c, int kt, int S) __attribute__((always_inline)) {
     uint4* const dst = L(S);
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
   };
   // Zero the chunks of stage kt (slot S) that lie past K.
-  auto zero_tail = [&](int kt, int S) {
+  auto zero_tail = [&](int kt, int S) __attribute__((always_inline)) {
     for (int p = tid; p < kStage; p += kThreads) {
       const int c = (p & 7) ^ ((p >> 4) & 7);
       if (kt * BK + c * 8 >= K) L(S)[p] = uint4{0, 0, 0, 0};
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
 
   uint4 fa[2][MI], fb[2][NI];
-  auto read_frags = [&](int S, int kk, int fs) {
+  auto read_frags = [&](int S, int kk, int fs) __attribute__((always_inline)) {
     // The lane terms are made opaque here so that the bases are recomputed
     // (a few adds) rather than eight of them held across the loop.
     int x = fr_x;
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       for (int j = 0; j < NI; ++j) fb[fs][j] = L(S)[bb + j * 32 * kCpr];
     }
   };
-  auto conv_fb = [&](int fs) {
+  auto conv_fb = [&](int fs) __attribute__((always_inline)) {
     if constexpr (CVT == kCvtBf16ToF16) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) fb[fs][j] = bf16x8_to_f16x8(fb[fs][j]);
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
 
   f32x16 acc[MI][NI];
-  auto mfma_block = [&](int fs, int cs) {
+  auto mfma_block = [&](int fs, int cs) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
   // The first three k-slices of stage kt (slot S); set 0 holds slice 0 on entry,
   // set 1 holds slice 3 on exit.
-  auto slices012 = [&](int S) {
+  auto slices012 = [&](int S) __attribute__((always_inline)) {
     read_frags(S, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(0, 1);
@@ -464,35 +473,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     mfma_block(0, 1);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto slice3 = [&]() {
+  auto slice3 = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(1, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   Ctx cur;
+  // After the stage barrier: the fourth slice's 16 MFMAs (fragment set 1) with
+  // the DMA of stage kt+2 and the reads of the next stage's first fragments
+  // (set 0) issued between them, so the matrix unit is not idle while the
+  // wave issues the loads; converting kinds convert set 0 in the second half,
+  // once its reads have landed.
+  auto boundary = [&](int kt, int S) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue(cur, kt + 2, S);
+    read_frags(S ^ 1, 0, 0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        if constexpr (!F16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[1][i]), __builtin_bit_cast(bf16x8, fb[1][j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, fa[1][i]), __builtin_bit_cast(f16x8, fb[1][j]), acc[i][j], 0, 0, 0);
+      }
+    conv_fb(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);     // SALU (DMA setup)
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read (DMA)
+      if (q >= 2 && q < 6) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU (read addresses)
+        __builtin_amdgcn_sched_group_barrier(0x100, AKM || BKM ? 3 : 2, 0);   // DS read
+      }
+      if (CVT != kCvtNone && q >= 8) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // conversion
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   // Steady stage: stage kt+1 needs no zero fill and stage kt+2 belongs to this tile.
-  auto steady = [&](int kt, int S) {
+  auto steady = [&](int kt, int S) __attribute__((always_inline)) {
     slices012(S);
     MOE_WAIT_VM(0);   // stage kt+1 has landed (the only one in flight)
     MOE_BARRIER();    // ... for every wave, and every wave is done with slot S
-    issue(cur, kt + 2, S);
-    read_frags(S ^ 1, 0, 0);
-    slice3();
+    boundary(kt, S);
   };
   // The first stage of a unit that follows a per-wave epilogue: stage kt+1 was
   // issued before that epilogue's NST stores, so waiting until at most NST
   // memory operations are in flight is enough (the stores drain meanwhile).
-  auto steady_relaxed = [&](int kt, int S) {
+  auto steady_relaxed = [&](int kt, int S) __attribute__((always_inline)) {
     slices012(S);
     MOE_WAIT_VM(kWaitAfterStores);
     MOE_BARRIER();
-    issue(cur, kt + 2, S);
-    read_frags(S ^ 1, 0, 0);
-    slice3();
+    boundary(kt, S);
   };
   // Any stage before the last two: zero-fills stage kt+1 where it passes K.
-  auto stage = [&](int kt, int S) {
+  auto stage = [&](int kt, int S) __attribute__((always_inline)) {
     slices012(S);
     MOE_WAIT_VM(0);
     MOE_BARRIER();
