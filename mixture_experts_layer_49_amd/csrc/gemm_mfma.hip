@@ -258,7 +258,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   const int64_t full = n_x / P;
   const int rem = static_cast<int>(n_x - full * P);
   int S = 1;
-  if (!SEGK && rem > 0 && max_split > 1) S = max(1, min(min(P / rem, max_split), nk2 / 8));
+  // Each split keeps >= 64 stages: shorter pieces lose more to the partial
+  // store and the fix-up than they gain (measured on 64-stage tiles).
+  if (!SEGK && rem > 0 && max_split > 1) S = max(1, min(min(P / rem, max_split), nk2 / 64));
   const int64_t n_units = full + (w < rem * S ? 1 : 0);
   if (n_units == 0) return;
   // Unit q of this workgroup: a whole tile of round q, or (q == full) its
@@ -652,27 +654,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     __threadfence();   // acquire: the other splits' partials
     const float* const first = part + static_cast<int64_t>(xcd * P + tail) * (BM * BN);
     const int64_t step = static_cast<int64_t>(rem) * (BM * BN);   // split si sits at slot si * rem + tail
+    // QU items per thread per pass, and the values of all kMaxSplit slots
+    // loaded before any is added (slots past S re-read slot S - 1 and are not
+    // added), so the pass has QU * kMaxSplit loads in flight instead of one.
+    constexpr int QU = VPC == 8 ? 1 : 2;
+    constexpr int NV = VPC / 4;   // float4 per item
 #pragma unroll 1
-    for (int q = tid; q < BM * BN / VPC; q += kThreads) {
-      const int row = q / (BN / VPC);
-      const int col = (q % (BN / VPC)) * VPC;
-      const int grow = c_m0 + row;
-      const int gcol = c_n0 + col;
-      if (grow >= c_seg1 || gcol >= N) continue;
-      const float* src = first + row * BN + col;
-      float4 a = *reinterpret_cast<const float4*>(src);
-      float4 b = VPC == 8 ? *reinterpret_cast<const float4*>(src + 4) : a;
-#pragma unroll 1
-      for (int si = 1; si < S; ++si) {
-        src += step;
-        const float4 a2 = *reinterpret_cast<const float4*>(src);
-        a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-        if (VPC == 8) {
-          const float4 b2 = *reinterpret_cast<const float4*>(src + 4);
-          b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+    for (int q0 = tid; q0 < BM * BN / VPC; q0 += kThreads * QU) {
+      float4 v[kMaxSplit][QU][NV];
+#pragma unroll
+      for (int si = 0; si < kMaxSplit; ++si)
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          const int q = q0 + u * kThreads;
+          const float* src = first + min(si, S - 1) * step + (q / (BN / VPC)) * BN + (q % (BN / VPC)) * VPC;
+#pragma unroll
+          for (int h = 0; h < NV; ++h) v[si][u][h] = *reinterpret_cast<const float4*>(src + 4 * h);
         }
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int q = q0 + u * kThreads;
+        const int row = q / (BN / VPC);
+        const int col = (q % (BN / VPC)) * VPC;
+        float4 a = v[0][u][0];
+        float4 b = v[0][u][NV - 1];
+#pragma unroll
+        for (int si = 1; si < kMaxSplit; ++si) {
+          if (si >= S) break;
+          const float4 a2 = v[si][u][0];
+          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+          if (VPC == 8) {
+            const float4 b2 = v[si][u][NV - 1];
+            b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+          }
+        }
+        const int grow = c_m0 + row, gcol = c_n0 + col;
+        if (grow < c_seg1 && gcol < N) emit(c_e, grow, gcol, a, b);
       }
-      emit(c_e, grow, gcol, a, b);
     }
   };
 
