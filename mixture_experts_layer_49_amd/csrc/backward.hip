@@ -188,17 +188,18 @@ __global__ __launch_bounds__(kThreads) void gate_backward_kernel(
 // Partial sums over token chunks: workgroup (cb, ch) takes columns
 // 256 cb .. +255 and tokens [ch * chunk, (ch + 1) * chunk). Thread (cg, tl):
 // columns 4 cg .. +3, tokens tl, tl + 4, ... in 256-token sub-chunks; experts
-// 8 at a time. The four token lanes meet in LDS in lane order. Column block 0
+// 16 at a time. The four token lanes meet in LDS in lane order. Column block 0
 // also sums the chunk's dl columns (the bias gradient), in a fixed order.
 constexpr int kWgSub = 256;
 constexpr int kWgTU = 8;                       // tokens per lane per pass
 constexpr int kWgRows = kWgSub + 4 * kWgTU;    // staged dl rows: a pass may run 4 TU - 4 past n
+constexpr int kWgE = 16;                       // experts per pass over x
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void gate_wgrad_partial_kernel(
     const float* __restrict__ dl, const void* __restrict__ x, int64_t T, int64_t d, int E,
     int64_t chunk, float* __restrict__ part, float* __restrict__ part_b) {
-  __shared__ float s_dl[kWgRows][8];   // rows >= n hold zeros
+  __shared__ float s_dl[kWgRows][kWgE];   // rows >= n hold zeros
   __shared__ float4 s_red[4][8][64];
   __shared__ float s_bias[kThreads];
   const int tid = threadIdx.x, cg = tid & 63, tl = tid >> 6;
@@ -206,18 +207,18 @@ __global__ __launch_bounds__(kThreads) void gate_wgrad_partial_kernel(
   const int64_t t0 = ch * chunk, t1 = min(t0 + chunk, T);
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 256 + 4 * cg;
   const bool col_ok = c0 < d;
-  for (int e0 = 0; e0 < E; e0 += 8) {
-    float4 acc[8];
+  for (int e0 = 0; e0 < E; e0 += kWgE) {
+    float4 acc[kWgE];
     float bsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = float4{0, 0, 0, 0};
+    for (int e = 0; e < kWgE; ++e) acc[e] = float4{0, 0, 0, 0};
     for (int64_t s0 = t0; s0 < t1; s0 += kWgSub) {
       const int n = static_cast<int>(min<int64_t>(kWgSub, t1 - s0));
       __syncthreads();
-      // Thread tid stages expert e0 + (tid & 7) of tokens tid / 8, + 32, ...
-      // and keeps their sum for the bias gradient.
-      for (int i = tid; i < kWgRows * 8; i += kThreads) {
-        const int tt = i >> 3, e = i & 7;
+      // Thread tid stages expert e0 + (tid % kWgE) of tokens tid / kWgE,
+      // + 256 / kWgE, ... and keeps their sum for the bias gradient.
+      for (int i = tid; i < kWgRows * kWgE; i += kThreads) {
+        const int tt = i / kWgE, e = i % kWgE;
         const float v = (tt < n && e0 + e < E) ? dl[(s0 + tt) * E + e0 + e] : 0.f;
         s_dl[tt][e] = v;
         bsum += v;
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void gate_wgrad_partial_kernel(
           for (int u = 0; u < TU; ++u) {
             const int tt = tb + 4 * u;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < kWgE; ++e) {
               const float a = s_dl[tt][e];
               acc[e].x = fmaf(a, xv[u].x, acc[e].x);
               acc[e].y = fmaf(a, xv[u].y, acc[e].y);
@@ -263,25 +264,29 @@ __global__ __launch_bounds__(kThreads) void gate_wgrad_partial_kernel(
         }
       }
     }
-    __syncthreads();
+    // the four token lanes meet in LDS, eight experts at a time
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_red[tl][e][cg] = acc[e];
-    __syncthreads();
-    if (tl == 0 && col_ok) {
-      for (int e = 0; e < 8 && e0 + e < E; ++e) {
-        const float4 a = s_red[0][e][cg], b = s_red[1][e][cg], c = s_red[2][e][cg], f = s_red[3][e][cg];
-        const float4 s = float4{((a.x + b.x) + c.x) + f.x, ((a.y + b.y) + c.y) + f.y,
-                                ((a.z + b.z) + c.z) + f.z, ((a.w + b.w) + c.w) + f.w};
-        *reinterpret_cast<float4*>(part + (ch * E + e0 + e) * d + c0) = s;
+    for (int h = 0; h < kWgE / 8; ++h) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_red[tl][e][cg] = acc[8 * h + e];
+      __syncthreads();
+      if (tl == 0 && col_ok) {
+        for (int e = 0; e < 8 && e0 + 8 * h + e < E; ++e) {
+          const float4 a = s_red[0][e][cg], b = s_red[1][e][cg], c = s_red[2][e][cg], f = s_red[3][e][cg];
+          const float4 s = float4{((a.x + b.x) + c.x) + f.x, ((a.y + b.y) + c.y) + f.y,
+                                  ((a.z + b.z) + c.z) + f.z, ((a.w + b.w) + c.w) + f.w};
+          *reinterpret_cast<float4*>(part + (ch * E + e0 + 8 * h + e) * d + c0) = s;
+        }
       }
     }
-    // Bias (column block 0): the 32 threads of each expert add up in tid order.
+    // Bias (column block 0): the threads of each expert add up in tid order.
     if (blockIdx.x == 0) {
       s_bias[tid] = bsum;
       __syncthreads();
-      if (tid < 8 && e0 + tid < E) {
+      if (tid < kWgE && e0 + tid < E) {
         float b = 0.f;
-        for (int q = 0; q < kThreads / 8; ++q) b += s_bias[tid + 8 * q];
+        for (int q = 0; q < kThreads / kWgE; ++q) b += s_bias[tid + kWgE * q];
         part_b[ch * E + e0 + tid] = b;
       }
       __syncthreads();
@@ -371,62 +376,43 @@ __global__ __launch_bounds__(kThreads) void dispatch_backward_kernel(
   }
 }
 
-// Few experts: a thread owns one 4-column group of dx for kDispTok tokens and
-// keeps the gate weight's E values of those columns in registers.
+// A thread owns one 4-column group of dx for kDispTok tokens: it sums the
+// tokens' kept rows of dx_perm, then adds the gate term 16 experts at a time
+// with those experts' gate-weight columns in registers (loaded once for all
+// kDispTok tokens). Rows and weights come through range-checked buffer loads,
+// so a dropped slot or an expert past E reads zeros without a branch.
 constexpr int kDispTok = 16;
-constexpr int kDispMaxE = 16;
+constexpr int kDispEChunk = 16;
 
 template <bool WG_BF16, int KM>
-__global__ __launch_bounds__(kThreads) void dispatch_backward_fewe_kernel(
+__global__ __launch_bounds__(kThreads) void dispatch_backward_tok_kernel(
     const float* __restrict__ dx_perm, const int32_t* __restrict__ dest, const float* __restrict__ dl,
     const void* __restrict__ wg, int64_t T, int k, int64_t d, int E, float* __restrict__ dx) {
-  // TU tokens' rows are loaded together (TU * KM 16-byte loads in flight).
-  constexpr int TU = KM <= 2 ? 4 : 1;
-  __shared__ float s_dl[kDispTok][kDispMaxE];
+  constexpr int TU = KM <= 2 ? 4 : 1;   // tokens whose rows are loaded together
+  __shared__ float s_dl[kDispTok][kMaxE];
   __shared__ int s_dest[kDispTok][kMaxK];
   const int tid = threadIdx.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kDispTok;
   const bool gate = dl != nullptr;
+  const int e_pad = (E + kDispEChunk - 1) / kDispEChunk * kDispEChunk;
   for (int i = tid; i < kDispTok * kMaxK; i += kThreads) {
     const int tt = i / kMaxK, j = i % kMaxK;
     s_dest[tt][j] = (t0 + tt < T && j < k) ? dest[(t0 + tt) * k + j] : -1;
   }
   if (gate)
-    for (int i = tid; i < kDispTok * kDispMaxE; i += kThreads) {
-      const int tt = i / kDispMaxE, e = i % kDispMaxE;
+    for (int i = tid; i < kDispTok * e_pad; i += kThreads) {
+      const int tt = i / e_pad, e = i % e_pad;
       s_dl[tt][e] = (t0 + tt < T && e < E) ? dl[(t0 + tt) * E + e] : 0.f;
     }
   __syncthreads();
   const int64_t d4 = d >> 2;
   const int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
   if (v >= d4) return;
-  // The gate weight's columns, loaded once for all kDispTok tokens; experts
-  // past E read zeros through the buffer range check.
-  float4 w[kDispMaxE];
-  {
-    const int eb = WG_BF16 ? 2 : 4;
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(wg), 0, gate ? static_cast<int>(static_cast<int64_t>(E) * d * eb) : 0, 0x00020000);
-#pragma unroll
-    for (int e = 0; e < kDispMaxE; ++e) {
-      const uint32_t off = static_cast<uint32_t>((static_cast<int64_t>(e) * d + 4 * v) * eb);
-      if constexpr (WG_BF16) {
-        const uint2 b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wr, off, 0, 0));
-        w[e] = float4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
-                      __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
-      } else {
-        w[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // dx_perm rows through a buffer resource: a dropped slot's load gets an
-  // offset past the range and returns zeros, so the loads need no branch.
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(dx_perm), 0, 0x7fffffff, 0x00020000);
-#pragma unroll 1
+  float4 acc[kDispTok];
+#pragma unroll
   for (int tt0 = 0; tt0 < kDispTok; tt0 += TU) {
-    if (t0 + tt0 >= T) break;
     float4 o[TU][KM];
 #pragma unroll
     for (int u = 0; u < TU; ++u)
@@ -439,27 +425,49 @@ __global__ __launch_bounds__(kThreads) void dispatch_backward_fewe_kernel(
     __builtin_amdgcn_sched_barrier(0);   // the group's loads before its sums
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
-      if (t0 + tt0 + u >= T) break;
-      float4 acc = float4{0, 0, 0, 0};
+      float4 a = float4{0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < KM; ++j)
+      for (int j = 0; j < KM; ++j)   // slot order; a dropped slot is skipped
         if (s_dest[tt0 + u][j] >= 0) {
-          acc.x += o[u][j].x; acc.y += o[u][j].y; acc.z += o[u][j].z; acc.w += o[u][j].w;
+          a.x += o[u][j].x; a.y += o[u][j].y; a.z += o[u][j].z; a.w += o[u][j].w;
         }
-      if (gate) {
-#pragma unroll
-        for (int e = 0; e < kDispMaxE; ++e) {
-          // zero weights and zero s_dl past E: adding a * w = 0 changes nothing
-          const float a = s_dl[tt0 + u][e];
-          acc.x = fmaf(a, w[e].x, acc.x);
-          acc.y = fmaf(a, w[e].y, acc.y);
-          acc.z = fmaf(a, w[e].z, acc.z);
-          acc.w = fmaf(a, w[e].w, acc.w);
-        }
-      }
-      reinterpret_cast<float4*>(dx)[(t0 + tt0 + u) * d4 + v] = acc;
+      acc[tt0 + u] = a;
     }
   }
+  if (gate) {
+    const int eb = WG_BF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(wg), 0, static_cast<int>(static_cast<int64_t>(E) * d * eb), 0x00020000);
+#pragma unroll 1
+    for (int e0 = 0; e0 < E; e0 += kDispEChunk) {
+      float4 w[kDispEChunk];
+#pragma unroll
+      for (int e = 0; e < kDispEChunk; ++e) {
+        const uint32_t off = static_cast<uint32_t>((static_cast<int64_t>(e0 + e) * d + 4 * v) * eb);
+        if constexpr (WG_BF16) {
+          const uint2 b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wr, off, 0, 0));
+          w[e] = float4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                        __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
+        } else {
+          w[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+        }
+      }
+      // experts past E carry zero weights and zero s_dl: their terms add 0
+#pragma unroll
+      for (int tt = 0; tt < kDispTok; ++tt)
+#pragma unroll
+        for (int e = 0; e < kDispEChunk; ++e) {
+          const float a = s_dl[tt][e0 + e];
+          acc[tt].x = fmaf(a, w[e].x, acc[tt].x);
+          acc[tt].y = fmaf(a, w[e].y, acc[tt].y);
+          acc[tt].z = fmaf(a, w[e].z, acc[tt].z);
+          acc[tt].w = fmaf(a, w[e].w, acc[tt].w);
+        }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kDispTok; ++tt)
+    if (t0 + tt < T) reinterpret_cast<float4*>(dx)[(t0 + tt) * d4 + v] = acc[tt];
 }
 
 // ------------------------------------------------------------ f32 expert GEMMs
@@ -662,16 +670,17 @@ hipError_t launch_dispatch_backward(const float* dx_perm, const int32_t* dest, c
                                     const void* wg, int64_t T, int k, int64_t d, int E, int dtype,
                                     float* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (E <= kDispMaxE && (T + kDispTok - 1) / kDispTok <= 65535 &&
-      static_cast<int64_t>(T) * k * d * 4 < 0x7fffffffLL) {   // grouped rows <= T k
+  if ((T + kDispTok - 1) / kDispTok <= 65535 &&
+      static_cast<int64_t>(T) * k * d * 4 < 0x7fffffffLL &&   // grouped rows <= T k
+      static_cast<int64_t>(E) * d * 4 < 0x7fffffffLL) {
     const dim3 g(static_cast<unsigned>(((d >> 2) + kThreads - 1) / kThreads),
                  static_cast<unsigned>((T + kDispTok - 1) / kDispTok));
     if (k <= 2) {
-      if (dtype == 1) hipLaunchKernelGGL((dispatch_backward_fewe_kernel<true, 2>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
-      else hipLaunchKernelGGL((dispatch_backward_fewe_kernel<false, 2>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
+      if (dtype == 1) hipLaunchKernelGGL((dispatch_backward_tok_kernel<true, 2>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
+      else hipLaunchKernelGGL((dispatch_backward_tok_kernel<false, 2>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
     } else {
-      if (dtype == 1) hipLaunchKernelGGL((dispatch_backward_fewe_kernel<true, kMaxK>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
-      else hipLaunchKernelGGL((dispatch_backward_fewe_kernel<false, kMaxK>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
+      if (dtype == 1) hipLaunchKernelGGL((dispatch_backward_tok_kernel<true, kMaxK>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
+      else hipLaunchKernelGGL((dispatch_backward_tok_kernel<false, kMaxK>), g, dim3(kThreads), 0, s, dx_perm, dest, dl, wg, T, k, d, E, dx);
     }
     return hipGetLastError();
   }
