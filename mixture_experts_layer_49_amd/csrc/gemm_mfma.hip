@@ -190,6 +190,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   constexpr int NST = MI * 4 * ITEMS * (Op::kSaveZ ? 2 : 1);      // stores per lane per tile
   static_assert(ITEMS * VPC * kWave == 8 * (BN / WN), "a chunk is 8 rows of the quadrant");
   constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+  // A steady stage's loads leave in three parts: kSpread0 between the MFMAs
+  // after the stage barrier, kSpreadPer in each of the next two k-slices, so
+  // the TA queue does not fill and hold up the MFMA issue behind it. The
+  // K-segmented kinds (short tiles of both-k-major operands) measured slower
+  // that way and issue the whole stage at the barrier.
+  constexpr int kSpread0 = SEGK ? kLoadsPerStage : kLoadsPerStage / 2;
+  constexpr int kSpreadPer = (kLoadsPerStage - kSpread0) / 2;
+  static_assert(kSpread0 + 2 * kSpreadPer == kLoadsPerStage, "the parts cover the stage");
   // After a per-wave epilogue the memory operations in flight are, oldest
   // first: the next unit's stage klo, its stage klo+1, then the NST stores.
   constexpr int kWaitFirstStage = kLoadsPerStage + NST < 62 ? kLoadsPerStage + NST : 62;
@@ -362,23 +370,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
   };
 
-  auto issue = [&](const Ctx& c, int kt, int S) __attribute__((always_inline)) {
+  // Loads j0 .. j1-1 of stage kt into slot S: the A loads are 0 .. kLoadsA-1,
+  // the B loads follow.
+  auto issue_range = [&](const Ctx& c, int kt, int S, int j0, int j1) __attribute__((always_inline)) {
     uint4* const dst = L(S);
 #pragma unroll
-    for (int j = 0; j < kLoadsA; ++j) {
-      const int blk = j * kWaves + wave;
-      const uint32_t so = AKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * a_rb)
-                              : (blk * kRowsPerLoad * a_rb + static_cast<uint32_t>(kt) * BK * 2u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16, ld_voff_a, so, 0, 0);
+    for (int jj = j0; jj < j1; ++jj) {
+      if (jj < kLoadsA) {
+        const int blk = jj * kWaves + wave;
+        const uint32_t so = AKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * a_rb)
+                                : (blk * kRowsPerLoad * a_rb + static_cast<uint32_t>(kt) * BK * 2u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16, ld_voff_a, so, 0, 0);
+      } else {
+        const int blk = (jj - kLoadsA) * kWaves + wave;
+        const uint32_t so = BKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * b_rb)
+                                : (blk * kRowsPerLoad * b_rb + static_cast<uint32_t>(kt) * BK * 2u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(dst + BM * kCpr + blk * kWave), 16,
+                                                 ld_voff_b, so, 0, 0);
+      }
     }
-#pragma unroll
-    for (int j = 0; j < kLoadsB; ++j) {
-      const int blk = j * kWaves + wave;
-      const uint32_t so = BKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * b_rb)
-                              : (blk * kRowsPerLoad * b_rb + static_cast<uint32_t>(kt) * BK * 2u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(dst + BM * kCpr + blk * kWave), 16,
-                                               ld_voff_b, so, 0, 0);
-    }
+  };
+  auto issue = [&](const Ctx& c, int kt, int S) __attribute__((always_inline)) {
+    issue_range(c, kt, S, 0, kLoadsPerStage);
   };
   // Zero the chunks of stage kt (slot S) that lie past K.
   auto zero_tail = [&](int kt, int S) __attribute__((always_inline)) {
@@ -388,6 +401,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
   };
 
+  Ctx cur;
+  // A steady boundary left loads kSpread0 .. of the stage after the current one
+  // for the next k-slices to issue.
+  bool pend = false;
   uint4 fa[2][MI], fb[2][NI];
   auto read_frags = [&](int S, int kk, int fs) __attribute__((always_inline)) {
     // The lane terms are made opaque here so that the bases are recomputed
@@ -435,7 +452,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
 
   f32x16 acc[MI][NI];
-  auto mfma_block = [&](int fs, int cs) __attribute__((always_inline)) {
+  // 16 MFMAs of fragment set fs; converting kinds convert set cs between them.
+  // ND (a compile-time count) loads j0 .. j0+ND-1 of stage kt (slot S) are
+  // issued between them as well, one after every 16/ND-th MFMA.
+  auto mfma_block = [&](int fs, int cs, auto nd_c, int kt, int S, int j0) __attribute__((always_inline)) {
+    constexpr int ND = decltype(nd_c)::value;
+    if constexpr (ND > 0) issue_range(cur, kt, S, j0, j0 + ND);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -456,40 +478,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       for (int q = 0; q < 12; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (ND > 0 && q * ND % 12 < ND) {
+          __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+    } else if constexpr (ND > 0) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if ((q + 15) * ND % 16 < ND) {   // after MFMA 1, 1 + 16/ND, ...
+          __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
       }
     }
   };
+  using NoLoads = std::integral_constant<int, 0>;
+  using SliceLoads = std::integral_constant<int, kSpreadPer>;
   // The first three k-slices of stage kt (slot S); set 0 holds slice 0 on entry,
-  // set 1 holds slice 3 on exit.
-  auto slices012 = [&](int S) __attribute__((always_inline)) {
+  // set 1 holds slice 3 on exit. PEND (compile time): the loads kSpread0 ..
+  // of stage kt+1 (slot S^1) go out during slices 0 and 1.
+  auto slices012 = [&](int S, int kt, auto pend_c) __attribute__((always_inline)) {
+    constexpr bool PEND = decltype(pend_c)::value;
+    using L01 = std::conditional_t<PEND, SliceLoads, NoLoads>;
     read_frags(S, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(0, 1);
+    mfma_block(0, 1, L01{}, kt + 1, S ^ 1, kSpread0);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(S, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(1, 0);
+    mfma_block(1, 0, L01{}, kt + 1, S ^ 1, kSpread0 + kSpreadPer);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(S, 3, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(0, 1);
+    mfma_block(0, 1, NoLoads{}, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // Loads of stage kt+1 (slot S^1) a steady boundary left, issued at once
+  // where no steady stage follows.
+  auto flush_pending = [&](int kt, int S) __attribute__((always_inline)) {
+    if (pend) issue_range(cur, kt + 1, S ^ 1, kSpread0, kLoadsPerStage);
+    pend = false;
   };
   auto slice3 = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(1, 0);
+    mfma_block(1, 0, NoLoads{}, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  Ctx cur;
   // After the stage barrier: the fourth slice's 16 MFMAs (fragment set 1) with
-  // the DMA of stage kt+2 and the reads of the next stage's first fragments
-  // (set 0) issued between them, so the matrix unit is not idle while the
-  // wave issues the loads; converting kinds convert set 0 in the second half,
-  // once its reads have landed.
+  // the first kSpread0 loads of stage kt+2 and the reads of the next stage's
+  // first fragments (set 0) issued between them, so the matrix unit is not
+  // idle while the wave issues the loads; converting kinds convert set 0 in
+  // the second half, once its reads have landed. The rest of stage kt+2
+  // follows during the next stage's first two slices.
   auto boundary = [&](int kt, int S) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    issue(cur, kt + 2, S);
+    issue_range(cur, kt + 2, S, 0, kSpread0);
     read_frags(S ^ 1, 0, 0);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -506,8 +552,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);     // SALU (DMA setup)
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read (DMA)
+      if (q * kSpread0 % 16 < kSpread0) {
+        __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);   // SALU (DMA setup)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
+      }
       if (q >= 2 && q < 6) {
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU (read addresses)
         __builtin_amdgcn_sched_group_barrier(0x100, AKM || BKM ? 3 : 2, 0);   // DS read
@@ -518,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   };
   // Steady stage: stage kt+1 needs no zero fill and stage kt+2 belongs to this tile.
   auto steady = [&](int kt, int S) __attribute__((always_inline)) {
-    slices012(S);
+    slices012(S, kt, std::true_type{});
     MOE_WAIT_VM(0);   // stage kt+1 has landed (the only one in flight)
     MOE_BARRIER();    // ... for every wave, and every wave is done with slot S
     boundary(kt, S);
@@ -527,14 +575,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   // issued before that epilogue's NST stores, so waiting until at most NST
   // memory operations are in flight is enough (the stores drain meanwhile).
   auto steady_relaxed = [&](int kt, int S) __attribute__((always_inline)) {
-    slices012(S);
+    slices012(S, kt, std::false_type{});
     MOE_WAIT_VM(kWaitAfterStores);
     MOE_BARRIER();
     boundary(kt, S);
   };
   // Any stage before the last two: zero-fills stage kt+1 where it passes K.
   auto stage = [&](int kt, int S) __attribute__((always_inline)) {
-    slices012(S);
+    flush_pending(kt, S);
+    slices012(S, kt, std::false_type{});
     MOE_WAIT_VM(0);
     MOE_BARRIER();
     if (kt + 1 >= kz) {
@@ -833,6 +882,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       steady(kt, 0);
       steady(kt + 1, 1);
     }
+    pend = kt > u.klo;   // a steady boundary came last
     for (; kt + 2 < khi; kt += 2) {
       stage(kt, 0);
       stage(kt + 1, 1);
@@ -841,7 +891,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     // unit's first stage, slot 1 then stages this unit's outputs.
     const int m0 = cur.m0, n0 = cur.n0, seg1 = cur.seg1, te = cur.e, tail = u.tail;
     const bool has_next = q + 1 < n_units;
-    slices012(0);
+    flush_pending(kt, 0);
+    slices012(0, kt, std::false_type{});
     MOE_WAIT_VM(0);
     MOE_BARRIER();
     if (kt + 1 >= kz) {
@@ -855,7 +906,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
     read_frags(1, 0, 0);
     slice3();
-    slices012(1);
+    slices012(1, kt + 1, std::false_type{});
     slice3();
 
     MOE_BARRIER();   // every wave is done reading slot 1
