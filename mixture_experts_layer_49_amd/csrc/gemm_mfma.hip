@@ -56,8 +56,9 @@
 // L2, and within the XCD the workgroups take consecutive tiles. Row-segmented
 // lists run expert, n-panel, m-tile and are cut into equal tile counts; when
 // the last round of an XCD has fewer tiles than workgroups, those tiles are
-// split along K over the idle workgroups (needs the workspace; see the
-// epilogue). K-segmented lists run expert, group of eight m-tiles, n-tile,
+// split along K over the idle workgroups (needs the workspace): each piece
+// stores its float32 partial sum, and a second kernel adds the pieces up in
+// split order and applies the epilogue. K-segmented lists run expert, group of eight m-tiles, n-tile,
 // m-tile (a round of an XCD's 32 workgroups then shares eight A and four B
 // blocks; measured best against groups of 4 and 16) and are cut into equal
 // shares of k-steps, since an expert's tiles cost its row count.
@@ -172,11 +173,78 @@ __device__ __forceinline__ int seg_k_steps(const int* s_off, int e) {
   return max(2, (nk + 1) & ~1);
 }
 
+// How an XCD's share of a row-segmented tile list runs: tiles r_beg ..
+// r_beg + n_x - 1, `full` whole rounds over its P workgroups, then rem tiles,
+// each split into S k-ranges when rem < P and the workspace allows it.
+struct RowPlan {
+  int64_t r_beg, n_x, full;
+  int rem, S;
+};
+__device__ __forceinline__ RowPlan row_plan(int64_t total, int xcd, int P, int nk2, int max_split) {
+  RowPlan p;
+  p.r_beg = total * xcd / 8;
+  p.n_x = total * (xcd + 1) / 8 - p.r_beg;
+  p.full = p.n_x / P;
+  p.rem = static_cast<int>(p.n_x - p.full * P);
+  p.S = 1;
+  // Pieces keep >= 64 stages when they only fill a last round (measured on
+  // 64-stage tiles: shorter ones lost more to the partial store and the
+  // fix-up than they gained); when the whole launch is a partial round,
+  // pieces of 16 stages still pay.
+  if (p.rem > 0 && max_split > 1)
+    p.S = max(1, min(min(P / p.rem, max_split), nk2 / (p.full == 0 ? 16 : 64)));
+  return p;
+}
+
+// VPC consecutive outputs at element offset `at` (and of Z), given as floats
+// (b holds values 4..7 when VPC is 8): GELU -> fp16 (and the fp16
+// pre-activation); f32; or the GELU backward: bf16(value * gelu'(z)) with z
+// read from Z.
+template <class Op>
+__device__ __forceinline__ void emit_values(void* Cout, uint16_t* Z, int64_t at, const float4& a,
+                                            const float4& b) {
+  if constexpr (Op::kEpi == kEpiGelu) {
+    const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
+    const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
+    const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
+    const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Cout) + at) =
+        uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+    if constexpr (Op::kSaveZ) {
+      const f16x2 z0 = {static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)};
+      const f16x2 z1 = {static_cast<_Float16>(a.z), static_cast<_Float16>(a.w)};
+      const f16x2 z2 = {static_cast<_Float16>(b.x), static_cast<_Float16>(b.y)};
+      const f16x2 z3 = {static_cast<_Float16>(b.z), static_cast<_Float16>(b.w)};
+      *reinterpret_cast<uint4*>(Z + at) =
+          uint4{__builtin_bit_cast(uint32_t, z0), __builtin_bit_cast(uint32_t, z1),
+                __builtin_bit_cast(uint32_t, z2), __builtin_bit_cast(uint32_t, z3)};
+    }
+  } else if constexpr (Op::kEpi == kEpiDGelu) {
+    const uint4 zr = *reinterpret_cast<const uint4*>(Z + at);
+    const f16x2 z0 = __builtin_bit_cast(f16x2, zr.x), z1 = __builtin_bit_cast(f16x2, zr.y);
+    const f16x2 z2 = __builtin_bit_cast(f16x2, zr.z), z3 = __builtin_bit_cast(f16x2, zr.w);
+    const bf16x2 q0 = {static_cast<__bf16>(a.x * gelu_tanh_grad_fast(static_cast<float>(z0[0]))),
+                       static_cast<__bf16>(a.y * gelu_tanh_grad_fast(static_cast<float>(z0[1])))};
+    const bf16x2 q1 = {static_cast<__bf16>(a.z * gelu_tanh_grad_fast(static_cast<float>(z1[0]))),
+                       static_cast<__bf16>(a.w * gelu_tanh_grad_fast(static_cast<float>(z1[1])))};
+    const bf16x2 q2 = {static_cast<__bf16>(b.x * gelu_tanh_grad_fast(static_cast<float>(z2[0]))),
+                       static_cast<__bf16>(b.y * gelu_tanh_grad_fast(static_cast<float>(z2[1])))};
+    const bf16x2 q3 = {static_cast<__bf16>(b.z * gelu_tanh_grad_fast(static_cast<float>(z3[0]))),
+                       static_cast<__bf16>(b.w * gelu_tanh_grad_fast(static_cast<float>(z3[1])))};
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Cout) + at) =
+        uint4{__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+              __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)};
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(Cout) + at) = a;
+  }
+}
+
 template <class Op>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int M, int N,
     int K, const uint16_t* __restrict__ B, void* __restrict__ Cout, uint16_t* __restrict__ Z,
-    float* __restrict__ part, int* __restrict__ cnt, int max_split) {
+    float* __restrict__ part, int max_split) {
   constexpr bool AKM = Op::kAKM, BKM = Op::kBKM, SEGK = Op::kSegK, F16 = Op::kF16;
   constexpr int CVT = Op::kCvt, EPI = Op::kEpi;
   // Both operands K-contiguous: chunks past K hold the next row's values and
@@ -208,7 +276,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_tmp[kMaxE];
   __shared__ long long s_cost[SEGK ? kMaxE + 1 : 1];
-  __shared__ int s_ticket;
   __shared__ float s_epi[kWaves][8 * kEpiPitch];   // per-wave epilogue staging
   // Stage slot S (0 or 1, a compile-time value at every use).
   auto L = [&](int S) -> uint4* { return S ? st1 : st0; };
@@ -265,10 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   }
   const int64_t full = n_x / P;
   const int rem = static_cast<int>(n_x - full * P);
-  int S = 1;
-  // Each split keeps >= 64 stages: shorter pieces lose more to the partial
-  // store and the fix-up than they gain (measured on 64-stage tiles).
-  if (!SEGK && rem > 0 && max_split > 1) S = max(1, min(min(P / rem, max_split), nk2 / 64));
+  const int S = SEGK ? 1 : row_plan(static_cast<int64_t>(s_pref[E]) * tiles_n, xcd, P, nk2, max_split).S;
   const int64_t n_units = full + (w < rem * S ? 1 : 0);
   if (n_units == 0) return;
   // Unit q of this workgroup: a whole tile of round q, or (q == full) its
@@ -595,46 +659,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     slice3();
   };
 
-  // Output of VPC consecutive values (row, col .. col+VPC-1) of the tile, given
-  // as floats; 16 B per store. GELU -> fp16 (and the fp16 pre-activation);
-  // f32; or the GELU backward: bf16(value * gelu'(z)) with z read from Z.
   auto emit = [&](int c_e, int grow, int gcol, const float4& a, const float4& b) {
     const int64_t at = (SEGK ? static_cast<int64_t>(c_e) * M + grow : static_cast<int64_t>(grow)) * N + gcol;
-    if constexpr (EPI == kEpiGelu) {
-      const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
-      const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
-      const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
-      const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Cout) + at) =
-          uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-      if constexpr (Op::kSaveZ) {
-        const f16x2 z0 = {static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)};
-        const f16x2 z1 = {static_cast<_Float16>(a.z), static_cast<_Float16>(a.w)};
-        const f16x2 z2 = {static_cast<_Float16>(b.x), static_cast<_Float16>(b.y)};
-        const f16x2 z3 = {static_cast<_Float16>(b.z), static_cast<_Float16>(b.w)};
-        *reinterpret_cast<uint4*>(Z + at) =
-            uint4{__builtin_bit_cast(uint32_t, z0), __builtin_bit_cast(uint32_t, z1),
-                  __builtin_bit_cast(uint32_t, z2), __builtin_bit_cast(uint32_t, z3)};
-      }
-    } else if constexpr (EPI == kEpiDGelu) {
-      const uint4 zr = *reinterpret_cast<const uint4*>(Z + at);
-      const f16x2 z0 = __builtin_bit_cast(f16x2, zr.x), z1 = __builtin_bit_cast(f16x2, zr.y);
-      const f16x2 z2 = __builtin_bit_cast(f16x2, zr.z), z3 = __builtin_bit_cast(f16x2, zr.w);
-      const bf16x2 q0 = {static_cast<__bf16>(a.x * gelu_tanh_grad_fast(static_cast<float>(z0[0]))),
-                         static_cast<__bf16>(a.y * gelu_tanh_grad_fast(static_cast<float>(z0[1])))};
-      const bf16x2 q1 = {static_cast<__bf16>(a.z * gelu_tanh_grad_fast(static_cast<float>(z1[0]))),
-                         static_cast<__bf16>(a.w * gelu_tanh_grad_fast(static_cast<float>(z1[1])))};
-      const bf16x2 q2 = {static_cast<__bf16>(b.x * gelu_tanh_grad_fast(static_cast<float>(z2[0]))),
-                         static_cast<__bf16>(b.y * gelu_tanh_grad_fast(static_cast<float>(z2[1])))};
-      const bf16x2 q3 = {static_cast<__bf16>(b.z * gelu_tanh_grad_fast(static_cast<float>(z3[0]))),
-                         static_cast<__bf16>(b.w * gelu_tanh_grad_fast(static_cast<float>(z3[1])))};
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Cout) + at) =
-          uint4{__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
-                __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)};
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(Cout) + at) = a;
-    }
+    emit_values<Op>(Cout, Z, at, a, b);
   };
   // Epilogue through LDS slot 1 in four passes of 64 rows: a pass first copies
   // the raw f32 accumulators of its rows into LDS (no arithmetic, so the 256
@@ -644,9 +671,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   // Staged element (row, col) of a 128-column half sits at column
   // col ^ (32 * ((row >> 2) & 1)), so the two half-waves of a write (rows r
   // and r + 4) land on different banks.
-  // A split tile then takes a ticket; the last of its S splits to arrive adds
-  // the S partials up in split order (the sum does not depend on who arrives
-  // last) and emits the tile.
+  // split_fixup_kernel later adds a split tile's S partials up in split
+  // order (the sum does not depend on which piece finished last) and emits it.
   auto epilogue = [&](int c_m0, int c_n0, int c_seg1, int c_e, int tail) {
     float* const h0 = reinterpret_cast<float*>(st1);
     float* const h1 = reinterpret_cast<float*>(st1 + kStage / 2);
@@ -684,7 +710,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
           emit(c_e, grow, gcol, a, b);
         }
       } else {
-#pragma unroll 1
+#pragma unroll 4
         for (int q = tid; q < 64 * BN / 4; q += kThreads) {
           const int row = q / (BN / 4);
           const int col = (q % (BN / 4)) * 4;
@@ -693,53 +719,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
         }
       }
       MOE_BARRIER();
-    }
-    if (tail < 0) return;
-    __threadfence();   // this thread's part of the partial is visible device-wide ...
-    __syncthreads();   // ... for every thread, before the ticket is taken
-    if (tid == 0) s_ticket = atomicAdd(cnt + xcd * P + tail, 1);
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(s_ticket) != S - 1) return;
-    __threadfence();   // acquire: the other splits' partials
-    const float* const first = part + static_cast<int64_t>(xcd * P + tail) * (BM * BN);
-    const int64_t step = static_cast<int64_t>(rem) * (BM * BN);   // split si sits at slot si * rem + tail
-    // QU items per thread per pass, and the values of all kMaxSplit slots
-    // loaded before any is added (slots past S re-read slot S - 1 and are not
-    // added), so the pass has QU * kMaxSplit loads in flight instead of one.
-    constexpr int QU = VPC == 8 ? 1 : 2;
-    constexpr int NV = VPC / 4;   // float4 per item
-#pragma unroll 1
-    for (int q0 = tid; q0 < BM * BN / VPC; q0 += kThreads * QU) {
-      float4 v[kMaxSplit][QU][NV];
-#pragma unroll
-      for (int si = 0; si < kMaxSplit; ++si)
-#pragma unroll
-        for (int u = 0; u < QU; ++u) {
-          const int q = q0 + u * kThreads;
-          const float* src = first + min(si, S - 1) * step + (q / (BN / VPC)) * BN + (q % (BN / VPC)) * VPC;
-#pragma unroll
-          for (int h = 0; h < NV; ++h) v[si][u][h] = *reinterpret_cast<const float4*>(src + 4 * h);
-        }
-#pragma unroll
-      for (int u = 0; u < QU; ++u) {
-        const int q = q0 + u * kThreads;
-        const int row = q / (BN / VPC);
-        const int col = (q % (BN / VPC)) * VPC;
-        float4 a = v[0][u][0];
-        float4 b = v[0][u][NV - 1];
-#pragma unroll
-        for (int si = 1; si < kMaxSplit; ++si) {
-          if (si >= S) break;
-          const float4 a2 = v[si][u][0];
-          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-          if (VPC == 8) {
-            const float4 b2 = v[si][u][NV - 1];
-            b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
-          }
-        }
-        const int grow = c_m0 + row, gcol = c_n0 + col;
-        if (grow < c_seg1 && gcol < N) emit(c_e, grow, gcol, a, b);
-      }
     }
   };
 
@@ -928,9 +907,70 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   }
 }
 
-__global__ void zero_ints_kernel(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+// Split tiles of a row-segmented launch: workgroup b takes the quarter
+// b / 8 % 4 (64 rows) of split tile b / 32 of XCD b % 8's last round, adds
+// its S partials in split order and emits the outputs. The tile list and the
+// splits are derived from offsets[] exactly as the GEMM derived them (P
+// workgroups per XCD). The kernel boundary orders the partial stores before
+// these loads, so the pieces need no fence or ticket.
+template <class Op>
+__global__ __launch_bounds__(kThreads) void split_fixup_kernel(
+    const int32_t* __restrict__ offsets, int E, int N, int K, int P, int max_split,
+    const float* __restrict__ part, void* __restrict__ Cout, uint16_t* __restrict__ Z) {
+  constexpr int VPC = Op::kEpi == kEpiF32 ? 4 : 8;
+  constexpr int NV = VPC / 4;
+  __shared__ int s_pref[kMaxE + 1];
+  __shared__ int s_tmp[kMaxE];
+  build_tile_prefix(offsets, E, BM, s_pref, s_tmp);
+  const int xcd = blockIdx.x & 7, quarter = (blockIdx.x >> 3) & 3, tr = blockIdx.x >> 5;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int nk2 = (((K + BK - 1) / BK) + 1) & ~1;
+  const RowPlan pl = row_plan(static_cast<int64_t>(s_pref[E]) * tiles_n, xcd, P, nk2, max_split);
+  if (pl.S == 1 || tr >= pl.rem) return;
+  const Tile tl = find_tile(s_pref, E, tiles_n, pl.r_beg + pl.full * P + tr);
+  const int e0 = offsets[tl.e], seg1 = offsets[tl.e + 1];
+  const int m0 = e0 + tl.mi * BM, n0 = tl.nt * BN;
+  const float* const first = part + static_cast<int64_t>(xcd * P + tr) * (BM * BN);
+  const int64_t step = static_cast<int64_t>(pl.rem) * (BM * BN);   // piece si sits at slot si * rem + tr
+  const int S = pl.S;
+  // Two items per thread per pass, the values of all kMaxSplit slots loaded
+  // before any is added (slots past S re-read slot S - 1 and are not added).
+  constexpr int QU = 2;
+  constexpr int ITEMS = 64 * BN / VPC;
+#pragma unroll 1
+  for (int q0 = threadIdx.x; q0 < ITEMS; q0 += kThreads * QU) {
+    float4 v[kMaxSplit][QU][NV];
+#pragma unroll
+    for (int si = 0; si < kMaxSplit; ++si)
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int q = min(q0 + u * kThreads, ITEMS - 1);
+        const int row = quarter * 64 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
+        const float* src = first + min(si, S - 1) * step + row * BN + col;
+#pragma unroll
+        for (int h = 0; h < NV; ++h) v[si][u][h] = *reinterpret_cast<const float4*>(src + 4 * h);
+      }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int q = q0 + u * kThreads;
+      const int row = quarter * 64 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
+      float4 a = v[0][u][0], b = v[0][u][NV - 1];
+#pragma unroll
+      for (int si = 1; si < kMaxSplit; ++si) {
+        if (si < S) {
+          const float4 a2 = v[si][u][0];
+          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+          if constexpr (NV == 2) {
+            const float4 b2 = v[si][u][1];
+            b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+          }
+        }
+      }
+      const int grow = m0 + row, gcol = n0 + col;
+      if (q < ITEMS && grow < seg1 && gcol < N)
+        emit_values<Op>(Cout, Z, static_cast<int64_t>(grow) * N + gcol, a, b);
+    }
+  }
 }
 
 // One workgroup per CU, a multiple of 8 (one group per XCD).
@@ -938,17 +978,24 @@ int ffn_mfma_grid() { return (device_cu_count() + 7) / 8 * 8; }
 
 template <class Op>
 void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int E, int M, int N,
-               int K, const void* B, void* C, void* Z, float* part, int* cnt, int max_split) {
+               int K, const void* B, void* C, void* Z, float* part, int max_split) {
   hipLaunchKernelGGL(gemm_mfma_kernel<Op>, g, dim3(kThreads), 0, s, static_cast<const uint16_t*>(A),
                      offsets, E, M, N, K, static_cast<const uint16_t*>(B), C,
-                     static_cast<uint16_t*>(Z), part, cnt, max_split);
+                     static_cast<uint16_t*>(Z), part, max_split);
+  // A tile can split only into pieces of >= 16 stages: with fewer than 32
+  // stages per tile nothing is split and there is nothing to add up.
+  const int nk2 = (((K + BK - 1) / BK) + 1) & ~1;
+  if constexpr (!Op::kSegK) {
+    if (max_split > 1 && nk2 >= 32)
+      hipLaunchKernelGGL(split_fixup_kernel<Op>, dim3(4 * g.x), dim3(kThreads), 0, s, offsets, E, N, K,
+                         static_cast<int>(g.x / 8), max_split, part, C, static_cast<uint16_t*>(Z));
+  }
 }
 
 }  // namespace
 
 size_t ffn_mfma_workspace_bytes() {
-  const size_t g = static_cast<size_t>(ffn_mfma_grid());
-  return g * kPartBytes + g * sizeof(int);
+  return static_cast<size_t>(ffn_mfma_grid()) * kPartBytes;
 }
 
 hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
@@ -958,7 +1005,6 @@ hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets
   const int grid_max = ffn_mfma_grid();
   int64_t g = grid_max;
   float* part = nullptr;
-  int* cnt = nullptr;
   int max_split = 1;
   if (seg_k) {
     // Every expert's M x N block is written, zeros for an expert with no rows.
@@ -969,13 +1015,10 @@ hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets
     if (rows_max == 0) return hipSuccess;
     const int64_t tiles_n = (N + BN - 1) / BN;
     const int64_t upper = (rows_max / BM + E) * tiles_n;   // >= sum_e ceil(kept_e / BM) * tiles_n
-    // Split tiles need the workspace: G partial tiles, then one counter per
-    // workgroup slot, zeroed here (by a kernel, so the call can be captured).
+    // Split tiles need the workspace: one partial tile per workgroup slot.
     if (ws != nullptr) {
       part = static_cast<float*>(ws);
-      cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + static_cast<size_t>(grid_max) * kPartBytes);
       max_split = kMaxSplit;
-      hipLaunchKernelGGL(zero_ints_kernel, dim3((grid_max + 255) / 256), dim3(256), 0, s, cnt, grid_max);
     }
     // Without splitting, workgroups beyond the tile count would find no work;
     // with it, a short list still spreads over every XCD's workgroups.
@@ -984,14 +1027,14 @@ hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets
   const dim3 grid(static_cast<unsigned>(g));
   switch (kind) {
     case GemmKind::kUp:
-      if (Z != nullptr) launch_op<OpUpZ>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split);
-      else launch_op<OpUp>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split);
+      if (Z != nullptr) launch_op<OpUpZ>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split);
+      else launch_op<OpUp>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split);
       break;
-    case GemmKind::kDown: launch_op<OpDown>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split); break;
-    case GemmKind::kDh: launch_op<OpDh>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split); break;
-    case GemmKind::kDx: launch_op<OpDx>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, max_split); break;
-    case GemmKind::kDw2: launch_op<OpDw2>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, 1); break;
-    case GemmKind::kDw1: launch_op<OpDw1>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, cnt, 1); break;
+    case GemmKind::kDown: launch_op<OpDown>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
+    case GemmKind::kDh: launch_op<OpDh>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
+    case GemmKind::kDx: launch_op<OpDx>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
+    case GemmKind::kDw2: launch_op<OpDw2>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, 1); break;
+    case GemmKind::kDw1: launch_op<OpDw1>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, 1); break;
   }
   return hipGetLastError();
 }

@@ -33,9 +33,10 @@ SMALL = [
     I.small("receiver", T=700, d=128, d_ff=256, E=8, k=1, cf=1.25, routed=False, seed=14),
     I.small("single-token", T=1, d=64, d_ff=64, E=4, k=2, cf=1.25, seed=15),
     I.small("multi-tile", T=1200, d=512, d_ff=576, E=3, k=2, cf=1.25, seed=16),
-    # few tiles, long K: output tiles split along K (pieces keep >= 64 stages
-    # of 64): the down-projection 2-way with a K tail (8200), the
-    # up-projection 8-way (K = 32768)
+    # few tiles, long K: output tiles split along K (each launch is under one
+    # round of tiles, so pieces may be as short as 16 stages of 64): the
+    # down-projection 8-way with a K tail (8200), the up-projection 8-way
+    # (K = 32768)
     I.small("split-k2-ragged", T=300, d=1024, d_ff=8200, E=2, k=2, cf=1.25, seed=17),
     I.small("split-k8", T=200, d=32768, d_ff=256, E=1, k=1, cf=1.25, seed=18),
 ]
