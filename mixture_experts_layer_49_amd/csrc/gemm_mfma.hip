@@ -187,12 +187,11 @@ __device__ __forceinline__ RowPlan row_plan(int64_t total, int xcd, int P, int n
   p.full = p.n_x / P;
   p.rem = static_cast<int>(p.n_x - p.full * P);
   p.S = 1;
-  // Pieces keep >= 64 stages when they only fill a last round (measured on
-  // 64-stage tiles: shorter ones lost more to the partial store and the
-  // fix-up than they gained); when the whole launch is a partial round,
-  // pieces of 16 stages still pay.
+  // Pieces keep >= 32 stages when they only fill a last round (measured on
+  // 64-stage tiles: 2-way splits gain 4-7%); when the whole launch is a
+  // partial round, pieces of 16 stages still pay.
   if (p.rem > 0 && max_split > 1)
-    p.S = max(1, min(min(P / p.rem, max_split), nk2 / (p.full == 0 ? 16 : 64)));
+    p.S = max(1, min(min(P / p.rem, max_split), nk2 / (p.full == 0 ? 16 : 32)));
   return p;
 }
 
