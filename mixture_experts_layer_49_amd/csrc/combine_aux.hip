@@ -90,11 +90,23 @@ __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const float* _
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * chunk;
   const int64_t t1 = min(t0 + chunk, T);
   double acc = 0.0;
-  if (g < G)
-    for (int64_t t = t0 + g; t < t1; t += G) {
-      const double v = static_cast<double>(probs[t * E + e]);
-      acc += SQUARE ? v * v : v;
+  if (g < G) {
+    // Eight rows' loads in flight at a time (rows past the chunk re-read its
+    // last row and are not added); the sum still runs in row order.
+    constexpr int U = 8;
+    for (int64_t tb = t0 + g; tb < t1; tb += static_cast<int64_t>(U) * G) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = probs[min(tb + static_cast<int64_t>(u) * G, t1 - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (tb + static_cast<int64_t>(u) * G < t1) {
+          const double x = static_cast<double>(v[u]);
+          acc += SQUARE ? x * x : x;
+        }
+      }
     }
+  }
   s[tid] = acc;
   __syncthreads();
   if (tid < E) {
@@ -117,8 +129,18 @@ __global__ __launch_bounds__(kMaxE) void aux_final_kernel(const double* __restri
   const int G = kMaxE / E;
   const int e_t = tid % E, g_t = tid / E;
   double acc = 0.0;
-  if (g_t < G)
-    for (int b = g_t; b < nblocks; b += G) acc += part[static_cast<int64_t>(b) * E + e_t];
+  if (g_t < G) {
+    // Eight partials in flight at a time, added in block order.
+    constexpr int U = 8;
+    for (int b0 = g_t; b0 < nblocks; b0 += U * G) {
+      double v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = part[static_cast<int64_t>(min(b0 + u * G, nblocks - 1)) * E + e_t];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (b0 + u * G < nblocks) acc += v[u];
+    }
+  }
   g_part[tid] = acc;
   __syncthreads();
   const int e = tid;

@@ -72,11 +72,19 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(const int32_t* __restrict__
   const int e = threadIdx.x;
   int32_t kept = 0;
   if (e < E) {
+    // Eight chunks' counts in flight at a time, scanned in chunk order.
+    constexpr int U = 8;
     int32_t run = 0;
-    for (int b = 0; b < nchunks; ++b) {
-      const int32_t c = chunk_cnt[static_cast<int64_t>(b) * E + e];
-      chunk_base[static_cast<int64_t>(b) * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nchunks; b0 += U) {
+      int32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        c[u] = b0 + u < nchunks ? chunk_cnt[static_cast<int64_t>(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u < nchunks) chunk_base[static_cast<int64_t>(b0 + u) * E + e] = run;
+        run += c[u];
+      }
     }
     counts[e] = run;
     kept = (cap < 0 || run < cap) ? run : static_cast<int32_t>(cap);
