@@ -195,9 +195,9 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
                     int32_t dtype, float* y_perm, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
-/* Bytes of expert-FFN workspace for the current device: one 256 x 256 float32
- * partial tile per compute unit (64 MiB on a 256-CU MI355X) for MOE_BF16; 0
- * for MOE_F32 (whose kernels never split). */
+/* Bytes of expert-FFN workspace for the current device: two 256 x 256
+ * float32 partial tiles per compute unit (128 MiB on a 256-CU MI355X) for
+ * MOE_BF16; 0 for MOE_F32 (whose kernels never split). */
 size_t moe_ffn_workspace_bytes(int32_t dtype);
 
 /* Weighted combine back to token order (EP tutorial 2.1 step 5; 2.2: a

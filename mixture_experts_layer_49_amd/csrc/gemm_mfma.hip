@@ -88,6 +88,7 @@ static_assert(NS == 2 && BK == 64 && kWaves % 2 == 0, "the pipeline below assume
 static_assert(BM == 256 && BN == 256, "the k-major LDS layout assumes 256-wide tiles");
 constexpr size_t kPartBytes = static_cast<size_t>(BM) * BN * sizeof(float);   // one split partial
 constexpr int kMaxSplit = 8;
+constexpr int kPiecesPerWg = 2;   // split pieces one workgroup may run (workspace slots per workgroup)
 constexpr int kEpiCost = 4;   // epilogue of a tile, in k-steps (K-segmented load balance)
 constexpr int kSegGroup = 8;  // m-tiles per group of the K-segmented tile order
 constexpr int kEpiPitch = 136;   // floats per row of a wave's epilogue staging buffer (see epilogue_wave)
@@ -174,8 +175,14 @@ __device__ __forceinline__ int seg_k_steps(const int* s_off, int e) {
 }
 
 // How an XCD's share of a row-segmented tile list runs: tiles r_beg ..
-// r_beg + n_x - 1, `full` whole rounds over its P workgroups, then rem tiles,
-// each split into S k-ranges when rem < P and the workspace allows it.
+// r_beg + n_x - 1, `full` whole rounds over its P workgroups, then the rem
+// tiles left, each split into S k-ranges when the workspace allows it. The
+// rem * S pieces go round-robin over the P workgroups, at most kPiecesPerWg
+// each, and S is the count that ends the last round soonest: the round
+// takes ceil(rem S / P) / S of a tile (ties: fewer pieces). Pieces keep >= 32
+// stages when they only fill a last round (measured on 64-stage tiles:
+// 2-way splits gain 4-7%); when the whole launch is a partial round, pieces of
+// 16 stages still pay.
 struct RowPlan {
   int64_t r_beg, n_x, full;
   int rem, S;
@@ -187,11 +194,19 @@ __device__ __forceinline__ RowPlan row_plan(int64_t total, int xcd, int P, int n
   p.full = p.n_x / P;
   p.rem = static_cast<int>(p.n_x - p.full * P);
   p.S = 1;
-  // Pieces keep >= 32 stages when they only fill a last round (measured on
-  // 64-stage tiles: 2-way splits gain 4-7%); when the whole launch is a
-  // partial round, pieces of 16 stages still pay.
-  if (p.rem > 0 && max_split > 1)
-    p.S = max(1, min(min(P / p.rem, max_split), nk2 / (p.full == 0 ? 16 : 32)));
+  if (p.rem > 0 && max_split > 1) {
+    const int smax = min(max_split, nk2 / (p.full == 0 ? 16 : 32));
+    int best_num = 1, best_den = 1;   // last round = best_num / best_den tiles
+    for (int s = 2; s <= smax; ++s) {
+      if (p.rem * s > kPiecesPerWg * P) break;
+      const int num = (p.rem * s + P - 1) / P;
+      if (num * best_den < best_num * s) {
+        best_num = num;
+        best_den = s;
+      }
+    }
+    p.S = best_den;
+  }
   return p;
 }
 
@@ -332,13 +347,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   const int64_t full = n_x / P;
   const int rem = static_cast<int>(n_x - full * P);
   const int S = SEGK ? 1 : row_plan(static_cast<int64_t>(s_pref[E]) * tiles_n, xcd, P, nk2, max_split).S;
-  const int64_t n_units = full + (w < rem * S ? 1 : 0);
+  const int64_t n_units = full + (S == 1 ? (w < rem ? 1 : 0)
+                                          : (w < rem * S ? 1 : 0) + (w + P < rem * S ? 1 : 0));
   if (n_units == 0) return;
-  // Unit q of this workgroup: a whole tile of round q, or (q == full) its
-  // share of the last round: split u / rem of tile u % rem, u = w.
+  // Unit q of this workgroup: a whole tile of round q, or (q >= full) piece
+  // u = (q - full) P + w of the last round: split u / rem of tile u % rem.
   struct Unit {
     int64_t tile;
-    int klo, khi, tail;   // tail: index of the split tile in this XCD's last round, or -1
+    int klo, khi, tail;   // tail: the piece index u, or -1 for a whole tile
   };
   auto unit = [&](int64_t q) {
     Unit u;
@@ -351,11 +367,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
         u.khi = nk2;
       u.tail = -1;
     } else {
-      const int tr = w % rem, si = w / rem, np = nk2 / 2;
+      const int pc = static_cast<int>(q - full) * P + w;
+      const int tr = pc % rem, si = pc / rem, np = nk2 / 2;
       u.tile = r_beg + full * P + tr;
       u.klo = 2 * (si * np / S);
       u.khi = 2 * ((si + 1) * np / S);
-      u.tail = tr;
+      u.tail = pc;
     }
     return u;
   };
@@ -676,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     float* const h0 = reinterpret_cast<float*>(st1);
     float* const h1 = reinterpret_cast<float*>(st1 + kStage / 2);
     float* const hw = wn == 0 ? h0 : h1;   // this wave's 128-column half
-    float* const mine = part + static_cast<int64_t>(xcd * P + w) * (BM * BN);
+    float* const mine = part + static_cast<int64_t>(xcd * kPiecesPerWg * P + tail) * (BM * BN);
 #pragma unroll
     for (int p = 0; p < BM / 64; ++p) {
       if (wm == p / 2) {
@@ -929,8 +946,9 @@ __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
   const Tile tl = find_tile(s_pref, E, tiles_n, pl.r_beg + pl.full * P + tr);
   const int e0 = offsets[tl.e], seg1 = offsets[tl.e + 1];
   const int m0 = e0 + tl.mi * BM, n0 = tl.nt * BN;
-  const float* const first = part + static_cast<int64_t>(xcd * P + tr) * (BM * BN);
-  const int64_t step = static_cast<int64_t>(pl.rem) * (BM * BN);   // piece si sits at slot si * rem + tr
+  // piece si of the tile is u = si * rem + tr, at slot u of the XCD's kPiecesPerWg P
+  const float* const first = part + static_cast<int64_t>(xcd * kPiecesPerWg * P + tr) * (BM * BN);
+  const int64_t step = static_cast<int64_t>(pl.rem) * (BM * BN);
   const int S = pl.S;
   // Two items per thread per pass, the values of all kMaxSplit slots loaded
   // before any is added (slots past S re-read slot S - 1 and are not added).
@@ -994,7 +1012,7 @@ void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int
 }  // namespace
 
 size_t ffn_mfma_workspace_bytes() {
-  return static_cast<size_t>(ffn_mfma_grid()) * kPartBytes;
+  return static_cast<size_t>(ffn_mfma_grid()) * kPiecesPerWg * kPartBytes;
 }
 
 hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
@@ -1014,7 +1032,7 @@ hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets
     if (rows_max == 0) return hipSuccess;
     const int64_t tiles_n = (N + BN - 1) / BN;
     const int64_t upper = (rows_max / BM + E) * tiles_n;   // >= sum_e ceil(kept_e / BM) * tiles_n
-    // Split tiles need the workspace: one partial tile per workgroup slot.
+    // Split tiles need the workspace: kPiecesPerWg partial tiles per workgroup.
     if (ws != nullptr) {
       part = static_cast<float*>(ws);
       max_split = kMaxSplit;

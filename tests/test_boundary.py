@@ -187,8 +187,8 @@ def test_ffn_workspace_bytes():
     L = ops.lib()
     assert L.moe_ffn_workspace_bytes(0) == 0           # f32 kernels never split a tile
     n = L.moe_ffn_workspace_bytes(1)
-    # one 256 x 256 f32 partial tile per workgroup slot (a multiple of 8 slots)
-    assert n > 0 and n % (8 * 256 * 256 * 4) == 0, n
+    # two 256 x 256 f32 partial tiles per workgroup (a multiple of 8 workgroups)
+    assert n > 0 and n % (2 * 8 * 256 * 256 * 4) == 0, n
 
 
 def test_binding_raises_typed_errors():
