@@ -63,9 +63,10 @@ GEMM_SOURCES = ["mixture_experts_layer_49_amd/csrc/gemm_mfma.hip",
 
 def measured_traffic(which: str, workload: str):
     """HBM bytes per launch of one GEMM kind (up, down, dh, dx, dw2, dw1) from
-    the committed rocprofv3 summary (profiles/gemm_mfma_<which>_<workload>.md),
-    or None when there is none or the kernel source changed after the counters
-    were taken."""
+    the committed rocprofv3 summary (profiles/gemm_mfma_<which>_<workload>.md;
+    the GEMM kernel plus its split fix-up kernel when tiles split, the two
+    kernels the launch's HIP events time), or None when there is none or the
+    kernel source changed after the counters were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "gemm_mfma_%s_%s.md" % (which, workload))
