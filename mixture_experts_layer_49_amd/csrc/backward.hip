@@ -294,14 +294,139 @@ __global__ __launch_bounds__(kThreads) void gate_wgrad_partial_kernel(
   }
 }
 
+// Wide gates (E > 16): the same partial sums on the f32 matrix cores
+// (v_mfma_f32_32x32x2_f32, twice the rate of plain f32 FMAs, products exact as
+// with FMAs). Workgroup (cb, ch, eb) takes columns 256 cb .. +255, experts
+// 64 eb .. +63 and the tokens of chunk ch; wave w holds the 64 x 64 block of
+// experts x columns 256 cb + 64 w .. +63 in four 32 x 32 accumulator tiles.
+// Sixteen tokens at a time are staged in LDS (dl as f32, x as stored), the
+// next sixteen loaded into registers meanwhile; an MFMA takes two tokens:
+// lane l gives dl[t0 + l / 32][e0 + l % 32] and x[t0 + l / 32][c0 + l % 32].
+// Column block 0 also sums the chunk's dl columns (the bias gradient) in
+// token order.
+constexpr int kWgMt = 16;   // tokens per staged block
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void gate_wgrad_mfma_kernel(
+    const float* __restrict__ dl, const void* __restrict__ x, int64_t T, int64_t d, int E,
+    int64_t chunk, float* __restrict__ part, float* __restrict__ part_b) {
+  using XT = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int XV = 16 / sizeof(XT);            // x elements per 16-byte load
+  constexpr int XL = kWgMt * 256 / XV / kThreads;   // 16-byte x loads per thread per block
+  __shared__ float s_dl[2][kWgMt][64];
+  __shared__ XT s_x[2][kWgMt][256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t ch = blockIdx.y;
+  const int64_t t0 = ch * chunk, t1 = min(t0 + chunk, T);
+  const int64_t cb = static_cast<int64_t>(blockIdx.x) * 256;
+  const int e0 = blockIdx.z * 64;
+  // Registers for the next block: dl token tid / 16, experts 4 (tid % 16) .. +3;
+  // x token (tid XL + h) / (256 / XV), columns XV ((tid XL + h) % (256 / XV)) .. .
+  float rd[4];
+  uint4 rx[XL];
+  auto load_block = [&](int64_t tb) {
+    const int tt = tid >> 4, eq = 4 * (tid & 15);
+    const int64_t t = tb + tt;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + eq + u;
+      rd[u] = (t < t1 && e < E) ? dl[t * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < XL; ++h) {
+      const int f = tid * XL + h;
+      const int xt = f / (256 / XV), xc = (f % (256 / XV)) * XV;
+      const int64_t tx = tb + xt, c = cb + xc;
+      rx[h] = (tx < t1 && c < d) ? *reinterpret_cast<const uint4*>(static_cast<const XT*>(x) + tx * d + c)
+                                 : uint4{0, 0, 0, 0};
+    }
+  };
+  auto store_block = [&](int buf) {
+    const int tt = tid >> 4, eq = 4 * (tid & 15);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s_dl[buf][tt][eq + u] = rd[u];
+#pragma unroll
+    for (int h = 0; h < XL; ++h) {
+      const int f = tid * XL + h;
+      const int xt = f / (256 / XV), xc = (f % (256 / XV)) * XV;
+      *reinterpret_cast<uint4*>(&s_x[buf][xt][xc]) = rx[h];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+  float bsum = 0.f;   // bias: thread tid < 64 sums expert e0 + tid
+  const int l32 = lane & 31, hl = lane >> 5;
+  int buf = 0;
+  if (t0 < t1) {
+    load_block(t0);
+    store_block(0);
+  }
+  for (int64_t tb = t0; tb < t1; tb += kWgMt) {
+    __syncthreads();   // block tb is in buffer buf; buffer buf ^ 1 is free
+    const bool more = tb + kWgMt < t1;
+    if (more) load_block(tb + kWgMt);
+    if (blockIdx.x == 0 && tid < 64) {
+#pragma unroll
+      for (int tt = 0; tt < kWgMt; ++tt) bsum += s_dl[buf][tt][tid];
+    }
+#pragma unroll
+    for (int p = 0; p < kWgMt / 2; ++p) {
+      const int tt = 2 * p + hl;
+      float a[2], b[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) a[mb] = s_dl[buf][tt][32 * mb + l32];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const XT v = s_x[buf][tt][64 * wave + 32 * nb + l32];
+        if constexpr (BF16) b[nb] = __uint_as_float(static_cast<uint32_t>(v) << 16);
+        else b[nb] = v;
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+    }
+    if (more) store_block(buf ^ 1);
+    buf ^= 1;
+  }
+  // D layout of a 32 x 32 tile: lane l holds column l % 32, rows
+  // 8 (r / 4) + 4 (l / 32) + r % 4 in register r.
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t c = cb + 64 * wave + 32 * nb + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = e0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (e < E && c < d) part[(ch * E + e) * d + c] = acc[mb][nb][r];
+      }
+    }
+  if (blockIdx.x == 0 && tid < 64 && e0 + tid < E) part_b[ch * E + e0 + tid] = bsum;
+}
+
 __global__ __launch_bounds__(kThreads) void gate_wgrad_final_kernel(
     const float* __restrict__ part, const float* __restrict__ part_b, int nch, int64_t d, int E,
     float* __restrict__ dwg, float* __restrict__ db) {
   const int64_t n = static_cast<int64_t>(E) * d;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    // Eight chunks' partials in flight at a time, added in chunk order.
+    constexpr int U = 8;
     float s = 0.f;
-    for (int c = 0; c < nch; ++c) s += part[c * n + i];
+    for (int c0 = 0; c0 < nch; c0 += U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = part[static_cast<int64_t>(min(c0 + u, nch - 1)) * n + i];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + u < nch) s += v[u];
+    }
     dwg[i] = s;
   }
   if (blockIdx.x == 0 && db != nullptr) {
@@ -653,7 +778,11 @@ hipError_t launch_gate_wgrad(const float* dl, const void* x, int64_t T, int64_t 
   const int64_t chunk = T > 0 ? (T + nch - 1) / nch : 0;
   float* part = ws;
   float* part_b = ws + static_cast<size_t>(nch) * E * d;
-  if (T > 0) {
+  if (T > 0 && E > kWgE) {
+    const dim3 g(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(nch), static_cast<unsigned>((E + 63) / 64));
+    if (dtype == 1) hipLaunchKernelGGL(gate_wgrad_mfma_kernel<true>, g, dim3(kThreads), 0, s, dl, x, T, d, E, chunk, part, part_b);
+    else hipLaunchKernelGGL(gate_wgrad_mfma_kernel<false>, g, dim3(kThreads), 0, s, dl, x, T, d, E, chunk, part, part_b);
+  } else if (T > 0) {
     const dim3 g(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(nch));
     if (dtype == 1) hipLaunchKernelGGL(gate_wgrad_partial_kernel<true>, g, dim3(kThreads), 0, s, dl, x, T, d, E, chunk, part, part_b);
     else hipLaunchKernelGGL(gate_wgrad_partial_kernel<false>, g, dim3(kThreads), 0, s, dl, x, T, d, E, chunk, part, part_b);

@@ -197,11 +197,15 @@ def test_backward_full_size_sampled():
     close(gpu["db"], dl.sum(axis=0), "f32", "db = sum_t d_logits")
 
 
-@pytest.mark.parametrize("T,d,E,dt", [(20000, 256, 8, "bf16"), (9000, 72, 20, "f32"), (3, 64, 5, "bf16")])
+@pytest.mark.parametrize("T,d,E,dt", [(20000, 256, 8, "bf16"), (9000, 72, 20, "f32"), (3, 64, 5, "bf16"),
+                                      (4100, 520, 70, "bf16"), (16384, 2048, 64, "bf16")])
 def test_gate_weight_grads_any_batch(T, d, E, dt):
     """dWg = d_logits^T x and db = column sums, for batches whose token chunks
     are longer than one staging block (T > 8192), an expert count that is not a
-    multiple of 8, and a batch of three tokens; against float64."""
+    multiple of 8, a batch of three tokens, and wide gates (the f32-MFMA path:
+    20 experts with f32 x; 70, which spills into a second 64-expert block,
+    with ragged tokens and columns; the 64-expert workload's shape); against
+    float64."""
     rng = np.random.default_rng(T + d + E)
     dl = rng.standard_normal((T, E)).astype(np.float32)
     x_np = rng.standard_normal((T, d)).astype(np.float32)

@@ -39,6 +39,10 @@ SMALL = [
     # (K = 32768)
     I.small("split-k2-ragged", T=300, d=1024, d_ff=8200, E=2, k=2, cf=1.25, seed=17),
     I.small("split-k8", T=200, d=32768, d_ff=256, E=1, k=1, cf=1.25, seed=18),
+    # gates of 17..64 experts run 64-token router workgroups (four 16-token
+    # tiles): token counts that leave a ragged last workgroup, and a d tail
+    I.small("router-tiles-e40", T=517, d=200, d_ff=128, E=40, k=3, cf=1.25, seed=19),
+    I.small("router-tiles-e17", T=77, d=520, d_ff=64, E=17, k=2, cf=1.25, seed=20),
 ]
 FULL = list(I.CONFIGS)              # the five workloads at their real sizes
 FULL_ORACLE_FFN = {"tiny-fp32", "e16-zipf-bias"}   # oracle FFN on every token
