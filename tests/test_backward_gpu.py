@@ -38,6 +38,11 @@ CASES = [
     I.small("bwd-multi-tile", T=1200, d=512, d_ff=576, E=3, k=2, cf=1.25, seed=16),
     I.small("bwd-split-k2-ragged", T=300, d=1024, d_ff=1032, E=2, k=2, cf=1.25, seed=17),
     I.small("bwd-long-rows", T=2000, d=256, d_ff=512, E=2, k=1, cf=1.25, seed=19),
+    # wide gates (the gate weight gradients on the f32 matrix cores, dispatch^T
+    # with several 16-expert gate chunks): ragged tokens and columns, bf16 and
+    # f32 gates
+    I.small("bwd-wide-gate", T=517, d=200, d_ff=128, E=40, k=2, cf=1.25, seed=21),
+    I.small("bwd-wide-gate-f32", dtype="f32", T=333, d=36, d_ff=52, E=24, k=3, cf=1.25, seed=22),
 ]
 # routing knobs: (flags, temperature, noise scale, z_coeff)
 VARIANTS = {"plain": (0, 1.0, 0.0, 0.0), "renorm-temp-noise-zloss": (ops.MOE_RENORM, 1.6, 0.3, 0.05)}
