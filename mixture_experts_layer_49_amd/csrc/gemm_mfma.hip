@@ -274,10 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
   // A steady stage's loads leave in three parts: kSpread0 between the MFMAs
   // after the stage barrier, kSpreadPer in each of the next two k-slices, so
-  // the TA queue does not fill and hold up the MFMA issue behind it. The
-  // K-segmented kinds (short tiles of both-k-major operands) measured slower
-  // that way and issue the whole stage at the barrier.
-  constexpr int kSpread0 = SEGK ? kLoadsPerStage : kLoadsPerStage / 2;
+  // the TA queue does not fill and hold up the MFMA issue behind it. Measured
+  // per kind: 8/4/4 for the plain and k-major-B kinds, 12/2/2 for the
+  // converting down-projection (its slices carry the conversion VALU work);
+  // the K-segmented kinds (short tiles of both-k-major operands) issue the
+  // whole stage at the barrier.
+  constexpr int kSpread0 = SEGK ? kLoadsPerStage : (CVT != kCvtNone ? 12 : kLoadsPerStage / 2);
   constexpr int kSpreadPer = (kLoadsPerStage - kSpread0) / 2;
   static_assert(kSpread0 + 2 * kSpreadPer == kLoadsPerStage, "the parts cover the stage");
   // After a per-wave epilogue the memory operations in flight are, oldest
