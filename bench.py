@@ -56,20 +56,26 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-GEMM_SOURCES = ["mixture_experts_layer_49_amd/csrc/gemm_mfma.hip",
-                "mixture_experts_layer_49_amd/csrc/ffn_common.h",
-                "mixture_experts_layer_49_amd/csrc/moe_internal.h"]
+# the sources each GEMM kernel family is built from (hashed into its summaries)
+GEMM_SOURCES = {
+    "gemm_mfma": ["mixture_experts_layer_49_amd/csrc/gemm_mfma.hip",
+                  "mixture_experts_layer_49_amd/csrc/ffn_common.h",
+                  "mixture_experts_layer_49_amd/csrc/moe_internal.h"],
+    "gemm_frag": ["mixture_experts_layer_49_amd/csrc/gemm_frag.hip",
+                  "mixture_experts_layer_49_amd/csrc/ffn_common.h",
+                  "mixture_experts_layer_49_amd/csrc/moe_internal.h"],
+}
 
 
-def measured_traffic(which: str, workload: str):
+def measured_traffic(which: str, workload: str, family: str = "gemm_mfma"):
     """HBM bytes per launch of one GEMM kind (up, down, dh, dx, dw2, dw1) from
-    the committed rocprofv3 summary (profiles/gemm_mfma_<which>_<workload>.md;
-    the GEMM kernel plus its split fix-up kernel when tiles split, the two
-    kernels the launch's HIP events time), or None when there is none or the
-    kernel source changed after the counters were taken."""
+    the committed rocprofv3 summary (profiles/<family>_<which>_<workload>.md;
+    for gemm_mfma the GEMM kernel plus its split fix-up kernel when tiles
+    split, the two kernels the launch's HIP events time), or None when there
+    is none or the kernel source changed after the counters were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "gemm_mfma_%s_%s.md" % (which, workload))
+    path = os.path.join(ROOT, "profiles", "%s_%s_%s.md" % (family, which, workload))
     if not os.path.exists(path):
         return None
     fields = {}
@@ -78,7 +84,7 @@ def measured_traffic(which: str, workload: str):
             key, val = line.split(":", 1)
             fields[key] = val.strip()
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in GEMM_SOURCES[family]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
         return None
@@ -334,9 +340,14 @@ def main(argv=None) -> int:
         rec(1)
         ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
         rec(2)
-        ops.moe_permute(x, b.src, b.offsets, b.rows_max, b.x_perm)
-        rec(3)
-        ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
+        if b.frag:
+            ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
+            rec(3)
+            ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, b.h)
+        else:
+            ops.moe_permute(x, b.src, b.offsets, b.rows_max, b.x_perm)
+            rec(3)
+            ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
         rec(4)
         ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
         rec(5)
@@ -388,6 +399,9 @@ def main(argv=None) -> int:
         if "TFLOP/s" in v:
             v["mfma_frac"] = v["TFLOP/s"] / PEAK_MFMA_TFLOPS
     dom = "up_gelu" if per[3] >= per[4] else "down"
+    dom_frag = dom == "up_gelu" and b.frag
+    dom_kernel = ("up_frag_kernel" if dom_frag else
+                  "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else "down"))
     achieved = breakdown[dom]["TFLOP/s"]
     ffn_tflops = (flops_up + flops_down) / ((per[3] + per[4]) * 1e-3) / 1e12
 
@@ -407,11 +421,12 @@ def main(argv=None) -> int:
         "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
                    "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
                    "max_over_mean_load": float(counts.max() / counts.mean()),
+                   "activation_layout": "fragment-ordered" if b.frag else "row-major",
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else "down"),
-                     "bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
-                     "traffic": measured_traffic("up" if dom == "up_gelu" else "down", cfg.name),
+        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
+                     "traffic": measured_traffic("up" if dom == "up_gelu" else "down", cfg.name,
+                                                 "gemm_frag" if dom_frag else "gemm_mfma"),
                      "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
                      "launch_us": us[dom]},
         "ffn_mfma_frac": ffn_tflops / PEAK_MFMA_TFLOPS,

@@ -14,6 +14,10 @@
  *   moe_combine      weighted return to token order            (tutorial 2.1 step 5)
  *   moe_aux_loss     L_aux = alpha * E * sum_i f_i * P_i       (tutorial 5.1)
  *
+ * For bf16 layers without a backward, moe_dispatch_plan + moe_permute_frag +
+ * moe_expert_up_gelu_frag + moe_expert_down compute the same dispatch and FFN
+ * with the activations in matrix-core fragment order (faster up-projection).
+ *
  * The backward (see the section near the end) runs the same path in reverse:
  * moe_combine_backward, moe_expert_down_backward, moe_expert_up_backward,
  * moe_expert_weight_grads, moe_gate_backward, moe_gate_weight_grads,
@@ -199,6 +203,38 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
  * float32 partial tiles per compute unit (128 MiB on a 256-CU MI355X) for
  * MOE_BF16; 0 for MOE_F32 (whose kernels never split). */
 size_t moe_ffn_workspace_bytes(int32_t dtype);
+
+/* Up-projection from a fragment-ordered copy of x_perm (bf16 layers; same h
+ * as moe_expert_up_gelu with a NULL workspace, bit for bit). The copy holds
+ * the permuted rows of EP tutorial 5.3 laid out for the matrix cores: each
+ * expert segment is padded with zero rows to a multiple of 32 (padded segment
+ * e starts at pad[e] = sum over e' < e of roundup(offsets[e'+1] - offsets[e'],
+ * 32)), and element (padded row r, column c) sits at element
+ *   ((r / 32) * (d / 16) + c / 16) * 512 + ((r % 32) + 32 * ((c / 8) % 2)) * 8 + c % 8,
+ * so every 32-row x 16-column block is one contiguous 1 KiB piece.
+ *
+ * moe_frag_rows: padded row count to allocate for x_frag ([moe_frag_rows, d]
+ *   bf16), an upper bound on pad[E] for any offsets with offsets[E] <= rows_max;
+ *   -1 for rows_max < 0 or E outside [1, MOE_MAX_E].
+ * moe_permute_frag: x_frag from x [T, d] bf16 and the plan's src/offsets
+ *   (as written by moe_dispatch_plan); writes rows [0, pad[E]) of x_frag,
+ *   zeros in the padding rows. d a multiple of 16.
+ * moe_expert_up_gelu_frag: h[r] = fp16(gelu_tanh(W1[e] . x_perm[r])) for every
+ *   expert e and unpadded row r in [offsets[e], offsets[e+1]) (ETP page w1;
+ *   EP tutorial 2.1 step 4), h [rows_max, d_ff] row-major as for
+ *   moe_expert_up_gelu; rows >= offsets[E] not touched. d a multiple of 256,
+ *   d_ff of 8, d and d_ff <= 2^20. No output tile is split along K.
+ * Pointers 16-byte aligned device memory; offsets read only by the kernels.
+ * Both calls take bf16 data only (no dtype argument).
+ * Errors: MOE_ERR_ALIGN for d, d_ff or a pointer that breaks the rules above;
+ *   MOE_ERR_SHAPE for E or sizes out of range; MOE_ERR_ARG for a NULL pointer
+ *   when rows_max > 0. */
+int64_t moe_frag_rows(int64_t rows_max, int32_t E);
+int moe_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t* offsets,
+                     int32_t E, int64_t rows_max, void* x_frag, hipStream_t stream);
+int moe_expert_up_gelu_frag(const void* x_frag, const int32_t* offsets, int32_t E,
+                            int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                            void* h, hipStream_t stream);
 
 /* Weighted combine back to token order (EP tutorial 2.1 step 5; 2.2: a
  * dropped slot takes no part):

@@ -279,6 +279,31 @@ int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E, in
                     "moe_expert_up_gelu launch");
 }
 
+int64_t moe_frag_rows(int64_t rows_max, int32_t E) {
+  if (rows_max < 0 || E < 1 || E > MOE_MAX_E) return -1;
+  return moe::frag_rows(rows_max, E);
+}
+
+int moe_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t* offsets,
+                     int32_t E, int64_t rows_max, void* x_frag, hipStream_t stream) {
+  MOE_TRY(check_permute(x, d, MOE_BF16, src, offsets, E, rows_max, x_frag));
+  if (d % 16 != 0) return fail(MOE_ERR_ALIGN, "d = %lld must be a multiple of 16", static_cast<long long>(d));
+  if (rows_max > 0x7fffffffLL - 32LL * MOE_MAX_E || d > (1 << 20))
+    return fail(MOE_ERR_SHAPE, "moe_permute_frag needs rows_max < 2^31 - 8192 and d <= 2^20");
+  return hip_status(moe::launch_permute_frag(x, d, src, offsets, E, rows_max, x_frag, stream),
+                    "moe_permute_frag launch");
+}
+
+int moe_expert_up_gelu_frag(const void* x_frag, const int32_t* offsets, int32_t E, int64_t rows_max,
+                            int64_t d, int64_t d_ff, const void* w1, void* h, hipStream_t stream) {
+  MOE_TRY(check_ffn(x_frag, offsets, E, rows_max, d, d_ff, w1, MOE_BF16, h));
+  if (d % 256 != 0) return fail(MOE_ERR_ALIGN, "d = %lld must be a multiple of 256", static_cast<long long>(d));
+  if (rows_max > 0x7fffffffLL - 32LL * MOE_MAX_E)
+    return fail(MOE_ERR_SHAPE, "moe_expert_up_gelu_frag needs rows_max < 2^31 - 8192");
+  return hip_status(moe::launch_up_gelu_frag(x_frag, offsets, E, rows_max, d, d_ff, w1, h, stream),
+                    "moe_expert_up_gelu_frag launch");
+}
+
 int moe_expert_down(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,
                     int64_t d_ff, const void* w2, int32_t dtype, float* y_perm, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {

@@ -1,0 +1,412 @@
+// Up-projection + GELU-tanh of the grouped expert FFN (ETP page
+// "ETP专家并行加速MoE模型": each expert's up-projection w1; EP tutorial
+// "专家并行：混合专家模型的分布式训练方案", section 2.1 steps 3-4: the permuted
+// tokens of each expert go through its FFN) with the activation operand in
+// MFMA-fragment order, for bf16 layers.
+//
+// Fragment order. The rows of each expert segment are padded to a multiple of
+// 32 (padded segment e starts at row pad[e] = sum over e' < e of
+// round_up(kept_e', 32)); element (padded row r, k) of x_frag sits at
+//   ((r / 32) (d / 16) + k / 16) 512 + ((r % 32) + 32 ((k / 8) % 2)) 8 + k % 8,
+// so each 32-row x 16-k block is 1 KiB in the lane order of the MFMA A operand
+// (lane l: row l % 32, k = 8 (l / 32) .. +7). Padding rows hold zeros.
+//
+// permute_frag_kernel writes it from x and src[] (the gather of the permute,
+// EP tutorial section 5.3: tokens of one expert made contiguous), staging a
+// 32-row x 256-column block in LDS so that both the row reads and the
+// fragment writes are whole 16-byte-per-lane wave accesses.
+//
+// up_frag_kernel: C = x_perm W1[e]^T over the segments, h = fp16(gelu_tanh(C))
+// row-major [rows, d_ff] at the unpadded rows (the same h as the row-major
+// path, bit for bit: every MFMA sees the same operands in the same order).
+// 256 x 256 tiles, four waves as 4 x 1 (wave w: rows 64 w .. +63, all 256
+// columns, 2 x 8 accumulator tiles of 32 x 32). Each wave loads its A
+// fragments straight into registers (1 KiB contiguous per wave load, four
+// stages of register buffers, issued three stages ahead); only W1 goes through
+// LDS, in a ring of four 32 KiB slots filled by LDS-DMA three stages ahead.
+// One barrier per 64-deep stage. Tiles continue across a workgroup's units:
+// the last three stages of a tile prefetch the next tile's first three, so
+// those loads are in flight during the per-wave epilogue.
+#include "ffn_common.h"
+
+namespace moe {
+namespace {
+
+using namespace ffn;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef unsigned int u32x4v __attribute__((__vector_size__(16)));
+
+constexpr int FBM = 256, FBN = 256, FBK = 64;
+constexpr int kFT = 256;                       // threads
+constexpr int kFW = kFT / kWave;               // waves (4)
+constexpr int FMI = 2, FNI = 8;                // 32 x 32 accumulator tiles per wave
+constexpr int kFABuf = 4;                      // A register buffers (stages)
+constexpr int kFCpr = FBK / 8;                 // 16-byte chunks per W1 row of a stage (8)
+constexpr int kFSlotU4 = FBN * kFCpr;          // uint4 per LDS slot (32 KiB)
+constexpr int kFBLoads = FBN / 8 / kFW;        // LDS-DMA loads per wave per stage (8)
+constexpr int kFAFrag = FMI * 4;               // A fragments per wave per stage (8)
+constexpr int kFEpiP = 136;                    // floats per row of a wave's epilogue buffer
+
+#define FR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define FR_BARRIER()                                        \
+  do {                                                      \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      \
+    __builtin_amdgcn_s_barrier();                           \
+    asm volatile("" ::: "memory");                          \
+  } while (0)
+
+// s_pad[e] = padded start row of segment e (e = 0..E), from offsets[]; every
+// thread of the block calls. s_tmp: kMaxE ints of scratch.
+__device__ void build_pad_offsets(const int32_t* __restrict__ offsets, int E, int* s_pad, int* s_tmp) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kMaxE; e += blockDim.x)
+    s_tmp[e] = e < E ? (offsets[e + 1] - offsets[e] + 31) / 32 * 32 : 0;
+  __syncthreads();
+  int* in = s_tmp;
+  int* out = s_pad + 1;
+  for (int o = 1; o < kMaxE; o <<= 1) {   // inclusive Hillis-Steele scan
+    for (int e = tid; e < kMaxE; e += blockDim.x) out[e] = in[e] + (e >= o ? in[e - o] : 0);
+    __syncthreads();
+    int* t = in;
+    in = out;
+    out = t;
+  }
+  for (int e = tid; e < kMaxE; e += blockDim.x) s_pad[e + 1] = in[e];   // 8 steps: result in s_tmp
+  if (tid == 0) s_pad[0] = 0;
+  __syncthreads();
+}
+
+// Workgroup (b, cb): padded block b (32 rows), columns 256 cb .. +255.
+__global__ __launch_bounds__(256) void permute_frag_kernel(
+    const uint4* __restrict__ x, int64_t d, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ offsets, int E, uint4* __restrict__ x_frag) {
+  __shared__ int s_pad[kMaxE + 1];
+  __shared__ int s_tmp[kMaxE];
+  __shared__ uint4 s_blk[32][32 + 1];   // 32 rows x 32 chunks of 16 bytes (+1: no bank aliasing)
+  build_pad_offsets(offsets, E, s_pad, s_tmp);
+  const int b = blockIdx.x;
+  if (b * 32 >= s_pad[E]) return;
+  int lo = 0, hi = E;   // the segment holding padded row 32 b: largest e with s_pad[e] <= 32 b
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pad[mid] <= b * 32) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo;
+  const int p0 = b * 32 - s_pad[e];                 // first row of the block within the segment
+  const int kept = offsets[e + 1] - offsets[e];
+  const int64_t d16 = d >> 3;                       // 16-byte chunks per row
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 32;   // first chunk of this column block
+  const int tid = threadIdx.x;
+  // Read: thread t takes chunks (t % 32) of rows t / 32, + 8, + 16, + 24.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rr = tid / 32 + 8 * u, cc = tid % 32;
+    const int p = p0 + rr;
+    uint4 v = uint4{0, 0, 0, 0};
+    if (p < kept && c0 + cc < d16) {
+      const int64_t row = src[offsets[e] + p];
+      v = x[row * d16 + c0 + cc];
+    }
+    s_blk[rr][cc] = v;
+  }
+  __syncthreads();
+  // Write: fragment s (16 k = chunks 2 s, 2 s + 1) of the block is 64 units of
+  // 16 bytes, unit l = row l % 32, chunk 2 s + l / 32; thread t writes units
+  // (t % 64) of fragments t / 64, + 4, + 8, + 12.
+  const int64_t frag0 = static_cast<int64_t>(b) * (d >> 4) + (c0 >> 1);   // first fragment of the column block
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int fs = tid / 64 + 4 * u, l = tid % 64;
+    if (c0 + 2 * fs >= d16) continue;
+    x_frag[(frag0 + fs) * 64 + l] = s_blk[l % 32][2 * fs + l / 32];
+  }
+}
+
+struct FCtx {
+  __amdgpu_buffer_rsrc_t a, b;
+  int m0, n0, seg1;
+};
+
+__device__ __forceinline__ void fr_store16(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const u32x4v x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, 0, 0);
+}
+
+__global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
+    const uint16_t* __restrict__ Afrag, const int32_t* __restrict__ offsets, int E, int N, int K,
+    const uint16_t* __restrict__ B, uint16_t* __restrict__ H) {
+  // One LDS variable per slot: with a single array the compiler cannot tell
+  // the slot being read from the ones the DMA is filling and waits for all.
+  __shared__ uint4 sb0[kFSlotU4];
+  __shared__ uint4 sb1[kFSlotU4];
+  __shared__ uint4 sb2[kFSlotU4];
+  __shared__ uint4 sb3[kFSlotU4];
+  __shared__ int s_pref[kMaxE + 1];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_pad[kMaxE + 1];
+  __shared__ int s_tmp[kMaxE];
+  __shared__ float s_epi[kFW][8 * kFEpiP];
+  auto SL = [&](int S) -> uint4* { return S == 0 ? sb0 : (S == 1 ? sb1 : (S == 2 ? sb2 : sb3)); };
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += kFT) s_off[e] = offsets[e];
+  build_tile_prefix(offsets, E, FBM, s_pref, s_tmp);
+  build_pad_offsets(offsets, E, s_pad, s_tmp);
+  const int tiles_n = (N + FBN - 1) / FBN;
+  const int nk = K / FBK;   // the host checks K % 256 == 0: nk is a multiple of 4
+  // Tile list as in the row-segmented GEMM: eight contiguous ranges, one per
+  // XCD (workgroup b runs on XCD b % 8), taken round-robin by its P workgroups.
+  const int P = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, w = blockIdx.x >> 3;
+  const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pref[E])) * tiles_n;
+  const int64_t r_beg = total * xcd / 8;
+  const int64_t n_x = total * (xcd + 1) / 8 - r_beg;
+  const int64_t n_units = n_x / P + (w < n_x % P ? 1 : 0);
+  if (n_units == 0) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const uint32_t b_rb = static_cast<uint32_t>(K) * 2u;
+  const uint32_t a_blk = static_cast<uint32_t>(K) * 64u;   // bytes per 32-row block of x_frag
+  // LDS-DMA of W1: wave-wide load j fills rows 8 (4 j + wave) + lane / 8 of
+  // the slot at physical chunk lane % 8, fetching logical chunk
+  // (lane % 8) ^ ((row >> 1) & 7); fragment reads undo the XOR.
+  const uint32_t ld_voff_b = (lane >> 3) * b_rb + (((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16u);
+  const int fr_x = hl ^ ((l32 >> 1) & 7);
+
+  auto make_ctx = [&](int64_t q, FCtx& c) {
+    const Tile tl = find_tile(s_pref, E, tiles_n, r_beg + w + q * P);
+    const int te = __builtin_amdgcn_readfirstlane(tl.e);
+    c.seg1 = __builtin_amdgcn_readfirstlane(s_off[te + 1]);
+    c.m0 = __builtin_amdgcn_readfirstlane(s_off[te] + tl.mi * FBM);
+    c.n0 = __builtin_amdgcn_readfirstlane(tl.nt * FBN);
+    const int pad_blk = __builtin_amdgcn_readfirstlane(s_pad[te] / 32 + tl.mi * (FBM / 32));
+    const int blocks = (min(c.seg1 - c.m0, FBM) + 31) / 32;
+    c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Afrag) + static_cast<int64_t>(pad_blk) * (a_blk / 2),
+                                            0, static_cast<int>(blocks * a_blk), 0x00020000);
+    const int b_rows = min(N - c.n0, FBN);
+    c.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B + (static_cast<int64_t>(te) * N + c.n0) * K),
+                                            0, static_cast<int>(b_rows * b_rb), 0x00020000);
+  };
+
+  uint4 fa[kFABuf][kFAFrag];   // [stage buffer][4 i + slice]
+  uint4 fb[2][FNI];
+  f32x16 acc[FMI][FNI];
+
+  // A fragments f0 .. f1-1 (f = 4 i + slice) of stage kt into buffer AB.
+  auto issue_a = [&](const FCtx& c, int kt, auto ab_c, int f0, int f1) __attribute__((always_inline)) {
+    constexpr int AB = decltype(ab_c)::value;
+#pragma unroll
+    for (int f = f0; f < f1; ++f) {
+      const int i = f >> 2, s = f & 3;
+      const uint32_t so = static_cast<uint32_t>(2 * wave + i) * a_blk + static_cast<uint32_t>(4 * kt + s) * 1024u;
+      fa[AB][f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          c.a, static_cast<uint32_t>(lane) * 16u, so, 0));
+    }
+  };
+  // W1 loads j0 .. j1-1 of stage kt into slot S.
+  auto issue_b = [&](const FCtx& c, int kt, int S, int j0, int j1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      const int blk = j * kFW + wave;
+      const uint32_t so = blk * 8 * b_rb + static_cast<uint32_t>(kt) * FBK * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(SL(S) + blk * kWave), 16, ld_voff_b, so, 0, 0);
+    }
+  };
+  auto read_b = [&](int S, int kk, int fs) __attribute__((always_inline)) {
+    int x = fr_x;
+    asm volatile("" : "+v"(x));   // recomputed per read rather than kept live
+    const int base = l32 * kFCpr + (x ^ (kk * 2));
+#pragma unroll
+    for (int j = 0; j < FNI; ++j) fb[fs][j] = SL(S)[base + j * 32 * kFCpr];
+  };
+  auto mfma_slice = [&](auto ab_c, int s, int fs) __attribute__((always_inline)) {
+    constexpr int AB = decltype(ab_c)::value;
+#pragma unroll
+    for (int i = 0; i < FMI; ++i)
+#pragma unroll
+      for (int j = 0; j < FNI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+  };
+  // NV memory loads (issued just before) spread over a slice's 16 MFMAs.
+  auto interleave = [&](auto nv_c) __attribute__((always_inline)) {
+    constexpr int NV = decltype(nv_c)::value;
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+      if (qq * NV % 16 < NV) {
+        __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);   // SALU (offsets, M0)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+      }
+    }
+  };
+
+  FCtx cur, nxt;
+  make_ctx(0, cur);
+  if (n_units > 1) make_ctx(1, nxt);
+  else nxt = cur;   // past the last unit the prefetches re-read this one (never used)
+  // Prologue: stages 0, 1, 2 of the first unit.
+  issue_a(cur, 0, std::integral_constant<int, 0>{}, 0, kFAFrag);
+  issue_b(cur, 0, 0, 0, kFBLoads);
+  issue_a(cur, 1, std::integral_constant<int, 1>{}, 0, kFAFrag);
+  issue_b(cur, 1, 1, 0, kFBLoads);
+  issue_a(cur, 2, std::integral_constant<int, 2>{}, 0, kFAFrag);
+  issue_b(cur, 2, 2, 0, kFBLoads);
+
+  // Stage kt (slot and A buffer SB = kt % 4, compile time) of unit q. It
+  // prefetches stage kt+3 of unit q or, past the end, of unit q+1 (after the
+  // last unit: an in-bounds stage into buffers nobody reads, so every stage
+  // issues the same 16 loads). Loads per slice: A 0-3 and W1 0-1, A 4-7 and
+  // W1 2-4, W1 5-7. At the end of slice 2 it waits for stage kt+1, whose
+  // loads are older than the 16 of each of stages kt-1 and kt and, in the
+  // first two stages after a per-wave epilogue, that epilogue's NST stores.
+  int64_t q = 0;
+  bool after_epi = false;
+  auto stage = [&](auto sb_c, int kt) __attribute__((always_inline)) {
+    constexpr int SB = decltype(sb_c)::value;
+    constexpr int SN = (SB + 3) % 4;     // slot and buffer of stage kt+3 (those of kt-1)
+    constexpr int S1 = (SB + 1) % 4;     // of stage kt+1
+    const int kp = kt + 3;
+    const bool pre_cur = kp < nk;
+    const FCtx pc = pre_cur ? cur : nxt;
+    const int pk = pre_cur ? kp : kp - nk;
+    read_b(SB, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(pc, pk, std::integral_constant<int, SN>{}, 0, 4);
+    issue_b(pc, pk, SN, 0, 2);
+    mfma_slice(std::integral_constant<int, SB>{}, 0, 0);
+    interleave(std::integral_constant<int, 6>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(SB, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(pc, pk, std::integral_constant<int, SN>{}, 4, 8);
+    issue_b(pc, pk, SN, 2, 5);
+    mfma_slice(std::integral_constant<int, SB>{}, 1, 1);
+    interleave(std::integral_constant<int, 7>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(SB, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(pc, pk, SN, 5, 8);
+    mfma_slice(std::integral_constant<int, SB>{}, 2, 0);
+    interleave(std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage kt+1 has landed; every wave is done with slot SB.
+    if (after_epi && kt < 2) FR_WAIT_VM(62);
+    else FR_WAIT_VM(32);
+    FR_BARRIER();
+    read_b(S1, 0, 0);
+    mfma_slice(std::integral_constant<int, SB>{}, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Per-wave epilogue of a tile: chunks of 8 rows x 128 columns of the wave's
+  // 64 x 256 block staged through its LDS buffer, then GELU, fp16 and 16-byte
+  // stores; lanes outside the output get an offset past the buffer's range
+  // and are dropped, so every lane issues exactly NST stores.
+  constexpr int ITEMS = 8 * 128 / 8 / kWave;   // 16-byte items per lane per chunk (2)
+  constexpr int NST = FMI * 4 * 2 * ITEMS;      // 32 stores per lane per tile
+  static_assert(NST == 32, "the waits above count 32 stores after an epilogue");
+  auto epilogue = [&](int c_m0, int c_n0, int c_seg1) {
+    float* const buf = s_epi[wave];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int el32 = ln & 31, ehl = ln >> 5;
+    const int rows_ok = min(c_seg1 - c_m0, FBM), cols_ok = min(N - c_n0, FBN);
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+        H + (static_cast<int64_t>(c_m0) * N + c_n0), 0, rows_ok * N * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < FMI; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {
+          // register 4 c + rr of tile (i, j) holds row 8 c + 4 (lane / 32) + rr, column 32 j + lane % 32
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              buf[(4 * ehl + rr) * kFEpiP + 32 * jj + el32] = acc[i][4 * jh + jj][4 * c + rr];
+#pragma unroll
+          for (int it = 0; it < ITEMS; ++it) {
+            const int f = ln + kWave * it;
+            const int row = f >> 4, col = (f & 15) << 3;
+            const float4 a = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col);
+            const float4 b = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col + 4);
+            const int trow = 64 * wave + 32 * i + 8 * c + row, tcol = 128 * jh + col;
+            const uint32_t voff = (trow < rows_ok && tcol < cols_ok)
+                                      ? static_cast<uint32_t>((trow * N + tcol) * 2) : 0x80000000u;
+            const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
+            const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
+            const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
+            const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
+            fr_store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
+                       out, voff);
+          }
+        }
+  };
+
+  for (;;) {
+    // Stage 0 of this unit has landed (older than stages 1-2's loads and, after
+    // an epilogue, its stores).
+    if (after_epi) FR_WAIT_VM(62);
+    else FR_WAIT_VM(32);
+    FR_BARRIER();
+    read_b(0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FMI; ++i)
+#pragma unroll
+      for (int j = 0; j < FNI; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int kt = 0; kt < nk; kt += 4) {
+      stage(std::integral_constant<int, 0>{}, kt);
+      stage(std::integral_constant<int, 1>{}, kt + 1);
+      stage(std::integral_constant<int, 2>{}, kt + 2);
+      stage(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    const int m0 = cur.m0, n0 = cur.n0, seg1 = cur.seg1;
+    ++q;
+    const bool has_next = q < n_units;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");   // the stores stay after the prefetches
+    epilogue(m0, n0, seg1);
+    if (!has_next) {
+      FR_WAIT_VM(0);   // the last prefetches (some into LDS) end before the workgroup
+      break;
+    }
+    cur = nxt;
+    if (q + 1 < n_units) make_ctx(q + 1, nxt);
+    else nxt = cur;
+    after_epi = true;
+  }
+}
+
+}  // namespace
+
+int64_t frag_rows(int64_t rows_max, int E) { return (rows_max + 31 * static_cast<int64_t>(E) + 31) / 32 * 32; }
+
+hipError_t launch_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t* offsets,
+                               int E, int64_t rows_max, void* x_frag, hipStream_t s) {
+  if (rows_max <= 0) return hipSuccess;
+  const dim3 g(static_cast<unsigned>(frag_rows(rows_max, E) / 32), static_cast<unsigned>((d + 255) / 256));
+  hipLaunchKernelGGL(permute_frag_kernel, g, dim3(256), 0, s, static_cast<const uint4*>(x), d, src, offsets, E,
+                     static_cast<uint4*>(x_frag));
+  return hipGetLastError();
+}
+
+hipError_t launch_up_gelu_frag(const void* x_frag, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
+                               int64_t d_ff, const void* w1, void* h, hipStream_t s) {
+  if (rows_max <= 0) return hipSuccess;
+  int64_t g = (device_cu_count() + 7) / 8 * 8;
+  const int64_t upper = (rows_max / FBM + E) * ((d_ff + FBN - 1) / FBN);   // >= the tile count
+  if (upper < g) g = (upper + 7) / 8 * 8;
+  hipLaunchKernelGGL(up_frag_kernel, dim3(static_cast<unsigned>(g)), dim3(kFT), 0, s, static_cast<const uint16_t*>(x_frag), offsets, E,
+                     static_cast<int>(d_ff), static_cast<int>(d), static_cast<const uint16_t*>(w1),
+                     static_cast<uint16_t*>(h));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
-           "moe_ffn_workspace_bytes", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
+           "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
            "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
            "moe_expert_up_backward", "moe_expert_weight_grads", "moe_gate_backward",
            "moe_gate_weight_grads_workspace_bytes", "moe_gate_weight_grads", "moe_dispatch_backward",
@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
         "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
         "moe_ffn_workspace_bytes": (SZ, [I32]),
+        "moe_frag_rows": (I64, [I64, I32]),
+        "moe_permute_frag": (ctypes.c_int, [P, I64, P, P, I32, I64, P, P]),
+        "moe_expert_up_gelu_frag": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P]),
         "moe_combine": (ctypes.c_int, [P, P, P, I64, I32, I64, P, I32, P]),
         "moe_aux_loss_workspace_bytes": (SZ, [I64, I32]),
         "moe_aux_loss": (ctypes.c_int, [P, P, I64, I32, I32, F32, P, P, SZ, P]),
@@ -261,6 +264,43 @@ def moe_expert_down(h, offsets, w2, rows_max: int, y_perm=None, workspace=None, 
     return y_perm
 
 
+def moe_frag_rows(rows_max: int, E: int) -> int:
+    """Rows to allocate for the fragment-ordered copy of x_perm."""
+    return int(lib().moe_frag_rows(rows_max, E))
+
+
+def frag_eligible(dtype, d: int) -> bool:
+    """Whether moe_forward takes the fragment-ordered up-projection for this
+    layer: bf16, d a multiple of 256 and at least 4096. Measured on the
+    workloads: 4-8% faster than the row-major permute + up-projection at
+    d = 4096 (each tile runs 64 stages of 64), even at d = 2048 and slower at
+    d = 1024, where the row-major kernel's split of a short last round of
+    tiles along K (which this kernel does not do) and its cheaper permute
+    weigh more."""
+    return dtype == torch.bfloat16 and d % 256 == 0 and d >= 4096
+
+
+def moe_permute_frag(x, src, offsets, rows_max: int, x_frag=None, stream=None):
+    """x_perm rows in matrix-core fragment order, expert segments padded to
+    multiples of 32 rows (bf16)."""
+    d = x.shape[1]
+    E = offsets.numel() - 1
+    if x_frag is None:
+        x_frag = _empty((max(moe_frag_rows(rows_max, E), 1), d), x.dtype, x)
+    _check(lib().moe_permute_frag(_ptr(x), d, _ptr(src), _ptr(offsets), E, rows_max, _ptr(x_frag),
+                                  _stream(stream)))
+    return x_frag
+
+
+def moe_expert_up_gelu_frag(x_frag, offsets, w1, rows_max: int, h=None, stream=None):
+    """moe_expert_up_gelu (without a workspace) from the fragment-ordered copy."""
+    E, d_ff, d = w1.shape
+    h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x_frag) if h is None else h
+    _check(lib().moe_expert_up_gelu_frag(_ptr(x_frag), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
+                                         _ptr(h), _stream(stream)))
+    return h
+
+
 def moe_grouped_ffn(x_perm, offsets, w1, w2, rows_max: int, h=None, y_perm=None, workspace=None,
                     stream=None):
     E, d_ff, d = w1.shape
@@ -404,7 +444,7 @@ class MoEBuffers:
     repeated forwards allocate nothing."""
 
     def __init__(self, T, d, d_ff, E, k, capacity, dtype, device, routed=True, want_probs=True,
-                 save_for_backward=False):
+                 save_for_backward=False, frag=None):
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
         self.T, self.d, self.d_ff, self.E, self.k, self.capacity = T, d, d_ff, E, k, capacity
         self.rows_max = moe_rows_max(T, k, E, capacity)
@@ -416,7 +456,15 @@ class MoEBuffers:
         self.offsets = z((E + 1,), torch.int32)
         self.dest = z((T, k), torch.int32)
         self.src = z((R,), torch.int32)
-        self.x_perm = z((R, d), dtype)
+        # bf16 forward without a backward: the permuted rows in fragment order
+        # (x_frag) instead of row-major (x_perm); frag=None picks it when eligible
+        if frag is None:
+            frag = frag_eligible(dtype, d) and not save_for_backward
+        if frag and (save_for_backward or dtype != torch.bfloat16 or d % 256 != 0):
+            raise ValueError("the fragment-ordered path needs bf16, d % 256 == 0 and no backward")
+        self.frag = bool(frag)
+        self.x_perm = None if self.frag else z((R, d), dtype)
+        self.x_frag = z((max(moe_frag_rows(self.rows_max, E), 1), d), dtype) if self.frag else None
         self.h = z((R, d_ff), hidden_dtype(dtype))
         # the pre-activation, kept for the backward
         self.z = z((R, d_ff), hidden_dtype(dtype)) if save_for_backward else None
@@ -439,7 +487,10 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     stream. With `w_gate` None, `topk_idx`/`topk_w` are taken as given (a
     receiver's share: the rows it got and their weights). With
     `save_for_backward` the up-projection also keeps the pre-activation and
-    the router its log-sum-exp (what moe_backward needs)."""
+    the router its log-sum-exp (what moe_backward needs). Without a backward,
+    bf16 layers that frag_eligible() accepts run the permute and the
+    up-projection on the fragment-ordered copy (bufs.frag; the same h bit for
+    bit as the row-major up-projection without a workspace)."""
     T, d = x.shape
     E, d_ff, _ = w1.shape
     routed = w_gate is not None
@@ -458,15 +509,23 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     else:
         idx, w = topk_idx, topk_w
     bufs.used_idx, bufs.used_w = idx, w   # the routing the layer ran with (given or computed)
-    moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
-                 bufs.x_perm, bufs.ws_dispatch, stream)
-    if bufs.z is not None:
-        moe_expert_up_gelu_z(bufs.x_perm, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.z,
-                             bufs.ws_ffn, stream)
+    if bufs.frag:
+        moe_dispatch_plan(idx, E, capacity, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
+                          bufs.ws_dispatch, stream)
+        moe_permute_frag(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_frag, stream)
+        moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, stream)
         moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn, stream)
     else:
-        moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
-                        bufs.ws_ffn, stream)
+        moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
+                     bufs.x_perm, bufs.ws_dispatch, stream)
+        if bufs.z is not None:
+            moe_expert_up_gelu_z(bufs.x_perm, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.z,
+                                 bufs.ws_ffn, stream)
+            moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn,
+                            stream)
+        else:
+            moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
+                            bufs.ws_ffn, stream)
     moe_combine(bufs.y_perm, bufs.dest, w, d, torch.float32, bufs.y, stream)
     if routed and bufs.probs is not None:
         moe_aux_loss(bufs.probs, bufs.counts, k, alpha, bufs.loss, bufs.ws_aux, stream)

@@ -75,3 +75,24 @@ def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
 def cached_inputs(cfg: I.MoEConfig):
     say("  generating inputs for %s" % (cfg,))
     return I.make_inputs(cfg)
+
+
+def unfrag(x_frag, offsets, d: int):
+    """Row-major x_perm rows [offsets[E], d] read back from the fragment-ordered
+    copy, and the padding rows of every segment, from the layout's definition:
+    segment e starts at padded row pad[e] = sum of roundup(kept, 32) before it,
+    and element (padded row r, column c) sits at
+    ((r // 32) (d // 16) + c // 16) 512 + ((r % 32) + 32 ((c // 8) % 2)) 8 + c % 8."""
+    off = [int(v) for v in offsets]
+    kept = [b - a for a, b in zip(off[:-1], off[1:])]
+    pad_total = sum((n + 31) // 32 * 32 for n in kept)
+    flat = x_frag.reshape(-1)[: pad_total * d]
+    # (block, 16-column group, column half, row in block, column in half)
+    rows = flat.reshape(pad_total // 32, d // 16, 2, 32, 8).permute(0, 3, 1, 2, 4).reshape(pad_total, d)
+    parts, pads, p = [], [], 0
+    for n in kept:
+        parts.append(rows[p:p + n])
+        pads.append(rows[p + n:p + (n + 31) // 32 * 32])
+        p += (n + 31) // 32 * 32
+    cat = lambda ts: torch.cat(ts) if ts else rows[:0]
+    return cat(parts), cat(pads), pad_total

@@ -183,6 +183,32 @@ def test_ffn_combine_aux_argument_errors():
     assert L.moe_aux_loss(FAKE, FAKE, 10, 8, 9, 0.01, FAKE, FAKE, 1 << 20, None) == -3
 
 
+def test_fragment_path_argument_errors_and_sizes():
+    L = ops.lib()
+    # padded rows: every segment rounds up to 32, so rows_max + 31 E, rounded up to 32, bounds them
+    assert L.moe_frag_rows(0, 1) == 32
+    assert L.moe_frag_rows(10240, 8) == 10496
+    assert L.moe_frag_rows(1, 256) == (1 + 31 * 256 + 31) // 32 * 32
+    assert L.moe_frag_rows(-1, 8) == -1 and L.moe_frag_rows(10, 0) == -1 and L.moe_frag_rows(10, 257) == -1
+    # moe_permute_frag(x, d, src, offsets, E, rows_max, x_frag, stream)
+    assert L.moe_permute_frag(FAKE, 264, FAKE, FAKE, 8, 10, FAKE, None) == -6      # d % 16
+    assert L.moe_permute_frag(FAKE, 60, FAKE, FAKE, 8, 10, FAKE, None) == -6       # d % 8
+    assert L.moe_permute_frag(None, 256, FAKE, FAKE, 8, 10, FAKE, None) == -1
+    assert L.moe_permute_frag(FAKE, 256, FAKE, None, 8, 10, FAKE, None) == -1
+    assert L.moe_permute_frag(FAKE, 256, FAKE, FAKE, 0, 10, FAKE, None) == -3
+    assert L.moe_permute_frag(FAKE, 256, FAKE, FAKE, 8, -1, FAKE, None) == -1
+    assert L.moe_permute_frag(FAKE, 256, FAKE, FAKE, 8, 10, ctypes.c_void_p((1 << 20) + 4), None) == -6
+    assert L.moe_permute_frag(None, 256, None, None, 8, 0, None, None) == 0
+    # moe_expert_up_gelu_frag(x_frag, offsets, E, rows_max, d, d_ff, w1, h, stream)
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 264, 128, FAKE, FAKE, None) == -6   # d % 256
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 130, FAKE, FAKE, None) == -6   # d_ff % 8
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 300, 10, 256, 128, FAKE, FAKE, None) == -3
+    assert L.moe_expert_up_gelu_frag(FAKE, None, 8, 10, 256, 128, FAKE, FAKE, None) == -1
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 128, FAKE, None, None) == -1
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 1 << 21, 128, FAKE, FAKE, None) == -3
+    assert L.moe_expert_up_gelu_frag(None, None, 8, 0, 256, 128, None, None, None) == 0
+
+
 def test_ffn_workspace_bytes():
     L = ops.lib()
     assert L.moe_ffn_workspace_bytes(0) == 0           # f32 kernels never split a tile

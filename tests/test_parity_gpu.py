@@ -17,7 +17,7 @@ import torch
 from mixture_experts_layer_49_amd import inputs as I
 from mixture_experts_layer_49_amd import ops
 from oracle import moe_oracle as O
-from parity_helpers import (GAP, cached_inputs, close, close_f32, dev, host, say, topk_gap)
+from parity_helpers import (GAP, cached_inputs, close, close_f32, dev, host, say, topk_gap, unfrag)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,19 +64,24 @@ def gpu_tensors(inp, cfg):
     return t
 
 
-def gpu_forward(inp, cfg, flags=0):
+def gpu_forward(inp, cfg, flags=0, frag=None):
+    """The layer forward; frag None lets moe_forward pick the path (the
+    fragment-ordered one where ops.frag_eligible), True or False forces one."""
     t = gpu_tensors(inp, cfg)
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    bufs = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, t["x"].dtype, t["x"].device,
+                          cfg.routed, frag=frag)
     b = ops.moe_forward(t["x"], t["w1"], t["w2"], cfg.k, C, w_gate=t.get("w_gate"),
                         bias=t.get("bias"), topk_idx=t.get("topk_idx"),
-                        topk_w=t.get("topk_w"), alpha=cfg.alpha, flags=flags)
+                        topk_w=t.get("topk_w"), alpha=cfg.alpha, flags=flags, bufs=bufs)
     torch.cuda.synchronize()
     R = int(host(b.offsets)[-1])
+    x_perm = unfrag(b.x_frag.cpu(), host(b.offsets), cfg.d)[0] if b.frag else b.x_perm[:R]
     out = {"C": C, "R": R, "rows_max": b.rows_max,
            "topk_idx": host(b.topk_idx) if cfg.routed else inp["topk_idx"],
            "topk_w": host(b.topk_w) if cfg.routed else inp["topk_w"],
            "counts": host(b.counts), "offsets": host(b.offsets), "dest": host(b.dest),
-           "src": host(b.src)[:R], "x_perm": b.x_perm[:R], "y_perm": host(b.y_perm)[:R],
+           "src": host(b.src)[:R], "x_perm": x_perm, "frag": b.frag, "y_perm": host(b.y_perm)[:R],
            "y": host(b.y)}
     if cfg.routed:
         out["probs"] = host(b.probs)
@@ -278,16 +283,19 @@ def test_dispatch_ignores_invalid_and_repeated_ids():
 
 
 # -------------------------------------------------------------- whole layer --
-def check_layer(inp, cfg, sample=None):
-    g, _ = gpu_forward(inp, cfg)
+def check_layer(inp, cfg, sample=None, frag=None):
+    g, t = gpu_forward(inp, cfg, frag=frag)
     gin = {"x": inp["x"], "w1": inp["w1"], "w2": inp["w2"],
            "topk_idx": g["topk_idx"], "topk_w": g["topk_w"]}
     ref = O.forward(gin, cfg.dtype, cfg.k, cfg.cf, cfg.alpha, sample_tokens=sample)
-    say("  %s: C=%d R=%d (rows_max %d)" % (cfg.name, g["C"], g["R"], g["rows_max"]))
+    say("  %s: C=%d R=%d (rows_max %d, %s path)" % (cfg.name, g["C"], g["R"], g["rows_max"],
+                                                   "fragment-ordered" if g["frag"] else "row-major"))
     np.testing.assert_array_equal(g["counts"], ref["counts"])
     np.testing.assert_array_equal(g["offsets"], ref["offsets"])
     np.testing.assert_array_equal(g["dest"], ref["dest"])
     np.testing.assert_array_equal(g["src"], ref["src"])
+    # the permuted rows (read back from the fragment order on that path): bit-exact
+    assert torch.equal(g["x_perm"].cpu(), t["x"].cpu()[torch.from_numpy(ref["src"]).long()])
     rows = ref["y_perm_rows"]
     if rows.size:
         close(g["y_perm"][rows], ref["y_perm"][rows], cfg.dtype, "y_perm")
@@ -309,6 +317,17 @@ def test_layer_small(cfg):
     g = check_layer(I.make_inputs(cfg), cfg)
     if cfg.name == "all-dropped":
         assert g["R"] == 0 and not g["y"].any()
+
+
+FRAG_SMALL = [c for c in SMALL if c.dtype == "bf16" and c.d % 256 == 0]
+
+
+@pytest.mark.parametrize("cfg", FRAG_SMALL, ids=ids(FRAG_SMALL))
+def test_layer_small_fragment_path(cfg):
+    """The layer with the fragment-ordered permute and up-projection forced
+    (moe_forward picks it by itself only from d = 4096)."""
+    g = check_layer(I.make_inputs(cfg), cfg, frag=True)
+    assert g["frag"]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=ids(FULL))
@@ -393,7 +412,7 @@ def test_combine_bf16_output():
 def test_ffn_halves_equal_whole():
     cfg = I.small("halves", T=400, d=256, d_ff=384, E=4, k=2, seed=61)
     inp = I.make_inputs(cfg)
-    g, t = gpu_forward(inp, cfg)
+    g, t = gpu_forward(inp, cfg, frag=False)
     x = t["x"]
     idx = dev(g["topk_idx"].astype(np.int32), "f32")
     C = g["C"]
@@ -418,7 +437,7 @@ def test_split_tiles_match_unsplit(name):
     run two pieces."""
     cfg = next(c for c in SMALL + FULL if c.name == name)
     inp = cached_inputs(cfg) if cfg in FULL else I.make_inputs(cfg)
-    g, t = gpu_forward(inp, cfg)
+    g, t = gpu_forward(inp, cfg, frag=False)
     idx = dev(g["topk_idx"].astype(np.int32), "f32")
     _, off, _, _, xp = ops.moe_dispatch(idx, cfg.E, g["C"], t["x"])
     rows = g["rows_max"]
