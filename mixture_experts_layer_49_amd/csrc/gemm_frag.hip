@@ -12,8 +12,8 @@
 // (lane l: row l % 32, k = 8 (l / 32) .. +7). Padding rows hold zeros.
 //
 // permute_frag_kernel writes it from x and src[] (the gather of the permute,
-// EP tutorial section 5.3: tokens of one expert made contiguous), staging a
-// 32-row x 256-column block in LDS so that both the row reads and the
+// EP tutorial section 5.3: tokens of one expert made contiguous), staging
+// 32-row x 256-column blocks in LDS so that both the row reads and the
 // fragment writes are whole 16-byte-per-lane wave accesses.
 //
 // up_frag_kernel: C = x_perm W1[e]^T over the segments, h = fp16(gelu_tanh(C))
@@ -77,50 +77,100 @@ __device__ void build_pad_offsets(const int32_t* __restrict__ offsets, int E, in
   __syncthreads();
 }
 
-// Workgroup (b, cb): padded block b (32 rows), columns 256 cb .. +255.
+// The segment holding padded row t (a multiple of 32), found by each wave on
+// its own (no barrier): lane j takes experts 4 j .. 4 j + 3 (E <= 256), sums
+// their padded lengths, and a wave-wide inclusive scan gives every lane its
+// range of padded rows. Returns false when t is past the last segment.
+struct SegPos {
+  int e, p0, seg0, kept;   // expert, t's row within the segment, its first row, its rows
+};
+__device__ __forceinline__ bool find_padded_segment(const int32_t* __restrict__ offsets, int E, int t, SegPos& sp) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int o[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) o[i] = offsets[min(4 * lane + i, E)];
+  int rk[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rk[i] = (o[i + 1] - o[i] + 31) & ~31;   // 0 past expert E-1: both ends are offsets[E]
+    sum += rk[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int v = __shfl_up(incl, dd, kWave);
+    if (lane >= dd) incl += v;
+  }
+  const int excl = incl - sum;
+  const unsigned long long hit = __ballot(excl <= t && t < incl);
+  if (hit == 0) return false;
+  const int L = __builtin_ctzll(hit);
+  // in lane L: step over its experts that end at or before t
+  int e = 4 * lane, base = excl;
+  bool past = true;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    past = past && t >= base + rk[i];
+    if (past) {
+      base += rk[i];
+      e = 4 * lane + i + 1;
+    }
+  }
+  const int ie = e - 4 * lane;
+  const int seg0 = ie == 0 ? o[0] : ie == 1 ? o[1] : ie == 2 ? o[2] : o[3];
+  const int seg1 = ie == 0 ? o[1] : ie == 1 ? o[2] : ie == 2 ? o[3] : o[4];
+  sp.e = __shfl(e, L, kWave);
+  sp.p0 = t - __shfl(base, L, kWave);
+  sp.seg0 = __shfl(seg0, L, kWave);
+  sp.kept = __shfl(seg1 - seg0, L, kWave);
+  return true;
+}
+
+constexpr int kPermCB = 4;   // 256-column blocks per permute workgroup
+
+// Workgroup (b, g): padded block b (32 rows), columns 256 kPermCB g .. +256 kPermCB - 1.
+// Thread t reads 16-byte chunk t % 32 of rows t / 32 + 8 u (u = 0..3) of each
+// column block, all 4 kPermCB loads in flight; then, block by block, the
+// 32 x 256 piece goes through LDS and leaves as 16 fragments of 1 KiB: unit l
+// of fragment fs (16 columns = chunks 2 fs, 2 fs + 1) is row l % 32, chunk
+// 2 fs + l / 32, and thread t writes units t % 64 of fragments t / 64 + 4 u.
 __global__ __launch_bounds__(256) void permute_frag_kernel(
     const uint4* __restrict__ x, int64_t d, const int32_t* __restrict__ src,
     const int32_t* __restrict__ offsets, int E, uint4* __restrict__ x_frag) {
-  __shared__ int s_pad[kMaxE + 1];
-  __shared__ int s_tmp[kMaxE];
-  __shared__ uint4 s_blk[32][32 + 1];   // 32 rows x 32 chunks of 16 bytes (+1: no bank aliasing)
-  build_pad_offsets(offsets, E, s_pad, s_tmp);
+  __shared__ uint4 s_blk[2][32][32 + 1];   // two column blocks; +1: no bank aliasing
   const int b = blockIdx.x;
-  if (b * 32 >= s_pad[E]) return;
-  int lo = 0, hi = E;   // the segment holding padded row 32 b: largest e with s_pad[e] <= 32 b
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_pad[mid] <= b * 32) lo = mid;
-    else hi = mid;
-  }
-  const int e = lo;
-  const int p0 = b * 32 - s_pad[e];                 // first row of the block within the segment
-  const int kept = offsets[e + 1] - offsets[e];
-  const int64_t d16 = d >> 3;                       // 16-byte chunks per row
-  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 32;   // first chunk of this column block
-  const int tid = threadIdx.x;
-  // Read: thread t takes chunks (t % 32) of rows t / 32, + 8, + 16, + 24.
+  SegPos sp;
+  if (!find_padded_segment(offsets, E, b * 32, sp)) return;   // uniform over the workgroup
+  const int64_t d16 = d >> 3;   // 16-byte chunks per row
+  const int tid = threadIdx.x, cc = tid % 32;
+  int64_t row[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int rr = tid / 32 + 8 * u, cc = tid % 32;
-    const int p = p0 + rr;
-    uint4 v = uint4{0, 0, 0, 0};
-    if (p < kept && c0 + cc < d16) {
-      const int64_t row = src[offsets[e] + p];
-      v = x[row * d16 + c0 + cc];
+    const int p = sp.p0 + tid / 32 + 8 * u;
+    row[u] = p < sp.kept ? static_cast<int64_t>(src[sp.seg0 + p]) : -1;
+  }
+  uint4 v[kPermCB][4];
+#pragma unroll
+  for (int c = 0; c < kPermCB; ++c) {
+    const int64_t ch = (static_cast<int64_t>(blockIdx.y) * kPermCB + c) * 32 + cc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[c][u] = (row[u] >= 0 && ch < d16) ? x[row[u] * d16 + ch] : uint4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int c = 0; c < kPermCB; ++c) {
+    const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * kPermCB + c) * 32;   // first chunk of the block
+    if (c0 >= d16) break;   // uniform
+    auto& blk = s_blk[c & 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) blk[tid / 32 + 8 * u][cc] = v[c][u];
+    __syncthreads();   // also: every thread is done reading this buffer two blocks ago
+    const int64_t frag0 = static_cast<int64_t>(b) * (d >> 4) + (c0 >> 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int fs = tid / 64 + 4 * u, l = tid % 64;
+      if (c0 + 2 * fs < d16) x_frag[(frag0 + fs) * 64 + l] = blk[l % 32][2 * fs + l / 32];
     }
-    s_blk[rr][cc] = v;
-  }
-  __syncthreads();
-  // Write: fragment s (16 k = chunks 2 s, 2 s + 1) of the block is 64 units of
-  // 16 bytes, unit l = row l % 32, chunk 2 s + l / 32; thread t writes units
-  // (t % 64) of fragments t / 64, + 4, + 8, + 12.
-  const int64_t frag0 = static_cast<int64_t>(b) * (d >> 4) + (c0 >> 1);   // first fragment of the column block
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int fs = tid / 64 + 4 * u, l = tid % 64;
-    if (c0 + 2 * fs >= d16) continue;
-    x_frag[(frag0 + fs) * 64 + l] = s_blk[l % 32][2 * fs + l / 32];
   }
 }
 
@@ -391,7 +441,8 @@ int64_t frag_rows(int64_t rows_max, int E) { return (rows_max + 31 * static_cast
 hipError_t launch_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t* offsets,
                                int E, int64_t rows_max, void* x_frag, hipStream_t s) {
   if (rows_max <= 0) return hipSuccess;
-  const dim3 g(static_cast<unsigned>(frag_rows(rows_max, E) / 32), static_cast<unsigned>((d + 255) / 256));
+  const dim3 g(static_cast<unsigned>(frag_rows(rows_max, E) / 32),
+               static_cast<unsigned>((d + 256 * kPermCB - 1) / (256 * kPermCB)));
   hipLaunchKernelGGL(permute_frag_kernel, g, dim3(256), 0, s, static_cast<const uint4*>(x), d, src, offsets, E,
                      static_cast<uint4*>(x_frag));
   return hipGetLastError();
