@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <mutex>
 
+#include "gemm_frag.h"
 #include "moe_internal.h"
 
 namespace {

@@ -28,6 +28,7 @@
 // the last three stages of a tile prefetch the next tile's first three, so
 // those loads are in flight during the per-wave epilogue.
 #include "ffn_common.h"
+#include "gemm_frag.h"
 
 namespace moe {
 namespace {

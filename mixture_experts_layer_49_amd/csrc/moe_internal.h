@@ -89,13 +89,6 @@ inline hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets
                           B, C, nullptr, ws, s);
 }
 
-// bf16 up-projection from the fragment-ordered copy of x_perm (gemm_frag.hip).
-int64_t frag_rows(int64_t rows_max, int E);
-hipError_t launch_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t* offsets,
-                               int E, int64_t rows_max, void* x_frag, hipStream_t s);
-hipError_t launch_up_gelu_frag(const void* x_frag, const int32_t* offsets, int E, int64_t rows_max,
-                               int64_t d, int64_t d_ff, const void* w1, void* h, hipStream_t s);
-
 // Workspace bytes of the expert FFN on the current device (0 for f32 layers).
 size_t ffn_workspace_bytes(int dtype);
 size_t ffn_mfma_workspace_bytes();
