@@ -323,6 +323,9 @@ def main(argv=None) -> int:
     given_w = dev(inp["topk_w"], False) if not cfg.routed else None
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
     b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed)
+    # inference weight format: W2 in fp16, converted once (exact; the kernels
+    # would otherwise convert each W2 value in registers on every step)
+    w2h = ops.moe_weights_bf16_to_f16(w2) if bf else None
     stream = torch.cuda.current_stream()
 
     names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]
@@ -350,7 +353,10 @@ def main(argv=None) -> int:
             rec(3)
             ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
         rec(4)
-        ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
+        if w2h is not None:
+            ops.moe_expert_down_f16w(b.h, b.offsets, w2h, b.rows_max, b.y_perm, b.ws_ffn)
+        else:
+            ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
         rec(5)
         ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
         rec(6)
@@ -402,7 +408,8 @@ def main(argv=None) -> int:
     dom = "up_gelu" if per[3] >= per[4] else "down"
     dom_frag = dom == "up_gelu" and b.frag
     dom_kernel = ("up_frag_kernel" if dom_frag else
-                  "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else "down"))
+                  "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else
+                                             "down_f16w" if w2h is not None else "down"))
     achieved = breakdown[dom]["TFLOP/s"]
     ffn_tflops = (flops_up + flops_down) / ((per[3] + per[4]) * 1e-3) / 1e12
 
@@ -423,10 +430,12 @@ def main(argv=None) -> int:
                    "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
                    "max_over_mean_load": float(counts.max() / counts.mean()),
                    "activation_layout": "fragment-ordered" if b.frag else "row-major",
+                   "w2_storage": "fp16 (converted once from the bf16 weights, exact)" if bf else "f32",
                    "parallelism": "single GPU"},
         "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
-                     "traffic": measured_traffic("up" if dom == "up_gelu" else "down", cfg.name,
+                     "traffic": measured_traffic("up" if dom == "up_gelu" else
+                                                 "down_f16w" if w2h is not None else "down", cfg.name,
                                                  "gemm_frag" if dom_frag else "gemm_mfma"),
                      "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
                      "launch_us": us[dom]},

@@ -199,6 +199,20 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
                     int32_t dtype, float* y_perm, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/* W2 stored in fp16, for bf16 layers (an inference-time weight format; the
+ * down-projection of moe_expert_down converts every bf16 W2 value to fp16 in
+ * registers before the fp16 x fp16 products, this does it once up front).
+ * moe_weights_bf16_to_f16: w_f16[i] = fp16(w[i]) for i < n, round to nearest
+ *   even (exact for bf16 values inside the fp16 normal range; the same
+ *   rounding the kernels apply). 16-byte aligned device pointers.
+ * moe_expert_down_f16w: moe_expert_down (dtype MOE_BF16) with w2_f16 [E, d,
+ *   d_ff] fp16 = moe_weights_bf16_to_f16(W2); y_perm bit-identical to
+ *   moe_expert_down on the bf16 W2 with the same workspace argument. */
+int moe_weights_bf16_to_f16(const void* w, int64_t n, void* w_f16, hipStream_t stream);
+int moe_expert_down_f16w(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max,
+                         int64_t d, int64_t d_ff, const void* w2_f16, float* y_perm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of expert-FFN workspace for the current device: two 256 x 256
  * float32 partial tiles per compute unit (128 MiB on a 256-CU MI355X) for
  * MOE_BF16; 0 for MOE_F32 (whose kernels never split). */

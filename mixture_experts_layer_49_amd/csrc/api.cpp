@@ -315,6 +315,25 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E, int64_t ro
                     "moe_expert_down launch");
 }
 
+int moe_weights_bf16_to_f16(const void* w, int64_t n, void* w_f16, hipStream_t stream) {
+  if (n < 0) return fail(MOE_ERR_ARG, "n = %lld < 0", static_cast<long long>(n));
+  if (n == 0) return MOE_OK;
+  MOE_NONNULL(w);
+  MOE_NONNULL(w_f16);
+  MOE_TRY(check_ptr16("w", w));
+  MOE_TRY(check_ptr16("w_f16", w_f16));
+  return hip_status(moe::launch_bf16_to_f16(w, n, w_f16, stream), "moe_weights_bf16_to_f16 launch");
+}
+
+int moe_expert_down_f16w(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,
+                         int64_t d_ff, const void* w2_f16, float* y_perm, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_ffn(h, offsets, E, rows_max, d, d_ff, w2_f16, MOE_BF16, y_perm));
+  MOE_TRY(check_ffn_ws(MOE_BF16, workspace, workspace_bytes));
+  return hip_status(moe::launch_down_f16w(h, offsets, E, rows_max, d, d_ff, w2_f16, y_perm, workspace, stream),
+                    "moe_expert_down_f16w launch");
+}
+
 int moe_grouped_ffn(const void* x_perm, const int32_t* offsets, int32_t E, int64_t rows_max,
                     int64_t d, int64_t d_ff, const void* w1, const void* w2, int32_t dtype,
                     void* h, float* y_perm, void* workspace, size_t workspace_bytes,

@@ -116,6 +116,7 @@ struct GemmOp {
 using OpUp = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, false>;
 using OpUpZ = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, true>;
 using OpDown = GemmOp<false, false, false, true, kCvtBf16ToF16, kEpiF32, false>;
+using OpDownF16 = GemmOp<false, false, false, true, kCvtNone, kEpiF32, false>;
 using OpDh = GemmOp<false, true, false, false, kCvtNone, kEpiDGelu, false>;
 using OpDx = GemmOp<false, true, false, false, kCvtNone, kEpiF32, false>;
 using OpDw2 = GemmOp<true, true, true, false, kCvtF16ToBf16, kEpiF32, false>;
@@ -1050,6 +1051,9 @@ hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets
       else launch_op<OpUp>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split);
       break;
     case GemmKind::kDown: launch_op<OpDown>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
+    case GemmKind::kDownF16:
+      launch_op<OpDownF16>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split);
+      break;
     case GemmKind::kDh: launch_op<OpDh>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
     case GemmKind::kDx: launch_op<OpDx>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
     case GemmKind::kDw2: launch_op<OpDw2>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, 1); break;

@@ -120,6 +120,44 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
                             w2, dtype, y_perm, nullptr, ws, s);
 }
 
+namespace {
+
+// Eight bf16 values per thread and step, grid-stride; the tail (n % 8) by the
+// first threads one value each.
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint4* __restrict__ src, int64_t n8,
+                                                          uint4* __restrict__ dst, const uint16_t* __restrict__ src_tail,
+                                                          int tail, uint16_t* __restrict__ dst_tail) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8; i += stride)
+    dst[i] = bf16x8_to_f16x8(src[i]);
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < tail) {
+    const _Float16 h = static_cast<_Float16>(bf16_to_f32(src_tail[t]));
+    dst_tail[t] = __builtin_bit_cast(uint16_t, h);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bf16_to_f16(const void* src, int64_t n, void* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  int64_t g = (n8 + 255) / 256;
+  g = g < 1 ? 1 : (g > 8192 ? 8192 : g);
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), n8, static_cast<uint4*>(dst),
+                     static_cast<const uint16_t*>(src) + n8 * 8, static_cast<int>(n - n8 * 8),
+                     static_cast<uint16_t*>(dst) + n8 * 8);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_f16w(const void* h, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
+                            int64_t d_ff, const void* w2_f16, float* y_perm, void* ws, hipStream_t s) {
+  if (rows_max == 0) return hipSuccess;
+  return launch_gemm_mfma(GemmKind::kDownF16, h, offsets, E, rows_max, 0, static_cast<int>(d),
+                          static_cast<int>(d_ff), w2_f16, y_perm, nullptr, ws, s);
+}
+
 size_t ffn_workspace_bytes(int dtype) { return dtype == 1 ? ffn_mfma_workspace_bytes() : 0; }
 
 }  // namespace moe

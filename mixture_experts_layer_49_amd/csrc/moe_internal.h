@@ -71,6 +71,7 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
 //   kUp:   A [R, K] bf16,  B = W1 [E, N, K] bf16 -> C = fp16 gelu(A B^T)
 //          (and, with Z, the fp16 pre-activation A B^T in Z [R, N])
 //   kDown: A [R, K] fp16,  B = W2 [E, N, K] bf16 -> C = A B^T f32
+//   kDownF16: as kDown with W2 stored as fp16 (no conversion in the kernel)
 //   kDh:   A [R, K] bf16,  B = W2 [E, K, N] bf16 -> C = bf16((A B) * gelu'(Z)), Z [R, N] fp16
 //   kDx:   A [R, K] bf16,  B = W1 [E, K, N] bf16 -> C = A B f32
 // K-segmented kinds (the contraction runs over each expert's rows):
@@ -78,7 +79,7 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
 //   kDw1:  A [R, M] bf16,  B [R, N] bf16 -> C[e] = A_e^T B_e f32 [E, M, N]
 // With a workspace, output tiles of a short last round of a row-segmented
 // kind are split along K.
-enum class GemmKind { kUp, kDown, kDh, kDx, kDw2, kDw1 };
+enum class GemmKind { kUp, kDown, kDownF16, kDh, kDx, kDw2, kDw1 };
 hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
                             int64_t rows_max, int M, int N, int K, const void* B, void* C,
                             void* Z, void* ws, hipStream_t s);
@@ -92,6 +93,11 @@ inline hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets
 // Workspace bytes of the expert FFN on the current device (0 for f32 layers).
 size_t ffn_workspace_bytes(int dtype);
 size_t ffn_mfma_workspace_bytes();
+
+// W2 in fp16 for the down-projection (grouped_ffn.hip): n bf16 values -> fp16, RNE.
+hipError_t launch_bf16_to_f16(const void* src, int64_t n, void* dst, hipStream_t s);
+hipError_t launch_down_f16w(const void* h, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
+                            int64_t d_ff, const void* w2_f16, float* y_perm, void* ws, hipStream_t s);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                           int64_t T, int k, int64_t d, void* y, int out_dtype, hipStream_t s);

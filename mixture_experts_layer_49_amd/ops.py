@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
-           "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
+           "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag",
+           "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
            "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
            "moe_expert_up_backward", "moe_expert_weight_grads", "moe_gate_backward",
            "moe_gate_weight_grads_workspace_bytes", "moe_gate_weight_grads", "moe_dispatch_backward",
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
         "moe_ffn_workspace_bytes": (SZ, [I32]),
         "moe_frag_rows": (I64, [I64, I32]),
+        "moe_weights_bf16_to_f16": (ctypes.c_int, [P, I64, P, P]),
+        "moe_expert_down_f16w": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P, SZ, P]),
         "moe_permute_frag": (ctypes.c_int, [P, I64, P, P, I32, I64, P, P]),
         "moe_expert_up_gelu_frag": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P]),
         "moe_combine": (ctypes.c_int, [P, P, P, I64, I32, I64, P, I32, P]),
@@ -301,6 +304,23 @@ def moe_expert_up_gelu_frag(x_frag, offsets, w1, rows_max: int, h=None, stream=N
     return h
 
 
+def moe_weights_bf16_to_f16(w, out=None, stream=None):
+    """fp16 copy of a bf16 weight (round to nearest even), for the
+    down-projection's fp16 products."""
+    out = torch.empty(w.shape, dtype=torch.float16, device=w.device) if out is None else out
+    _check(lib().moe_weights_bf16_to_f16(_ptr(w), w.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_expert_down_f16w(h, offsets, w2_f16, rows_max: int, y_perm=None, workspace=None, stream=None):
+    """moe_expert_down of a bf16 layer with W2 given as moe_weights_bf16_to_f16(W2)."""
+    E, d, d_ff = w2_f16.shape
+    y_perm = _empty((max(rows_max, 1), d), torch.float32, h) if y_perm is None else y_perm
+    _check(lib().moe_expert_down_f16w(_ptr(h), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w2_f16),
+                                      _ptr(y_perm), _ptr(workspace), _ws_size(workspace), _stream(stream)))
+    return y_perm
+
+
 def moe_grouped_ffn(x_perm, offsets, w1, w2, rows_max: int, h=None, y_perm=None, workspace=None,
                     stream=None):
     E, d_ff, d = w1.shape
@@ -482,7 +502,7 @@ class MoEBuffers:
 def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_idx=None,
                 topk_w=None, alpha: float = 0.01, flags: int = 0, bufs: MoEBuffers = None,
                 stream=None, save_for_backward: bool = False, temperature: float = 1.0,
-                noise=None) -> MoEBuffers:
+                noise=None, w2_f16=None) -> MoEBuffers:
     """router -> dispatch -> grouped FFN -> combine -> aux loss, all on one
     stream. With `w_gate` None, `topk_idx`/`topk_w` are taken as given (a
     receiver's share: the rows it got and their weights). With
@@ -490,7 +510,10 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     the router its log-sum-exp (what moe_backward needs). Without a backward,
     bf16 layers that frag_eligible() accepts run the permute and the
     up-projection on the fragment-ordered copy (bufs.frag; the same h bit for
-    bit as the row-major up-projection without a workspace)."""
+    bit as the row-major up-projection without a workspace). `w2_f16`, for
+    bf16 layers: moe_weights_bf16_to_f16(w2), prepared once; the
+    down-projection then reads it instead of converting W2 in registers
+    (y_perm bit for bit the same)."""
     T, d = x.shape
     E, d_ff, _ = w1.shape
     routed = w_gate is not None
@@ -509,20 +532,34 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     else:
         idx, w = topk_idx, topk_w
     bufs.used_idx, bufs.used_w = idx, w   # the routing the layer ran with (given or computed)
+    if w2_f16 is not None and x.dtype != torch.bfloat16:
+        raise ValueError("w2_f16 is for bf16 layers")
+
+    def down():
+        if w2_f16 is not None:
+            moe_expert_down_f16w(bufs.h, bufs.offsets, w2_f16, bufs.rows_max, bufs.y_perm,
+                                 bufs.ws_ffn, stream)
+        else:
+            moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn,
+                            stream)
+
     if bufs.frag:
         moe_dispatch_plan(idx, E, capacity, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                           bufs.ws_dispatch, stream)
         moe_permute_frag(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_frag, stream)
         moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, stream)
-        moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn, stream)
+        down()
     else:
         moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                      bufs.x_perm, bufs.ws_dispatch, stream)
         if bufs.z is not None:
             moe_expert_up_gelu_z(bufs.x_perm, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.z,
                                  bufs.ws_ffn, stream)
-            moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn,
-                            stream)
+            down()
+        elif w2_f16 is not None:
+            moe_expert_up_gelu(bufs.x_perm, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.ws_ffn,
+                               stream)
+            down()
         else:
             moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
                             bufs.ws_ffn, stream)

@@ -209,6 +209,22 @@ def test_fragment_path_argument_errors_and_sizes():
     assert L.moe_expert_up_gelu_frag(None, None, 8, 0, 256, 128, None, None, None) == 0
 
 
+def test_f16_weight_argument_errors():
+    L = ops.lib()
+    # moe_weights_bf16_to_f16(w, n, w_f16, stream)
+    assert L.moe_weights_bf16_to_f16(FAKE, -1, FAKE, None) == -1
+    assert L.moe_weights_bf16_to_f16(None, 0, None, None) == 0
+    assert L.moe_weights_bf16_to_f16(None, 8, FAKE, None) == -1
+    assert L.moe_weights_bf16_to_f16(FAKE, 8, ctypes.c_void_p((1 << 20) + 2), None) == -6
+    # moe_expert_down_f16w(h, offsets, E, rows_max, d, d_ff, w2_f16, y_perm, ws, ws_bytes, stream)
+    need = L.moe_ffn_workspace_bytes(1)
+    assert L.moe_expert_down_f16w(FAKE, FAKE, 0, 10, 64, 128, FAKE, FAKE, None, 0, None) == -3
+    assert L.moe_expert_down_f16w(FAKE, FAKE, 8, 10, 60, 128, FAKE, FAKE, None, 0, None) == -6
+    assert L.moe_expert_down_f16w(FAKE, None, 8, 10, 64, 128, FAKE, FAKE, None, 0, None) == -1
+    assert L.moe_expert_down_f16w(FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, FAKE, need - 1, None) == -4
+    assert L.moe_expert_down_f16w(None, None, 8, 0, 64, 128, None, None, None, 0, None) == 0
+
+
 def test_ffn_workspace_bytes():
     L = ops.lib()
     assert L.moe_ffn_workspace_bytes(0) == 0           # f32 kernels never split a tile

@@ -96,3 +96,60 @@ def test_frag_large_experts_shape():
     1280 rows), with ragged segment lengths."""
     counts = [1283, 1250, 1301, 1222, 1279, 1340, 1197, 1368]
     run_case(counts, d=4096, d_ff=16384, seed=4)
+
+
+# ---------------------------------------------------------------- fp16 W2 --
+def test_weights_bf16_to_f16_every_value():
+    """All 65536 bf16 bit patterns (plus a ragged tail of 5): the conversion
+    against torch's bf16 -> fp16 (round to nearest even); NaNs stay NaN."""
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    w = torch.cat([bits, bits[1000:1005]]).view(torch.bfloat16)
+    got = ops.moe_weights_bf16_to_f16(w.to("cuda:0"))
+    torch.cuda.synchronize()
+    got = got.cpu()
+    want = w.to(torch.float16)
+    nan = torch.isnan(want)
+    assert torch.equal(torch.isnan(got), nan)
+    assert torch.equal(got[~nan].view(torch.int16), want[~nan].view(torch.int16))
+
+
+@pytest.mark.parametrize("counts,d,d_ff", [([37, 0, 300, 1, 64], 512, 776),
+                                           ([150, 290], 1024, 8200),
+                                           ([1283, 1250, 1301, 1222, 1279, 1340, 1197, 1368], 4096, 16384)])
+def test_down_f16w_equals_in_register_conversion(counts, d, d_ff):
+    """The down-projection on the fp16 copy of W2 against the one converting
+    bf16 W2 in registers: bit-identical, with and without split tiles."""
+    g = torch.Generator().manual_seed(7)
+    E, R = len(counts), int(sum(counts))
+    rows_max = R + 9
+    say("  case E=%d R=%d d=%d d_ff=%d" % (E, R, d, d_ff))
+    h = torch.randn(rows_max, d_ff, generator=g).to(torch.float16).to("cuda:0")
+    w2 = (torch.randn(E, d, d_ff, generator=g) / d_ff ** 0.5).to(torch.bfloat16).to("cuda:0")
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device="cuda:0")
+    w2h = ops.moe_weights_bf16_to_f16(w2)
+    ws = torch.empty(ops.moe_ffn_workspace_bytes(torch.bfloat16), dtype=torch.uint8, device="cuda:0")
+    for workspace in (None, ws):
+        a = ops.moe_expert_down(h, off, w2, rows_max, workspace=workspace)
+        b = ops.moe_expert_down_f16w(h, off, w2h, rows_max, workspace=workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(a[:R].view(torch.int32), b[:R].view(torch.int32)), \
+            "workspace %s: max|diff| %.3g" % (workspace is not None, (a[:R] - b[:R]).abs().max().item())
+
+
+@pytest.mark.parametrize("frag", [False, True])
+def test_forward_with_f16_w2_is_bit_identical(frag):
+    """The layer forward given moe_weights_bf16_to_f16(W2) against the same
+    forward converting W2 in registers: the same y, bit for bit."""
+    from mixture_experts_layer_49_amd import inputs as I
+    from parity_helpers import dev
+    cfg = I.small("f16w", T=600, d=256, d_ff=512, E=4, k=2, cf=1.25, seed=71)
+    inp = I.make_inputs(cfg)
+    x, w1, w2, wg = (dev(inp[n], "bf16") for n in ("x", "w1", "w2", "w_gate"))
+    C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    ys = []
+    for w2h in (None, ops.moe_weights_bf16_to_f16(w2)):
+        b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, frag=frag)
+        ops.moe_forward(x, w1, w2, cfg.k, C, w_gate=wg, bufs=b, w2_f16=w2h)
+        torch.cuda.synchronize()
+        ys.append(b.y.clone())
+    assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32))
