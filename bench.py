@@ -326,6 +326,9 @@ def main(argv=None) -> int:
     # inference weight format: W2 in fp16, converted once (exact; the kernels
     # would otherwise convert each W2 value in registers on every step)
     w2h = ops.moe_weights_bf16_to_f16(w2) if bf else None
+    # fragment-ordered path: h stays in fragment order for the down-projection
+    hfrag = (torch.empty((ops.moe_frag_rows(b.rows_max, cfg.E), cfg.d_ff), dtype=torch.float16,
+                         device=x.device) if b.frag and cfg.d_ff % 256 == 0 else None)
     stream = torch.cuda.current_stream()
 
     names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]
@@ -344,6 +347,19 @@ def main(argv=None) -> int:
         rec(1)
         ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
         rec(2)
+        if hfrag is not None:
+            ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
+            rec(3)
+            ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, hfrag, True)
+            rec(4)
+            ops.moe_expert_down_frag(hfrag, b.offsets, w2h, b.rows_max, b.y_perm, b.ws_ffn)
+            rec(5)
+            ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
+            rec(6)
+            if cfg.routed:
+                ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
+            rec(7)
+            return
         if b.frag:
             ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
             rec(3)
@@ -406,10 +422,12 @@ def main(argv=None) -> int:
         if "TFLOP/s" in v:
             v["mfma_frac"] = v["TFLOP/s"] / PEAK_MFMA_TFLOPS
     dom = "up_gelu" if per[3] >= per[4] else "down"
-    dom_frag = dom == "up_gelu" and b.frag
-    dom_kernel = ("up_frag_kernel" if dom_frag else
-                  "grouped_gemm_mfma<%s>" % ("up" if dom == "up_gelu" else
-                                             "down_f16w" if w2h is not None else "down"))
+    dom_frag = b.frag and (dom == "up_gelu" or hfrag is not None)
+    dom_which = ("up" if dom == "up_gelu" else
+                 "down" if hfrag is not None or w2h is None else "down_f16w")
+    dom_kernel = ("frag_gemm_kernel<%s>" % ("up_frag" if hfrag is not None else "up_rows")
+                  if dom_frag and dom == "up_gelu" else
+                  "frag_gemm_kernel<down>" if dom_frag else "grouped_gemm_mfma<%s>" % dom_which)
     achieved = breakdown[dom]["TFLOP/s"]
     ffn_tflops = (flops_up + flops_down) / ((per[3] + per[4]) * 1e-3) / 1e12
 
@@ -429,13 +447,13 @@ def main(argv=None) -> int:
         "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
                    "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
                    "max_over_mean_load": float(counts.max() / counts.mean()),
-                   "activation_layout": "fragment-ordered" if b.frag else "row-major",
+                   "activation_layout": ("fragment-ordered x and h" if hfrag is not None else
+                                         "fragment-ordered x" if b.frag else "row-major"),
                    "w2_storage": "fp16 (converted once from the bf16 weights, exact)" if bf else "f32",
                    "parallelism": "single GPU"},
         "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
-                     "traffic": measured_traffic("up" if dom == "up_gelu" else
-                                                 "down_f16w" if w2h is not None else "down", cfg.name,
+                     "traffic": measured_traffic(dom_which, cfg.name,
                                                  "gemm_frag" if dom_frag else "gemm_mfma"),
                      "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
                      "launch_us": us[dom]},

@@ -53,6 +53,7 @@ extern "C" {
 #endif
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum { MOE_ORDER_ROWS = 0, MOE_ORDER_FRAG = 1 };   /* layout of h (moe_expert_up_gelu_frag) */
 
 typedef enum {
   MOE_OK = 0,
@@ -235,9 +236,20 @@ size_t moe_ffn_workspace_bytes(int32_t dtype);
  *   zeros in the padding rows. d a multiple of 16.
  * moe_expert_up_gelu_frag: h[r] = fp16(gelu_tanh(W1[e] . x_perm[r])) for every
  *   expert e and unpadded row r in [offsets[e], offsets[e+1]) (ETP page w1;
- *   EP tutorial 2.1 step 4), h [rows_max, d_ff] row-major as for
- *   moe_expert_up_gelu; rows >= offsets[E] not touched. d a multiple of 256,
- *   d_ff of 8, d and d_ff <= 2^20. No output tile is split along K.
+ *   EP tutorial 2.1 step 4). h_order MOE_ORDER_ROWS: h [rows_max, d_ff]
+ *   row-major as for moe_expert_up_gelu, rows >= offsets[E] not touched;
+ *   MOE_ORDER_FRAG: h [moe_frag_rows(rows_max, E), d_ff] in the fragment order
+ *   above (K = d_ff), rows [0, pad[E]) written, padding rows zero, d_ff a
+ *   multiple of 256. d a multiple of 256, d_ff of 8, d and d_ff <= 2^20. No
+ *   output tile is split along K.
+ * moe_expert_down_frag: y_perm[r] = W2[e] . h[r] (float32, row-major
+ *   [rows_max, d], rows >= offsets[E] not touched; ETP page w2) from h in
+ *   fragment order and w2_f16 = moe_weights_bf16_to_f16(W2) [E, d, d_ff];
+ *   d_ff a multiple of 256. Without a workspace, bit-identical to
+ *   moe_expert_down_f16w without one; with moe_ffn_workspace_bytes of
+ *   workspace, the tiles of a short last round are split along K (pieces of
+ *   whole 256-deep quads, so the sums may round differently from the
+ *   row-major kernel's splits; fixed order, deterministic).
  * Pointers 16-byte aligned device memory; offsets read only by the kernels.
  * Both calls take bf16 data only (no dtype argument).
  * Errors: MOE_ERR_ALIGN for d, d_ff or a pointer that breaks the rules above;
@@ -248,7 +260,10 @@ int moe_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t
                      int32_t E, int64_t rows_max, void* x_frag, hipStream_t stream);
 int moe_expert_up_gelu_frag(const void* x_frag, const int32_t* offsets, int32_t E,
                             int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
-                            void* h, hipStream_t stream);
+                            void* h, int32_t h_order, hipStream_t stream);
+int moe_expert_down_frag(const void* h_frag, const int32_t* offsets, int32_t E, int64_t rows_max,
+                         int64_t d, int64_t d_ff, const void* w2_f16, float* y_perm,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Weighted combine back to token order (EP tutorial 2.1 step 5; 2.2: a
  * dropped slot takes no part):

@@ -296,13 +296,32 @@ int moe_permute_frag(const void* x, int64_t d, const int32_t* src, const int32_t
 }
 
 int moe_expert_up_gelu_frag(const void* x_frag, const int32_t* offsets, int32_t E, int64_t rows_max,
-                            int64_t d, int64_t d_ff, const void* w1, void* h, hipStream_t stream) {
+                            int64_t d, int64_t d_ff, const void* w1, void* h, int32_t h_order,
+                            hipStream_t stream) {
   MOE_TRY(check_ffn(x_frag, offsets, E, rows_max, d, d_ff, w1, MOE_BF16, h));
   if (d % 256 != 0) return fail(MOE_ERR_ALIGN, "d = %lld must be a multiple of 256", static_cast<long long>(d));
+  if (h_order != MOE_ORDER_ROWS && h_order != MOE_ORDER_FRAG)
+    return fail(MOE_ERR_ARG, "h_order %d is neither MOE_ORDER_ROWS nor MOE_ORDER_FRAG", h_order);
+  if (h_order == MOE_ORDER_FRAG && d_ff % 256 != 0)
+    return fail(MOE_ERR_ALIGN, "h in fragment order needs d_ff = %lld a multiple of 256", static_cast<long long>(d_ff));
   if (rows_max > 0x7fffffffLL - 32LL * MOE_MAX_E)
     return fail(MOE_ERR_SHAPE, "moe_expert_up_gelu_frag needs rows_max < 2^31 - 8192");
-  return hip_status(moe::launch_up_gelu_frag(x_frag, offsets, E, rows_max, d, d_ff, w1, h, stream),
+  return hip_status(moe::launch_up_gelu_frag(x_frag, offsets, E, rows_max, d, d_ff, w1, h,
+                                             h_order == MOE_ORDER_FRAG, stream),
                     "moe_expert_up_gelu_frag launch");
+}
+
+int moe_expert_down_frag(const void* h_frag, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,
+                         int64_t d_ff, const void* w2_f16, float* y_perm, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_ffn(h_frag, offsets, E, rows_max, d, d_ff, w2_f16, MOE_BF16, y_perm));
+  MOE_TRY(check_ffn_ws(MOE_BF16, workspace, workspace_bytes));
+  if (d_ff % 256 != 0)
+    return fail(MOE_ERR_ALIGN, "d_ff = %lld must be a multiple of 256", static_cast<long long>(d_ff));
+  if (rows_max > 0x7fffffffLL - 32LL * MOE_MAX_E)
+    return fail(MOE_ERR_SHAPE, "moe_expert_down_frag needs rows_max < 2^31 - 8192");
+  return hip_status(moe::launch_down_frag(h_frag, offsets, E, rows_max, d, d_ff, w2_f16, y_perm, workspace, stream),
+                    "moe_expert_down_frag launch");
 }
 
 int moe_expert_down(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,

@@ -59,6 +59,44 @@ __device__ __forceinline__ Tile find_tile(const int* s_pref, int E, int tiles_n,
   return t;
 }
 
+constexpr int kPiecesPerWg = 2;   // split pieces one workgroup may run (workspace slots per workgroup)
+
+// How an XCD's share of a row-segmented tile list runs: tiles r_beg ..
+// r_beg + n_x - 1, `full` whole rounds over its P workgroups, then the rem
+// tiles left, each split into S k-ranges when the workspace allows it. The
+// rem * S pieces go round-robin over the P workgroups, at most kPiecesPerWg
+// each, and S is the count that ends the last round soonest: the round
+// takes ceil(rem S / P) / S of a tile (ties: fewer pieces). Pieces keep >= 32
+// stages when they only fill a last round (measured on 64-stage tiles:
+// 2-way splits gain 4-7%); when the whole launch is a partial round, pieces of
+// 16 stages still pay.
+struct RowPlan {
+  int64_t r_beg, n_x, full;
+  int rem, S;
+};
+__device__ __forceinline__ RowPlan row_plan(int64_t total, int xcd, int P, int nk2, int max_split) {
+  RowPlan p;
+  p.r_beg = total * xcd / 8;
+  p.n_x = total * (xcd + 1) / 8 - p.r_beg;
+  p.full = p.n_x / P;
+  p.rem = static_cast<int>(p.n_x - p.full * P);
+  p.S = 1;
+  if (p.rem > 0 && max_split > 1) {
+    const int smax = min(max_split, nk2 / (p.full == 0 ? 16 : 32));
+    int best_num = 1, best_den = 1;   // last round = best_num / best_den tiles
+    for (int s = 2; s <= smax; ++s) {
+      if (p.rem * s > kPiecesPerWg * P) break;
+      const int num = (p.rem * s + P - 1) / P;
+      if (num * best_den < best_num * s) {
+        best_num = num;
+        best_den = s;
+      }
+    }
+    p.S = best_den;
+  }
+  return p;
+}
+
 // gelu_tanh(z) = z/2 (1 + tanh(u)) = z * sigmoid(2u), u = sqrt(2/pi)(z + 0.044715 z^3)
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float u = 0.7978845608028654f * fmaf(0.044715f * z, z * z, z);

@@ -47,7 +47,10 @@ constexpr int kFCpr = FBK / 8;                 // 16-byte chunks per W1 row of a
 constexpr int kFSlotU4 = FBN * kFCpr;          // uint4 per LDS slot (32 KiB)
 constexpr int kFBLoads = FBN / 8 / kFW;        // LDS-DMA loads per wave per stage (8)
 constexpr int kFAFrag = FMI * 4;               // A fragments per wave per stage (8)
-constexpr int kFEpiP = 136;                    // floats per row of a wave's epilogue buffer
+constexpr int kFEpiP = 136;                    // floats per row of a wave's epilogue buffer (8 rows)
+constexpr int kFFragP = 40;                    // the same for the fragment epilogue (32 rows)
+static_assert(8 * kFEpiP <= 32 * kFFragP, "one per-wave buffer serves both epilogues");
+constexpr int kFragMaxSplit = 8;               // as the row-major GEMM (its fix-up kernel sums up to 8)
 
 #define FR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 #define FR_BARRIER()                                        \
@@ -175,19 +178,33 @@ __global__ __launch_bounds__(256) void permute_frag_kernel(
   }
 }
 
+// What one instance computes from a fragment-ordered A:
+//   kFragUpRows: C = A W1[e]^T, bf16; h = fp16(gelu_tanh(C)) row-major [rows, N]
+//   kFragUpFrag: the same h written in fragment order (padded rows; the K of
+//                the down-projection is N)
+//   kFragDown:   C = A W2[e]^T, fp16 A (h) and fp16 W2; y_perm f32 row-major
+//                [rows, N]; with a workspace, the tiles of a short last round
+//                split along K like the row-major GEMM's (same plan), their
+//                f32 partial sums added by its fix-up kernel
+enum FragKind { kFragUpRows, kFragUpFrag, kFragDown };
+
 struct FCtx {
   __amdgpu_buffer_rsrc_t a, b;
-  int m0, n0, seg1;
+  int m0, n0, seg1, pad_blk, blocks;
+  int klo, khi, tail;   // the unit's stages [klo, khi); tail: split piece index, or -1
 };
 
-__device__ __forceinline__ void fr_store16(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+__device__ __forceinline__ void fr_store16(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                           uint32_t soff = 0) {
   const u32x4v x = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
 }
 
-__global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
+template <int KIND>
+__global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     const uint16_t* __restrict__ Afrag, const int32_t* __restrict__ offsets, int E, int N, int K,
-    const uint16_t* __restrict__ B, uint16_t* __restrict__ H) {
+    const uint16_t* __restrict__ B, void* __restrict__ Cout, float* __restrict__ part, int max_split) {
+  constexpr bool DOWN = KIND == kFragDown, HFRAG = KIND == kFragUpFrag;
   // One LDS variable per slot: with a single array the compiler cannot tell
   // the slot being read from the ones the DMA is filling and waits for all.
   __shared__ uint4 sb0[kFSlotU4];
@@ -198,7 +215,7 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pad[kMaxE + 1];
   __shared__ int s_tmp[kMaxE];
-  __shared__ float s_epi[kFW][8 * kFEpiP];
+  __shared__ float s_epi[kFW][32 * kFFragP];   // per-wave epilogue staging
   auto SL = [&](int S) -> uint4* { return S == 0 ? sb0 : (S == 1 ? sb1 : (S == 2 ? sb2 : sb3)); };
   const int tid = threadIdx.x;
   for (int e = tid; e <= E; e += kFT) s_off[e] = offsets[e];
@@ -208,12 +225,16 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
   const int nk = K / FBK;   // the host checks K % 256 == 0: nk is a multiple of 4
   // Tile list as in the row-segmented GEMM: eight contiguous ranges, one per
   // XCD (workgroup b runs on XCD b % 8), taken round-robin by its P workgroups.
+  // With splitting (DOWN with a workspace) the XCD's last round is cut into
+  // pieces exactly as row_plan says, so the fix-up kernel finds them.
   const int P = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, w = blockIdx.x >> 3;
   const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pref[E])) * tiles_n;
-  const int64_t r_beg = total * xcd / 8;
-  const int64_t n_x = total * (xcd + 1) / 8 - r_beg;
-  const int64_t n_units = n_x / P + (w < n_x % P ? 1 : 0);
+  const RowPlan pl = row_plan(total, xcd, P, nk, DOWN ? max_split : 1);
+  const int S = pl.S, rem = pl.rem, nq = nk / 4;
+  const int64_t full = pl.full;
+  const int64_t n_units = full + (S == 1 ? (w < rem ? 1 : 0)
+                                          : (w < rem * S ? 1 : 0) + (w + P < rem * S ? 1 : 0));
   if (n_units == 0) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -226,14 +247,33 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
   const uint32_t ld_voff_b = (lane >> 3) * b_rb + (((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16u);
   const int fr_x = hl ^ ((l32 >> 1) & 7);
 
+  // Unit q: a whole tile of round q, or (q >= full) piece pc = (q - full) P + w
+  // of the last round: k-range pc / rem (in quads of stages) of tile pc % rem.
   auto make_ctx = [&](int64_t q, FCtx& c) {
-    const Tile tl = find_tile(s_pref, E, tiles_n, r_beg + w + q * P);
+    int64_t tile;
+    int klo = 0, khi = nk, tail = -1;
+    if (q < full || S == 1) {
+      tile = pl.r_beg + w + q * P;
+    } else {
+      const int pc = static_cast<int>(q - full) * P + w;
+      const int tr = pc % rem, si = pc / rem;
+      tile = pl.r_beg + full * P + tr;
+      klo = 4 * (si * nq / S);
+      khi = 4 * ((si + 1) * nq / S);
+      tail = pc;
+    }
+    c.klo = __builtin_amdgcn_readfirstlane(klo);
+    c.khi = __builtin_amdgcn_readfirstlane(khi);
+    c.tail = __builtin_amdgcn_readfirstlane(tail);
+    const Tile tl = find_tile(s_pref, E, tiles_n, tile);
     const int te = __builtin_amdgcn_readfirstlane(tl.e);
     c.seg1 = __builtin_amdgcn_readfirstlane(s_off[te + 1]);
     c.m0 = __builtin_amdgcn_readfirstlane(s_off[te] + tl.mi * FBM);
     c.n0 = __builtin_amdgcn_readfirstlane(tl.nt * FBN);
     const int pad_blk = __builtin_amdgcn_readfirstlane(s_pad[te] / 32 + tl.mi * (FBM / 32));
     const int blocks = (min(c.seg1 - c.m0, FBM) + 31) / 32;
+    c.pad_blk = pad_blk;
+    c.blocks = blocks;
     c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Afrag) + static_cast<int64_t>(pad_blk) * (a_blk / 2),
                                             0, static_cast<int>(blocks * a_blk), 0x00020000);
     const int b_rows = min(N - c.n0, FBN);
@@ -278,8 +318,12 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
     for (int i = 0; i < FMI; ++i)
 #pragma unroll
       for (int j = 0; j < FNI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+        if constexpr (DOWN)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(f16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
   };
   // NV memory loads (issued just before) spread over a slice's 16 MFMAs.
   auto interleave = [&](auto nv_c) __attribute__((always_inline)) {
@@ -298,13 +342,14 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
   make_ctx(0, cur);
   if (n_units > 1) make_ctx(1, nxt);
   else nxt = cur;   // past the last unit the prefetches re-read this one (never used)
-  // Prologue: stages 0, 1, 2 of the first unit.
-  issue_a(cur, 0, std::integral_constant<int, 0>{}, 0, kFAFrag);
-  issue_b(cur, 0, 0, 0, kFBLoads);
-  issue_a(cur, 1, std::integral_constant<int, 1>{}, 0, kFAFrag);
-  issue_b(cur, 1, 1, 0, kFBLoads);
-  issue_a(cur, 2, std::integral_constant<int, 2>{}, 0, kFAFrag);
-  issue_b(cur, 2, 2, 0, kFBLoads);
+  // Prologue: the first three stages of the first unit (klo is a multiple of
+  // four, so stage kt always uses slot and A buffer kt % 4).
+  issue_a(cur, cur.klo, std::integral_constant<int, 0>{}, 0, kFAFrag);
+  issue_b(cur, cur.klo, 0, 0, kFBLoads);
+  issue_a(cur, cur.klo + 1, std::integral_constant<int, 1>{}, 0, kFAFrag);
+  issue_b(cur, cur.klo + 1, 1, 0, kFBLoads);
+  issue_a(cur, cur.klo + 2, std::integral_constant<int, 2>{}, 0, kFAFrag);
+  issue_b(cur, cur.klo + 2, 2, 0, kFBLoads);
 
   // Stage kt (slot and A buffer SB = kt % 4, compile time) of unit q. It
   // prefetches stage kt+3 of unit q or, past the end, of unit q+1 (after the
@@ -320,9 +365,9 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
     constexpr int SN = (SB + 3) % 4;     // slot and buffer of stage kt+3 (those of kt-1)
     constexpr int S1 = (SB + 1) % 4;     // of stage kt+1
     const int kp = kt + 3;
-    const bool pre_cur = kp < nk;
+    const bool pre_cur = kp < cur.khi;
     const FCtx pc = pre_cur ? cur : nxt;
-    const int pk = pre_cur ? kp : kp - nk;
+    const int pk = pre_cur ? kp : nxt.klo + (kp - cur.khi);
     read_b(SB, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     issue_a(pc, pk, std::integral_constant<int, SN>{}, 0, 4);
@@ -344,7 +389,7 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
     interleave(std::integral_constant<int, 3>{});
     __builtin_amdgcn_sched_barrier(0);
     // Stage kt+1 has landed; every wave is done with slot SB.
-    if (after_epi && kt < 2) FR_WAIT_VM(62);
+    if (after_epi && kt - cur.klo < 2) FR_WAIT_VM(62);
     else FR_WAIT_VM(32);
     FR_BARRIER();
     read_b(S1, 0, 0);
@@ -358,6 +403,9 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
   // and are dropped, so every lane issues exactly NST stores.
   constexpr int ITEMS = 8 * 128 / 8 / kWave;   // 16-byte items per lane per chunk (2)
   constexpr int NST = FMI * 4 * 2 * ITEMS;      // 32 stores per lane per tile
+  // The waits above count 32 stores after an epilogue; the register-direct
+  // fragment epilogue issues 32 too, the f32 one 64 (the waits then also
+  // cover the oldest 32 of those stores: more waiting, never less).
   static_assert(NST == 32, "the waits above count 32 stores after an epilogue");
   auto epilogue = [&](int c_m0, int c_n0, int c_seg1) {
     float* const buf = s_epi[wave];
@@ -366,7 +414,7 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
     const int el32 = ln & 31, ehl = ln >> 5;
     const int rows_ok = min(c_seg1 - c_m0, FBM), cols_ok = min(N - c_n0, FBN);
     const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
-        H + (static_cast<int64_t>(c_m0) * N + c_n0), 0, rows_ok * N * 2, 0x00020000);
+        static_cast<uint16_t*>(Cout) + (static_cast<int64_t>(c_m0) * N + c_n0), 0, rows_ok * N * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < FMI; ++i)
 #pragma unroll
@@ -399,6 +447,90 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
         }
   };
 
+  // h in fragment order: each 32 x 32 accumulator tile goes through the
+  // wave's LDS buffer (rows 40 floats apart: the two half-waves of a write sit
+  // 32 banks apart), then lane l reads row l % 32, columns 8 (l / 32) .. +7 and
+  // 16 + 8 (l / 32) .. +7 -- unit l of the tile's two fragments -- applies
+  // GELU and fp16 and writes each with one 16-byte store (1 KiB per wave
+  // store). Blocks past the padded segment are past the buffer's range and
+  // dropped; rows inside the last block but past the segment hold GELU(0) = 0
+  // (their A rows are zero). 32 stores per lane per tile, as NST.
+  auto epilogue_frag = [&](const FCtx& c) {
+    float* const buf = s_epi[wave];
+    const uint32_t h_blk = static_cast<uint32_t>(N) * 64u;   // bytes per 32-row block of h
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint16_t*>(Cout) + static_cast<int64_t>(c.pad_blk) * (h_blk / 2), 0,
+        static_cast<int>(c.blocks * h_blk), 0x00020000);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int el32 = ln & 31, ehl = ln >> 5;
+    const uint32_t lo = static_cast<uint32_t>(ln) * 16u;
+#pragma unroll
+    for (int i = 0; i < FMI; ++i)
+#pragma unroll
+      for (int j = 0; j < FNI; ++j) {
+        // register r of tile (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) buf[(8 * (r >> 2) + 4 * ehl + (r & 3)) * kFFragP + el32] = acc[i][j][r];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float4 a = *reinterpret_cast<const float4*>(buf + el32 * kFFragP + 16 * p + 8 * ehl);
+          const float4 b = *reinterpret_cast<const float4*>(buf + el32 * kFFragP + 16 * p + 8 * ehl + 4);
+          const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
+          const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
+          const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
+          const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
+          const uint32_t kg = static_cast<uint32_t>(c.n0 + 32 * j + 16 * p) / 16u;
+          const uint32_t so = static_cast<uint32_t>(2 * wave + i) * h_blk + kg * 1024u;
+          fr_store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
+                     out, lo, so);
+        }
+      }
+  };
+
+  // f32 output (down-projection): as the row-major h epilogue, eight values
+  // per item in two 16-byte stores; a split piece writes its whole 256 x 256
+  // partial sum, row-major, to its workspace slot xcd * 2 P + piece.
+  auto epilogue_down = [&](const FCtx& c) {
+    float* const buf = s_epi[wave];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int el32 = ln & 31, ehl = ln >> 5;
+    const bool piece = c.tail >= 0;
+    const int pitch = piece ? FBN : N;
+    const int rows_ok = piece ? FBM : min(c.seg1 - c.m0, FBM), cols_ok = piece ? FBN : min(N - c.n0, FBN);
+    float* const base = piece ? part + static_cast<int64_t>(xcd * kPiecesPerWg * P + c.tail) * (FBM * FBN)
+                              : static_cast<float*>(Cout) + static_cast<int64_t>(c.m0) * N + c.n0;
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(base, 0, rows_ok * pitch * 4, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < FMI; ++i)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              buf[(4 * ehl + rr) * kFEpiP + 32 * jj + el32] = acc[i][4 * jh + jj][4 * cc + rr];
+#pragma unroll
+          for (int it = 0; it < ITEMS; ++it) {
+            const int f = ln + kWave * it;
+            const int row = f >> 4, col = (f & 15) << 3;
+            const float4 a = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col);
+            const float4 b = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col + 4);
+            const int trow = 64 * wave + 32 * i + 8 * cc + row, tcol = 128 * jh + col;
+            const bool ok = trow < rows_ok && tcol < cols_ok;
+            const uint32_t voff = ok ? static_cast<uint32_t>((trow * pitch + tcol) * 4) : 0x80000000u;
+            fr_store16(uint4{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w)},
+                       out, voff);
+            fr_store16(uint4{__float_as_uint(b.x), __float_as_uint(b.y), __float_as_uint(b.z), __float_as_uint(b.w)},
+                       out, ok ? voff + 16u : 0x80000000u);
+          }
+        }
+  };
+
   for (;;) {
     // Stage 0 of this unit has landed (older than stages 1-2's loads and, after
     // an epilogue, its stores).
@@ -412,18 +544,20 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
       for (int j = 0; j < FNI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    for (int kt = 0; kt < nk; kt += 4) {
+    for (int kt = cur.klo; kt < cur.khi; kt += 4) {
       stage(std::integral_constant<int, 0>{}, kt);
       stage(std::integral_constant<int, 1>{}, kt + 1);
       stage(std::integral_constant<int, 2>{}, kt + 2);
       stage(std::integral_constant<int, 3>{}, kt + 3);
     }
-    const int m0 = cur.m0, n0 = cur.n0, seg1 = cur.seg1;
+    const FCtx done = cur;
     ++q;
     const bool has_next = q < n_units;
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");   // the stores stay after the prefetches
-    epilogue(m0, n0, seg1);
+    if constexpr (KIND == kFragUpRows) epilogue(done.m0, done.n0, done.seg1);
+    else if constexpr (HFRAG) epilogue_frag(done);
+    else epilogue_down(done);
     if (!has_next) {
       FR_WAIT_VM(0);   // the last prefetches (some into LDS) end before the workgroup
       break;
@@ -436,6 +570,15 @@ __global__ __launch_bounds__(kFT, 1) void up_frag_kernel(
 }
 
 }  // namespace
+
+// One workgroup per CU (a multiple of 8); without splitting, no more than the
+// tile count needs.
+dim3 frag_grid(int64_t rows_max, int E, int64_t n, bool split) {
+  int64_t g = (device_cu_count() + 7) / 8 * 8;
+  const int64_t upper = (rows_max / FBM + E) * ((n + FBN - 1) / FBN);   // >= the tile count
+  if (!split && upper < g) g = (upper + 7) / 8 * 8;
+  return dim3(static_cast<unsigned>(g));
+}
 
 int64_t frag_rows(int64_t rows_max, int E) { return (rows_max + 31 * static_cast<int64_t>(E) + 31) / 32 * 32; }
 
@@ -450,14 +593,34 @@ hipError_t launch_permute_frag(const void* x, int64_t d, const int32_t* src, con
 }
 
 hipError_t launch_up_gelu_frag(const void* x_frag, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
-                               int64_t d_ff, const void* w1, void* h, hipStream_t s) {
+                               int64_t d_ff, const void* w1, void* h, bool h_frag_order, hipStream_t s) {
   if (rows_max <= 0) return hipSuccess;
-  int64_t g = (device_cu_count() + 7) / 8 * 8;
-  const int64_t upper = (rows_max / FBM + E) * ((d_ff + FBN - 1) / FBN);   // >= the tile count
-  if (upper < g) g = (upper + 7) / 8 * 8;
-  hipLaunchKernelGGL(up_frag_kernel, dim3(static_cast<unsigned>(g)), dim3(kFT), 0, s, static_cast<const uint16_t*>(x_frag), offsets, E,
-                     static_cast<int>(d_ff), static_cast<int>(d), static_cast<const uint16_t*>(w1),
-                     static_cast<uint16_t*>(h));
+  const dim3 g = frag_grid(rows_max, E, d_ff, false);
+  if (h_frag_order)
+    hipLaunchKernelGGL(frag_gemm_kernel<kFragUpFrag>, g, dim3(kFT), 0, s, static_cast<const uint16_t*>(x_frag), offsets,
+                       E, static_cast<int>(d_ff), static_cast<int>(d), static_cast<const uint16_t*>(w1), h, nullptr, 1);
+  else
+    hipLaunchKernelGGL(frag_gemm_kernel<kFragUpRows>, g, dim3(kFT), 0, s, static_cast<const uint16_t*>(x_frag), offsets,
+                       E, static_cast<int>(d_ff), static_cast<int>(d), static_cast<const uint16_t*>(w1), h, nullptr, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_frag(const void* h_frag, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
+                            int64_t d_ff, const void* w2_f16, float* y_perm, void* ws, hipStream_t s) {
+  if (rows_max <= 0) return hipSuccess;
+  const bool split = ws != nullptr;
+  const dim3 g = frag_grid(rows_max, E, d, split);
+  const int max_split = split ? kFragMaxSplit : 1;
+  hipLaunchKernelGGL(frag_gemm_kernel<kFragDown>, g, dim3(kFT), 0, s, static_cast<const uint16_t*>(h_frag), offsets, E,
+                     static_cast<int>(d), static_cast<int>(d_ff), static_cast<const uint16_t*>(w2_f16), y_perm,
+                     static_cast<float*>(ws), max_split);
+  // pieces are at least 16 stages: with fewer than 32 stages nothing splits
+  if (split && d_ff / FBK >= 32) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_fixup_down(offsets, E, static_cast<int>(d), static_cast<int>(d_ff), static_cast<int>(g.x),
+                                   max_split, static_cast<const float*>(ws), y_perm, s);
+  }
   return hipGetLastError();
 }
 

@@ -88,7 +88,6 @@ static_assert(NS == 2 && BK == 64 && kWaves % 2 == 0, "the pipeline below assume
 static_assert(BM == 256 && BN == 256, "the k-major LDS layout assumes 256-wide tiles");
 constexpr size_t kPartBytes = static_cast<size_t>(BM) * BN * sizeof(float);   // one split partial
 constexpr int kMaxSplit = 8;
-constexpr int kPiecesPerWg = 2;   // split pieces one workgroup may run (workspace slots per workgroup)
 constexpr int kEpiCost = 4;   // epilogue of a tile, in k-steps (K-segmented load balance)
 constexpr int kSegGroup = 8;  // m-tiles per group of the K-segmented tile order
 constexpr int kEpiPitch = 136;   // floats per row of a wave's epilogue staging buffer (see epilogue_wave)
@@ -173,42 +172,6 @@ __device__ __forceinline__ uint32_t kmajor_dma_offset(int lane, int p, uint32_t 
 __device__ __forceinline__ int seg_k_steps(const int* s_off, int e) {
   const int nk = (s_off[e + 1] - s_off[e] + BK - 1) / BK;
   return max(2, (nk + 1) & ~1);
-}
-
-// How an XCD's share of a row-segmented tile list runs: tiles r_beg ..
-// r_beg + n_x - 1, `full` whole rounds over its P workgroups, then the rem
-// tiles left, each split into S k-ranges when the workspace allows it. The
-// rem * S pieces go round-robin over the P workgroups, at most kPiecesPerWg
-// each, and S is the count that ends the last round soonest: the round
-// takes ceil(rem S / P) / S of a tile (ties: fewer pieces). Pieces keep >= 32
-// stages when they only fill a last round (measured on 64-stage tiles:
-// 2-way splits gain 4-7%); when the whole launch is a partial round, pieces of
-// 16 stages still pay.
-struct RowPlan {
-  int64_t r_beg, n_x, full;
-  int rem, S;
-};
-__device__ __forceinline__ RowPlan row_plan(int64_t total, int xcd, int P, int nk2, int max_split) {
-  RowPlan p;
-  p.r_beg = total * xcd / 8;
-  p.n_x = total * (xcd + 1) / 8 - p.r_beg;
-  p.full = p.n_x / P;
-  p.rem = static_cast<int>(p.n_x - p.full * P);
-  p.S = 1;
-  if (p.rem > 0 && max_split > 1) {
-    const int smax = min(max_split, nk2 / (p.full == 0 ? 16 : 32));
-    int best_num = 1, best_den = 1;   // last round = best_num / best_den tiles
-    for (int s = 2; s <= smax; ++s) {
-      if (p.rem * s > kPiecesPerWg * P) break;
-      const int num = (p.rem * s + P - 1) / P;
-      if (num * best_den < best_num * s) {
-        best_num = num;
-        best_den = s;
-      }
-    }
-    p.S = best_den;
-  }
-  return p;
 }
 
 // VPC consecutive outputs at element offset `at` (and of Z), given as floats
@@ -1013,6 +976,13 @@ void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int
 }
 
 }  // namespace
+
+hipError_t launch_split_fixup_down(const int32_t* offsets, int E, int N, int K, int grid, int max_split,
+                                   const float* part, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(split_fixup_kernel<OpDownF16>, dim3(4 * grid), dim3(kThreads), 0, s, offsets, E, N, K, grid / 8,
+                     max_split, part, y, nullptr);
+  return hipGetLastError();
+}
 
 size_t ffn_mfma_workspace_bytes() {
   return static_cast<size_t>(ffn_mfma_grid()) * kPiecesPerWg * kPartBytes;

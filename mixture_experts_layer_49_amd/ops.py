@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag",
-           "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
+           "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_expert_down_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
            "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
            "moe_expert_up_backward", "moe_expert_weight_grads", "moe_gate_backward",
            "moe_gate_weight_grads_workspace_bytes", "moe_gate_weight_grads", "moe_dispatch_backward",
@@ -73,7 +73,8 @@ def lib() -> ctypes.CDLL:
         "moe_weights_bf16_to_f16": (ctypes.c_int, [P, I64, P, P]),
         "moe_expert_down_f16w": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P, SZ, P]),
         "moe_permute_frag": (ctypes.c_int, [P, I64, P, P, I32, I64, P, P]),
-        "moe_expert_up_gelu_frag": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P]),
+        "moe_expert_up_gelu_frag": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P]),
+        "moe_expert_down_frag": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P, SZ, P]),
         "moe_combine": (ctypes.c_int, [P, P, P, I64, I32, I64, P, I32, P]),
         "moe_aux_loss_workspace_bytes": (SZ, [I64, I32]),
         "moe_aux_loss": (ctypes.c_int, [P, P, I64, I32, I32, F32, P, P, SZ, P]),
@@ -295,13 +296,33 @@ def moe_permute_frag(x, src, offsets, rows_max: int, x_frag=None, stream=None):
     return x_frag
 
 
-def moe_expert_up_gelu_frag(x_frag, offsets, w1, rows_max: int, h=None, stream=None):
-    """moe_expert_up_gelu (without a workspace) from the fragment-ordered copy."""
+MOE_ORDER_ROWS, MOE_ORDER_FRAG = 0, 1
+
+
+def moe_expert_up_gelu_frag(x_frag, offsets, w1, rows_max: int, h=None, frag_out: bool = False,
+                            stream=None):
+    """moe_expert_up_gelu (without a workspace) from the fragment-ordered copy;
+    h row-major [rows_max, d_ff], or with frag_out in fragment order
+    [moe_frag_rows(rows_max, E), d_ff] (what moe_expert_down_frag reads)."""
     E, d_ff, d = w1.shape
-    h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x_frag) if h is None else h
+    if h is None:
+        rows = moe_frag_rows(rows_max, E) if frag_out else rows_max
+        h = _empty((max(rows, 1), d_ff), hidden_dtype(w1.dtype), x_frag)
     _check(lib().moe_expert_up_gelu_frag(_ptr(x_frag), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w1),
-                                         _ptr(h), _stream(stream)))
+                                         _ptr(h), MOE_ORDER_FRAG if frag_out else MOE_ORDER_ROWS,
+                                         _stream(stream)))
     return h
+
+
+def moe_expert_down_frag(h_frag, offsets, w2_f16, rows_max: int, y_perm=None, workspace=None,
+                         stream=None):
+    """Down-projection from fragment-ordered h on W2 in fp16."""
+    E, d, d_ff = w2_f16.shape
+    y_perm = _empty((max(rows_max, 1), d), torch.float32, h_frag) if y_perm is None else y_perm
+    _check(lib().moe_expert_down_frag(_ptr(h_frag), _ptr(offsets), E, rows_max, d, d_ff, _ptr(w2_f16),
+                                      _ptr(y_perm), _ptr(workspace), _ws_size(workspace),
+                                      _stream(stream)))
+    return y_perm
 
 
 def moe_weights_bf16_to_f16(w, out=None, stream=None):
@@ -485,6 +506,8 @@ class MoEBuffers:
         self.frag = bool(frag)
         self.x_perm = None if self.frag else z((R, d), dtype)
         self.x_frag = z((max(moe_frag_rows(self.rows_max, E), 1), d), dtype) if self.frag else None
+        # h in fragment order, allocated by the first forward that uses it
+        self.h_frag = None
         self.h = z((R, d_ff), hidden_dtype(dtype))
         # the pre-activation, kept for the backward
         self.z = z((R, d_ff), hidden_dtype(dtype)) if save_for_backward else None
@@ -513,7 +536,10 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     bit as the row-major up-projection without a workspace). `w2_f16`, for
     bf16 layers: moe_weights_bf16_to_f16(w2), prepared once; the
     down-projection then reads it instead of converting W2 in registers
-    (y_perm bit for bit the same)."""
+    (y_perm bit for bit the same), and on the fragment-ordered path with
+    d_ff % 256 == 0, h stays in fragment order (bufs.h_frag) for a
+    down-projection that loads it straight into registers (bufs.h is then not
+    written)."""
     T, d = x.shape
     E, d_ff, _ = w1.shape
     routed = w_gate is not None
@@ -547,8 +573,18 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
         moe_dispatch_plan(idx, E, capacity, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                           bufs.ws_dispatch, stream)
         moe_permute_frag(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_frag, stream)
-        moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, stream)
-        down()
+        if w2_f16 is not None and d_ff % 256 == 0:
+            # h stays in fragment order between the two projections
+            if bufs.h_frag is None:
+                bufs.h_frag = torch.empty((max(moe_frag_rows(bufs.rows_max, E), 1), d_ff),
+                                          dtype=torch.float16, device=x.device)
+            moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h_frag, True,
+                                    stream)
+            moe_expert_down_frag(bufs.h_frag, bufs.offsets, w2_f16, bufs.rows_max, bufs.y_perm,
+                                 bufs.ws_ffn, stream)
+        else:
+            moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, False, stream)
+            down()
     else:
         moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                      bufs.x_perm, bufs.ws_dispatch, stream)

@@ -199,14 +199,23 @@ def test_fragment_path_argument_errors_and_sizes():
     assert L.moe_permute_frag(FAKE, 256, FAKE, FAKE, 8, -1, FAKE, None) == -1
     assert L.moe_permute_frag(FAKE, 256, FAKE, FAKE, 8, 10, ctypes.c_void_p((1 << 20) + 4), None) == -6
     assert L.moe_permute_frag(None, 256, None, None, 8, 0, None, None) == 0
-    # moe_expert_up_gelu_frag(x_frag, offsets, E, rows_max, d, d_ff, w1, h, stream)
-    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 264, 128, FAKE, FAKE, None) == -6   # d % 256
-    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 130, FAKE, FAKE, None) == -6   # d_ff % 8
-    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 300, 10, 256, 128, FAKE, FAKE, None) == -3
-    assert L.moe_expert_up_gelu_frag(FAKE, None, 8, 10, 256, 128, FAKE, FAKE, None) == -1
-    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 128, FAKE, None, None) == -1
-    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 1 << 21, 128, FAKE, FAKE, None) == -3
-    assert L.moe_expert_up_gelu_frag(None, None, 8, 0, 256, 128, None, None, None) == 0
+    # moe_expert_up_gelu_frag(x_frag, offsets, E, rows_max, d, d_ff, w1, h, h_order, stream)
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 128, FAKE, FAKE, 2, None) == -1   # h_order
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 264, FAKE, FAKE, 1, None) == -6   # frag h: d_ff % 256
+    # moe_expert_down_frag(h_frag, offsets, E, rows_max, d, d_ff, w2_f16, y_perm, ws, ws_bytes, stream)
+    need = L.moe_ffn_workspace_bytes(1)
+    assert L.moe_expert_down_frag(FAKE, FAKE, 8, 10, 256, 264, FAKE, FAKE, None, 0, None) == -6
+    assert L.moe_expert_down_frag(FAKE, None, 8, 10, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert L.moe_expert_down_frag(FAKE, FAKE, 8, 10, 256, 256, FAKE, FAKE, FAKE, need - 1, None) == -4
+    assert L.moe_expert_down_frag(FAKE, FAKE, 0, 10, 256, 256, FAKE, FAKE, None, 0, None) == -3
+    assert L.moe_expert_down_frag(None, None, 8, 0, 256, 256, None, None, None, 0, None) == 0
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 264, 128, FAKE, FAKE, 0, None) == -6   # d % 256
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 130, FAKE, FAKE, 0, None) == -6   # d_ff % 8
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 300, 10, 256, 128, FAKE, FAKE, 0, None) == -3
+    assert L.moe_expert_up_gelu_frag(FAKE, None, 8, 10, 256, 128, FAKE, FAKE, 0, None) == -1
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 256, 128, FAKE, None, 0, None) == -1
+    assert L.moe_expert_up_gelu_frag(FAKE, FAKE, 8, 10, 1 << 21, 128, FAKE, FAKE, 0, None) == -3
+    assert L.moe_expert_up_gelu_frag(None, None, 8, 0, 256, 128, None, None, 0, None) == 0
 
 
 def test_f16_weight_argument_errors():

@@ -52,6 +52,24 @@ def run_case(counts, d, d_ff, slack=17, seed=0):
         say("  %d values differ, first at %s" % (bad.shape[0], bad[:4].tolist()))
     assert same, "h differs from the row-major up-projection"
     assert (h[R:].view(torch.int16) == SENT_H).all(), "rows past offsets[E] written"
+    if d_ff % 256 == 0:
+        # h in fragment order: the same values, padding rows zero, nothing past the padded segments;
+        # then the down-projection from it against the row-major one on the same h (no workspace)
+        hf = torch.full((ops.moe_frag_rows(rows_max, E), d_ff), SENT_H, dtype=torch.int16,
+                        device="cuda:0").view(torch.float16)
+        ops.moe_expert_up_gelu_frag(x_frag, off, w1, rows_max, h=hf, frag_out=True)
+        w2h = (torch.randn(E, d, d_ff, generator=g) / d_ff ** 0.5).to(torch.float16).to("cuda:0")
+        y_ref = ops.moe_expert_down_f16w(h_ref, off, w2h, rows_max)
+        y = torch.full((max(rows_max, 1), d), float("nan"), device="cuda:0")
+        ops.moe_expert_down_frag(hf, off, w2h, rows_max, y_perm=y)
+        torch.cuda.synchronize()
+        hrows, hpads, hpt = unfrag(hf.cpu(), counts_to_offsets(counts), d_ff)
+        assert torch.equal(hrows.view(torch.int16), h_ref[:R].cpu().view(torch.int16)), "fragment-ordered h differs"
+        assert (hpads.view(torch.int16) == 0).all(), "padding rows of h are not zero"
+        assert (hf.view(torch.int16)[hpt:].cpu() == SENT_H).all(), "rows past the padded segments of h written"
+        assert torch.equal(y[:R].view(torch.int32), y_ref[:R].view(torch.int32)), \
+            "down-projection from fragment-ordered h differs: max|diff| %.3g" % (y[:R] - y_ref[:R]).abs().max().item()
+        assert torch.isnan(y[R:]).all(), "rows past offsets[E] of y_perm written"
     return R
 
 
@@ -153,3 +171,42 @@ def test_forward_with_f16_w2_is_bit_identical(frag):
         torch.cuda.synchronize()
         ys.append(b.y.clone())
     assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("counts,d,d_ff", [([1283, 1250, 1301, 1222, 1279, 1340, 1197, 1368], 4096, 16384),
+                                           ([700, 720, 690, 745, 701, 680, 730, 747], 4096, 16384),
+                                           ([150, 290, 77], 512, 8192)])
+def test_down_frag_split_tiles(counts, d, d_ff):
+    """The fragment-ordered down-projection with the workspace (a short last
+    round split along K, pieces added up by the fix-up kernel) against the
+    same without it: equal up to float32 summation order, the same on every
+    call. The first shape leaves half a round of tiles (2-way split), the
+    second (the receiver share's) and third other splits."""
+    g = torch.Generator().manual_seed(11)
+    E, R = len(counts), int(sum(counts))
+    rows_max = R + 5
+    say("  case E=%d R=%d d=%d d_ff=%d" % (E, R, d, d_ff))
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device="cuda:0")
+    # h in fragment order, written by the up-projection (its padding rows zero)
+    x = torch.randn(R, d, generator=g).to(torch.bfloat16).to("cuda:0")
+    w1 = (torch.randn(E, d_ff, d, generator=g) / d ** 0.5).to(torch.bfloat16).to("cuda:0")
+    src = torch.arange(R, dtype=torch.int32, device="cuda:0")
+    xf = ops.moe_permute_frag(x, src, off, rows_max)
+    hf = ops.moe_expert_up_gelu_frag(xf, off, w1, rows_max, frag_out=True)
+    del w1, x
+    w2h = (torch.randn(E, d, d_ff, generator=g) / d_ff ** 0.5).to(torch.float16).to("cuda:0")
+    ws = torch.empty(ops.moe_ffn_workspace_bytes(torch.bfloat16), dtype=torch.uint8, device="cuda:0")
+    ws.fill_(0x7F)
+    yu = ops.moe_expert_down_frag(hf, off, w2h, rows_max)
+    ys = ops.moe_expert_down_frag(hf, off, w2h, rows_max, workspace=ws)
+    ys2 = ops.moe_expert_down_frag(hf, off, w2h, rows_max, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[:R], ys2[:R])
+    a, b = ys[:R].double(), yu[:R].double()
+    err = ((a - b).abs().max() / b.pow(2).mean().sqrt()).item()
+    moved = (a != b).float().mean().item()
+    say("  split vs unsplit: max|diff|/rms %.2e, %.2f%% of values differ" % (err, 100 * moved))
+    # float32 sums of 16384 products in another order: the difference grows
+    # like sqrt(K) * 2^-24 times the terms' size (measured up to 1.2e-5 of the
+    # output RMS); the row-major GEMM's split test allows 1e-3
+    assert err <= 1e-4, err

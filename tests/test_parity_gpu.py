@@ -64,16 +64,17 @@ def gpu_tensors(inp, cfg):
     return t
 
 
-def gpu_forward(inp, cfg, flags=0, frag=None):
+def gpu_forward(inp, cfg, flags=0, frag=None, f16w=False):
     """The layer forward; frag None lets moe_forward pick the path (the
     fragment-ordered one where ops.frag_eligible), True or False forces one."""
     t = gpu_tensors(inp, cfg)
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
     bufs = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, t["x"].dtype, t["x"].device,
                           cfg.routed, frag=frag)
+    w2h = ops.moe_weights_bf16_to_f16(t["w2"]) if f16w else None
     b = ops.moe_forward(t["x"], t["w1"], t["w2"], cfg.k, C, w_gate=t.get("w_gate"),
                         bias=t.get("bias"), topk_idx=t.get("topk_idx"),
-                        topk_w=t.get("topk_w"), alpha=cfg.alpha, flags=flags, bufs=bufs)
+                        topk_w=t.get("topk_w"), alpha=cfg.alpha, flags=flags, bufs=bufs, w2_f16=w2h)
     torch.cuda.synchronize()
     R = int(host(b.offsets)[-1])
     x_perm = unfrag(b.x_frag.cpu(), host(b.offsets), cfg.d)[0] if b.frag else b.x_perm[:R]
@@ -283,8 +284,8 @@ def test_dispatch_ignores_invalid_and_repeated_ids():
 
 
 # -------------------------------------------------------------- whole layer --
-def check_layer(inp, cfg, sample=None, frag=None):
-    g, t = gpu_forward(inp, cfg, frag=frag)
+def check_layer(inp, cfg, sample=None, frag=None, f16w=False):
+    g, t = gpu_forward(inp, cfg, frag=frag, f16w=f16w)
     gin = {"x": inp["x"], "w1": inp["w1"], "w2": inp["w2"],
            "topk_idx": g["topk_idx"], "topk_w": g["topk_w"]}
     ref = O.forward(gin, cfg.dtype, cfg.k, cfg.cf, cfg.alpha, sample_tokens=sample)
@@ -328,6 +329,24 @@ def test_layer_small_fragment_path(cfg):
     (moe_forward picks it by itself only from d = 4096)."""
     g = check_layer(I.make_inputs(cfg), cfg, frag=True)
     assert g["frag"]
+
+
+@pytest.mark.parametrize("cfg", FRAG_SMALL, ids=ids(FRAG_SMALL))
+def test_layer_small_fragment_h_f16_w2(cfg):
+    """The inference path end to end: fragment-ordered x and (where d_ff is a
+    multiple of 256) h, W2 in fp16, against the oracle."""
+    g = check_layer(I.make_inputs(cfg), cfg, frag=True, f16w=True)
+    assert g["frag"]
+
+
+@pytest.mark.parametrize("name", ["large-experts-e8", "ep8-receiver-share"])
+def test_layer_full_fragment_h_f16_w2(name):
+    """As bench.py runs the d = 4096 workloads (fragment-ordered x and h, W2 in
+    fp16, split down-projection tiles), against the oracle on sampled tokens."""
+    cfg = next(c for c in FULL if c.name == name)
+    rng = np.random.default_rng(1000 + cfg.seed)
+    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 40, replace=False)]))
+    check_layer(cached_inputs(cfg), cfg, sample, frag=True, f16w=True)
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=ids(FULL))
