@@ -63,6 +63,7 @@ GEMM_SOURCES = {
                   "mixture_experts_layer_49_amd/csrc/moe_internal.h"],
     "gemm_frag": ["mixture_experts_layer_49_amd/csrc/gemm_frag.hip",
                   "mixture_experts_layer_49_amd/csrc/gemm_frag.h",
+                  "mixture_experts_layer_49_amd/csrc/gemm_mfma.hip",   # the split fix-up kernel
                   "mixture_experts_layer_49_amd/csrc/ffn_common.h",
                   "mixture_experts_layer_49_amd/csrc/moe_internal.h"],
 }
