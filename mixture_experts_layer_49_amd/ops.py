@@ -274,14 +274,13 @@ def moe_frag_rows(rows_max: int, E: int) -> int:
 
 
 def frag_eligible(dtype, d: int) -> bool:
-    """Whether moe_forward takes the fragment-ordered up-projection for this
-    layer: bf16, d a multiple of 256 and at least 4096. Measured on the
-    workloads: 4-8% faster than the row-major permute + up-projection at
-    d = 4096 (each tile runs 64 stages of 64), even at d = 2048 and slower at
-    d = 1024, where the row-major kernel's split of a short last round of
-    tiles along K (which this kernel does not do) and its cheaper permute
-    weigh more."""
-    return dtype == torch.bfloat16 and d % 256 == 0 and d >= 4096
+    """Whether moe_forward takes the fragment-ordered path for this layer:
+    bf16, d a multiple of 256 and at least 2048. Measured on the workloads,
+    whole forward with fp16 W2 (x and h in fragment order): -8% at d = 4096,
+    -4% at d = 2048 (64 experts), +3% at d = 1024 (16 experts), where the
+    up-projection's short last round of tiles, which the row-major kernel
+    splits along K and this one does not, weighs more."""
+    return dtype == torch.bfloat16 and d % 256 == 0 and d >= 2048
 
 
 def moe_permute_frag(x, src, offsets, rows_max: int, x_frag=None, stream=None):

@@ -326,7 +326,7 @@ FRAG_SMALL = [c for c in SMALL if c.dtype == "bf16" and c.d % 256 == 0]
 @pytest.mark.parametrize("cfg", FRAG_SMALL, ids=ids(FRAG_SMALL))
 def test_layer_small_fragment_path(cfg):
     """The layer with the fragment-ordered permute and up-projection forced
-    (moe_forward picks it by itself only from d = 4096)."""
+    (moe_forward picks it by itself only from d = 2048)."""
     g = check_layer(I.make_inputs(cfg), cfg, frag=True)
     assert g["frag"]
 
@@ -339,10 +339,11 @@ def test_layer_small_fragment_h_f16_w2(cfg):
     assert g["frag"]
 
 
-@pytest.mark.parametrize("name", ["large-experts-e8", "ep8-receiver-share"])
+@pytest.mark.parametrize("name", ["large-experts-e8", "ep8-receiver-share", "fine-grained-e64"])
 def test_layer_full_fragment_h_f16_w2(name):
-    """As bench.py runs the d = 4096 workloads (fragment-ordered x and h, W2 in
-    fp16, split down-projection tiles), against the oracle on sampled tokens."""
+    """As bench.py runs the d >= 2048 workloads (fragment-ordered x and h, W2
+    in fp16, split down-projection tiles), against the oracle on sampled
+    tokens."""
     cfg = next(c for c in FULL if c.name == name)
     rng = np.random.default_rng(1000 + cfg.seed)
     sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 40, replace=False)]))
