@@ -43,6 +43,9 @@ SMALL = [
     # tiles): token counts that leave a ragged last workgroup, and a d tail
     I.small("router-tiles-e40", T=517, d=200, d_ff=128, E=40, k=3, cf=1.25, seed=19),
     I.small("router-tiles-e17", T=77, d=520, d_ff=64, E=17, k=2, cf=1.25, seed=20),
+    # capacity 0 at a shape the fragment-ordered path takes: every slot
+    # dropped, no grouped rows, every kernel of the path a no-op
+    I.small("all-dropped-frag", T=64, d=256, d_ff=256, E=4, k=2, cf=0.01, seed=21),
 ]
 FULL = list(I.CONFIGS)              # the five workloads at their real sizes
 FULL_ORACLE_FFN = {"tiny-fp32", "e16-zipf-bias"}   # oracle FFN on every token
@@ -316,7 +319,7 @@ def check_layer(inp, cfg, sample=None, frag=None, f16w=False):
 @pytest.mark.parametrize("cfg", SMALL, ids=ids(SMALL))
 def test_layer_small(cfg):
     g = check_layer(I.make_inputs(cfg), cfg)
-    if cfg.name == "all-dropped":
+    if cfg.name.startswith("all-dropped"):
         assert g["R"] == 0 and not g["y"].any()
 
 
@@ -411,6 +414,24 @@ def test_empty_batch():
     b.offsets.fill_(7)
     b.loss.fill_(7)
     ops.moe_forward(x, w1, w2, 2, 0, w_gate=wg, bufs=b)
+    torch.cuda.synchronize()
+    assert (host(b.counts) == 0).all() and (host(b.offsets) == 0).all()
+    assert float(host(b.loss)[0]) == 0.0
+
+
+@pytest.mark.parametrize("frag", [False, True])
+def test_empty_batch_bf16_d256(frag):
+    """T = 0 on both paths (fragment-ordered with fp16 W2): a no-op that
+    leaves zero counts, offsets and loss."""
+    x = torch.empty(0, 256, device="cuda:0", dtype=torch.bfloat16)
+    wg = torch.randn(4, 256, device="cuda:0").to(torch.bfloat16)
+    w1 = torch.randn(4, 256, 256, device="cuda:0").to(torch.bfloat16)
+    w2 = torch.randn(4, 256, 256, device="cuda:0").to(torch.bfloat16)
+    b = ops.MoEBuffers(0, 256, 256, 4, 2, 0, torch.bfloat16, "cuda:0", frag=frag)
+    b.counts.fill_(7)
+    b.offsets.fill_(7)
+    b.loss.fill_(7)
+    ops.moe_forward(x, w1, w2, 2, 0, w_gate=wg, bufs=b, w2_f16=ops.moe_weights_bf16_to_f16(w2))
     torch.cuda.synchronize()
     assert (host(b.counts) == 0).all() and (host(b.offsets) == 0).all()
     assert float(host(b.loss)[0]) == 0.0
