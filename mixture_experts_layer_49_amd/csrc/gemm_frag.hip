@@ -1,32 +1,36 @@
-// Up-projection + GELU-tanh of the grouped expert FFN (ETP page
-// "ETP专家并行加速MoE模型": each expert's up-projection w1; EP tutorial
+// The grouped expert FFN of bf16 layers with the activations in
+// MFMA-fragment order (ETP page "ETP专家并行加速MoE模型": each expert's
+// up-projection w1 and down-projection w2; EP tutorial
 // "专家并行：混合专家模型的分布式训练方案", section 2.1 steps 3-4: the permuted
-// tokens of each expert go through its FFN) with the activation operand in
-// MFMA-fragment order, for bf16 layers.
+// tokens of each expert go through its FFN).
 //
 // Fragment order. The rows of each expert segment are padded to a multiple of
 // 32 (padded segment e starts at row pad[e] = sum over e' < e of
-// round_up(kept_e', 32)); element (padded row r, k) of x_frag sits at
-//   ((r / 32) (d / 16) + k / 16) 512 + ((r % 32) + 32 ((k / 8) % 2)) 8 + k % 8,
+// round_up(kept_e', 32)); element (padded row r, k) of an activation with K
+// columns sits at
+//   ((r / 32) (K / 16) + k / 16) 512 + ((r % 32) + 32 ((k / 8) % 2)) 8 + k % 8,
 // so each 32-row x 16-k block is 1 KiB in the lane order of the MFMA A operand
-// (lane l: row l % 32, k = 8 (l / 32) .. +7). Padding rows hold zeros.
+// (lane l: row l % 32, k = 8 (l / 32) .. +7). Padding rows hold zeros. x_frag
+// (K = d) feeds the up-projection, h_frag (K = d_ff) the down-projection.
 //
-// permute_frag_kernel writes it from x and src[] (the gather of the permute,
-// EP tutorial section 5.3: tokens of one expert made contiguous), staging
-// 32-row x 256-column blocks in LDS so that both the row reads and the
-// fragment writes are whole 16-byte-per-lane wave accesses.
+// permute_frag_kernel writes x_frag from x and src[] (the gather of the
+// permute, EP tutorial section 5.3: tokens of one expert made contiguous),
+// staging 32-row x 256-column blocks in LDS so that both the row reads and
+// the fragment writes are whole 16-byte-per-lane wave accesses.
 //
-// up_frag_kernel: C = x_perm W1[e]^T over the segments, h = fp16(gelu_tanh(C))
-// row-major [rows, d_ff] at the unpadded rows (the same h as the row-major
-// path, bit for bit: every MFMA sees the same operands in the same order).
-// 256 x 256 tiles, four waves as 4 x 1 (wave w: rows 64 w .. +63, all 256
-// columns, 2 x 8 accumulator tiles of 32 x 32). Each wave loads its A
-// fragments straight into registers (1 KiB contiguous per wave load, four
-// stages of register buffers, issued three stages ahead); only W1 goes through
-// LDS, in a ring of four 32 KiB slots filled by LDS-DMA three stages ahead.
-// One barrier per 64-deep stage. Tiles continue across a workgroup's units:
-// the last three stages of a tile prefetch the next tile's first three, so
-// those loads are in flight during the per-wave epilogue.
+// frag_gemm_kernel<KIND>: C = A B[e]^T over the segments, A fragment-ordered,
+// B = W1 or W2 [E, N, K] K-contiguous. 256 x 256 tiles, four waves as 4 x 1
+// (wave w: rows 64 w .. +63, all 256 columns, 2 x 8 accumulator tiles of
+// 32 x 32). Each wave loads its A fragments straight into registers (1 KiB
+// contiguous per wave load, four stages of register buffers, issued three
+// stages ahead); only B goes through LDS, in a ring of four 32 KiB slots
+// filled by LDS-DMA three stages ahead. One barrier per 64-deep stage. Tiles
+// continue across a workgroup's units: the last three stages of a tile
+// prefetch the next tile's first three, so those loads are in flight during
+// the per-wave epilogue. The kinds (below) differ in the MFMA input type and
+// the epilogue; every MFMA sees the same operands in the same order as the
+// row-major GEMM's, so the results are bit-identical to it without a
+// workspace.
 #include "ffn_common.h"
 #include "gemm_frag.h"
 
