@@ -219,8 +219,10 @@ int moe_expert_down_f16w(const void* h, const int32_t* offsets, int32_t E, int64
  * MOE_BF16; 0 for MOE_F32 (whose kernels never split). */
 size_t moe_ffn_workspace_bytes(int32_t dtype);
 
-/* Up-projection from a fragment-ordered copy of x_perm (bf16 layers; same h
- * as moe_expert_up_gelu with a NULL workspace, bit for bit). The copy holds
+/* The expert FFN of bf16 layers on fragment-ordered activations (inference:
+ * moe_permute_frag, then moe_expert_up_gelu_frag with MOE_ORDER_FRAG, then
+ * moe_expert_down_frag; the same h and y_perm, bit for bit, as the row-major
+ * calls without a workspace). The fragment-ordered copy of x_perm holds
  * the permuted rows of EP tutorial 5.3 laid out for the matrix cores: each
  * expert segment is padded with zero rows to a multiple of 32 (padded segment
  * e starts at pad[e] = sum over e' < e of roundup(offsets[e'+1] - offsets[e'],
@@ -250,8 +252,9 @@ size_t moe_ffn_workspace_bytes(int32_t dtype);
  *   workspace, the tiles of a short last round are split along K (pieces of
  *   whole 256-deep quads, so the sums may round differently from the
  *   row-major kernel's splits; fixed order, deterministic).
- * Pointers 16-byte aligned device memory; offsets read only by the kernels.
- * Both calls take bf16 data only (no dtype argument).
+ * Pointers 16-byte aligned device memory; offsets (and src) read only by the
+ * kernels, and must be as moe_dispatch_plan writes them. These calls take
+ * bf16 data only (no dtype argument).
  * Errors: MOE_ERR_ALIGN for d, d_ff or a pointer that breaks the rules above;
  *   MOE_ERR_SHAPE for E or sizes out of range; MOE_ERR_ARG for a NULL pointer
  *   when rows_max > 0. */
