@@ -26,10 +26,9 @@ Plain numpy in float64, written step by step from the pages:
 
 Readings where the pages are silent (each also listed in the design notes):
   * probabilities are a softmax over all E logits, taken before top-k;
-  * experts are ranked on their logits rounded to float32 (the precision the
-    kernels rank in), larger first, ties to the lower expert index; the
-    combine weight of a chosen expert is its softmax probability (not
-    renormalised unless `renorm`);
+  * experts are ranked on their logits (float64 here), larger first, ties to
+    the lower expert index; the combine weight of a chosen expert is its
+    softmax probability (not renormalised unless `renorm`);
   * the capacity formula's "total tokens" is n = T (the tokens entering the
     layer); round() is round-half-even; cf <= 0 disables dropping;
   * dropping keeps, per expert, the first C assignments in token order;
@@ -90,13 +89,12 @@ def softmax(logits: np.ndarray) -> np.ndarray:
 def topk(logits: np.ndarray, probs: np.ndarray, k: int, renorm: bool = False):
     """Top-k experts per token (EP tutorial 1.1 and 2.1 step 1).
 
-    Key: float32(logit) descending, then expert index ascending. Slot j holds
-    the j-th best expert. Weight = the expert's softmax probability.
+    Key: logit descending, then expert index ascending. Slot j holds the j-th
+    best expert. Weight = the expert's softmax probability.
     Returns (idx [T,k] int64, w [T,k] float64)."""
     T, E = logits.shape
-    l32 = logits.astype(np.float32)
     eidx = np.broadcast_to(np.arange(E), (T, E))
-    order = np.lexsort((eidx, -l32), axis=-1)   # primary key is the last one
+    order = np.lexsort((eidx, -logits), axis=-1)   # primary key is the last one
     idx = order[:, :k].astype(np.int64)
     w = np.take_along_axis(probs, idx, axis=1)
     if renorm:

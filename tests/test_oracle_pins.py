@@ -109,19 +109,20 @@ def test_topk_vs_brute_force_subsets(seed):
     rng = np.random.default_rng(seed)
     E = 5
     l = rng.integers(-2, 3, size=(12, E)).astype(float)   # many exact ties
-    l32 = l.astype(np.float32)
     p = O.softmax(l)
     for k in range(1, E + 1):
         idx, _ = O.topk(l, p, k)
         for t in range(12):
-            assert list(idx[t]) == _brute_topk(l32[t], k)
+            assert list(idx[t]) == _brute_topk(l[t], k)
 
 
-def test_topk_ranks_in_float32():
-    # two logits that differ only below float32 resolution tie -> lower index
-    l = np.array([[1.0, 1.0 + 1e-12, 0.0]])
-    idx, _ = O.topk(l, O.softmax(l), 1)
-    assert idx[0, 0] == 0
+def test_topk_ranks_the_exact_logits():
+    # the ranking is on the logits as given: a difference far below float32
+    # resolution still decides, and only exactly equal logits go to the lower
+    # index
+    l = np.array([[1.0, 1.0 + 1e-12, 0.0], [1.0, 1.0, 0.0], [0.5, 0.5 - 1e-15, 0.5]])
+    idx, _ = O.topk(l, O.softmax(l), 2)
+    np.testing.assert_array_equal(idx, [[1, 0], [0, 1], [0, 2]])
 
 
 def test_topk_renorm_sums_to_one():
