@@ -317,18 +317,23 @@ def gate_backward(dw: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, prob
 
 
 def expert_backward(x_rows: np.ndarray, d_out_rows: np.ndarray, w1_e: np.ndarray,
-                    w2_e: np.ndarray, fcols=None) -> dict:
+                    w2_e: np.ndarray, fcols=None, weight_grads: bool = True) -> dict:
     """One expert's FFN backward on a block of its rows (optionally only the
     hidden units `fcols`): z = X W1^T, h = gelu(z), dz = (D W2) * gelu'(z),
-    dW1 = dz^T X, dW2 = D^T h and, over all hidden units, dx_perm = dz W1."""
+    dW1 = dz^T X, dW2 = D^T h (left out when not `weight_grads`) and, over all
+    hidden units, dx_perm = dz W1 and the rows' forward output y = h W2^T
+    (what the combine weights' gradient needs)."""
     w1s = w1_e if fcols is None else w1_e[fcols]
     w2s = w2_e if fcols is None else w2_e[:, fcols]
     z = x_rows @ w1s.T
     h = gelu_tanh(z)
     dz = (d_out_rows @ w2s) * gelu_tanh_grad(z)
-    out = {"z": z, "h": h, "dz": dz, "dw1": dz.T @ x_rows, "dw2": d_out_rows.T @ h}
+    out = {"z": z, "h": h, "dz": dz}
+    if weight_grads:
+        out["dw1"], out["dw2"] = dz.T @ x_rows, d_out_rows.T @ h
     if fcols is None:
         out["dx_perm"] = dz @ w1_e
+        out["y"] = h @ w2_e.T
     return out
 
 

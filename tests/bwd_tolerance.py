@@ -32,7 +32,7 @@ K_SIGMA = 7.0
 _S3 = np.sqrt(3.0)
 
 
-def expert_sigmas(x_rows, d_out_rows, w1_e, w2_e, fcols=None) -> dict:
+def expert_sigmas(x_rows, d_out_rows, w1_e, w2_e, fcols=None, weight_grads=True) -> dict:
     """Error standard deviations of one expert block, in the shapes that
     O.expert_backward returns for the same arguments."""
     w1s = w1_e if fcols is None else w1_e[fcols]
@@ -47,11 +47,42 @@ def expert_sigmas(x_rows, d_out_rows, w1_e, w2_e, fcols=None) -> dict:
     s_dh = np.sqrt(s_dout ** 2 @ w2s ** 2)
     s_dz = np.sqrt((g * s_dh) ** 2 + (dh * s_z) ** 2 + (U_BF16 / _S3 * dz) ** 2)
     s_h = np.sqrt((U_FP16 / _S3 * h) ** 2 + (U_BF16 / _S3 * h) ** 2 + (g * s_z) ** 2)
-    out = {"z": s_z, "dz": s_dz, "dw1": np.sqrt(s_dz.T ** 2 @ x_rows ** 2),
-           "dw2": np.sqrt(s_dout.T ** 2 @ h ** 2 + d_out_rows.T ** 2 @ s_h ** 2)}
+    out = {"z": s_z, "dz": s_dz}
+    if weight_grads:
+        out["dw1"] = np.sqrt(s_dz.T ** 2 @ x_rows ** 2)
+        out["dw2"] = np.sqrt(s_dout.T ** 2 @ h ** 2 + d_out_rows.T ** 2 @ s_h ** 2)
     if fcols is None:
         out["dx_perm"] = np.sqrt(s_dz ** 2 @ w1_e ** 2)
     return out
+
+
+def expert_sigmas_torch(x_rows, d_out_rows, w1_e, w2_e, weight_grads=True) -> dict:
+    """expert_sigmas without `fcols`, the same chain in float32 torch CPU ops
+    (multi-threaded: the full-size case has 21 M hidden values per expert).
+    GELU and its derivative are the tanh form's formulas written out here;
+    they only scale the error model."""
+    import torch
+
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    x, d_out, w1, w2 = f(x_rows), f(d_out_rows), f(w1_e), f(w2_e)
+    c = float(np.sqrt(2.0 / np.pi))
+    z = x @ w1.T
+    th = torch.tanh(c * (z + 0.044715 * z * z * z))
+    h = 0.5 * z * (1.0 + th)
+    g = 0.5 * (1.0 + th) + 0.5 * z * (1.0 - th * th) * c * (1.0 + 3.0 * 0.044715 * z * z)
+    dh = d_out @ w2
+    dz = dh * g
+    ub, uf = U_BF16 / _S3, U_FP16 / _S3
+    s_dout = ub * d_out.abs()
+    s_z = uf * z.abs()
+    s_dh = torch.sqrt(s_dout.square() @ w2.square())
+    s_dz = torch.sqrt((g * s_dh).square() + (dh * s_z).square() + (ub * dz).square())
+    out = {"z": s_z, "dz": s_dz, "dx_perm": torch.sqrt(s_dz.square() @ w1.square())}
+    if weight_grads:
+        s_h = torch.sqrt((uf * h).square() + (ub * h).square() + (g * s_z).square())
+        out["dw1"] = torch.sqrt(s_dz.T.square() @ x.square())
+        out["dw2"] = torch.sqrt(s_dout.T.square() @ h.square() + d_out.T.square() @ s_h.square())
+    return {k: v.double().numpy() for k, v in out.items()}
 
 
 def layer_sigmas(inp, fwd, ref, dtype="bf16") -> dict:

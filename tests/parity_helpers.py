@@ -32,6 +32,9 @@ def dev(a, dtype: str):
 
 
 def host(t) -> np.ndarray:
+    """Device tensor -> numpy. Slice to the written rows before calling: rows
+    past them hold whatever the allocation held, signalling-NaN patterns
+    included, and converting those raises floating-point warnings."""
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy().astype(np.float64)
     return t.cpu().numpy()

@@ -10,8 +10,9 @@ the error their 16-bit storage roundings imply, element by element (the
 model and its derivation: bwd_tolerance.py); the gate's outputs (dw, d_logits,
 dWg, db), which see only f32 arithmetic on the forward's outputs, within
 2e-2 max-abs / rms as the forward.
-The full-size bench workload compares sampled tokens, rows and hidden units,
-and checks the gate weight gradient as the product it is.
+The full-size bench workload compares every kept row and every token, the
+whole weight gradients of two experts, and the gate weight gradient as the
+product it is.
 """
 import numpy as np
 import pytest
@@ -20,7 +21,7 @@ import torch
 from mixture_experts_layer_49_amd import inputs as I
 from mixture_experts_layer_49_amd import ops
 from oracle import moe_oracle as O
-from bwd_tolerance import expert_sigmas, layer_sigmas, within
+from bwd_tolerance import expert_sigmas_torch, layer_sigmas, within
 from parity_helpers import cached_inputs, close, dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -71,12 +72,12 @@ def run_gpu(inp, cfg, variant="plain", aux_grad=0.7):
     fwd = {"topk_idx": host(b.topk_idx).astype(np.int64) if cfg.routed else inp["topk_idx"].astype(np.int64),
            "topk_w": host(b.topk_w) if cfg.routed else inp["topk_w"],
            "counts": host(b.counts), "offsets": host(b.offsets).astype(np.int64),
-           "dest": host(b.dest).astype(np.int64), "src": host(b.src)[:R].astype(np.int64)}
+           "dest": host(b.dest).astype(np.int64), "src": host(b.src[:R]).astype(np.int64)}
     if cfg.routed:
         fwd["probs"] = host(b.probs)
-        fwd["lse"] = host(b.lse)[:cfg.T]
-    gpu = {"z_perm": host(b.z)[:R], "d_out_perm": host(g.d_out_perm)[:R], "dw": host(g.d_topk_w),
-           "dz_perm": host(g.dz)[:R], "dx_perm": host(g.dx_perm)[:R], "dw1": host(g.dw1),
+        fwd["lse"] = host(b.lse[:cfg.T])
+    gpu = {"z_perm": host(b.z[:R]), "d_out_perm": host(g.d_out_perm[:R]), "dw": host(g.d_topk_w),
+           "dz_perm": host(g.dz[:R]), "dx_perm": host(g.dx_perm[:R]), "dw1": host(g.dw1),
            "dw2": host(g.dw2), "dx": host(g.dx)}
     if cfg.routed:
         gpu.update(dl=host(g.d_logits), dwg=host(g.dw_gate), db=host(g.d_bias))
@@ -139,67 +140,59 @@ def test_backward_is_deterministic():
         np.testing.assert_array_equal(a[n], b[n], err_msg=n)
 
 
-def test_backward_full_size_sampled():
-    """large-experts-e8 at its real size: sampled tokens, rows and hidden
-    units against the oracle; the gate weight gradient as d_logits^T x."""
+@pytest.mark.timeout(900)
+def test_backward_full_size():
+    """large-experts-e8 at its real size against the oracle: every kept row's
+    z, dz and dx_perm, every token's combine-weight gradient, d_logits and
+    dx, and the whole weight gradients dW1, dW2 of the first and the last
+    expert; the gate weight gradient as the product d_logits^T x."""
     cfg = I.config("large-experts-e8")
     inp = cached_inputs(cfg)
     gpu, fwd, dy, knobs, _ = run_gpu(inp, cfg)
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     R = int(fwd["offsets"][-1])
-    rng = np.random.default_rng(5)
-    toks = np.sort(rng.choice(T, 48, replace=False))
-    need = fwd["dest"][toks]
     x = O.decode(inp["x"], cfg.dtype)
     # every kept row's output gradient: w * dy
     d_out_all, _ = O.combine_backward(dy, np.zeros((R, d)), fwd["dest"], fwd["topk_w"], R)
     within(gpu["d_out_perm"], d_out_all, 2.0 ** -8 / np.sqrt(3) * np.abs(d_out_all), "d_out_perm")
     y_perm = np.zeros((R, d))
-    dxp = {}
+    dx_perm = np.zeros((R, d))
+    s_dx_perm = np.zeros((R, d))
+    whole = (0, E - 1)      # experts whose weight gradients are checked whole
     for e in range(E):
         a, b = int(fwd["offsets"][e]), int(fwd["offsets"][e + 1])
-        rows = [int(r) for r in need[need >= 0] if a <= r < b]
+        if a == b:
+            continue
         w1e, w2e = O.decode(inp["w1"][e], cfg.dtype), O.decode(inp["w2"][e], cfg.dtype)
-        if rows:
-            xr = x[fwd["src"][rows]]
-            y_perm[rows] = O.expert_ffn(xr, w1e, w2e)
-            g = O.expert_backward(xr, d_out_all[rows], w1e, w2e)
-            sg = expert_sigmas(xr, d_out_all[rows], w1e, w2e)
-            within(gpu["z_perm"][rows], g["z"], sg["z"], "z, expert %d rows %s" % (e, rows))
-            within(gpu["dz_perm"][rows], g["dz"], sg["dz"], "dz, expert %d" % e)
-            within(gpu["dx_perm"][rows], g["dx_perm"], sg["dx_perm"], "dx_perm, expert %d" % e)
-            for i, r in enumerate(rows):
-                dxp[r] = (g["dx_perm"][i], sg["dx_perm"][i])
-        if e in (0, 3, 7):
-            # weight gradients of sampled hidden units, over every row of the expert
-            fcols = np.sort(rng.choice(cfg.d_ff, 6, replace=False))
-            xr = x[fwd["src"][a:b]]
-            g = O.expert_backward(xr, d_out_all[a:b], w1e, w2e, fcols)
-            sg = expert_sigmas(xr, d_out_all[a:b], w1e, w2e, fcols)
-            within(gpu["dw1"][e][fcols], g["dw1"], sg["dw1"], "dW1[%d] rows %s" % (e, fcols))
-            within(gpu["dw2"][e][:, fcols], g["dw2"], sg["dw2"], "dW2[%d] cols %s" % (e, fcols))
-        del w1e, w2e
-    # combine backward and the gate backward on the sampled tokens
-    _, dw_s = O.combine_backward(dy[toks], y_perm, need, fwd["topk_w"][toks], R)
-    close(gpu["dw"][toks], dw_s, cfg.dtype, "sampled dw")
-    dl_s = O.gate_backward(dw_s, fwd["topk_idx"][toks], fwd["topk_w"][toks], fwd["probs"][toks],
-                           fwd["counts"], k, cfg.alpha, 0.7, n_tokens=T)
-    close(gpu["dl"][toks], dl_s, cfg.dtype, "sampled d_logits")
+        xr = x[fwd["src"][a:b]]
+        g = O.expert_backward(xr, d_out_all[a:b], w1e, w2e, weight_grads=e in whole)
+        y_perm[a:b] = g["y"]
+        sg = expert_sigmas_torch(xr, d_out_all[a:b], w1e, w2e, weight_grads=e in whole)
+        within(gpu["z_perm"][a:b], g["z"], sg["z"], "z, expert %d (%d rows)" % (e, b - a))
+        within(gpu["dz_perm"][a:b], g["dz"], sg["dz"], "dz, expert %d" % e)
+        within(gpu["dx_perm"][a:b], g["dx_perm"], sg["dx_perm"], "dx_perm, expert %d" % e)
+        dx_perm[a:b], s_dx_perm[a:b] = g["dx_perm"], sg["dx_perm"]
+        if e in whole:
+            within(gpu["dw1"][e], g["dw1"], sg["dw1"], "dW1[%d], every hidden unit" % e)
+            within(gpu["dw2"][e], g["dw2"], sg["dw2"], "dW2[%d], every hidden unit" % e)
+        del w1e, w2e, g, sg
+    # combine backward and the gate backward on every token
+    _, dw = O.combine_backward(dy, y_perm, fwd["dest"], fwd["topk_w"], R)
+    close(gpu["dw"], dw, cfg.dtype, "dw, every token")
+    dl = O.gate_backward(dw, fwd["topk_idx"], fwd["topk_w"], fwd["probs"], fwd["counts"], k,
+                         cfg.alpha, 0.7)
+    close(gpu["dl"], dl, cfg.dtype, "d_logits, every token")
     wg = O.decode(inp["w_gate"], cfg.dtype)
-    ref_dx = np.zeros((len(toks), d))
-    var = np.zeros((len(toks), d))
-    for i, t in enumerate(toks):
-        for r in fwd["dest"][t]:
-            if r >= 0:
-                ref_dx[i] += dxp[int(r)][0]
-                var[i] += dxp[int(r)][1] ** 2
-        ref_dx[i] += dl_s[i] @ wg
-    extra = 2e-2 * float(np.sqrt(np.mean(dl_s ** 2))) * np.abs(wg).sum(axis=0)
-    within(gpu["dx"][toks], ref_dx, np.sqrt(var), "dx, sampled tokens", extra)
+    ref_dx = dl @ wg
+    var = np.zeros((T, d))
+    np.add.at(ref_dx, fwd["src"], dx_perm)
+    np.add.at(var, fwd["src"], s_dx_perm ** 2)
+    extra = 2e-2 * float(np.sqrt(np.mean(dl ** 2))) * np.abs(wg).sum(axis=0)
+    within(gpu["dx"], ref_dx, np.sqrt(var), "dx, every token", extra)
     # gate weight gradient: the product of the GPU's own d_logits with x
-    dl = gpu["dl"].astype(np.float64)
-    close(gpu["dwg"], dl.T @ x, "f32", "dWg = d_logits^T x")
-    close(gpu["db"], dl.sum(axis=0), "f32", "db = sum_t d_logits")
+    dlg = gpu["dl"].astype(np.float64)
+    close(gpu["dwg"], dlg.T @ x, "f32", "dWg = d_logits^T x")
+    close(gpu["db"], dlg.sum(axis=0), "f32", "db = sum_t d_logits")
 
 
 @pytest.mark.parametrize("T,d,E,dt", [(20000, 256, 8, "bf16"), (9000, 72, 20, "f32"), (3, 64, 5, "bf16"),

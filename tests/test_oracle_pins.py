@@ -477,8 +477,17 @@ def test_backward_slices_agree_with_the_whole():
     np.testing.assert_allclose(part["dw1"], g["dw1"][e][fcols], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(part["dw2"], g["dw2"][e][:, fcols], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(part["dz"], g["dz_perm"][a:b][:, fcols], rtol=1e-12, atol=1e-12)
+    # without the weight gradients: the same row gradients, no dW keys
+    rows = O.expert_backward(xp, g["d_out_perm"][a:b], inp["w1"][e], inp["w2"][e],
+                             weight_grads=False)
+    assert "dw1" not in rows and "dw2" not in rows
+    np.testing.assert_allclose(rows["dx_perm"], g["dx_perm"][a:b], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rows["z"], g["z_perm"][a:b], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rows["y"], O.expert_ffn(xp, inp["w1"][e], inp["w2"][e]),
+                               rtol=1e-12, atol=1e-12)
     toks = np.array([0, 7, 30])
     dl = O.gate_backward(g["dw"][toks], fwd["topk_idx"][toks], fwd["topk_w"][toks],
                          fwd["probs"][toks], fwd["counts"], k, 0.1, 0.5, True, 1.0,
                          fwd["lse"][toks], 0.2, n_tokens=T)
     np.testing.assert_allclose(dl, g["dl"][toks], rtol=1e-12, atol=1e-14)
+
