@@ -323,13 +323,13 @@ def main(argv=None) -> int:
     given_idx = dev(inp["topk_idx"], False) if not cfg.routed else None
     given_w = dev(inp["topk_w"], False) if not cfg.routed else None
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
-    b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed)
-    # inference weight format: W2 in fp16, converted once (exact; the kernels
-    # would otherwise convert each W2 value in registers on every step)
+    b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed,
+                       w2_f16=bf)
+    # inference weight format: W2 in fp16, converted once (the kernels would
+    # otherwise convert each W2 value in registers on every step, the same way)
     w2h = ops.moe_weights_bf16_to_f16(w2) if bf else None
     # fragment-ordered path: h stays in fragment order for the down-projection
-    hfrag = (torch.empty((ops.moe_frag_rows(b.rows_max, cfg.E), cfg.d_ff), dtype=torch.float16,
-                         device=x.device) if b.frag and cfg.d_ff % 256 == 0 else None)
+    hfrag = b.h_frag
     stream = torch.cuda.current_stream()
 
     names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]

@@ -204,12 +204,23 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
  * down-projection of moe_expert_down converts every bf16 W2 value to fp16 in
  * registers before the fp16 x fp16 products, this does it once up front).
  * moe_weights_bf16_to_f16: w_f16[i] = fp16(w[i]) for i < n, round to nearest
- *   even (exact for bf16 values inside the fp16 normal range; the same
- *   rounding the kernels apply). 16-byte aligned device pointers.
+ *   even, the same rounding the kernels apply. It is exact for 0 and for
+ *   2^-17 <= |w| <= 65280; smaller values lose low bits in the fp16
+ *   subnormal range (down to 0 below 2^-25), finite values of magnitude
+ *   65536 and above become +-inf, infinities and NaNs stay what they are.
+ *   16-byte aligned device pointers. `report` (nullable, device, 8-byte
+ *   aligned, two counters): when given, report[0] = how many finite nonzero
+ *   values lost bits, report[1] = how many finite values became +-inf; the
+ *   call sets both (no clearing needed), and they are exact counts whatever
+ *   order the GPU adds in. With n = 0 and a report it writes two zeros.
  * moe_expert_down_f16w: moe_expert_down (dtype MOE_BF16) with w2_f16 [E, d,
  *   d_ff] fp16 = moe_weights_bf16_to_f16(W2); y_perm bit-identical to
- *   moe_expert_down on the bf16 W2 with the same workspace argument. */
-int moe_weights_bf16_to_f16(const void* w, int64_t n, void* w_f16, hipStream_t stream);
+ *   moe_expert_down on the bf16 W2 with the same workspace argument.
+ * The hidden activation h of bf16 layers is fp16 too (moe_grouped_ffn): a
+ * |gelu(z)| of 65520 or more is stored as +-inf, and the output rows that
+ * use it become inf or NaN; nothing checks for it. */
+int moe_weights_bf16_to_f16(const void* w, int64_t n, void* w_f16, uint64_t* report,
+                            hipStream_t stream);
 int moe_expert_down_f16w(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max,
                          int64_t d, int64_t d_ff, const void* w2_f16, float* y_perm,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -334,14 +334,19 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E, int64_t ro
                     "moe_expert_down launch");
 }
 
-int moe_weights_bf16_to_f16(const void* w, int64_t n, void* w_f16, hipStream_t stream) {
+int moe_weights_bf16_to_f16(const void* w, int64_t n, void* w_f16, uint64_t* report,
+                            hipStream_t stream) {
   if (n < 0) return fail(MOE_ERR_ARG, "n = %lld < 0", static_cast<long long>(n));
-  if (n == 0) return MOE_OK;
-  MOE_NONNULL(w);
-  MOE_NONNULL(w_f16);
-  MOE_TRY(check_ptr16("w", w));
-  MOE_TRY(check_ptr16("w_f16", w_f16));
-  return hip_status(moe::launch_bf16_to_f16(w, n, w_f16, stream), "moe_weights_bf16_to_f16 launch");
+  if ((reinterpret_cast<uintptr_t>(report) & 7u) != 0)
+    return fail(MOE_ERR_ALIGN, "report is not 8-byte aligned");
+  if (n > 0) {
+    MOE_NONNULL(w);
+    MOE_NONNULL(w_f16);
+    MOE_TRY(check_ptr16("w", w));
+    MOE_TRY(check_ptr16("w_f16", w_f16));
+  }
+  return hip_status(moe::launch_bf16_to_f16(w, n, w_f16, report, stream),
+                    "moe_weights_bf16_to_f16 launch");
 }
 
 int moe_expert_down_f16w(const void* h, const int32_t* offsets, int32_t E, int64_t rows_max, int64_t d,

@@ -13,7 +13,11 @@
 // of a bf16 layer is kept as IEEE fp16, not bf16: same size, three more
 // significand bits, which cuts the rounding error it adds to the layer output
 // about eight-fold; the down-projection then multiplies fp16 by fp16, W2's
-// bf16 values being converted exactly on their way into LDS.
+// bf16 values being rounded to fp16 (nearest even) on their way into LDS.
+// That rounding is exact for 2^-17 <= |w| <= 65280 and for 0: smaller values
+// lose low bits (fp16 subnormals), larger finite ones become +-inf. h itself
+// saturates the same way: |gelu(z)| >= 65520 is stored as +-inf, and the
+// output rows that use it are then inf or NaN.
 //
 // f32 layers run on the plain 64x64 LDS-tiled FMA kernel below, over the same
 // device-side tile list.
@@ -122,32 +126,91 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
 
 namespace {
 
+// What rounding a bf16 value to fp16 did: bit 0 set when the fp16 value
+// differs from a finite nonzero input and is finite (low bits lost), bit 1
+// when a finite input became +-inf. Infinities and NaNs pass through
+// unflagged.
+__device__ __forceinline__ int f16_rounding_flags(float f, _Float16 h) {
+  const float back = static_cast<float>(h);
+  if (!__builtin_isfinite(f)) return 0;
+  if (__builtin_isinf(back)) return 2;
+  return back != f ? 1 : 0;
+}
+
 // Eight bf16 values per thread and step, grid-stride; the tail (n % 8) by the
-// first threads one value each.
+// first threads one value each. With REPORT, each wave adds its counts of
+// flagged values to report[0] (inexact) and report[1] (overflow) with one
+// vector atomic add per counter: integer sums, so the totals do not depend on
+// the order of the adds.
+template <bool REPORT>
 __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint4* __restrict__ src, int64_t n8,
                                                           uint4* __restrict__ dst, const uint16_t* __restrict__ src_tail,
-                                                          int tail, uint16_t* __restrict__ dst_tail) {
+                                                          int tail, uint16_t* __restrict__ dst_tail,
+                                                          unsigned long long* __restrict__ report) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8; i += stride)
-    dst[i] = bf16x8_to_f16x8(src[i]);
+  uint32_t n_inexact = 0, n_over = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = src[i];
+    const uint4 o = bf16x8_to_f16x8(v);
+    dst[i] = o;
+    if constexpr (REPORT) {
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w}, out[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f16x2 h = __builtin_bit_cast(f16x2, out[w]);
+        const int f0 = f16_rounding_flags(__uint_as_float(in[w] << 16), h[0]);
+        const int f1 = f16_rounding_flags(__uint_as_float(in[w] & 0xffff0000u), h[1]);
+        n_inexact += (f0 & 1) + (f1 & 1);
+        n_over += (f0 >> 1) + (f1 >> 1);
+      }
+    }
+  }
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t < tail) {
-    const _Float16 h = static_cast<_Float16>(bf16_to_f32(src_tail[t]));
+    const float f = bf16_to_f32(src_tail[t]);
+    const _Float16 h = static_cast<_Float16>(f);
     dst_tail[t] = __builtin_bit_cast(uint16_t, h);
+    if constexpr (REPORT) {
+      const int fl = f16_rounding_flags(f, h);
+      n_inexact += fl & 1;
+      n_over += fl >> 1;
+    }
   }
+  if constexpr (REPORT) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      n_inexact += __shfl_xor(n_inexact, o, kWave);
+      n_over += __shfl_xor(n_over, o, kWave);
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      if (n_inexact) atomicAdd(&report[0], static_cast<unsigned long long>(n_inexact));
+      if (n_over) atomicAdd(&report[1], static_cast<unsigned long long>(n_over));
+    }
+  }
+}
+
+__global__ void clear_report_kernel(unsigned long long* __restrict__ report) {
+  if (threadIdx.x < 2) report[threadIdx.x] = 0ull;
 }
 
 }  // namespace
 
-hipError_t launch_bf16_to_f16(const void* src, int64_t n, void* dst, hipStream_t s) {
+hipError_t launch_bf16_to_f16(const void* src, int64_t n, void* dst, uint64_t* report, hipStream_t s) {
+  if (report != nullptr) {
+    hipLaunchKernelGGL(clear_report_kernel, dim3(1), dim3(kWave), 0, s,
+                       reinterpret_cast<unsigned long long*>(report));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (n <= 0) return hipSuccess;
   const int64_t n8 = n / 8;
   int64_t g = (n8 + 255) / 256;
   g = g < 1 ? 1 : (g > 8192 ? 8192 : g);
-  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, s,
+  auto* kern = report != nullptr ? bf16_to_f16_kernel<true> : bf16_to_f16_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(g)), dim3(256), 0, s,
                      static_cast<const uint4*>(src), n8, static_cast<uint4*>(dst),
                      static_cast<const uint16_t*>(src) + n8 * 8, static_cast<int>(n - n8 * 8),
-                     static_cast<uint16_t*>(dst) + n8 * 8);
+                     static_cast<uint16_t*>(dst) + n8 * 8, reinterpret_cast<unsigned long long*>(report));
   return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ size_t ffn_workspace_bytes(int dtype);
 size_t ffn_mfma_workspace_bytes();
 
 // W2 in fp16 for the down-projection (grouped_ffn.hip): n bf16 values -> fp16, RNE.
-hipError_t launch_bf16_to_f16(const void* src, int64_t n, void* dst, hipStream_t s);
+hipError_t launch_bf16_to_f16(const void* src, int64_t n, void* dst, uint64_t* report, hipStream_t s);
 hipError_t launch_down_f16w(const void* h, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
                             int64_t d_ff, const void* w2_f16, float* y_perm, void* ws, hipStream_t s);
 

@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
         "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
         "moe_ffn_workspace_bytes": (SZ, [I32]),
         "moe_frag_rows": (I64, [I64, I32]),
-        "moe_weights_bf16_to_f16": (ctypes.c_int, [P, I64, P, P]),
+        "moe_weights_bf16_to_f16": (ctypes.c_int, [P, I64, P, P, P]),
         "moe_expert_down_f16w": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, P, SZ, P]),
         "moe_permute_frag": (ctypes.c_int, [P, I64, P, P, I32, I64, P, P]),
         "moe_expert_up_gelu_frag": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P]),
@@ -324,11 +324,16 @@ def moe_expert_down_frag(h_frag, offsets, w2_f16, rows_max: int, y_perm=None, wo
     return y_perm
 
 
-def moe_weights_bf16_to_f16(w, out=None, stream=None):
+def moe_weights_bf16_to_f16(w, out=None, report=None, stream=None):
     """fp16 copy of a bf16 weight (round to nearest even), for the
-    down-projection's fp16 products."""
+    down-projection's fp16 products. `report`: an int64 device tensor of two
+    elements to receive the counts of values that lost bits and of values
+    that became +-inf."""
     out = torch.empty(w.shape, dtype=torch.float16, device=w.device) if out is None else out
-    _check(lib().moe_weights_bf16_to_f16(_ptr(w), w.numel(), _ptr(out), _stream(stream)))
+    if report is not None and (report.dtype != torch.int64 or report.numel() < 2):
+        raise MoEError(-1, "report must be an int64 tensor of two elements")
+    _check(lib().moe_weights_bf16_to_f16(_ptr(w), w.numel(), _ptr(out), _ptr(report),
+                                         _stream(stream)))
     return out
 
 
@@ -484,7 +489,7 @@ class MoEBuffers:
     repeated forwards allocate nothing."""
 
     def __init__(self, T, d, d_ff, E, k, capacity, dtype, device, routed=True, want_probs=True,
-                 save_for_backward=False, frag=None):
+                 save_for_backward=False, frag=None, w2_f16=False):
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
         self.T, self.d, self.d_ff, self.E, self.k, self.capacity = T, d, d_ff, E, k, capacity
         self.rows_max = moe_rows_max(T, k, E, capacity)
@@ -505,9 +510,12 @@ class MoEBuffers:
         self.frag = bool(frag)
         self.x_perm = None if self.frag else z((R, d), dtype)
         self.x_frag = z((max(moe_frag_rows(self.rows_max, E), 1), d), dtype) if self.frag else None
-        # h in fragment order, allocated by the first forward that uses it
-        self.h_frag = None
-        self.h = z((R, d_ff), hidden_dtype(dtype))
+        # forwards that will pass W2 in fp16 (w2_f16) on the fragment-ordered
+        # path keep h in fragment order too when d_ff % 256 == 0: only that
+        # buffer is allocated, the row-major h is not
+        self.h_frag = (z((max(moe_frag_rows(self.rows_max, E), 1), d_ff), torch.float16)
+                       if self.frag and w2_f16 and d_ff % 256 == 0 else None)
+        self.h = z((R, d_ff), hidden_dtype(dtype)) if self.h_frag is None else None
         # the pre-activation, kept for the backward
         self.z = z((R, d_ff), hidden_dtype(dtype)) if save_for_backward else None
         self.lse = z((max(T, 1),), torch.float32) if (routed and save_for_backward) else None
@@ -536,15 +544,16 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     bf16 layers: moe_weights_bf16_to_f16(w2), prepared once; the
     down-projection then reads it instead of converting W2 in registers
     (y_perm bit for bit the same), and on the fragment-ordered path with
-    d_ff % 256 == 0, h stays in fragment order (bufs.h_frag) for a
-    down-projection that loads it straight into registers (bufs.h is then not
-    written)."""
+    d_ff % 256 == 0 and buffers made with w2_f16=True, h stays in fragment
+    order (bufs.h_frag) for a down-projection that loads it straight into
+    registers (bufs.h is then not allocated). Nothing here allocates when
+    `bufs` is given."""
     T, d = x.shape
     E, d_ff, _ = w1.shape
     routed = w_gate is not None
     if bufs is None:
         bufs = MoEBuffers(T, d, d_ff, E, k, capacity, x.dtype, x.device, routed,
-                          save_for_backward=save_for_backward)
+                          save_for_backward=save_for_backward, w2_f16=w2_f16 is not None)
     if routed:
         if temperature != 1.0 or noise is not None or bufs.lse is not None:
             moe_router_topk_ex(x, w_gate, bias, k, flags, temperature, noise,
@@ -572,16 +581,15 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
         moe_dispatch_plan(idx, E, capacity, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                           bufs.ws_dispatch, stream)
         moe_permute_frag(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_frag, stream)
-        if w2_f16 is not None and d_ff % 256 == 0:
+        if w2_f16 is not None and bufs.h_frag is not None:
             # h stays in fragment order between the two projections
-            if bufs.h_frag is None:
-                bufs.h_frag = torch.empty((max(moe_frag_rows(bufs.rows_max, E), 1), d_ff),
-                                          dtype=torch.float16, device=x.device)
             moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h_frag, True,
                                     stream)
             moe_expert_down_frag(bufs.h_frag, bufs.offsets, w2_f16, bufs.rows_max, bufs.y_perm,
                                  bufs.ws_ffn, stream)
         else:
+            if bufs.h is None:
+                raise MoEError(-1, "these buffers keep h in fragment order: pass w2_f16")
             moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, False, stream)
             down()
     else:

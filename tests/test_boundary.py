@@ -220,11 +220,12 @@ def test_fragment_path_argument_errors_and_sizes():
 
 def test_f16_weight_argument_errors():
     L = ops.lib()
-    # moe_weights_bf16_to_f16(w, n, w_f16, stream)
-    assert L.moe_weights_bf16_to_f16(FAKE, -1, FAKE, None) == -1
-    assert L.moe_weights_bf16_to_f16(None, 0, None, None) == 0
-    assert L.moe_weights_bf16_to_f16(None, 8, FAKE, None) == -1
-    assert L.moe_weights_bf16_to_f16(FAKE, 8, ctypes.c_void_p((1 << 20) + 2), None) == -6
+    # moe_weights_bf16_to_f16(w, n, w_f16, report, stream)
+    assert L.moe_weights_bf16_to_f16(FAKE, -1, FAKE, None, None) == -1
+    assert L.moe_weights_bf16_to_f16(None, 0, None, None, None) == 0
+    assert L.moe_weights_bf16_to_f16(None, 8, FAKE, None, None) == -1
+    assert L.moe_weights_bf16_to_f16(FAKE, 8, ctypes.c_void_p((1 << 20) + 2), None, None) == -6
+    assert L.moe_weights_bf16_to_f16(FAKE, 8, FAKE, ctypes.c_void_p((1 << 20) + 4), None) == -6
     # moe_expert_down_f16w(h, offsets, E, rows_max, d, d_ff, w2_f16, y_perm, ws, ws_bytes, stream)
     need = L.moe_ffn_workspace_bytes(1)
     assert L.moe_expert_down_f16w(FAKE, FAKE, 0, 10, 64, 128, FAKE, FAKE, None, 0, None) == -3

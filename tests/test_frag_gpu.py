@@ -131,6 +131,98 @@ def test_weights_bf16_to_f16_every_value():
     assert torch.equal(got[~nan].view(torch.int16), want[~nan].view(torch.int16))
 
 
+def _f16_flags(w_bf16: torch.Tensor):
+    """Host reference of the conversion report: (inexact, overflow) counts of
+    bf16 -> fp16 round to nearest even, from torch's CPU casts."""
+    f = w_bf16.float()
+    h = w_bf16.to(torch.float16).float()
+    fin = torch.isfinite(f)
+    over = fin & torch.isinf(h)
+    inexact = fin & ~torch.isinf(h) & (h != f)
+    return int(inexact.sum()), int(over.sum())
+
+
+def test_weights_bf16_to_f16_report_every_value():
+    """The report on all 65536 bf16 bit patterns (and a ragged tail): its two
+    counts equal the host's, and both follow the documented ranges: exact for
+    0 and 2^-17 <= |w| <= 65280, low bits lost below, +-inf from 65536 up."""
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    w = torch.cat([bits, bits[1000:1005]]).view(torch.bfloat16)
+    rep = torch.full((2,), -1, dtype=torch.int64, device="cuda:0")
+    ops.moe_weights_bf16_to_f16(w.to("cuda:0"), report=rep)
+    torch.cuda.synchronize()
+    got = tuple(int(v) for v in rep.cpu())
+    want = _f16_flags(w)
+    f = w.float().abs()
+    fin = torch.isfinite(f)
+    by_range = (int((fin & (f > 0) & (f < 2.0 ** -17)).sum()), int((fin & (f >= 65536.0)).sum()))
+    say("  report %s, host %s, by the documented ranges %s" % (got, want, by_range))
+    assert got == want == by_range
+
+
+def test_weights_bf16_to_f16_report_small_and_large_w2():
+    """W2 holding values of 2^-20 (with low bits that fp16 cannot hold) and
+    7e4 (beyond fp16): the report counts them, the converted values are the
+    round-to-nearest-even ones (2^-20 and +-inf), and a down-projection on
+    that W2 gives non-finite output exactly in the columns of the
+    overflowing weights of the rows that use them."""
+    g = torch.Generator().manual_seed(5)
+    E, d, d_ff = 2, 256, 512
+    w2 = (torch.randn(E, d, d_ff, generator=g) / d_ff ** 0.5).to(torch.bfloat16)
+    tiny = torch.tensor((1.0 + 2.0 ** -7) * 2.0 ** -20).to(torch.bfloat16)   # bits below 2^-24
+    w2[0, 3, 5] = tiny
+    w2[1, 200, 77] = -tiny
+    w2[1, 9, 300] = 7e4
+    w2[0, 100, 0] = -7e4
+    rep = torch.zeros(2, dtype=torch.int64, device="cuda:0")
+    w2h = ops.moe_weights_bf16_to_f16(w2.to("cuda:0"), report=rep)
+    torch.cuda.synchronize()
+    inexact, over = _f16_flags(w2)
+    assert tuple(int(v) for v in rep.cpu()) == (inexact, over) and over == 2 and inexact >= 2
+    hh = w2h.cpu()
+    assert float(hh[0, 3, 5]) == 2.0 ** -20 and float(hh[1, 200, 77]) == -(2.0 ** -20)
+    assert torch.isinf(hh[1, 9, 300]) and hh[1, 9, 300] > 0
+    assert torch.isinf(hh[0, 100, 0]) and hh[0, 100, 0] < 0
+    # down-projection on that W2: rows of expert 1 are non-finite in column 9,
+    # rows of expert 0 in column 100, every other value finite
+    rows = [40, 33]
+    off = torch.tensor([0, rows[0], rows[0] + rows[1]], dtype=torch.int32, device="cuda:0")
+    h = (torch.rand(sum(rows), d_ff, generator=g) + 0.5).to(torch.float16).to("cuda:0")
+    y = ops.moe_expert_down_f16w(h, off, w2h, sum(rows))
+    torch.cuda.synchronize()
+    bad = ~torch.isfinite(y[:sum(rows)].cpu())
+    want = torch.zeros_like(bad)
+    want[:rows[0], 100] = True
+    want[rows[0]:, 9] = True
+    assert torch.equal(bad, want)
+
+
+def test_hidden_overflow_gives_nonfinite_rows():
+    """h is fp16: a row whose pre-activation reaches 65520 or more stores
+    +-inf there, as documented, and only that token's output is non-finite."""
+    from mixture_experts_layer_49_amd import inputs as I
+    from parity_helpers import dev
+    cfg = I.small("h-overflow", T=64, d=256, d_ff=256, E=2, k=1, cf=0.0, seed=77)
+    inp = I.make_inputs(cfg)
+    x = dev(inp["x"], "bf16")
+    w1 = dev(inp["w1"], "bf16")
+    # token 7: x = 3e3 * sign(W1[e, 0, :]) for both experts, so that
+    # z[., 0] = 3e3 * sum |W1[e, 0, :]| is far above 65520
+    row = torch.sign(w1[:, 0, :].float()).sum(0)
+    x[7] = (3e3 * torch.where(row >= 0, 1.0, -1.0)).to(torch.bfloat16)
+    w1[1, 0] = w1[0, 0]
+    w2 = dev(inp["w2"], "bf16")
+    idx = torch.randint(0, 2, (cfg.T, 1), dtype=torch.int32, device="cuda:0")
+    wt = torch.ones(cfg.T, 1, device="cuda:0")
+    for frag in (False, True):
+        b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, 1, -1, x.dtype, x.device, routed=False,
+                           frag=frag)
+        ops.moe_forward(x, w1, w2, 1, -1, topk_idx=idx, topk_w=wt, bufs=b)
+        torch.cuda.synchronize()
+        fin = torch.isfinite(b.y.cpu()).all(dim=1)
+        assert not fin[7] and fin[torch.arange(cfg.T) != 7].all()
+
+
 @pytest.mark.parametrize("counts,d,d_ff", [([37, 0, 300, 1, 64], 512, 776),
                                            ([150, 290], 1024, 8200),
                                            ([1283, 1250, 1301, 1222, 1279, 1340, 1197, 1368], 4096, 16384)])
@@ -154,10 +246,12 @@ def test_down_f16w_equals_in_register_conversion(counts, d, d_ff):
             "workspace %s: max|diff| %.3g" % (workspace is not None, (a[:R] - b[:R]).abs().max().item())
 
 
-@pytest.mark.parametrize("frag", [False, True])
-def test_forward_with_f16_w2_is_bit_identical(frag):
+@pytest.mark.parametrize("frag,hfrag", [(False, False), (True, False), (True, True)])
+def test_forward_with_f16_w2_is_bit_identical(frag, hfrag):
     """The layer forward given moe_weights_bf16_to_f16(W2) against the same
-    forward converting W2 in registers: the same y, bit for bit."""
+    forward converting W2 in registers: the same y, bit for bit (with h
+    row-major, and on the fragment-ordered path also with h kept in
+    fragment order)."""
     from mixture_experts_layer_49_amd import inputs as I
     from parity_helpers import dev
     cfg = I.small("f16w", T=600, d=256, d_ff=512, E=4, k=2, cf=1.25, seed=71)
@@ -166,8 +260,10 @@ def test_forward_with_f16_w2_is_bit_identical(frag):
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
     ys = []
     for w2h in (None, ops.moe_weights_bf16_to_f16(w2)):
-        b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, frag=frag)
+        b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, frag=frag,
+                           w2_f16=hfrag and w2h is not None)
         ops.moe_forward(x, w1, w2, cfg.k, C, w_gate=wg, bufs=b, w2_f16=w2h)
+        assert (b.h_frag is not None) == (hfrag and w2h is not None)
         torch.cuda.synchronize()
         ys.append(b.y.clone())
     assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32))
