@@ -7,11 +7,18 @@ A step is the whole forward -- gate + softmax + top-k, dispatch (index build +
 permute), grouped expert FFN (up-projection + GELU, down-projection), weighted
 combine, aux loss -- over one batch of synthetic tokens already resident in
 HBM. Default workload: large-experts-e8 (T=8192 tokens, d=4096,
-d_ff=16384, E=8, top-2, capacity factor 1.25, bf16).
+d_ff=16384, E=8, top-2, capacity factor 1.25, bf16); the receiver share
+ep8-receiver-share (8192 received rows, 8 local experts of the same size,
+Zipf(1.2) loads) is timed after it with the same steps and reported under
+"also".
 
-Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
-kernel (timed live with HIP events on the launch stream), a per-call
-breakdown, and the CPU oracle timed on this host as a baseline.
+Before the warm-up steps an untimed ramp runs until the clocks have settled
+(its length is in the line). Prints ONE JSON line: tokens/s, ms per step,
+the roofline of the dominant kernel (timed live with HIP events on the
+launch stream), the graphics clock and socket power sampled over the timed
+steps, a per-call breakdown, the HBM-bound calls again with cold caches
+next to a plain-read and a copy reference of the same bytes, and the CPU
+oracle timed on this host as a baseline.
 
 With --backward a step is one training step of the layer instead: the
 forward keeping what the backward needs, then the whole backward (combine^T,
@@ -47,6 +54,9 @@ def parse(argv=None):
     # (about 60 ms of work) reach the sustained state.
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large-experts-e8")
+    ap.add_argument("--also", default="ep8-receiver-share",
+                    help="comma-separated workloads also timed (same steps and warm-up) and "
+                         "reported under 'also'; 'none' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward + backward) instead of the forward")
@@ -289,6 +299,355 @@ def bench_backward(args, cfg, inp, ops, torch, np):
     return 0
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clock and socket power from the SMU's metrics
+    table (amdsmi) in a thread, while the timed steps run."""
+
+    def __init__(self):
+        self.samples, self.power, self.error = [], [], None
+        self._stop = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:   # no SMI on this host: the line says so
+            self._smi, self.error = None, "amdsmi unavailable: %s" % e
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clk = m.get("current_gfxclks")
+        vals = [v for v in clk if isinstance(v, (int, float)) and 0 < v < 10000] if isinstance(clk, list) else []
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [m["current_gfxclk"]]
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)):
+            pw = m.get("average_socket_power")
+        return (sum(vals) / len(vals) if vals else None), (pw if isinstance(pw, (int, float)) else None)
+
+    def __enter__(self):
+        import threading
+
+        if self._smi is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    c, p = self._read()
+                except Exception as e:
+                    self.error = "amdsmi read failed: %s" % e
+                    return
+                if c is not None:
+                    self.samples.append(c)
+                if p is not None:
+                    self.power.append(p)
+                self._stop.wait(0.001)
+
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        if self._stop is not None:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"sclk_mhz": None, "samples": 0, "source": self.error or "no samples"}
+        s = sorted(self.samples)
+        return {"sclk_mhz": sum(s) / len(s), "sclk_mhz_min": s[0], "sclk_mhz_max": s[-1],
+                "samples": len(s), "socket_power_w": (sum(self.power) / len(self.power)
+                                                      if self.power else None),
+                "source": "amdsmi gpu_metrics current_gfxclk(s), sampled every ~1 ms over the "
+                          "timed steps and ~300 ms more of the same steps"}
+
+
+def clock_ramp(step, torch, stream, min_ms=400.0, max_ms=4000.0, window=5):
+    """Untimed steps until the clocks have settled: windows of `window` steps
+    until at least min_ms of work ran and three windows in a row agree to 1%
+    (at most max_ms). Returns what ran."""
+    times, total, n = [], 0.0, 0
+    while True:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(window):
+            step()
+        b.record(stream)
+        b.synchronize()
+        t = a.elapsed_time(b)
+        times.append(t / window)
+        total += t
+        n += window
+        settled = (len(times) >= 3 and abs(times[-1] - times[-2]) <= 0.01 * times[-1]
+                   and abs(times[-2] - times[-3]) <= 0.01 * times[-2])
+        if (total >= min_ms and settled) or total >= max_ms:
+            return {"steps": n, "ms": total, "settled": settled,
+                    "ms_per_step_first_last": [times[0], times[-1]]}
+
+
+def cold_us(fn, flush, torch, stream, reps=10):
+    """Median time of fn() with the caches flushed before each call (a plain
+    read of 1 GiB leaves the L2s and the 256 MiB infinity cache holding other,
+    clean lines: nothing has to be written back when the call's data comes
+    in)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for r in range(reps):
+        flush(r)
+        evs[r][0].record(stream)
+        fn()
+        evs[r][1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return t[len(t) // 2]
+
+
+def bench_lib():
+    """libmoe_bench.so: the streaming-read reference kernel."""
+    import ctypes
+
+    path = os.path.join(ROOT, "mixture_experts_layer_49_amd", "libmoe_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libmoe_bench.so is not built: run `python -m mixture_experts_layer_49_amd.build`")
+    L = ctypes.CDLL(path)
+    L.probe_stream_read.restype = ctypes.c_int
+    L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    return L
+
+
+def forward_workload(args, name, ops, torch, np, I, want_cpu):
+    """Times the layer forward on one workload; returns the result object."""
+    import ctypes
+
+    cfg = I.config(name)
+    t0 = time.perf_counter()
+    inp = I.make_inputs(cfg)
+    log("%s: inputs generated in %.1f s" % (name, time.perf_counter() - t0))
+
+    def dev(a, bf16):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf16 else t).to("cuda:0")
+
+    bf = cfg.dtype == "bf16"
+    x, w1, w2 = dev(inp["x"], bf), dev(inp["w1"], bf), dev(inp["w2"], bf)
+    wg = dev(inp["w_gate"], bf) if cfg.routed else None
+    bias = dev(inp["bias"], False) if cfg.routed and inp["bias"] is not None else None
+    given_idx = dev(inp["topk_idx"], False) if not cfg.routed else None
+    given_w = dev(inp["topk_w"], False) if not cfg.routed else None
+    C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed,
+                       w2_f16=bf)
+    # inference weight format: W2 in fp16, converted once (the kernels would
+    # otherwise round each W2 value to fp16 in registers on every step, the
+    # same way); the report counts values that lost bits or overflowed
+    w2_report = None
+    if bf:
+        rep = torch.zeros(2, dtype=torch.int64, device=x.device)
+        w2h = ops.moe_weights_bf16_to_f16(w2, report=rep)
+        w2_report = [int(v) for v in rep.cpu()]
+        del w2
+    else:
+        w2h = None
+    hfrag = b.h_frag
+    stream = torch.cuda.current_stream()
+
+    names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]
+
+    def k_router():
+        if cfg.routed:
+            ops.moe_router_topk(x, wg, bias, cfg.k, 0, True, b.topk_idx, b.topk_w, b.probs)
+
+    idx, w = (b.topk_idx, b.topk_w) if cfg.routed else (given_idx, given_w)
+
+    def k_plan():
+        ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
+
+    def k_permute():
+        if b.frag:
+            ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
+        else:
+            ops.moe_permute(x, b.src, b.offsets, b.rows_max, b.x_perm)
+
+    def k_up():
+        if hfrag is not None:
+            ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, hfrag, True)
+        elif b.frag:
+            ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, b.h)
+        else:
+            ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
+
+    def k_down():
+        if hfrag is not None:
+            ops.moe_expert_down_frag(hfrag, b.offsets, w2h, b.rows_max, b.y_perm, b.ws_ffn)
+        elif w2h is not None:
+            ops.moe_expert_down_f16w(b.h, b.offsets, w2h, b.rows_max, b.y_perm, b.ws_ffn)
+        else:
+            ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
+
+    def k_combine():
+        ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
+
+    def k_aux():
+        if cfg.routed:
+            ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
+
+    kernels = [k_router, k_plan, k_permute, k_up, k_down, k_combine, k_aux]
+
+    def step(ev=None):
+        for i, kern in enumerate(kernels):
+            if ev is not None:
+                ev[i].record(stream)
+            kern()
+        if ev is not None:
+            ev[len(kernels)].record(stream)
+
+    copy_probe(args, torch, x.device)
+    ramp = clock_ramp(step, torch, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # one set of boundary events per timed step, all on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with ClockSampler() as clk:
+        start.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        # the SMU's table refreshes every few tens of ms: keep sampling over
+        # about 300 ms more of the same steps (untimed)
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
+    us = dict(zip(names, (per * 1e3).tolist()))
+
+    counts = b.counts.cpu().numpy()
+    R = int(b.offsets.cpu().numpy()[-1])
+    T, d, dff, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
+    s = 2 if bf else 4
+    flops_up = 2.0 * R * d * dff
+    flops_down = 2.0 * R * dff * d
+    hbm = {"router": T * d * s + E * d * s + T * k * 8 + T * E * 4 if cfg.routed else 0,
+           "permute": 2 * R * d * s + R * 4,
+           "combine": R * d * 4 + T * d * 4 + T * k * 8}
+    breakdown = {
+        "router": {"us": us["router"]},
+        # the plan is integer work of a few hundred KB: latency, reported in us only
+        "dispatch_plan": {"us": us["dispatch_plan"], "bytes": T * k * 4 * 2 + R * 4 + 2 * E * 4},
+        "permute": {"us": us["permute"]},
+        "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (us["up_gelu"] * 1e-6) / 1e12},
+        "down": {"us": us["down"], "TFLOP/s": flops_down / (us["down"] * 1e-6) / 1e12},
+        "combine": {"us": us["combine"]},
+        "aux": {"us": us["aux"]},
+    }
+    for key, nb in hbm.items():
+        if nb and us[key] > 0:
+            breakdown[key].update(bytes=nb, **{"GB/s": nb / (us[key] * 1e-6) / 1e9})
+            breakdown[key]["hbm_frac"] = breakdown[key]["GB/s"] / PEAK_HBM_GBS
+    for key in ("up_gelu", "down"):
+        breakdown[key]["mfma_frac"] = breakdown[key]["TFLOP/s"] / PEAK_MFMA_TFLOPS
+
+    # the same HBM-bound kernels with cold caches, and the plain-read and
+    # copy references for the same bytes
+    L = bench_lib()
+    grid = 4096
+    sink = torch.empty(grid, dtype=torch.int32, device=x.device)
+    sptr, strm = ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
+
+    def stream_read(ptr, nbytes):
+        if L.probe_stream_read(ctypes.c_void_p(ptr), nbytes, sptr, grid, strm) != 0:
+            raise RuntimeError("probe_stream_read failed")
+
+    flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=x.device)
+    torch.cuda.synchronize()
+    flush = lambda r: stream_read(flush_buf.data_ptr(), flush_buf.numel())
+    cold = {}
+    for key, fn in (("router", k_router), ("permute", k_permute), ("combine", k_combine)):
+        if not hbm[key]:
+            continue
+        t = cold_us(fn, flush, torch, stream)
+        cold[key] = {"us": t, "bytes": hbm[key], "GB/s": hbm[key] / (t * 1e-6) / 1e9,
+                     "hbm_frac": hbm[key] / (t * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "in_pipeline_us": us[key]}
+    xb = x.numel() * x.element_size()
+    t = cold_us(lambda: stream_read(x.data_ptr(), xb), flush, torch, stream)
+    cold["read_floor"] = {"us": t, "bytes": xb, "GB/s": xb / (t * 1e-6) / 1e9,
+                          "hbm_frac": xb / (t * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                          "what": "plain streaming read of x (16-byte loads, 8 in flight per thread, "
+                                  "%d workgroups) after the same flush" % grid}
+    if "router" in cold:
+        cold["router"]["over_read_floor"] = cold["router"]["us"] / t
+    half = R * d * s
+    if half:
+        ca = torch.empty(half, dtype=torch.uint8, device=x.device)
+        cb = torch.empty_like(ca)
+        t = cold_us(lambda: cb.copy_(ca), flush, torch, stream)
+        cold["copy_floor"] = {"us": t, "bytes": 2 * half, "GB/s": 2 * half / (t * 1e-6) / 1e9,
+                              "hbm_frac": 2 * half / (t * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                              "what": "torch copy_ of the permute's bytes (R d s read + written) "
+                                      "after the same flush"}
+        cold["permute"]["over_copy_floor"] = cold["permute"]["us"] / t
+        del ca, cb
+    del flush_buf
+
+    dom = "up_gelu" if us["up_gelu"] >= us["down"] else "down"
+    dom_frag = b.frag and (dom == "up_gelu" or hfrag is not None)
+    dom_which = ("up" if dom == "up_gelu" else
+                 "down" if hfrag is not None or w2h is None else "down_f16w")
+    dom_kernel = ("frag_gemm_kernel<%s>" % ("up_frag" if hfrag is not None else "up_rows")
+                  if dom_frag and dom == "up_gelu" else
+                  "frag_gemm_kernel<down>" if dom_frag else "grouped_gemm_mfma<%s>" % dom_which)
+    achieved = breakdown[dom]["TFLOP/s"]
+    ffn_tflops = (flops_up + flops_down) / ((us["up_gelu"] + us["down"]) * 1e-6) / 1e12
+    clock = clk.summary()
+    out = {
+        "value": T * args.steps / (total_ms * 1e-3),
+        "unit": "tokens/s" if cfg.routed else "rows/s",
+        "ms_per_step": ms_per_step,
+        "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
+                   "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
+                   "max_over_mean_load": float(counts.max() / counts.mean()),
+                   "activation_layout": ("fragment-ordered x and h" if hfrag is not None else
+                                         "fragment-ordered x" if b.frag else "row-major"),
+                   "w2_storage": ("fp16, converted once from the bf16 weights (round to nearest "
+                                  "even; %d values lost low bits, %d overflowed)" % tuple(w2_report)
+                                  if bf else "f32"),
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
+                     "traffic": measured_traffic(dom_which, cfg.name,
+                                                 "gemm_frag" if dom_frag else "gemm_mfma"),
+                     "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
+                     "launch_us": us[dom]},
+        "ffn_mfma_frac": ffn_tflops / PEAK_MFMA_TFLOPS,
+        "clock": clock,
+        "ramp": ramp,
+        "breakdown": breakdown,
+        "hbm_cold": cold,
+    }
+    if clock.get("sclk_mhz"):
+        # the same fraction against the MFMA peak at the clock measured over the steps
+        out["roofline"]["frac_at_measured_sclk"] = achieved / (PEAK_MFMA_TFLOPS * clock["sclk_mhz"] / 2400.0)
+    if want_cpu:
+        log("timing the CPU oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(inp, cfg)
+    del b, x, w1, w2h, inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -305,165 +664,24 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    cfg = I.config(args.workload)
-    t0 = time.perf_counter()
-    inp = I.make_inputs(cfg)
-    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
     if args.backward:
+        cfg = I.config(args.workload)
+        t0 = time.perf_counter()
+        inp = I.make_inputs(cfg)
+        log("inputs generated in %.1f s" % (time.perf_counter() - t0))
         return bench_backward(args, cfg, inp, ops, torch, np)
 
-    def dev(a, bf16):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        return (t.view(torch.int16).view(torch.bfloat16) if bf16 else t).to("cuda:0")
-
-    bf = cfg.dtype == "bf16"
-    x, w1, w2 = dev(inp["x"], bf), dev(inp["w1"], bf), dev(inp["w2"], bf)
-    wg = dev(inp["w_gate"], bf) if cfg.routed else None
-    bias = dev(inp["bias"], False) if cfg.routed and inp["bias"] is not None else None
-    given_idx = dev(inp["topk_idx"], False) if not cfg.routed else None
-    given_w = dev(inp["topk_w"], False) if not cfg.routed else None
-    C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
-    b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed,
-                       w2_f16=bf)
-    # inference weight format: W2 in fp16, converted once (the kernels would
-    # otherwise convert each W2 value in registers on every step, the same way)
-    w2h = ops.moe_weights_bf16_to_f16(w2) if bf else None
-    # fragment-ordered path: h stays in fragment order for the down-projection
-    hfrag = b.h_frag
-    stream = torch.cuda.current_stream()
-
-    names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]
-    # one set of boundary events per timed step, all on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
-
-    def step(ev=None):
-        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
-        rec(0)
-        if cfg.routed:
-            ops.moe_router_topk(x, wg, bias, cfg.k, 0, True, b.topk_idx, b.topk_w, b.probs)
-            idx, w = b.topk_idx, b.topk_w
-        else:
-            idx, w = given_idx, given_w
-        rec(1)
-        ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
-        rec(2)
-        if hfrag is not None:
-            ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
-            rec(3)
-            ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, hfrag, True)
-            rec(4)
-            ops.moe_expert_down_frag(hfrag, b.offsets, w2h, b.rows_max, b.y_perm, b.ws_ffn)
-            rec(5)
-            ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
-            rec(6)
-            if cfg.routed:
-                ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
-            rec(7)
-            return
-        if b.frag:
-            ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
-            rec(3)
-            ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, b.h)
-        else:
-            ops.moe_permute(x, b.src, b.offsets, b.rows_max, b.x_perm)
-            rec(3)
-            ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
-        rec(4)
-        if w2h is not None:
-            ops.moe_expert_down_f16w(b.h, b.offsets, w2h, b.rows_max, b.y_perm, b.ws_ffn)
-        else:
-            ops.moe_expert_down(b.h, b.offsets, w2, b.rows_max, b.y_perm, b.ws_ffn)
-        rec(5)
-        ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
-        rec(6)
-        if cfg.routed:
-            ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
-        rec(7)
-
-    copy_probe(args, torch, x.device)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
-
-    counts = b.counts.cpu().numpy()
-    R = int(b.offsets.cpu().numpy()[-1])
-    T, d, dff, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
-    s = 2 if bf else 4
-    flops_up = 2.0 * R * d * dff
-    flops_down = 2.0 * R * dff * d
-    bytes_router = T * d * s + E * d * s + T * k * 8 + T * E * 4 if cfg.routed else 0
-    bytes_plan = T * k * 4 * 2 + R * 4 + 2 * E * 4
-    bytes_permute = 2 * R * d * s + R * 4
-    bytes_combine = R * d * 4 + T * d * 4 + T * k * 8
-    bytes_aux = T * E * 4 if cfg.routed else 0
-    us = dict(zip(names, (per * 1e3).tolist()))
-    breakdown = {
-        "router": {"us": us["router"], "GB/s": bytes_router / (per[0] * 1e-3) / 1e9 if per[0] else None},
-        # the plan is integer work of a few hundred KB: latency, reported in us only
-        "dispatch_plan": {"us": us["dispatch_plan"], "bytes": bytes_plan},
-        "permute": {"us": us["permute"], "GB/s": bytes_permute / (per[2] * 1e-3) / 1e9},
-        "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (per[3] * 1e-3) / 1e12},
-        "down": {"us": us["down"], "TFLOP/s": flops_down / (per[4] * 1e-3) / 1e12},
-        "combine": {"us": us["combine"], "GB/s": bytes_combine / (per[5] * 1e-3) / 1e9},
-        "aux": {"us": us["aux"]},
-    }
-    for key, v in breakdown.items():
-        if "GB/s" in v and v["GB/s"] is not None:
-            v["hbm_frac"] = v["GB/s"] / PEAK_HBM_GBS
-        if "TFLOP/s" in v:
-            v["mfma_frac"] = v["TFLOP/s"] / PEAK_MFMA_TFLOPS
-    dom = "up_gelu" if per[3] >= per[4] else "down"
-    dom_frag = b.frag and (dom == "up_gelu" or hfrag is not None)
-    dom_which = ("up" if dom == "up_gelu" else
-                 "down" if hfrag is not None or w2h is None else "down_f16w")
-    dom_kernel = ("frag_gemm_kernel<%s>" % ("up_frag" if hfrag is not None else "up_rows")
-                  if dom_frag and dom == "up_gelu" else
-                  "frag_gemm_kernel<down>" if dom_frag else "grouped_gemm_mfma<%s>" % dom_which)
-    achieved = breakdown[dom]["TFLOP/s"]
-    ffn_tflops = (flops_up + flops_down) / ((per[3] + per[4]) * 1e-3) / 1e12
-
-    out = {
-        "metric": METRIC,
-        "value": T * args.steps / (total_ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if bf else "f32",
-        "data": "synthetic (seeded; inputs resident in HBM before timing)",
-        "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
-                   "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
-                   "max_over_mean_load": float(counts.max() / counts.mean()),
-                   "activation_layout": ("fragment-ordered x and h" if hfrag is not None else
-                                         "fragment-ordered x" if b.frag else "row-major"),
-                   "w2_storage": "fp16 (converted once from the bf16 weights, exact)" if bf else "f32",
-                   "parallelism": "single GPU"},
-        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
-                     "traffic": measured_traffic(dom_which, cfg.name,
-                                                 "gemm_frag" if dom_frag else "gemm_mfma"),
-                     "flops_per_launch": flops_up if dom == "up_gelu" else flops_down,
-                     "launch_us": us[dom]},
-        "ffn_mfma_frac": ffn_tflops / PEAK_MFMA_TFLOPS,
-        "breakdown": breakdown,
-    }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(inp, cfg)
+    res = forward_workload(args, args.workload, ops, torch, np, I, not args.no_cpu_baseline)
+    out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if I.config(args.workload).dtype == "bf16" else "f32",
+           "data": "synthetic (seeded; inputs resident in HBM before timing)"}
+    out.update(res)
+    also = [n for n in args.also.split(",") if n and n != "none" and n != args.workload]
+    for name in also:
+        # the second target workload, same steps and warm-up, under its own key
+        out.setdefault("also", {})[name] = forward_workload(args, name, ops, torch, np, I, False)
     print(json.dumps(out))
     return 0
 

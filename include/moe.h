@@ -205,9 +205,10 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
  * registers before the fp16 x fp16 products, this does it once up front).
  * moe_weights_bf16_to_f16: w_f16[i] = fp16(w[i]) for i < n, round to nearest
  *   even, the same rounding the kernels apply. It is exact for 0 and for
- *   2^-17 <= |w| <= 65280; smaller values lose low bits in the fp16
- *   subnormal range (down to 0 below 2^-25), finite values of magnitude
- *   65536 and above become +-inf, infinities and NaNs stay what they are.
+ *   2^-17 <= |w| <= 65280; below 2^-17 only multiples of fp16's subnormal
+ *   step 2^-24 are kept exactly (the rest lose low bits, and nonzero values
+ *   under 2^-25 round to 0), finite values of magnitude 65536 and above
+ *   become +-inf, infinities and NaNs stay what they are.
  *   16-byte aligned device pointers. `report` (nullable, device, 8-byte
  *   aligned, two counters): when given, report[0] = how many finite nonzero
  *   values lost bits, report[1] = how many finite values became +-inf; the

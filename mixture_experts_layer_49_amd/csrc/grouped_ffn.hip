@@ -15,7 +15,7 @@
 // about eight-fold; the down-projection then multiplies fp16 by fp16, W2's
 // bf16 values being rounded to fp16 (nearest even) on their way into LDS.
 // That rounding is exact for 2^-17 <= |w| <= 65280 and for 0: smaller values
-// lose low bits (fp16 subnormals), larger finite ones become +-inf. h itself
+// may lose low bits (fp16 subnormals), larger finite ones become +-inf. h itself
 // saturates the same way: |gelu(z)| >= 65520 is stored as +-inf, and the
 // output rows that use it are then inf or NaN.
 //
