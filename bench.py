@@ -15,8 +15,9 @@ Zipf(1.2) loads) is timed after it with the same steps and reported under
 Before the warm-up steps an untimed ramp runs until the clocks have settled
 (its length is in the line). Prints ONE JSON line: tokens/s, ms per step,
 the roofline of the dominant kernel (timed live with HIP events on the
-launch stream), the graphics clock and socket power sampled over the timed
-steps, a per-call breakdown, the HBM-bound calls again with cold caches
+launch stream), the graphics clock under the dominant GEMM (from its
+profile) and right after the GEMMs (a live probe), a per-call
+breakdown, the HBM-bound calls again with cold caches
 next to a plain-read and a copy reference of the same bytes, and the CPU
 oracle timed on this host as a baseline.
 
@@ -60,6 +61,10 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward + backward) instead of the forward")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="time the vendor library's dense bf16 GEMM (torch.matmul -> hipBLASLt) on the "
+                         "workload's expert-GEMM shape (all kept rows as one M) instead of the layer: a "
+                         "reference for the clock and matrix-core busy fraction, not the metric")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps, as a "
                          "known-size reference for memory-traffic counters")
@@ -79,28 +84,39 @@ GEMM_SOURCES = {
 }
 
 
-def measured_traffic(which: str, workload: str, family: str = "gemm_mfma"):
-    """HBM bytes per launch of one GEMM kind (up, down, dh, dx, dw2, dw1) from
-    the committed rocprofv3 summary (profiles/<family>_<which>_<workload>.md;
-    for gemm_mfma the GEMM kernel plus its split fix-up kernel when tiles
-    split, the two kernels the launch's HIP events time), or None when there
-    is none or the kernel source changed after the counters were taken."""
+def profile_fields(which: str, workload: str, family: str = "gemm_mfma") -> dict:
+    """Fields of the committed rocprofv3 summary of one GEMM kind (up, down,
+    dh, dx, dw2, dw1) on one workload (profiles/<family>_<which>_<workload>.md),
+    or {} when there is none or the kernel sources changed after it was made."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "%s_%s_%s.md" % (family, which, workload))
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     for line in open(path):
-        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+        if ":" in line and not line.startswith(("#", "|", "`")):
             key, val = line.split(":", 1)
-            fields[key] = val.strip()
+            fields[key.strip()] = val.strip()
     h = hashlib.sha256()
     for f in GEMM_SOURCES[family]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
-    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
-        return None
-    return float(fields["traffic_bytes_per_launch"])
+    return fields if fields.get("source_sha256") == h.hexdigest() else {}
+
+
+def measured_traffic(which: str, workload: str, family: str = "gemm_mfma"):
+    """HBM bytes per launch of one GEMM kind from its committed summary (for
+    gemm_mfma the GEMM kernel plus its split fix-up kernel when tiles split,
+    the two kernels the launch's HIP events time), or None."""
+    v = profile_fields(which, workload, family).get("traffic_bytes_per_launch")
+    return float(v) if v else None
+
+
+def profiled_sclk(which: str, workload: str, family: str = "gemm_mfma"):
+    """The graphics clock under one GEMM launch from its committed summary:
+    GRBM_GUI_ACTIVE cycles per XCD / the launch's duration, or None."""
+    v = profile_fields(which, workload, family).get("sclk_mhz_under_kernel")
+    return float(v) if v else None
 
 
 def cpu_baseline(inp, cfg):
@@ -299,73 +315,6 @@ def bench_backward(args, cfg, inp, ops, torch, np):
     return 0
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock and socket power from the SMU's metrics
-    table (amdsmi) in a thread, while the timed steps run."""
-
-    def __init__(self):
-        self.samples, self.power, self.error = [], [], None
-        self._stop = None
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init()
-            self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
-        except Exception as e:   # no SMI on this host: the line says so
-            self._smi, self.error = None, "amdsmi unavailable: %s" % e
-
-    def _read(self):
-        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-        clk = m.get("current_gfxclks")
-        vals = [v for v in clk if isinstance(v, (int, float)) and 0 < v < 10000] if isinstance(clk, list) else []
-        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
-            vals = [m["current_gfxclk"]]
-        pw = m.get("current_socket_power")
-        if not isinstance(pw, (int, float)):
-            pw = m.get("average_socket_power")
-        return (sum(vals) / len(vals) if vals else None), (pw if isinstance(pw, (int, float)) else None)
-
-    def __enter__(self):
-        import threading
-
-        if self._smi is None:
-            return self
-        self._stop = threading.Event()
-
-        def run():
-            while not self._stop.is_set():
-                try:
-                    c, p = self._read()
-                except Exception as e:
-                    self.error = "amdsmi read failed: %s" % e
-                    return
-                if c is not None:
-                    self.samples.append(c)
-                if p is not None:
-                    self.power.append(p)
-                self._stop.wait(0.001)
-
-        self._t = threading.Thread(target=run, daemon=True)
-        self._t.start()
-        return self
-
-    def __exit__(self, *a):
-        if self._stop is not None:
-            self._stop.set()
-            self._t.join()
-
-    def summary(self):
-        if not self.samples:
-            return {"sclk_mhz": None, "samples": 0, "source": self.error or "no samples"}
-        s = sorted(self.samples)
-        return {"sclk_mhz": sum(s) / len(s), "sclk_mhz_min": s[0], "sclk_mhz_max": s[-1],
-                "samples": len(s), "socket_power_w": (sum(self.power) / len(self.power)
-                                                      if self.power else None),
-                "source": "amdsmi gpu_metrics current_gfxclk(s), sampled every ~1 ms over the "
-                          "timed steps and ~300 ms more of the same steps"}
-
-
 def clock_ramp(step, torch, stream, min_ms=400.0, max_ms=4000.0, window=5):
     """Untimed steps until the clocks have settled: windows of `window` steps
     until at least min_ms of work ran and three windows in a row agree to 1%
@@ -387,6 +336,42 @@ def clock_ramp(step, torch, stream, min_ms=400.0, max_ms=4000.0, window=5):
         if (total >= min_ms and settled) or total >= max_ms:
             return {"steps": n, "ms": total, "settled": settled,
                     "ms_per_step_first_last": [times[0], times[-1]]}
+
+
+def measure_clock(step, kernels, torch, stream, device, n=10, ticks=1000):
+    """The graphics clock right after each expert GEMM: after the timed steps,
+    n more steps (untimed) with a clock probe (libmoe_bench.so: shader-clock
+    counter against the 100 MHz counter over `ticks` real-time ticks, one
+    wave) launched right after the up- and after the down-projection. The
+    clock recovers within microseconds once the matrix cores go idle, so this
+    reads higher than the clock under the GEMM itself (GRBM_GUI_ACTIVE in the
+    profiles)."""
+    import ctypes
+
+    L = bench_lib()
+    buf = torch.zeros(4 * n, dtype=torch.int64, device=device)
+    strm = ctypes.c_void_p(stream.cuda_stream)
+
+    def probe(slot):
+        ptr = ctypes.c_void_p(buf.data_ptr() + 16 * slot)
+        if L.probe_clock(ptr, ticks, strm) != 0:
+            raise RuntimeError("probe_clock failed")
+
+    for i in range(n):
+        for j, kern in enumerate(kernels):
+            kern()
+            if j == 3:
+                probe(2 * i)
+            elif j == 4:
+                probe(2 * i + 1)
+    torch.cuda.synchronize()
+    v = buf.cpu().numpy().reshape(2 * n, 2).astype(float)
+    mhz = sorted(100.0 * v[:, 0] / v[:, 1])
+    return {"sclk_mhz": mhz[len(mhz) // 2], "sclk_mhz_min": mhz[0], "sclk_mhz_max": mhz[-1],
+            "probes": len(mhz),
+            "source": "shader-clock counter / 100 MHz counter over 10 us, one wave launched right "
+                      "after each expert GEMM of %d untimed steps (median); the clock recovers "
+                      "once the matrix cores idle" % n}
 
 
 def cold_us(fn, flush, torch, stream, reps=10):
@@ -515,20 +500,13 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with ClockSampler() as clk:
-        start.record(stream)
-        for i in range(args.steps):
-            step(evs[i])
-        stop.record(stream)
-        torch.cuda.synchronize()
-        # the SMU's table refreshes every few tens of ms: keep sampling over
-        # about 300 ms more of the same steps (untimed)
-        t_end = time.perf_counter() + 0.3
-        while time.perf_counter() < t_end:
-            for _ in range(10):
-                step()
-            torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    after = measure_clock(step, kernels, torch, stream, x.device)
     ms_per_step = total_ms / args.steps
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
     us = dict(zip(names, (per * 1e3).tolist()))
@@ -611,7 +589,13 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
                   "frag_gemm_kernel<down>" if dom_frag else "grouped_gemm_mfma<%s>" % dom_which)
     achieved = breakdown[dom]["TFLOP/s"]
     ffn_tflops = (flops_up + flops_down) / ((us["up_gelu"] + us["down"]) * 1e-6) / 1e12
-    clock = clk.summary()
+    fam = "gemm_frag" if dom_frag else "gemm_mfma"
+    under = profiled_sclk(dom_which, cfg.name, fam)
+    clock = {"under_dominant_gemm_mhz": under,
+             "under_source": ("rocprofv3 GRBM_GUI_ACTIVE per XCD / duration, profiles/%s_%s_%s.md "
+                              "(same kernel sources)" % (fam, dom_which, cfg.name)
+                              if under else "no profile summary of the current kernel sources"),
+             "after_gemm_probe": after}
     out = {
         "value": T * args.steps / (total_ms * 1e-3),
         "unit": "tokens/s" if cfg.routed else "rows/s",
@@ -637,15 +621,47 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
         "breakdown": breakdown,
         "hbm_cold": cold,
     }
-    if clock.get("sclk_mhz"):
-        # the same fraction against the MFMA peak at the clock measured over the steps
-        out["roofline"]["frac_at_measured_sclk"] = achieved / (PEAK_MFMA_TFLOPS * clock["sclk_mhz"] / 2400.0)
+    if under:
+        # the same fraction against the MFMA peak at the clock the kernel ran at
+        out["roofline"]["sclk_mhz"] = under
+        out["roofline"]["frac_at_sclk"] = achieved / (PEAK_MFMA_TFLOPS * under / 2400.0)
     if want_cpu:
         log("timing the CPU oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(inp, cfg)
     del b, x, w1, w2h, inp
     torch.cuda.empty_cache()
     return out
+
+
+def dense_reference(args, I, torch) -> int:
+    """torch.matmul (hipBLASLt) on one dense bf16 GEMM of the expert GEMM's
+    size: M = the workload's kept rows (T k, capped by E C), N = d_ff, K = d,
+    with the same clock ramp and step counts; one JSON line."""
+    cfg = I.config(args.workload)
+    C = round(cfg.T / cfg.E * cfg.cf)
+    M = min(cfg.T * cfg.k, cfg.E * C) if cfg.routed else cfg.T
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    A = torch.randn(M, cfg.d, device="cuda:0", generator=g).to(torch.bfloat16)
+    B = torch.randn(cfg.d_ff, cfg.d, device="cuda:0", generator=g).to(torch.bfloat16)
+    Cm = torch.empty(M, cfg.d_ff, device="cuda:0", dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    step = lambda: torch.matmul(A, B.t(), out=Cm)
+    ramp = clock_ramp(step, torch, stream)
+    for _ in range(args.warmup):
+        step()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / args.steps * 1e3
+    fl = 2.0 * M * cfg.d * cfg.d_ff
+    print(json.dumps({"metric": "dense bf16 GEMM reference (torch.matmul, vendor library), not the layer",
+                      "value": fl / (us * 1e-6) / 1e12, "unit": "TFLOP/s", "frac": fl / (us * 1e-6) / 1e12 /
+                      PEAK_MFMA_TFLOPS, "us": us, "shape": {"M": M, "N": cfg.d_ff, "K": cfg.d},
+                      "steps": args.steps, "warmup": args.warmup, "ramp": ramp, "dtype": "bf16"}))
+    return 0
 
 
 def main(argv=None) -> int:
@@ -664,6 +680,8 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.dense_reference:
+        return dense_reference(args, I, torch)
     if args.backward:
         cfg = I.config(args.workload)
         t0 = time.perf_counter()

@@ -172,7 +172,8 @@ int moe_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
  * Hidden-activation storage: f32 when dtype is MOE_F32; IEEE fp16 (RNE) when
  * dtype is MOE_BF16 -- the same two bytes as bf16 with three more significand
  * bits; the down-projection then runs fp16 x fp16 with W2's bf16 values
- * converted exactly to fp16. This needs |h| and |W2| below 65504.
+ * rounded to fp16 (nearest even; where that is exact: moe_weights_bf16_to_f16).
+ * |h| or |W2| of 65520 or more become +-inf there, and nothing checks for it.
  * Products accumulate in float32. Rows >= offsets[E] are not touched.
  * Limits: d, d_ff <= 2^22.
  * workspace / workspace_bytes: device scratch of at least

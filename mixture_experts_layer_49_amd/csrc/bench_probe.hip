@@ -2,6 +2,13 @@
 // the layer's library): a plain streaming read, the reference that the
 // HBM-bound kernels' cold-cache rates are compared with.
 //
+// probe_clock: one wave reads the shader-clock counter (s_memtime) and the
+// constant 100 MHz counter (s_memrealtime) at its start and again after about
+// `ticks` real-time ticks; (clock delta / real delta) * 100 MHz is the
+// graphics clock over that interval. Launched right after a kernel, it sees
+// the clock that kernel ran at (the power manager moves it on a millisecond
+// scale).
+//
 // probe_stream_read: every byte of [p, p + bytes) is read once with 16-byte
 // vector loads, U of them in flight per thread, grid-stride over 16-byte
 // chunks; each thread folds what it read into one word (xor) and each
@@ -42,9 +49,32 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   }
 }
 
+__global__ __launch_bounds__(64) void clock_kernel(unsigned long long* __restrict__ out, int ticks) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long r1 = r0;
+  // bounded spin: ends after `ticks` real-time ticks or 2^22 rounds
+  for (int i = 0; i < (1 << 22) && r1 - r0 < static_cast<unsigned long long>(ticks); ++i) {
+    __builtin_amdgcn_s_sleep(2);
+    r1 = __builtin_amdgcn_s_memrealtime();
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = t1 - t0;
+    out[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// out: device, two uint64 words (shader-clock ticks, 100 MHz ticks).
+int probe_clock(unsigned long long* out, int ticks, hipStream_t stream) {
+  if (out == nullptr || ticks < 1) return -1;
+  hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, stream, out, ticks);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // Returns 0 on success, -1 on bad arguments, -5 when the launch failed.
 // sink: device, at least `grid` uint32 words.
