@@ -158,6 +158,24 @@ int moe_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
                 const int32_t* offsets, int32_t E, int64_t rows_max, void* x_perm,
                 hipStream_t stream);
 
+/* moe_dispatch_plan without a workspace, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (minus the workspace) and
+ * the same outputs, bit for bit, as moe_dispatch_plan. The per-chunk counts
+ * live in a scratch array the library holds on each GPU it runs on
+ * (moe_dispatch_plan_noalloc_scratch_bytes(), 1 MiB, kept until the process
+ * ends); the call itself allocates nothing. A plan that needs more than that
+ * (moe_dispatch_workspace_bytes(T, k, E) above it: for example more than
+ * 131072 tokens with 256 experts) is rejected with MOE_ERR_WORKSPACE before
+ * anything is enqueued. Every call on one GPU shares that GPU's scratch:
+ * calls that may overlap in time on one GPU (other streams, other threads)
+ * race and must be ordered by the caller. Nothing in the scratch needs
+ * clearing between calls. */
+int moe_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                              int64_t capacity, int32_t* counts, int32_t* offsets,
+                              int32_t* dest, int32_t* src, hipStream_t stream);
+size_t moe_dispatch_plan_noalloc_scratch_bytes(void);
+
 /* Grouped expert FFN over the expert-major segments given by `offsets`
  * (ETP page: up-projection w1 then down-projection w2, e.g.
  * 4096 -> 16384 -> 4096; EP tutorial 2.1 step 4: each expert computes on its

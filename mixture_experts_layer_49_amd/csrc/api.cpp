@@ -195,7 +195,7 @@ namespace {
 
 int check_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t* counts,
                int32_t* offsets, int32_t* dest, int32_t* src, const void* workspace,
-               size_t workspace_bytes) {
+               size_t workspace_bytes, bool own_scratch = false) {
   MOE_TRY(check_experts(E, k));
   if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
   if (T * k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T * k must stay below 2^31");
@@ -206,6 +206,14 @@ int check_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t
     MOE_NONNULL(dest);
     MOE_NONNULL(src);
     const size_t need = moe_dispatch_workspace_bytes(T, k, E);
+    if (own_scratch) {
+      if (need > moe::noalloc_scratch_bytes())
+        return fail(MOE_ERR_WORKSPACE,
+                    "this plan needs %zu bytes of scratch; the library's static scratch holds %zu "
+                    "(use moe_dispatch_plan with a workspace)",
+                    need, moe::noalloc_scratch_bytes());
+      return MOE_OK;
+    }
     if (workspace == nullptr || workspace_bytes < need)
       return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
                   workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
@@ -241,6 +249,17 @@ int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, 
                                               src, static_cast<int32_t*>(workspace), stream),
                     "moe_dispatch_plan launch");
 }
+
+int moe_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                              int64_t capacity, int32_t* counts, int32_t* offsets, int32_t* dest,
+                              int32_t* src, hipStream_t stream) {
+  MOE_TRY(check_plan(topk_idx, T, k, E, counts, offsets, dest, src, nullptr, 0, true));
+  return hip_status(moe::launch_dispatch_plan_noalloc(topk_idx, T, k, E, capacity, counts, offsets,
+                                                      dest, src, stream),
+                    "moe_dispatch_plan_noalloc launch");
+}
+
+size_t moe_dispatch_plan_noalloc_scratch_bytes(void) { return moe::noalloc_scratch_bytes(); }
 
 int moe_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
                 const int32_t* offsets, int32_t E, int64_t rows_max, void* x_perm,

@@ -16,6 +16,8 @@
 //             chunk base + earlier waves' popcounts + popcount of lower lanes.
 //             Kept iff position < C. dest and src follow.
 //   4. gather x_perm[r] = x[src[r]] with 16-byte vector copies.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -178,6 +180,65 @@ hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E
   hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
                      chunk_base, offsets, dest, src);
   return hipGetLastError();
+}
+
+// Scratch of moe_dispatch_plan_noalloc: the per-chunk counts and bases that
+// moe_dispatch_plan keeps in its caller's workspace, here in device memory the
+// library holds itself (1 MiB on every GPU it runs on, until the process
+// ends). Host code never passes `scratch` itself to a kernel: on the host that
+// name stands for a host-side shadow, not a device address. The device
+// address of each GPU's copy is looked up once per device (below) and used
+// from then on.
+constexpr size_t kNoAllocInts = size_t{1} << 18;
+static __device__ __align__(256) int32_t scratch[kNoAllocInts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the GPU that `s` launches on, looked up
+// with that device current on the first call for it.
+hipError_t noalloc_scratch(hipStream_t s, int32_t** out) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return kNoAllocInts * sizeof(int32_t); }
+
+hipError_t launch_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                        int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                                        hipStream_t s) {
+  if (dispatch_ws_ints(T, E) > kNoAllocInts) return hipErrorInvalidValue;   // the C ABI checks first
+  int32_t* ws = nullptr;
+  if (T > 0) {
+    const hipError_t e = noalloc_scratch(s, &ws);
+    if (e != hipSuccess) return e;
+  }
+  // every scratch word the plan reads is written earlier in the same call
+  // (chunk counts by the histogram, bases by the scan): nothing to clear
+  return launch_dispatch_plan(topk_idx, T, k, E, cap, counts, offsets, dest, src, ws, s);
 }
 
 hipError_t launch_permute(const void* x, int64_t d, int elem_bytes, const int32_t* src,

@@ -111,6 +111,11 @@ hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T,
                            float alpha, float* loss, double* ws, hipStream_t s);
 
 size_t dispatch_ws_ints(int64_t T, int E);
+// The plan on the library's own per-GPU scratch (dispatch.hip).
+size_t noalloc_scratch_bytes();
+hipError_t launch_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                        int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                                        hipStream_t s);
 size_t aux_ws_doubles(int64_t T, int E);
 
 // Backward (backward.hip). Gradient storage of a layer: bf16 for dtype 1, f32

@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
-           "moe_dispatch", "moe_dispatch_plan", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
+           "moe_dispatch", "moe_dispatch_plan", "moe_dispatch_plan_noalloc",
+           "moe_dispatch_plan_noalloc_scratch_bytes", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag",
            "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_expert_down_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
            "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "moe_dispatch_workspace_bytes": (SZ, [I64, I32, I32]),
         "moe_dispatch": (ctypes.c_int, [P, I64, I32, I32, I64, P, I64, I32, P, P, P, P, P, P, SZ, P]),
         "moe_dispatch_plan": (ctypes.c_int, [P, I64, I32, I32, I64, P, P, P, P, P, SZ, P]),
+        "moe_dispatch_plan_noalloc": (ctypes.c_int, [P, I64, I32, I32, I64, P, P, P, P, P]),
+        "moe_dispatch_plan_noalloc_scratch_bytes": (SZ, []),
         "moe_permute": (ctypes.c_int, [P, I64, I32, P, P, I32, I64, P, P]),
         "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P, SZ, P]),
         "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
@@ -229,6 +232,20 @@ def moe_dispatch_plan(topk_idx, E: int, capacity: int, counts=None, offsets=None
                                    _ptr(dest), _ptr(src), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return counts, offsets, dest, src
+
+
+def moe_dispatch_plan_noalloc(topk_idx, E: int, capacity: int, counts, offsets, dest, src,
+                              stream=None):
+    """moe_dispatch_plan on the library's own scratch: every output buffer is
+    the caller's and nothing is allocated here or in the library."""
+    T, k = topk_idx.shape
+    _check(lib().moe_dispatch_plan_noalloc(_ptr(topk_idx), T, k, E, capacity, _ptr(counts),
+                                           _ptr(offsets), _ptr(dest), _ptr(src), _stream(stream)))
+    return counts, offsets, dest, src
+
+
+def moe_dispatch_plan_noalloc_scratch_bytes() -> int:
+    return lib().moe_dispatch_plan_noalloc_scratch_bytes()
 
 
 def moe_permute(x, src, offsets, rows_max: int, x_perm=None, stream=None):

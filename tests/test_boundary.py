@@ -147,6 +147,17 @@ def test_plan_and_permute_argument_errors():
     assert plan(9, ctypes.c_void_p((1 << 20) + 2)) == -6
     a = list(ok); a[1] = 0; a[0] = None; a[7] = None; a[8] = None; a[9] = None; a[10] = 0; a[5] = None
     assert L.moe_dispatch_plan(*a) == -1         # T == 0 still needs counts and offsets
+    # moe_dispatch_plan_noalloc(topk_idx, T, k, E, capacity, counts, offsets, dest, src, stream):
+    # the same checks without a workspace; a plan beyond the static scratch is
+    # refused before anything is enqueued
+    assert L.moe_dispatch_plan_noalloc_scratch_bytes() == 1 << 20
+    assert L.moe_dispatch_plan_noalloc(FAKE, 100, 2, 0, 30, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_dispatch_plan_noalloc(FAKE, 100, 9, 8, 30, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert L.moe_dispatch_plan_noalloc(FAKE, -1, 2, 8, 30, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert L.moe_dispatch_plan_noalloc(None, 100, 2, 8, 30, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert L.moe_dispatch_plan_noalloc(FAKE, 100, 2, 8, 30, FAKE, FAKE, None, FAKE, None) == -1
+    assert L.moe_dispatch_plan_noalloc(FAKE, 131073, 2, 256, 30, FAKE, FAKE, FAKE, FAKE, None) == -4
+    assert L.moe_dispatch_workspace_bytes(131072, 2, 256) == 1 << 20   # the largest that fits
     # moe_permute(x, d, dtype, src, offsets, E, rows_max, x_perm, stream)
     assert L.moe_permute(FAKE, 64, 1, FAKE, FAKE, 8, 10, FAKE, None) != -1
     assert L.moe_permute(FAKE, 60, 1, FAKE, FAKE, 8, 10, FAKE, None) == -6
