@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB names another build of the same library (the host-sanitizer build
+# libmoe_san.so, for instance); the default is the in-tree libmoe.so.
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_PKG, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_RENORM = 0x1

@@ -262,9 +262,8 @@ def test_layer_no_drop_equals_dense_masked_sum(k):
     logits = torch.nn.functional.linear(x, torch.from_numpy(inp["w_gate"]).double())
     p = torch.softmax(logits, dim=1)
     y = torch.zeros(T, d, dtype=torch.float64)
-    l32 = logits.float()
     for t in range(T):
-        chosen = sorted(range(E), key=lambda e: (-float(l32[t, e]), e))[:k]
+        chosen = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
         for e in chosen:
             h = torch.nn.functional.gelu(x[t] @ torch.from_numpy(inp["w1"][e]).double().T,
                                          approximate="tanh")
