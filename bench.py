@@ -441,7 +441,7 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     hfrag = b.h_frag
     stream = torch.cuda.current_stream()
 
-    names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine", "aux"]
+    names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine"]
 
     def k_router():
         if cfg.routed:
@@ -450,7 +450,12 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     idx, w = (b.topk_idx, b.topk_w) if cfg.routed else (given_idx, given_w)
 
     def k_plan():
-        ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
+        # routed layers: the plan with the aux loss folded in (moe_dispatch_plan_aux)
+        if cfg.routed:
+            ops.moe_dispatch_plan_aux(idx, b.probs, cfg.E, C, cfg.alpha, b.counts, b.offsets, b.dest, b.src,
+                                      b.loss, b.ws_plan_aux)
+        else:
+            ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
 
     def k_permute():
         if b.frag:
@@ -477,11 +482,7 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     def k_combine():
         ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
 
-    def k_aux():
-        if cfg.routed:
-            ops.moe_aux_loss(b.probs, b.counts, cfg.k, cfg.alpha, b.loss, b.ws_aux)
-
-    kernels = [k_router, k_plan, k_permute, k_up, k_down, k_combine, k_aux]
+    kernels = [k_router, k_plan, k_permute, k_up, k_down, k_combine]
 
     def step(ev=None):
         for i, kern in enumerate(kernels):
@@ -522,13 +523,14 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
            "combine": R * d * 4 + T * d * 4 + T * k * 8}
     breakdown = {
         "router": {"us": us["router"]},
-        # the plan is integer work of a few hundred KB: latency, reported in us only
-        "dispatch_plan": {"us": us["dispatch_plan"], "bytes": T * k * 4 * 2 + R * 4 + 2 * E * 4},
+        # the plan is integer work of a few hundred KB: latency, reported in us
+        # only; on routed layers it also forms the aux loss
+        "dispatch_plan": {"us": us["dispatch_plan"], "bytes": T * k * 4 * 2 + R * 4 + 2 * E * 4,
+                          "includes_aux_loss": bool(cfg.routed)},
         "permute": {"us": us["permute"]},
         "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (us["up_gelu"] * 1e-6) / 1e12},
         "down": {"us": us["down"], "TFLOP/s": flops_down / (us["down"] * 1e-6) / 1e12},
         "combine": {"us": us["combine"]},
-        "aux": {"us": us["aux"]},
     }
     for key, nb in hbm.items():
         if nb and us[key] > 0:

@@ -158,6 +158,21 @@ int moe_permute(const void* x, int64_t d, int32_t dtype, const int32_t* src,
                 const int32_t* offsets, int32_t E, int64_t rows_max, void* x_perm,
                 hipStream_t stream);
 
+/* moe_dispatch_plan and moe_aux_loss in one pass (the same outputs; the loss
+ * adds the same terms in another order, so it agrees to double rounding, not
+ * bit for bit): the plan's histogram also sums each 256-token chunk's
+ * softmax columns, and the plan's last step forms
+ * L = alpha * E * sum_i (counts_i / (T k)) * (sum_t probs[t, i] / T)
+ * (EP tutorial 5.1) -- two launches instead of five.
+ *   probs [T, E] f32 device, 16-byte aligned (the router's softmax), alpha the loss weight,
+ *   loss: device scalar (0 when T == 0).
+ * moe_dispatch_plan_aux_workspace_bytes: workspace size (8-byte aligned). */
+size_t moe_dispatch_plan_aux_workspace_bytes(int64_t T, int32_t k, int32_t E);
+int moe_dispatch_plan_aux(const int32_t* topk_idx, const float* probs, int64_t T, int32_t k,
+                          int32_t E, int64_t capacity, float alpha, int32_t* counts,
+                          int32_t* offsets, int32_t* dest, int32_t* src, float* loss,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* moe_dispatch_plan without a workspace, for callers that cannot allocate
  * device memory: code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid allocation. Same arguments (minus the workspace) and

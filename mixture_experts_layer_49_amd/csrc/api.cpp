@@ -250,6 +250,40 @@ int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, 
                     "moe_dispatch_plan launch");
 }
 
+size_t moe_dispatch_plan_aux_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  (void)k;
+  if (T <= 0 || E < 1) return 0;
+  return moe::dispatch_aux_ws_bytes(T, E);
+}
+
+int moe_dispatch_plan_aux(const int32_t* topk_idx, const float* probs, int64_t T, int32_t k, int32_t E,
+                          int64_t capacity, float alpha, int32_t* counts, int32_t* offsets, int32_t* dest,
+                          int32_t* src, float* loss, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  MOE_TRY(check_experts(E, k));
+  if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
+  if (T * k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T * k must stay below 2^31");
+  MOE_NONNULL(counts);
+  MOE_NONNULL(offsets);
+  MOE_NONNULL(loss);
+  if (T > 0) {
+    MOE_NONNULL(topk_idx);
+    MOE_NONNULL(probs);
+    MOE_NONNULL(dest);
+    MOE_NONNULL(src);
+    MOE_TRY(check_ptr16("probs", probs));
+    const size_t need = moe_dispatch_plan_aux_workspace_bytes(T, k, E);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                  workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+      return fail(MOE_ERR_ALIGN, "workspace is not 8-byte aligned");
+  }
+  return hip_status(moe::launch_dispatch_plan_aux(topk_idx, T, k, E, capacity, probs, alpha, counts, offsets,
+                                                  dest, src, loss, workspace, stream),
+                    "moe_dispatch_plan_aux launch");
+}
+
 int moe_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
                               int64_t capacity, int32_t* counts, int32_t* offsets, int32_t* dest,
                               int32_t* src, hipStream_t stream) {

@@ -202,6 +202,12 @@ size_t aux_ws_doubles(int64_t T, int E) {
   return static_cast<size_t>(kAuxBlocks) * E;
 }
 
+hipError_t launch_aux_final_chunks(const double* colsum, int nchunks, const int32_t* counts, int64_t T, int E,
+                                   int k, float alpha, float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(kMaxE), 0, s, colsum, nchunks, counts, T, E, k, alpha, loss);
+  return hipGetLastError();
+}
+
 hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T, int E, int k,
                            float alpha, float* loss, double* ws, hipStream_t s) {
   int nblocks = 0;

@@ -9,13 +9,21 @@
 //             a 64-bit mask of its lanes (tokens) that chose the expert
 //             (LDS atomicOr -- order-free); the chunk count per expert is the
 //             sum of popcounts.
-//   2. scan   one workgroup: per expert, an exclusive scan of the chunk counts
-//             over chunks (token order), the total count, kept = min(count, C)
-//             and the exclusive scan over experts -> offsets.
+//   2. scan   per expert, an exclusive scan of the chunk counts over chunks
+//             (token order), the total count, kept = min(count, C) and the
+//             exclusive scan over experts -> offsets. While all chunk counts
+//             fit in 32 KiB of LDS (chunks x experts <= 8192: every workload
+//             here), each place workgroup does this itself from the counts it
+//             loads whole, and workgroup 0 writes counts and offsets -- no
+//             launch of its own; beyond that, one scan workgroup.
 //   3. place  same masks again; an assignment's position inside its expert is
 //             chunk base + earlier waves' popcounts + popcount of lower lanes.
 //             Kept iff position < C. dest and src follow.
 //   4. gather x_perm[r] = x[src[r]] with 16-byte vector copies.
+// The aux loss (EP tutorial 5.1, L = alpha E sum_i f_i P_i) can ride along
+// (moe_dispatch_plan_aux): the histogram workgroups also add up their chunk's
+// softmax columns in double, in token order, and place workgroup 0 adds those
+// chunk sums in chunk order and forms L from them and the counts.
 #include <mutex>
 
 #include "moe_internal.h"
@@ -52,11 +60,79 @@ __device__ void build_masks(const int32_t* __restrict__ idx, int64_t T, int k, i
   __syncthreads();
 }
 
+// With probs (the aux loss): colsum[chunk, e] = sum over the chunk's tokens
+// of probs[t, e] in double, in a fixed order. When 4 divides E and E divides
+// 1024, thread (q = tid % (E/4), r = tid / (E/4)) reads experts 4q .. 4q+3 of
+// tokens r, r + R, ... (R = 1024 / E) as float4 loads, eight in flight, and
+// the R partial sums of each expert are then added in r order; otherwise
+// thread (e = tid % E, g = tid / E) adds tokens g, g + G, ... one value at a
+// time and the G sums are added in g order.
+template <bool AUX>
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx,
                                                         int64_t T, int k, int E,
-                                                        int32_t* __restrict__ chunk_cnt) {
+                                                        int32_t* __restrict__ chunk_cnt,
+                                                        const float* __restrict__ probs,
+                                                        double* __restrict__ colsum) {
   __shared__ unsigned long long mask[kWaves][kMaxE];
-  build_masks(idx, T, k, E, mask);
+  if constexpr (AUX) {
+    // the loads of this chunk's probabilities are issued first, so that they
+    // are in flight while the masks are built
+    __shared__ double s_sum[4 * kThreads];
+    const int tid = threadIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kThreads;
+    const int64_t t1 = min(t0 + kThreads, T);
+    constexpr int U = 8;
+    const bool vec = (E % 4) == 0 && (1024 % E) == 0;
+    int rows;   // partial sums per expert in s_sum, added in row order
+    if (vec) {
+      const int EQ = E / 4, q = tid % EQ, r = tid / EQ;
+      rows = kThreads / EQ;
+      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+      for (int64_t tb = t0 + r; tb < t1; tb += static_cast<int64_t>(U) * rows) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          v[u] = *reinterpret_cast<const float4*>(probs + min(tb + static_cast<int64_t>(u) * rows, t1 - 1) * E + 4 * q);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (tb + static_cast<int64_t>(u) * rows < t1) {
+            a0 += static_cast<double>(v[u].x);
+            a1 += static_cast<double>(v[u].y);
+            a2 += static_cast<double>(v[u].z);
+            a3 += static_cast<double>(v[u].w);
+          }
+        }
+      }
+      s_sum[r * E + 4 * q] = a0;
+      s_sum[r * E + 4 * q + 1] = a1;
+      s_sum[r * E + 4 * q + 2] = a2;
+      s_sum[r * E + 4 * q + 3] = a3;
+    } else {
+      const int G = kThreads / E;   // E <= 256 -> G >= 1
+      const int e = tid % E, g = tid / E;
+      rows = G;
+      double acc = 0.0;
+      if (g < G) {
+        for (int64_t tb = t0 + g; tb < t1; tb += static_cast<int64_t>(U) * G) {
+          float v[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) v[u] = probs[min(tb + static_cast<int64_t>(u) * G, t1 - 1) * E + e];
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (tb + static_cast<int64_t>(u) * G < t1) acc += static_cast<double>(v[u]);
+        }
+        s_sum[g * E + e] = acc;
+      }
+    }
+    build_masks(idx, T, k, E, mask);   // its barriers also order s_sum
+    if (tid < E) {
+      double tot = 0.0;
+      for (int rr = 0; rr < rows; ++rr) tot += s_sum[rr * E + tid];
+      colsum[static_cast<int64_t>(blockIdx.x) * E + tid] = tot;
+    }
+  } else {
+    build_masks(idx, T, k, E, mask);
+  }
   for (int e = threadIdx.x; e < E; e += kThreads) {
     int c = 0;
 #pragma unroll
@@ -134,6 +210,121 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const int32_t* __restri
   }
 }
 
+// place with the scan folded in (chunks x experts <= kScanLds): every
+// workgroup loads all chunk counts into LDS, scans them for its own chunk's
+// bases and for the offsets; workgroup 0 writes counts and offsets and, with
+// AUX, the aux loss from the chunk column sums.
+constexpr int kScanLds = 8192;
+template <bool AUX>
+__global__ __launch_bounds__(kThreads) void place_scan_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap, int nchunks,
+    const int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ dest, int32_t* __restrict__ src, const double* __restrict__ colsum,
+    float alpha, float* __restrict__ loss) {
+  __shared__ unsigned long long mask[kWaves][kMaxE];
+  __shared__ int32_t s_cnt[kScanLds];
+  __shared__ int32_t s_base[kMaxE];
+  __shared__ int32_t s_buf[2][kMaxE];
+  __shared__ double s_red[kMaxE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = nchunks * E;
+  // all chunk counts, 16 bytes per load where the count is a multiple of 4
+  if ((n & 3) == 0) {
+    const int4* c4 = reinterpret_cast<const int4*>(chunk_cnt);
+    for (int i = tid; i < n / 4; i += kThreads) reinterpret_cast<int4*>(s_cnt)[i] = c4[i];
+  } else {
+    for (int i = tid; i < n; i += kThreads) s_cnt[i] = chunk_cnt[i];
+  }
+  build_masks(idx, T, k, E, mask);   // its barriers also publish s_cnt
+  const int c = blockIdx.x;
+  int32_t kept = 0, total = 0;
+  if (tid < E) {
+    int32_t run = 0;
+    for (int cc = 0; cc < nchunks; ++cc) {
+      if (cc == c) s_base[tid] = run;
+      run += s_cnt[cc * E + tid];
+    }
+    total = run;
+    kept = (cap < 0 || run < cap) ? run : static_cast<int32_t>(cap);
+  }
+  // inclusive scan of kept over experts (Hillis-Steele), then exclusive
+  const int e = tid;
+  int cur = 0;
+  if (e < kMaxE) s_buf[0][e] = kept;
+  __syncthreads();
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    int v = 0;
+    if (e < kMaxE) {
+      v = s_buf[cur][e];
+      if (e >= o) v += s_buf[cur][e - o];
+      s_buf[cur ^ 1][e] = v;
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  // offsets[e] = s_buf[cur][e - 1] (0 for e = 0)
+  if (blockIdx.x == 0) {
+    if (e < E) {
+      counts[e] = total;
+      offsets[e + 1] = s_buf[cur][e];
+    }
+    if (e == 0) offsets[0] = 0;
+    if constexpr (AUX) {
+      double term = 0.0;
+      // thread (ee = tid % E, g = tid / E) adds the chunk sums g, g + G, ...
+      // of expert ee, eight in flight; the G group sums are added in g order
+      const int G = kThreads / E;
+      const int ee = tid % E, g = tid / E;
+      double part = 0.0;
+      if (g < G) {
+        constexpr int U = 8;
+        for (int c0 = g; c0 < nchunks; c0 += U * G) {
+          double v[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) v[u] = colsum[static_cast<int64_t>(min(c0 + u * G, nchunks - 1)) * E + ee];
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (c0 + u * G < nchunks) part += v[u];
+        }
+      }
+      s_red[tid] = part;
+      __syncthreads();
+      if (e < E && T > 0) {
+        double col = 0.0;
+        for (int gg = 0; gg < G; ++gg) col += s_red[gg * E + e];
+        const double P = col / static_cast<double>(T);
+        const double f = static_cast<double>(total) / (static_cast<double>(T) * k);
+        term = f * P;
+      }
+      __syncthreads();
+      s_red[e] = term;
+      __syncthreads();
+      for (int o = kMaxE / 2; o > 0; o >>= 1) {
+        if (e < o) s_red[e] += s_red[e + o];
+        __syncthreads();
+      }
+      if (e == 0) loss[0] = static_cast<float>(static_cast<double>(alpha) * E * s_red[0]);
+    }
+  }
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
+  if (t >= T) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int ej = slot_expert(idx, t, k, j, E);
+    int32_t out = -1;
+    if (ej >= 0) {
+      int64_t pos = s_base[ej];
+      for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][ej]);
+      pos += __popcll(mask[wave][ej] & below);
+      if (cap < 0 || pos < cap) {
+        out = (ej == 0 ? 0 : s_buf[cur][ej - 1]) + static_cast<int32_t>(pos);
+        src[out] = static_cast<int32_t>(t);
+      }
+    }
+    dest[t * k + j] = out;
+  }
+}
+
 // One workgroup per grouped row (grid-stride); 16-byte lanes.
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
                                                      const int32_t* __restrict__ src,
@@ -160,26 +351,76 @@ size_t dispatch_ws_ints(int64_t T, int E) {
   return static_cast<size_t>(2 * nchunks * E);
 }
 
-hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
-                                int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
-                                int32_t* ws, hipStream_t s) {
+namespace {
+
+__global__ void zero_float_kernel(float* __restrict__ a) {
+  if (threadIdx.x == 0) a[0] = 0.f;
+}
+
+hipError_t plan_impl(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap, int32_t* counts,
+                     int32_t* offsets, int32_t* dest, int32_t* src, int32_t* ws, const float* probs,
+                     double* colsum, float alpha, float* loss, hipStream_t s) {
   if (T == 0) {
     // Nothing routed: zero counts and offsets so later calls see empty
     // segments (a fill kernel, not a memset node, so the call can be captured).
     hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(kMaxE), 0, s, counts, E);
     hipLaunchKernelGGL(zero_kernel, dim3(2), dim3(kMaxE), 0, s, offsets, E + 1);
+    if (loss != nullptr) hipLaunchKernelGGL(zero_float_kernel, dim3(1), dim3(kWave), 0, s, loss);
     return hipGetLastError();
   }
   const int nchunks = static_cast<int>((T + kThreads - 1) / kThreads);
   int32_t* chunk_cnt = ws;
+  const bool aux = probs != nullptr;
+  if (aux)
+    hipLaunchKernelGGL(hist_kernel<true>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, chunk_cnt,
+                       probs, colsum);
+  else
+    hipLaunchKernelGGL(hist_kernel<false>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, chunk_cnt,
+                       nullptr, nullptr);
+  if (static_cast<int64_t>(nchunks) * E <= kScanLds) {
+    if (aux)
+      hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
+                         nchunks, chunk_cnt, counts, offsets, dest, src, colsum, alpha, loss);
+    else
+      hipLaunchKernelGGL(place_scan_kernel<false>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
+                         nchunks, chunk_cnt, counts, offsets, dest, src, nullptr, 0.f, nullptr);
+    return hipGetLastError();
+  }
   int32_t* chunk_base = ws + static_cast<int64_t>(nchunks) * E;
-  hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E,
-                     chunk_cnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxE), 0, s, chunk_cnt, chunk_base, nchunks, E,
                      cap, counts, offsets);
   hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
                      chunk_base, offsets, dest, src);
+  if (aux) {
+    // the chunk column sums are there already; the aux loss from them
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_aux_final_chunks(colsum, nchunks, counts, T, E, k, alpha, loss, s);
+  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+size_t dispatch_aux_ws_bytes(int64_t T, int E) {
+  const int64_t nchunks = (T + kThreads - 1) / kThreads;
+  return dispatch_ws_ints(T, E) * sizeof(int32_t) + static_cast<size_t>(nchunks * E) * sizeof(double);
+}
+
+hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                                int32_t* ws, hipStream_t s) {
+  return plan_impl(topk_idx, T, k, E, cap, counts, offsets, dest, src, ws, nullptr, nullptr, 0.f, nullptr, s);
+}
+
+hipError_t launch_dispatch_plan_aux(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                    const float* probs, float alpha, int32_t* counts, int32_t* offsets,
+                                    int32_t* dest, int32_t* src, float* loss, void* ws, hipStream_t s) {
+  // workspace: the plan's ints, then the chunk column sums (8-byte aligned:
+  // the plan's part is an even number of ints)
+  int32_t* wsi = static_cast<int32_t*>(ws);
+  double* colsum = reinterpret_cast<double*>(wsi + dispatch_ws_ints(T, E));
+  return plan_impl(topk_idx, T, k, E, cap, counts, offsets, dest, src, wsi, probs, colsum, alpha, loss, s);
 }
 
 // Scratch of moe_dispatch_plan_noalloc: the per-chunk counts and bases that

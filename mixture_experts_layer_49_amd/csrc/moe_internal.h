@@ -111,6 +111,15 @@ hipError_t launch_aux_loss(const float* probs, const int32_t* counts, int64_t T,
                            float alpha, float* loss, double* ws, hipStream_t s);
 
 size_t dispatch_ws_ints(int64_t T, int E);
+// The plan and the aux loss in one pass (dispatch.hip): the workspace holds
+// the plan's ints, then one double per (256-token chunk, expert).
+size_t dispatch_aux_ws_bytes(int64_t T, int E);
+hipError_t launch_dispatch_plan_aux(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
+                                    const float* probs, float alpha, int32_t* counts, int32_t* offsets,
+                                    int32_t* dest, int32_t* src, float* loss, void* ws, hipStream_t s);
+// The aux loss from per-chunk column sums of the probabilities (combine_aux.hip).
+hipError_t launch_aux_final_chunks(const double* colsum, int nchunks, const int32_t* counts, int64_t T, int E,
+                                   int k, float alpha, float* loss, hipStream_t s);
 // The plan on the library's own per-GPU scratch (dispatch.hip).
 size_t noalloc_scratch_bytes();
 hipError_t launch_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,

@@ -25,7 +25,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
-           "moe_dispatch", "moe_dispatch_plan", "moe_dispatch_plan_noalloc",
+           "moe_dispatch", "moe_dispatch_plan", "moe_dispatch_plan_aux",
+           "moe_dispatch_plan_aux_workspace_bytes", "moe_dispatch_plan_noalloc",
            "moe_dispatch_plan_noalloc_scratch_bytes", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag",
            "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_expert_down_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         "moe_dispatch": (ctypes.c_int, [P, I64, I32, I32, I64, P, I64, I32, P, P, P, P, P, P, SZ, P]),
         "moe_dispatch_plan": (ctypes.c_int, [P, I64, I32, I32, I64, P, P, P, P, P, SZ, P]),
         "moe_dispatch_plan_noalloc": (ctypes.c_int, [P, I64, I32, I32, I64, P, P, P, P, P]),
+        "moe_dispatch_plan_aux_workspace_bytes": (SZ, [I64, I32, I32]),
+        "moe_dispatch_plan_aux": (ctypes.c_int, [P, P, I64, I32, I32, I64, F32, P, P, P, P, P, P, SZ, P]),
         "moe_dispatch_plan_noalloc_scratch_bytes": (SZ, []),
         "moe_permute": (ctypes.c_int, [P, I64, I32, P, P, I32, I64, P, P]),
         "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P, SZ, P]),
@@ -234,6 +237,29 @@ def moe_dispatch_plan(topk_idx, E: int, capacity: int, counts=None, offsets=None
                                    _ptr(dest), _ptr(src), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return counts, offsets, dest, src
+
+
+def moe_dispatch_plan_aux_workspace_bytes(T: int, k: int, E: int) -> int:
+    return lib().moe_dispatch_plan_aux_workspace_bytes(T, k, E)
+
+
+def moe_dispatch_plan_aux(topk_idx, probs, E: int, capacity: int, alpha: float, counts=None,
+                          offsets=None, dest=None, src=None, loss=None, workspace=None, stream=None):
+    """moe_dispatch_plan and moe_aux_loss in one pass; returns counts,
+    offsets, dest, src, loss."""
+    T, k = topk_idx.shape
+    rows = moe_rows_max(T, k, E, capacity)
+    counts = _empty((E,), torch.int32, topk_idx) if counts is None else counts
+    offsets = _empty((E + 1,), torch.int32, topk_idx) if offsets is None else offsets
+    dest = _empty((T, k), torch.int32, topk_idx) if dest is None else dest
+    src = _empty((max(rows, 1),), torch.int32, topk_idx) if src is None else src
+    loss = _empty((1,), torch.float32, topk_idx) if loss is None else loss
+    if workspace is None:
+        workspace = _empty((max(moe_dispatch_plan_aux_workspace_bytes(T, k, E), 8),), torch.uint8, topk_idx)
+    _check(lib().moe_dispatch_plan_aux(_ptr(topk_idx), _ptr(probs), T, k, E, capacity, alpha,
+                                       _ptr(counts), _ptr(offsets), _ptr(dest), _ptr(src), _ptr(loss),
+                                       _ptr(workspace), _ws_size(workspace), _stream(stream)))
+    return counts, offsets, dest, src, loss
 
 
 def moe_dispatch_plan_noalloc(topk_idx, E: int, capacity: int, counts, offsets, dest, src,
@@ -542,6 +568,9 @@ class MoEBuffers:
         self.y = z((T, d), torch.float32)
         self.loss = z((1,), torch.float32)
         self.ws_dispatch = z((max(moe_dispatch_workspace_bytes(T, k, E), 4),), torch.uint8)
+        # the plan with the aux loss folded in (routed layers with probabilities)
+        self.ws_plan_aux = (z((max(moe_dispatch_plan_aux_workspace_bytes(T, k, E), 8),), torch.uint8)
+                            if self.probs is not None else None)
         self.ws_aux = z((max(moe_aux_loss_workspace_bytes(T, E), 8),), torch.uint8)
         self.used_idx, self.used_w = self.topk_idx, self.topk_w
         nb = moe_ffn_workspace_bytes(dtype)
@@ -596,9 +625,16 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
             moe_expert_down(bufs.h, bufs.offsets, w2, bufs.rows_max, bufs.y_perm, bufs.ws_ffn,
                             stream)
 
-    if bufs.frag:
+    # the dispatch plan, with the aux loss folded in where the router's
+    # probabilities are kept
+    aux_done = routed and bufs.probs is not None and bufs.ws_plan_aux is not None
+    if aux_done:
+        moe_dispatch_plan_aux(idx, bufs.probs, E, capacity, alpha, bufs.counts, bufs.offsets, bufs.dest,
+                              bufs.src, bufs.loss, bufs.ws_plan_aux, stream)
+    else:
         moe_dispatch_plan(idx, E, capacity, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
                           bufs.ws_dispatch, stream)
+    if bufs.frag:
         moe_permute_frag(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_frag, stream)
         if w2_f16 is not None and bufs.h_frag is not None:
             # h stays in fragment order between the two projections
@@ -612,8 +648,7 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
             moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, False, stream)
             down()
     else:
-        moe_dispatch(idx, E, capacity, x, bufs.counts, bufs.offsets, bufs.dest, bufs.src,
-                     bufs.x_perm, bufs.ws_dispatch, stream)
+        moe_permute(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_perm, stream)
         if bufs.z is not None:
             moe_expert_up_gelu_z(bufs.x_perm, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.z,
                                  bufs.ws_ffn, stream)
@@ -626,7 +661,7 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
             moe_grouped_ffn(bufs.x_perm, bufs.offsets, w1, w2, bufs.rows_max, bufs.h, bufs.y_perm,
                             bufs.ws_ffn, stream)
     moe_combine(bufs.y_perm, bufs.dest, w, d, torch.float32, bufs.y, stream)
-    if routed and bufs.probs is not None:
+    if routed and bufs.probs is not None and not aux_done:
         moe_aux_loss(bufs.probs, bufs.counts, k, alpha, bufs.loss, bufs.ws_aux, stream)
     return bufs
 

@@ -147,6 +147,21 @@ def test_plan_and_permute_argument_errors():
     assert plan(9, ctypes.c_void_p((1 << 20) + 2)) == -6
     a = list(ok); a[1] = 0; a[0] = None; a[7] = None; a[8] = None; a[9] = None; a[10] = 0; a[5] = None
     assert L.moe_dispatch_plan(*a) == -1         # T == 0 still needs counts and offsets
+    # moe_dispatch_plan_aux(topk_idx, probs, T, k, E, capacity, alpha, counts, offsets, dest, src,
+    #                       loss, ws, ws_bytes, stream)
+    need_aux = L.moe_dispatch_plan_aux_workspace_bytes(100, 2, 8)
+    assert need_aux == need + 1 * 8 * 8            # the plan's ints, then a double per (chunk, expert)
+    okx = [FAKE, FAKE, 100, 2, 8, 30, ctypes.c_float(0.01), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need_aux, None]
+
+    def plan_aux(i, v):
+        a = list(okx); a[i] = v
+        return L.moe_dispatch_plan_aux(*a)
+    assert plan_aux(4, 0) == -3                  # E = 0
+    assert plan_aux(1, None) == -1               # probs with T > 0
+    assert plan_aux(11, None) == -1              # loss
+    assert plan_aux(13, need_aux - 1) == -4      # workspace too small
+    assert plan_aux(12, ctypes.c_void_p((1 << 20) + 4)) == -6   # workspace alignment
+    assert plan_aux(1, ctypes.c_void_p((1 << 20) + 4)) == -6    # probs alignment
     # moe_dispatch_plan_noalloc(topk_idx, T, k, E, capacity, counts, offsets, dest, src, stream):
     # the same checks without a workspace; a plan beyond the static scratch is
     # refused before anything is enqueued

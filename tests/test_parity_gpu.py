@@ -265,6 +265,37 @@ def test_plan_then_permute_equals_dispatch(cfg):
     assert torch.equal(src[:R], ref[3][:R]) and torch.equal(xp[:R], ref[4][:R])
 
 
+@pytest.mark.parametrize("T,E,k,cf,seed", [(300, 6, 2, 1.25, 1), (517, 40, 3, 1.0, 2), (1, 4, 2, 1.25, 3),
+                                           (4096, 256, 8, 2.0, 4), (16384, 64, 2, 1.25, 5),
+                                           (70000, 64, 2, 1.25, 6), (0, 8, 2, 1.25, 7)])
+def test_plan_aux_equals_plan_then_aux_loss(T, E, k, cf, seed):
+    """moe_dispatch_plan_aux against moe_dispatch_plan + moe_aux_loss on the
+    same routing: the plan bit for bit, the loss to double rounding (its sums
+    run in another order) and to the oracle's 1e-5. 70000 tokens x 64 experts
+    has more chunk counts than the place workgroups keep in LDS: the plan then
+    runs its separate scan and the loss its separate final kernel."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    probs = torch.softmax(torch.from_numpy(logits), dim=1)
+    idx = torch.topk(probs, k, dim=1).indices.to(torch.int32)
+    C = ops.moe_capacity(T, E, cf)
+    alpha = 0.01
+    pd, idd = probs.to("cuda:0"), idx.to("cuda:0").contiguous()
+    ref = ops.moe_dispatch_plan(idd, E, C)
+    loss_ref = ops.moe_aux_loss(pd, ref[0], k, alpha)
+    got = ops.moe_dispatch_plan_aux(idd, pd, E, C, alpha)
+    torch.cuda.synchronize()
+    R = int(host(ref[1])[-1])
+    for a, b in zip(got[:3], ref[:3]):
+        assert torch.equal(a, b)
+    assert torch.equal(got[3][:R], ref[3][:R])
+    lg, lr = float(host(got[4])[0]), float(host(loss_ref)[0])
+    want = O.aux_loss(probs.double().numpy(), host(ref[0]), k, alpha) if T else 0.0
+    say("  T=%d E=%d: fused %.9g separate %.9g oracle %.9g" % (T, E, lg, lr, want))
+    assert abs(lg - lr) <= 2e-7 * abs(lr) + 1e-12
+    assert abs(lg - want) <= 1e-5 * abs(want) + 1e-12
+
+
 def test_dispatch_ignores_invalid_and_repeated_ids():
     """Ids outside [0,E) and repeats inside a token are skipped. Expected plan:
     the oracle's, with every skipped slot sent to an extra expert E placed
