@@ -494,8 +494,9 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
   };
 
   // f32 output (down-projection): as the row-major h epilogue, eight values
-  // per item in two 16-byte stores; a split piece writes its whole 256 x 256
-  // partial sum, row-major, to its workspace slot xcd * 2 P + piece.
+  // per item in two 16-byte stores; a split piece writes its 256 x 256
+  // partial sum (the rows inside the segment), row-major, to its workspace
+  // slot xcd * 2 P + piece.
   auto epilogue_down = [&](const FCtx& c) {
     float* const buf = s_epi[wave];
     int ln = lane;
@@ -503,7 +504,8 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     const int el32 = ln & 31, ehl = ln >> 5;
     const bool piece = c.tail >= 0;
     const int pitch = piece ? FBN : N;
-    const int rows_ok = piece ? FBM : min(c.seg1 - c.m0, FBM), cols_ok = piece ? FBN : min(N - c.n0, FBN);
+    // a piece stores only the rows inside the segment (the fix-up reads no others)
+    const int rows_ok = min(c.seg1 - c.m0, FBM), cols_ok = piece ? FBN : min(N - c.n0, FBN);
     float* const base = piece ? part + static_cast<int64_t>(xcd * kPiecesPerWg * P + c.tail) * (FBM * FBN)
                               : static_cast<float*>(Cout) + static_cast<int64_t>(c.m0) * N + c.n0;
     const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(base, 0, rows_ok * pitch * 4, 0x00020000);

@@ -696,6 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
         for (int q = tid; q < 64 * BN / 4; q += kThreads) {
           const int row = q / (BN / 4);
           const int col = (q % (BN / 4)) * 4;
+          if (c_m0 + p * 64 + row >= c_seg1) continue;   // rows past the segment: never read back
           const float* src = (col < 128 ? h0 : h1) + row * 128 + ((col & 127) ^ (((row >> 2) & 1) * 32));
           *reinterpret_cast<float4*>(mine + (p * 64 + row) * BN + col) = *reinterpret_cast<const float4*>(src);
         }
@@ -912,6 +913,8 @@ __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
   const Tile tl = find_tile(s_pref, E, tiles_n, pl.r_beg + pl.full * P + tr);
   const int e0 = offsets[tl.e], seg1 = offsets[tl.e + 1];
   const int m0 = e0 + tl.mi * BM, n0 = tl.nt * BN;
+  // a quarter wholly past the segment has nothing to add (its rows were not stored)
+  if (m0 + quarter * 64 >= seg1) return;
   // piece si of the tile is u = si * rem + tr, at slot u of the XCD's kPiecesPerWg P
   const float* const first = part + static_cast<int64_t>(xcd * kPiecesPerWg * P + tr) * (BM * BN);
   const int64_t step = static_cast<int64_t>(pl.rem) * (BM * BN);
@@ -930,8 +933,10 @@ __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
         const int q = min(q0 + u * kThreads, ITEMS - 1);
         const int row = quarter * 64 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
         const float* src = first + min(si, S - 1) * step + row * BN + col;
+        const bool live = m0 + row < seg1;   // rows past the segment were not stored
 #pragma unroll
-        for (int h = 0; h < NV; ++h) v[si][u][h] = *reinterpret_cast<const float4*>(src + 4 * h);
+        for (int h = 0; h < NV; ++h)
+          v[si][u][h] = live ? *reinterpret_cast<const float4*>(src + 4 * h) : float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
     for (int u = 0; u < QU; ++u) {

@@ -195,9 +195,11 @@ def test_router_renorm():
     ref, idx = check_routing(inp, cfg, flags=ops.MOE_RENORM)
 
 
-def test_router_ties_go_to_lower_index():
-    """Duplicate gate rows give exactly equal logits: the lower index wins."""
-    cfg = I.small("ties", T=64, d=64, d_ff=64, E=8, k=3, seed=22)
+@pytest.mark.parametrize("d", [64, 256])
+def test_router_ties_go_to_lower_index(d):
+    """Duplicate gate rows give exactly equal logits: the lower index wins
+    (d = 256: the kernel that keeps the gate weight in LDS)."""
+    cfg = I.small("ties", T=64, d=d, d_ff=64, E=8, k=3, seed=22)
     inp = I.make_inputs(cfg)
     wg = inp["w_gate"].copy()
     wg[5] = wg[2]
