@@ -15,7 +15,8 @@ Zipf(1.2) loads) is timed after it with the same steps and reported under
 Before the warm-up steps an untimed ramp runs until the clocks have settled
 (its length is in the line). Prints ONE JSON line: tokens/s, ms per step,
 the roofline of the dominant kernel (timed live with HIP events on the
-launch stream), the graphics clock under the dominant GEMM (from its
+launch stream, in a second pass of the same steps so that the events do not
+add to the whole-job time), the graphics clock under the dominant GEMM (from its
 profile) and right after the GEMMs (a live probe), a per-call
 breakdown, the HBM-bound calls again with cold caches
 next to a plain-read and a copy reference of the same bytes, and the CPU
@@ -177,6 +178,32 @@ def copy_probe(args, torch, device):
     del src_probe, dst_probe
 
 
+def timed_steps(step, steps, torch, stream):
+    """Milliseconds for `steps` back-to-back steps, bracketed by a device
+    synchronisation and two events on the launch stream; nothing else is
+    recorded inside, so the figure is the whole-job time."""
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop)
+
+
+def kernel_breakdown(step, evs, n, torch, stream, np):
+    """Mean milliseconds of each of the n calls of a step, from boundary events
+    recorded between the calls in a second pass of the same steps (each event
+    record costs a few microseconds of stream time, which is why the whole-job
+    time is taken without them)."""
+    torch.cuda.synchronize()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    return np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n)] for e in evs]).mean(0)
+
+
 def bench_backward(args, cfg, inp, ops, torch, np):
     """One training step per timed step; prints the JSON line."""
     from mixture_experts_layer_49_amd import inputs as I
@@ -250,14 +277,8 @@ def bench_backward(args, cfg, inp, ops, torch, np):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
+    total_ms = timed_steps(step, args.steps, torch, stream)
+    per = kernel_breakdown(step, evs, len(names), torch, stream, np)
     us = dict(zip(names, (per * 1e3).tolist()))
     R = int(b.offsets.cpu().numpy()[-1])
     s2 = 2 if bf else 4
@@ -307,6 +328,8 @@ def bench_backward(args, cfg, inp, ops, torch, np):
         "backward_ms": bwd_us * 1e-3,
         "backward_gemm_mfma_frac": 4 * gemm_flops / (sum(us[n] for n in ("down_bwd", "up_bwd", "dw2", "dw1")) * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS,
         "breakdown": breakdown,
+        "breakdown_pass": {"how": "events between the calls, in a second pass of the same steps",
+                           "ms_per_step": float(per.sum())},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (forward + backward) on the host ...")
@@ -500,16 +523,10 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     # one set of boundary events per timed step, all on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = timed_steps(step, args.steps, torch, stream)
     after = measure_clock(step, kernels, torch, stream, x.device)
     ms_per_step = total_ms / args.steps
-    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(names))] for e in evs]).mean(0)
+    per = kernel_breakdown(step, evs, len(names), torch, stream, np)
     us = dict(zip(names, (per * 1e3).tolist()))
 
     counts = b.counts.cpu().numpy()
@@ -595,8 +612,11 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     under = profiled_sclk(dom_which, cfg.name, fam)
     clock = {"under_dominant_gemm_mhz": under,
              "under_source": ("rocprofv3 GRBM_GUI_ACTIVE per XCD / duration, profiles/%s_%s_%s.md "
-                              "(same kernel sources)" % (fam, dom_which, cfg.name)
-                              if under else "no profile summary of the current kernel sources"),
+                              "(same kernel sources)" % (fam, dom_which, cfg.name) if under else
+                              "profiles/%s_%s_%s.md gives no clock: launches under 100 us are too "
+                              "short for the counter" % (fam, dom_which, cfg.name)
+                              if profile_fields(dom_which, cfg.name, fam) else
+                              "no profile summary of the current kernel sources"),
              "after_gemm_probe": after}
     out = {
         "value": T * args.steps / (total_ms * 1e-3),
@@ -621,6 +641,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
         "clock": clock,
         "ramp": ramp,
         "breakdown": breakdown,
+        "breakdown_pass": {"how": "events between the calls, in a second pass of the same steps",
+                           "ms_per_step": float(per.sum())},
         "hbm_cold": cold,
     }
     if under:
