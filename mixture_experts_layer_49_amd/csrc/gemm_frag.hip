@@ -24,8 +24,10 @@
 // 32 x 32). Each wave loads its A fragments straight into registers (1 KiB
 // contiguous per wave load, four stages of register buffers, issued three
 // stages ahead); only B goes through LDS, in a ring of four 32 KiB slots
-// filled by LDS-DMA three stages ahead. One barrier per 64-deep stage. Tiles
-// continue across a workgroup's units: the last three stages of a tile
+// filled by LDS-DMA three stages ahead. One barrier per 64-deep stage. The
+// k-loop is laid out instruction by instruction: each MFMA is followed by at
+// most one LDS fragment read and one memory load, so neither kind arrives in
+// bursts that hold up the next MFMA. Tiles continue across a workgroup's units: the last three stages of a tile
 // prefetch the next tile's first three, so those loads are in flight during
 // the per-wave epilogue. The kinds (below) differ in the MFMA input type and
 // the epilogue; every MFMA sees the same operands in the same order as the
@@ -309,37 +311,21 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(SL(S) + blk * kWave), 16, ld_voff_b, so, 0, 0);
     }
   };
-  auto read_b = [&](int S, int kk, int fs) __attribute__((always_inline)) {
-    int x = fr_x;
-    asm volatile("" : "+v"(x));   // recomputed per read rather than kept live
-    const int base = l32 * kFCpr + (x ^ (kk * 2));
-#pragma unroll
-    for (int j = 0; j < FNI; ++j) fb[fs][j] = SL(S)[base + j * 32 * kFCpr];
+  // B fragment j of k-slice kk of slot S into fb[fs][j].
+  auto rd = [&](int S, int kk, int fs, int j) __attribute__((always_inline)) {
+    fb[fs][j] = SL(S)[l32 * kFCpr + (fr_x ^ (kk * 2)) + j * 32 * kFCpr];
   };
-  auto mfma_slice = [&](auto ab_c, int s, int fs) __attribute__((always_inline)) {
+  // MFMA m of k-slice s: accumulator tile (m % 2, m / 2), so B fragment j is
+  // consumed by MFMAs 2 j and 2 j + 1.
+  auto mf = [&](auto ab_c, int s, int fs, int m) __attribute__((always_inline)) {
     constexpr int AB = decltype(ab_c)::value;
-#pragma unroll
-    for (int i = 0; i < FMI; ++i)
-#pragma unroll
-      for (int j = 0; j < FNI; ++j)
-        if constexpr (DOWN)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(f16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
-  };
-  // NV memory loads (issued just before) spread over a slice's 16 MFMAs.
-  auto interleave = [&](auto nv_c) __attribute__((always_inline)) {
-    constexpr int NV = decltype(nv_c)::value;
-#pragma unroll
-    for (int qq = 0; qq < 16; ++qq) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-      if (qq * NV % 16 < NV) {
-        __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);   // SALU (offsets, M0)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-      }
-    }
+    const int i = m & 1, j = m >> 1;
+    if constexpr (DOWN)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          __builtin_bit_cast(f16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(f16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
   };
 
   FCtx cur, nxt;
@@ -355,13 +341,45 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
   issue_a(cur, cur.klo + 2, std::integral_constant<int, 2>{}, 0, kFAFrag);
   issue_b(cur, cur.klo + 2, 2, 0, kFBLoads);
 
+  // One k-slice (16 MFMAs) in a fixed order: after MFMA m comes, for even m,
+  // the read of B fragment m / 2 of the next slice (from slot rS, k-slice
+  // rkk, into the other fb buffer) and, for m % 4 == 1, one memory load of
+  // stage pk (nA A fragments from a0, then nB W1 loads from b0). Each piece
+  // is fenced so the compiler keeps this order: every LDS read and memory
+  // instruction issues behind an MFMA that is already running, each
+  // fragment is read 16 MFMAs before its use, and a wave sends the memory
+  // pipeline one instruction per four MFMAs instead of bursts.
+  auto slice = [&](auto ab_c, auto sn_c, int s, int fs, int rS, int rkk, const FCtx& pc, int pk, int a0, int nA,
+                   int b0, int nB) __attribute__((always_inline)) {
+    constexpr int SN = decltype(sn_c)::value;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mf(ab_c, s, fs, m);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((m & 1) == 0) {
+        rd(rS, rkk, fs ^ 1, m >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int vi = m >> 2;
+      if ((m & 3) == 1 && vi < nA + nB) {
+        if (vi < nA) issue_a(pc, pk, std::integral_constant<int, SN>{}, a0 + vi, a0 + vi + 1);
+        else issue_b(pc, pk, SN, b0 + vi - nA, b0 + vi - nA + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // Stage kt (slot and A buffer SB = kt % 4, compile time) of unit q. It
   // prefetches stage kt+3 of unit q or, past the end, of unit q+1 (after the
   // last unit: an in-bounds stage into buffers nobody reads, so every stage
-  // issues the same 16 loads). Loads per slice: A 0-3 and W1 0-1, A 4-7 and
-  // W1 2-4, W1 5-7. At the end of slice 2 it waits for stage kt+1, whose
-  // loads are older than the 16 of each of stages kt-1 and kt and, in the
-  // first two stages after a per-wave epilogue, that epilogue's NST stores.
+  // issues the same 16 loads): A 0-3 in slice 0, A 4-7 in slice 1, W1 0-3 in
+  // slice 2, W1 4-7 in slice 3. After slice 2 it waits for stage kt+1, whose
+  // loads are older than the 16 of stage kt+2 and the 12 of stage kt+3
+  // issued so far and, in the first two stages after a per-wave epilogue,
+  // that epilogue's NST stores. The barrier then tells every wave that stage
+  // kt+1 is in LDS and that no wave reads slot SB any more (slice 3's
+  // fragments were read during slice 2), so slice 3 may read slot S1 and
+  // its W1 loads may fill the slot of stage kt-1.
   int64_t q = 0;
   bool after_epi = false;
   auto stage = [&](auto sb_c, int kt) __attribute__((always_inline)) {
@@ -372,32 +390,17 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     const bool pre_cur = kp < cur.khi;
     const FCtx pc = pre_cur ? cur : nxt;
     const int pk = pre_cur ? kp : nxt.klo + (kp - cur.khi);
-    read_b(SB, 1, 1);
+    using AB = std::integral_constant<int, SB>;
+    using SNc = std::integral_constant<int, SN>;
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(pc, pk, std::integral_constant<int, SN>{}, 0, 4);
-    issue_b(pc, pk, SN, 0, 2);
-    mfma_slice(std::integral_constant<int, SB>{}, 0, 0);
-    interleave(std::integral_constant<int, 6>{});
-    __builtin_amdgcn_sched_barrier(0);
-    read_b(SB, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(pc, pk, std::integral_constant<int, SN>{}, 4, 8);
-    issue_b(pc, pk, SN, 2, 5);
-    mfma_slice(std::integral_constant<int, SB>{}, 1, 1);
-    interleave(std::integral_constant<int, 7>{});
-    __builtin_amdgcn_sched_barrier(0);
-    read_b(SB, 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(pc, pk, SN, 5, 8);
-    mfma_slice(std::integral_constant<int, SB>{}, 2, 0);
-    interleave(std::integral_constant<int, 3>{});
-    __builtin_amdgcn_sched_barrier(0);
-    // Stage kt+1 has landed; every wave is done with slot SB.
-    if (after_epi && kt - cur.klo < 2) FR_WAIT_VM(62);
-    else FR_WAIT_VM(32);
+    slice(AB{}, SNc{}, 0, 0, SB, 1, pc, pk, 0, 4, 0, 0);
+    slice(AB{}, SNc{}, 1, 1, SB, 2, pc, pk, 4, 4, 0, 0);
+    slice(AB{}, SNc{}, 2, 0, SB, 3, pc, pk, 0, 0, 0, 4);
+    if (after_epi && kt - cur.klo < 2) FR_WAIT_VM(60);
+    else FR_WAIT_VM(28);
     FR_BARRIER();
-    read_b(S1, 0, 0);
-    mfma_slice(std::integral_constant<int, SB>{}, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    slice(AB{}, SNc{}, 3, 1, S1, 0, pc, pk, 0, 0, 4, 4);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -543,7 +546,8 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     if (after_epi) FR_WAIT_VM(62);
     else FR_WAIT_VM(32);
     FR_BARRIER();
-    read_b(0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < FNI; ++j) rd(0, 0, 0, j);
 #pragma unroll
     for (int i = 0; i < FMI; ++i)
 #pragma unroll
