@@ -17,7 +17,8 @@ Before the warm-up steps an untimed ramp runs until the clocks have settled
 the roofline of the dominant kernel (timed live with HIP events on the
 launch stream, in a second pass of the same steps so that the events do not
 add to the whole-job time), the graphics clock under the dominant GEMM (from its
-profile) and right after the GEMMs (a live probe), a per-call
+profile) and right after the GEMMs (a live probe), the matrix-core ceiling
+under the power cap (an MFMA-only loop with no memory traffic), a per-call
 breakdown, the HBM-bound calls again with cold caches
 next to a plain-read and a copy reference of the same bytes, and the CPU
 oracle timed on this host as a baseline.
@@ -414,8 +415,46 @@ def cold_us(fn, flush, torch, stream, reps=10):
     return t[len(t) // 2]
 
 
+def measure_mfma_ceiling(torch, stream, device, iters=20000, reps=5):
+    """The matrix-core ceiling under the power cap: libmoe_bench.so's MFMA-only
+    loop (v_mfma_f32_32x32x16_bf16 on register operands, one workgroup of four
+    waves per CU, no memory traffic), a few warm launches then `reps` timed
+    ones; its TFLOP/s, the fraction of the nominal peak and the clock it held
+    (shader-clock against 100 MHz ticks over workgroup 0's loop)."""
+    import ctypes
+
+    L = bench_lib()
+    grid = torch.cuda.get_device_properties(device).multi_processor_count
+    out = torch.empty(grid * 256, dtype=torch.float32, device=device)
+    clk = torch.zeros(2, dtype=torch.int64, device=device)
+    strm = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch():
+        if L.probe_mfma_loop(ctypes.c_void_p(out.data_ptr()), iters, ctypes.c_void_p(clk.data_ptr()), grid,
+                             strm) != 0:
+            raise RuntimeError("probe_mfma_loop failed")
+
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = float(grid) * 4 * iters * 16 * 32768.0
+    c = clk.cpu().numpy().astype(float)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"TFLOP/s": tf, "frac": tf / PEAK_MFMA_TFLOPS, "sclk_mhz": 100.0 * c[0] / c[1],
+            "what": "v_mfma_f32_32x32x16_bf16 on register operands, no memory traffic, one workgroup "
+                    "of 4 waves per CU (%d), %.2f ms per launch" % (grid, ms)}
+
+
 def bench_lib():
-    """libmoe_bench.so: the streaming-read reference kernel."""
+    """libmoe_bench.so: the streaming-read reference kernel, the clock probe
+    and the MFMA-only loop."""
     import ctypes
 
     path = os.path.join(ROOT, "mixture_experts_layer_49_amd", "libmoe_bench.so")
@@ -425,6 +464,8 @@ def bench_lib():
     L.probe_stream_read.restype = ctypes.c_int
     L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
+    L.probe_mfma_loop.restype = ctypes.c_int
+    L.probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return L
 
 
@@ -525,6 +566,7 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
            for _ in range(args.steps)]
     total_ms = timed_steps(step, args.steps, torch, stream)
     after = measure_clock(step, kernels, torch, stream, x.device)
+    ceiling = measure_mfma_ceiling(torch, stream, x.device)
     ms_per_step = total_ms / args.steps
     per = kernel_breakdown(step, evs, len(names), torch, stream, np)
     us = dict(zip(names, (per * 1e3).tolist()))
@@ -639,12 +681,16 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
                      "launch_us": us[dom]},
         "ffn_mfma_frac": ffn_tflops / PEAK_MFMA_TFLOPS,
         "clock": clock,
+        "mfma_ceiling": ceiling,
         "ramp": ramp,
         "breakdown": breakdown,
         "breakdown_pass": {"how": "events between the calls, in a second pass of the same steps",
                            "ms_per_step": float(per.sum())},
         "hbm_cold": cold,
     }
+    # the dominant GEMM against what the matrix cores reach on this chip with
+    # no memory traffic at all (the power cap holds the clock below 2.4 GHz)
+    out["roofline"]["frac_of_mfma_ceiling"] = achieved / ceiling["TFLOP/s"]
     if under:
         # the same fraction against the MFMA peak at the clock the kernel ran at
         out["roofline"]["sclk_mhz"] = under

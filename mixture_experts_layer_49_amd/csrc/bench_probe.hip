@@ -1,6 +1,7 @@
 // Measurement kernels for the benchmark only (libmoe_bench.so, separate from
 // the layer's library): a plain streaming read, the reference that the
-// HBM-bound kernels' cold-cache rates are compared with.
+// HBM-bound kernels' cold-cache rates are compared with; a clock probe; and
+// an MFMA-only loop, the reference for the matrix-core-bound kernels.
 //
 // probe_clock: one wave reads the shader-clock counter (s_memtime) and the
 // constant 100 MHz counter (s_memrealtime) at its start and again after about
@@ -8,6 +9,14 @@
 // graphics clock over that interval. Launched right after a kernel, it sees
 // the clock that kernel ran at (the power manager moves it on a millisecond
 // scale).
+//
+// probe_mfma_loop: the matrix-core ceiling under the power cap. One
+// workgroup of four waves per CU; each wave runs `iters` rounds of 16
+// independent v_mfma_f32_32x32x16_bf16 on operands held in registers (no
+// memory traffic), 16 accumulators of 32 x 32, and writes their sum to `out`
+// (grid x 256 floats) so nothing is optimised away. Workgroup 0 also records
+// the shader-clock and 100 MHz ticks over its loop in clk[0..1]. Flops per
+// launch: grid x 4 x iters x 16 x 32768.
 //
 // probe_stream_read: every byte of [p, p + bytes) is read once with 16-byte
 // vector loads, U of them in flight per thread, grid-stride over 16-byte
@@ -65,9 +74,62 @@ __global__ __launch_bounds__(64) void clock_kernel(unsigned long long* __restric
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8_t lcg_operand(unsigned s) {
+  bf16x8_t v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s = s * 1664525u + 1013904223u;
+    v[i] = static_cast<__bf16>(static_cast<float>((s >> 9) & 0xffffu) * (1.0f / 65536.0f) - 0.5f);
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out, int iters,
+                                                        unsigned long long* __restrict__ clk) {
+  const unsigned seed = blockIdx.x * 1000u + threadIdx.x * 7u;
+  bf16x8_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = lcg_operand(seed + i);
+    b[i] = lcg_operand(seed + 100u + i);
+  }
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  f32x16_t acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = f32x16_t{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], b[(i >> 2) & 3], acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// out: device, grid x 256 floats; clk: device, two uint64 words. Returns 0,
+// -1 on bad arguments, -5 when the launch failed.
+int probe_mfma_loop(float* out, int iters, unsigned long long* clk, int grid, hipStream_t stream) {
+  if (out == nullptr || clk == nullptr || iters < 1 || grid < 1) return -1;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, out, iters, clk);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 
 // out: device, two uint64 words (shader-clock ticks, 100 MHz ticks).
 int probe_clock(unsigned long long* out, int ticks, hipStream_t stream) {

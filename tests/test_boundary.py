@@ -360,3 +360,25 @@ def test_backward_argument_errors():
     assert disp(6, 12) == -6
     assert disp(7, 0) == -3
     assert disp(4, 0) == 0
+
+
+def test_bench_probe_library_exports_and_argument_checks():
+    """libmoe_bench.so (the benchmark's measurement kernels) loads, exports its
+    three probes, and rejects bad arguments before any launch."""
+    path = os.path.join(os.path.dirname(ops.LIB_PATH), "libmoe_bench.so")
+    if not os.path.exists(path):
+        pytest.skip("libmoe_bench.so not built")
+    L = ctypes.CDLL(path)
+    for name in ("probe_stream_read", "probe_clock", "probe_mfma_loop"):
+        assert hasattr(L, name), name
+    L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert L.probe_stream_read(None, 16, None, 1, None) == -1
+    assert L.probe_stream_read(ctypes.c_void_p(16), 15, ctypes.c_void_p(16), 1, None) == -1   # not a multiple of 16
+    assert L.probe_stream_read(ctypes.c_void_p(8), 16, ctypes.c_void_p(16), 1, None) == -1    # misaligned
+    assert L.probe_clock(None, 10, None) == -1
+    assert L.probe_clock(ctypes.c_void_p(16), 0, None) == -1
+    assert L.probe_mfma_loop(None, 1, ctypes.c_void_p(16), 1, None) == -1
+    assert L.probe_mfma_loop(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), 1, None) == -1
+    assert L.probe_mfma_loop(ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 0, None) == -1
