@@ -507,15 +507,27 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
 
     names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine"]
 
+    # routed bf16 layers with few enough (tile, expert) cells: the router counts
+    # its token tiles' choices and sums their softmax columns, and the plan (with
+    # the aux loss) is built from those in one launch
+    tiles = cfg.routed and b.tiles
+
     def k_router():
-        if cfg.routed:
+        if tiles:
+            ops.moe_router_topk_tiles(x, wg, bias, cfg.k, 0, True, True, b.topk_idx, b.topk_w, b.probs,
+                                      b.tile_counts, b.tile_colsum)
+        elif cfg.routed:
             ops.moe_router_topk(x, wg, bias, cfg.k, 0, True, b.topk_idx, b.topk_w, b.probs)
 
     idx, w = (b.topk_idx, b.topk_w) if cfg.routed else (given_idx, given_w)
 
     def k_plan():
-        # routed layers: the plan with the aux loss folded in (moe_dispatch_plan_aux)
-        if cfg.routed:
+        # routed layers: the plan with the aux loss folded in (moe_dispatch_plan_tiles
+        # or moe_dispatch_plan_aux)
+        if tiles:
+            ops.moe_dispatch_plan_tiles(idx, b.tile_counts, b.tile_colsum, cfg.E, C, cfg.alpha, b.counts,
+                                        b.offsets, b.dest, b.src, b.loss)
+        elif cfg.routed:
             ops.moe_dispatch_plan_aux(idx, b.probs, cfg.E, C, cfg.alpha, b.counts, b.offsets, b.dest, b.src,
                                       b.loss, b.ws_plan_aux)
         else:
@@ -585,7 +597,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
         # the plan is integer work of a few hundred KB: latency, reported in us
         # only; on routed layers it also forms the aux loss
         "dispatch_plan": {"us": us["dispatch_plan"], "bytes": T * k * 4 * 2 + R * 4 + 2 * E * 4,
-                          "includes_aux_loss": bool(cfg.routed)},
+                          "includes_aux_loss": bool(cfg.routed),
+                          "from_router_tiles": bool(tiles)},
         "permute": {"us": us["permute"]},
         "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (us["up_gelu"] * 1e-6) / 1e12},
         "down": {"us": us["down"], "TFLOP/s": flops_down / (us["down"] * 1e-6) / 1e12},

@@ -191,6 +191,36 @@ int moe_dispatch_plan_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int
                               int32_t* dest, int32_t* src, hipStream_t stream);
 size_t moe_dispatch_plan_noalloc_scratch_bytes(void);
 
+/* The router and the dispatch plan handing over per-tile counts, so the plan
+ * needs no histogram pass of its own (EP tutorial 2.1 steps 1-2: the gate
+ * picks each token's experts, then the dispatch plan is built from those
+ * choices; 2.2: drop beyond capacity; 5.1: the aux loss).
+ *   moe_router_tiles(T, E): how many token tiles the bf16 router works in
+ *     (16 tokens each, 64 for 17..64 experts); 0 for T <= 0 or E outside
+ *     1..MOE_MAX_E.
+ *   moe_router_topk_tiles: moe_router_topk for bf16 (other dtypes:
+ *     MOE_ERR_DTYPE), and per tile i and expert e
+ *       tile_counts [tiles, E] int32 out: how many of the tile's tokens chose e
+ *         (16-byte aligned, required)
+ *       tile_colsum [tiles, E] double out, nullable: the tile's softmax
+ *         probabilities of e added in double in token order (8-byte aligned)
+ *   moe_dispatch_plan_tiles: moe_dispatch_plan from those counts in one
+ *     launch and without a workspace; with tile_colsum (and a device scalar
+ *     `loss`, both or neither) also the aux loss as moe_aux_loss defines it,
+ *     its column sums added tile by tile in tile order. topk_idx must be the
+ *     router's output the counts came from. Needs tiles x E <= 8192
+ *     (MOE_ERR_SHAPE otherwise: use moe_dispatch_plan). counts, offsets,
+ *     dest and src are bit-identical to moe_dispatch_plan's. */
+int64_t moe_router_tiles(int64_t T, int32_t E);
+int moe_router_topk_tiles(const void* x, const void* w_gate, const float* bias, int64_t T,
+                          int64_t d, int32_t E, int32_t k, int32_t dtype, uint32_t flags,
+                          int32_t* topk_idx, float* topk_w, float* probs, int32_t* tile_counts,
+                          double* tile_colsum, hipStream_t stream);
+int moe_dispatch_plan_tiles(const int32_t* topk_idx, const int32_t* tile_counts,
+                            const double* tile_colsum, int64_t T, int32_t k, int32_t E,
+                            int64_t capacity, float alpha, int32_t* counts, int32_t* offsets,
+                            int32_t* dest, int32_t* src, float* loss, hipStream_t stream);
+
 /* Grouped expert FFN over the expert-major segments given by `offsets`
  * (ETP page: up-projection w1 then down-projection w2, e.g.
  * 4096 -> 16384 -> 4096; EP tutorial 2.1 step 4: each expert computes on its

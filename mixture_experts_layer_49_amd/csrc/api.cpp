@@ -175,7 +175,87 @@ int moe_router_topk_ex(const void* x, const void* w_gate, const float* bias, con
   a.topk_w = topk_w;
   a.probs = probs;
   a.lse = lse;
+  a.tile_cnt = nullptr;
+  a.tile_colsum = nullptr;
   return hip_status(moe::launch_router(a, stream), "moe_router_topk launch");
+}
+
+int64_t moe_router_tiles(int64_t T, int32_t E) {
+  if (T <= 0 || E < 1 || E > MOE_MAX_E) return 0;
+  const int64_t tt = moe::router_tile_tokens(E);
+  return (T + tt - 1) / tt;
+}
+
+int moe_router_topk_tiles(const void* x, const void* w_gate, const float* bias, int64_t T, int64_t d,
+                          int32_t E, int32_t k, int32_t dtype, uint32_t flags, int32_t* topk_idx,
+                          float* topk_w, float* probs, int32_t* tile_counts, double* tile_colsum,
+                          hipStream_t stream) {
+  MOE_TRY(check_dtype(dtype));
+  if (dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "per-tile counts come from the bf16 router only");
+  MOE_TRY(check_experts(E, k));
+  if (T < 0 || d <= 0) return fail(MOE_ERR_ARG, "need T >= 0 and d > 0");
+  if (T > (1LL << 31) / MOE_MAX_K) return fail(MOE_ERR_SHAPE, "T too large");
+  if (flags & ~MOE_RENORM) return fail(MOE_ERR_ARG, "unknown flag bits 0x%x", flags);
+  MOE_TRY(check_row("d", d, dtype));
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(x);
+  MOE_NONNULL(w_gate);
+  MOE_NONNULL(topk_idx);
+  MOE_NONNULL(topk_w);
+  MOE_NONNULL(tile_counts);
+  MOE_TRY(check_ptr16("x", x));
+  MOE_TRY(check_ptr16("w_gate", w_gate));
+  if ((reinterpret_cast<uintptr_t>(tile_colsum) & 7u) != 0)
+    return fail(MOE_ERR_ALIGN, "tile_colsum is not 8-byte aligned");
+  moe::RouterArgs a;
+  a.x = x;
+  a.wg = w_gate;
+  a.bias = bias;
+  a.noise = nullptr;
+  a.temperature = 1.0f;
+  a.T = T;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.dtype = dtype;
+  a.flags = flags;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.probs = probs;
+  a.lse = nullptr;
+  a.tile_cnt = tile_counts;
+  a.tile_colsum = tile_colsum;
+  return hip_status(moe::launch_router(a, stream), "moe_router_topk_tiles launch");
+}
+
+int moe_dispatch_plan_tiles(const int32_t* topk_idx, const int32_t* tile_counts, const double* tile_colsum,
+                            int64_t T, int32_t k, int32_t E, int64_t capacity, float alpha, int32_t* counts,
+                            int32_t* offsets, int32_t* dest, int32_t* src, float* loss, hipStream_t stream) {
+  MOE_TRY(check_experts(E, k));
+  if (T < 0) return fail(MOE_ERR_ARG, "need T >= 0");
+  if (T * k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T * k must stay below 2^31");
+  MOE_NONNULL(counts);
+  MOE_NONNULL(offsets);
+  if ((tile_colsum == nullptr) != (loss == nullptr))
+    return fail(MOE_ERR_ARG, "tile_colsum and loss go together (both or neither)");
+  const int64_t rows = moe_router_tiles(T, E);
+  if (rows * E > moe::dispatch_tiles_max())
+    return fail(MOE_ERR_SHAPE, "%lld tiles x %d experts exceed %d (use moe_dispatch_plan)",
+                static_cast<long long>(rows), E, moe::dispatch_tiles_max());
+  if (T > 0) {
+    MOE_NONNULL(topk_idx);
+    MOE_NONNULL(tile_counts);
+    MOE_NONNULL(dest);
+    MOE_NONNULL(src);
+    if ((reinterpret_cast<uintptr_t>(tile_counts) & 15u) != 0)
+      return fail(MOE_ERR_ALIGN, "tile_counts is not 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(tile_colsum) & 7u) != 0)
+      return fail(MOE_ERR_ALIGN, "tile_colsum is not 8-byte aligned");
+  }
+  return hip_status(moe::launch_dispatch_plan_tiles(topk_idx, tile_counts, tile_colsum, moe::router_tile_tokens(E),
+                                                    T, k, E, capacity, alpha, counts, offsets, dest, src, loss,
+                                                    stream),
+                    "moe_dispatch_plan_tiles launch");
 }
 
 int moe_router_topk(const void* x, const void* w_gate, const float* bias, int64_t T, int64_t d,

@@ -24,6 +24,9 @@
 // (moe_dispatch_plan_aux): the histogram workgroups also add up their chunk's
 // softmax columns in double, in token order, and place workgroup 0 adds those
 // chunk sums in chunk order and forms L from them and the counts.
+// moe_dispatch_plan_tiles skips step 1: the bf16 router already counted each
+// of its token tiles' choices per expert (and summed the tile's softmax
+// columns), so one place launch scans those rows instead.
 #include <mutex>
 
 #include "moe_internal.h"
@@ -210,14 +213,16 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const int32_t* __restri
   }
 }
 
-// place with the scan folded in (chunks x experts <= kScanLds): every
-// workgroup loads all chunk counts into LDS, scans them for its own chunk's
+// place with the scan folded in (count rows x experts <= kScanLds): every
+// workgroup loads all count rows into LDS, scans them for its own chunk's
 // bases and for the offsets; workgroup 0 writes counts and offsets and, with
-// AUX, the aux loss from the chunk column sums.
+// AUX, the aux loss from the rows' column sums. A count row covers
+// kThreads / tpc tokens: the histogram's chunks (tpc = 1) or the router's
+// token tiles (tpc = kThreads / tile tokens), so chunk c starts at row c tpc.
 constexpr int kScanLds = 8192;
 template <bool AUX>
 __global__ __launch_bounds__(kThreads) void place_scan_kernel(
-    const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap, int nchunks,
+    const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap, int nchunks, int tpc,
     const int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ dest, int32_t* __restrict__ src, const double* __restrict__ colsum,
     float alpha, float* __restrict__ loss) {
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
   __shared__ int32_t s_cnt[kScanLds];
   __shared__ int32_t s_base[kMaxE];
   __shared__ int32_t s_buf[2][kMaxE];
+  __shared__ int32_t s_part[2][kThreads];
   __shared__ double s_red[kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = nchunks * E;
@@ -236,16 +242,34 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
     for (int i = tid; i < n; i += kThreads) s_cnt[i] = chunk_cnt[i];
   }
   build_masks(idx, T, k, E, mask);   // its barriers also publish s_cnt
-  const int c = blockIdx.x;
+  // Per expert, the rows before this chunk's first (its base) and all rows
+  // (the total): thread (ee = tid % E, g = tid / E) adds rows g, g + G, ...,
+  // and the G partial sums meet in LDS (integer sums: any order is exact).
+  const int c0 = blockIdx.x * tpc;
+  {
+    const int G = kThreads / E, ee = tid % E, g = tid / E;
+    int32_t pre = 0, tot = 0;
+    if (g < G) {
+      for (int cc = g; cc < nchunks; cc += G) {
+        const int32_t v = s_cnt[cc * E + ee];
+        tot += v;
+        pre += cc < c0 ? v : 0;
+      }
+    }
+    s_part[0][tid] = pre;
+    s_part[1][tid] = tot;
+  }
+  __syncthreads();
   int32_t kept = 0, total = 0;
   if (tid < E) {
-    int32_t run = 0;
-    for (int cc = 0; cc < nchunks; ++cc) {
-      if (cc == c) s_base[tid] = run;
-      run += s_cnt[cc * E + tid];
+    const int G = kThreads / E;
+    int32_t base = 0;
+    for (int g = 0; g < G; ++g) {
+      base += s_part[0][g * E + tid];
+      total += s_part[1][g * E + tid];
     }
-    total = run;
-    kept = (cap < 0 || run < cap) ? run : static_cast<int32_t>(cap);
+    s_base[tid] = base;
+    kept = (cap < 0 || total < cap) ? total : static_cast<int32_t>(cap);
   }
   // inclusive scan of kept over experts (Hillis-Steele), then exclusive
   const int e = tid;
@@ -380,10 +404,10 @@ hipError_t plan_impl(const int32_t* topk_idx, int64_t T, int k, int E, int64_t c
   if (static_cast<int64_t>(nchunks) * E <= kScanLds) {
     if (aux)
       hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
-                         nchunks, chunk_cnt, counts, offsets, dest, src, colsum, alpha, loss);
+                         nchunks, 1, chunk_cnt, counts, offsets, dest, src, colsum, alpha, loss);
     else
       hipLaunchKernelGGL(place_scan_kernel<false>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
-                         nchunks, chunk_cnt, counts, offsets, dest, src, nullptr, 0.f, nullptr);
+                         nchunks, 1, chunk_cnt, counts, offsets, dest, src, nullptr, 0.f, nullptr);
     return hipGetLastError();
   }
   int32_t* chunk_base = ws + static_cast<int64_t>(nchunks) * E;
@@ -405,6 +429,28 @@ hipError_t plan_impl(const int32_t* topk_idx, int64_t T, int k, int E, int64_t c
 size_t dispatch_aux_ws_bytes(int64_t T, int E) {
   const int64_t nchunks = (T + kThreads - 1) / kThreads;
   return dispatch_ws_ints(T, E) * sizeof(int32_t) + static_cast<size_t>(nchunks * E) * sizeof(double);
+}
+
+int dispatch_tiles_max() { return kScanLds; }
+
+hipError_t launch_dispatch_plan_tiles(const int32_t* topk_idx, const int32_t* tile_cnt,
+                                      const double* tile_colsum, int tile_tokens, int64_t T, int k,
+                                      int E, int64_t cap, float alpha, int32_t* counts,
+                                      int32_t* offsets, int32_t* dest, int32_t* src, float* loss,
+                                      hipStream_t s) {
+  if (T == 0) return plan_impl(topk_idx, T, k, E, cap, counts, offsets, dest, src, nullptr, nullptr, nullptr,
+                               alpha, loss, s);
+  if (tile_tokens < 1 || kThreads % tile_tokens != 0) return hipErrorInvalidValue;
+  const int nchunks = static_cast<int>((T + kThreads - 1) / kThreads);
+  const int nrows = static_cast<int>((T + tile_tokens - 1) / tile_tokens);
+  const int tpc = kThreads / tile_tokens;
+  if (tile_colsum != nullptr)
+    hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
+                       nrows, tpc, tile_cnt, counts, offsets, dest, src, tile_colsum, alpha, loss);
+  else
+    hipLaunchKernelGGL(place_scan_kernel<false>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
+                       nrows, tpc, tile_cnt, counts, offsets, dest, src, nullptr, 0.f, nullptr);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,

@@ -45,12 +45,29 @@ struct RouterArgs {
   float* topk_w;
   float* probs;         // nullable [T, E]
   float* lse;           // nullable [T]: log sum_e exp(score)
+  // nullable (bf16 only): per token tile of router_tile_tokens(E) tokens, how
+  // many of its assignments name each expert, and (tile_colsum, nullable)
+  // the tile's probabilities summed per expert in double, in token order
+  int32_t* tile_cnt;    // [ntiles, E]
+  double* tile_colsum;  // [ntiles, E]
 };
+// Tokens per router workgroup for E experts (bf16 kernel).
+int router_tile_tokens(int E);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
 hipError_t launch_dispatch_plan(const int32_t* topk_idx, int64_t T, int k, int E, int64_t cap,
                                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                                 int32_t* ws, hipStream_t s);
+
+// The dispatch plan from the router's per-tile counts (tile_tokens tokens per
+// tile, dividing kDispatchTok; ntiles x E <= dispatch_tiles_max()): one
+// launch, no workspace. With tile_colsum (and loss) also the aux loss.
+int dispatch_tiles_max();
+hipError_t launch_dispatch_plan_tiles(const int32_t* topk_idx, const int32_t* tile_cnt,
+                                      const double* tile_colsum, int tile_tokens, int64_t T, int k,
+                                      int E, int64_t cap, float alpha, int32_t* counts,
+                                      int32_t* offsets, int32_t* dest, int32_t* src, float* loss,
+                                      hipStream_t s);
 
 hipError_t launch_permute(const void* x, int64_t d, int elem_bytes, const int32_t* src,
                           const int32_t* offsets, int E, int64_t rows_max, void* x_perm,

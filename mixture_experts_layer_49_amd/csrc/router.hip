@@ -28,10 +28,12 @@ constexpr int kChunk = 128;   // d-elements one wave consumes per step
 
 // Softmax + top-k for one token held by a 16-lane group; lane q owns experts
 // e = q + 16*i (i < NT). Invalid experts (e >= E) carry -inf and are skipped.
+// With s_cnt (LDS, E ints) the token's valid choices are counted into it;
+// with s_p (LDS, E floats) its probabilities are also left there.
 template <int NT>
 __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int64_t t,
                             int q, int32_t* topk_idx, float* topk_w, float* probs,
-                            float* lse) {
+                            float* lse, int* s_cnt = nullptr, float* s_p = nullptr) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NT; ++i) m = fmaxf(m, lg[i]);
@@ -54,6 +56,13 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
     for (int i = 0; i < NT; ++i) {
       const int e = q + 16 * i;
       if (e < E) probs[t * E + e] = ex[i] * inv_s;
+    }
+  }
+  if (s_p) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = q + 16 * i;
+      if (e < E) s_p[e] = ex[i] * inv_s;
     }
   }
   // k rounds of a (logit desc, index asc) arg-max over the unchosen experts.
@@ -101,6 +110,7 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
       if (j < k) {
         topk_idx[t * k + j] = esel[j];
         topk_w[t * k + j] = (flags & 1u) ? wsel[j] * norm : wsel[j];
+        if (s_cnt != nullptr && esel[j] >= 0) atomicAdd(&s_cnt[esel[j]], 1);   // integer: order-free
       }
     }
   }
@@ -112,9 +122,13 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, const float* __restrict__ noise, float temperature,
     int64_t T, int64_t d, int E, int k, uint32_t flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ probs, float* __restrict__ lse) {
+    float* __restrict__ topk_w, float* __restrict__ probs, float* __restrict__ lse,
+    int32_t* __restrict__ tile_cnt, double* __restrict__ tile_colsum) {
   __shared__ float red[4][kTok * TT][NT * 16];
+  __shared__ int s_cnt[kMaxE];
   const int tid = threadIdx.x;
+  if (tile_cnt != nullptr)
+    for (int e = tid; e < E; e += kThreads) s_cnt[e] = 0;   // published by the barrier below
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok * TT;
@@ -190,7 +204,23 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
       if (noise != nullptr && e < E && t < T) v += noise[t * E + e];
       lg[i] = (e < E) ? v / temperature : -INFINITY;
     }
-    if (t < T) softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, lse);
+    // The token's row of red[0] is read above by the same lanes that may now
+    // leave its probabilities there (tile_colsum).
+    if (t < T)
+      softmax_topk<NT>(lg, E, k, flags, t, q, topk_idx, topk_w, probs, lse,
+                       tile_cnt != nullptr ? s_cnt : nullptr, tile_colsum != nullptr ? &red[0][tok][0] : nullptr);
+  }
+  if (tile_cnt != nullptr) {
+    __syncthreads();
+    const int64_t ntok = min<int64_t>(kTok * TT, T - t0);
+    for (int e = tid; e < E; e += kThreads) {
+      tile_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = s_cnt[e];
+      if (tile_colsum != nullptr) {
+        double acc = 0.0;
+        for (int64_t tok = 0; tok < ntok; ++tok) acc += static_cast<double>(red[0][tok][e]);
+        tile_colsum[static_cast<int64_t>(blockIdx.x) * E + e] = acc;
+      }
+    }
   }
 }
 
@@ -239,7 +269,7 @@ hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((router_bf16_kernel<NT, TT>), grid, block, 0, s,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,
                        a.noise, a.temperature, a.T, a.d, a.E, a.k, a.flags, a.topk_idx, a.topk_w,
-                       a.probs, a.lse);
+                       a.probs, a.lse, a.tile_cnt, a.tile_colsum);
   else
     hipLaunchKernelGGL(router_f32_kernel<NT>, grid_f32, block, 0, s, static_cast<const float*>(a.x),
                        static_cast<const float*>(a.wg), a.bias, a.noise, a.temperature, a.T, a.d,
@@ -248,6 +278,13 @@ hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int router_tile_tokens(int E) {
+  const int nt = (E + 15) / 16;
+  const int tt = nt <= 1 ? router_tiles<1>() : nt <= 2 ? router_tiles<2>() : nt <= 4 ? router_tiles<4>()
+               : nt <= 8 ? router_tiles<8>() : router_tiles<16>();
+  return kTok * tt;
+}
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;

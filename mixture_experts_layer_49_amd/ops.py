@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_DTYPE", -3: "MOE_ERR_SHAP
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_ex", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_dispatch_plan", "moe_dispatch_plan_aux",
            "moe_dispatch_plan_aux_workspace_bytes", "moe_dispatch_plan_noalloc",
-           "moe_dispatch_plan_noalloc_scratch_bytes", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
+           "moe_dispatch_plan_noalloc_scratch_bytes", "moe_router_tiles", "moe_router_topk_tiles",
+           "moe_dispatch_plan_tiles", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag",
            "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_expert_down_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
            "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
         "moe_dispatch_plan_aux_workspace_bytes": (SZ, [I64, I32, I32]),
         "moe_dispatch_plan_aux": (ctypes.c_int, [P, P, I64, I32, I32, I64, F32, P, P, P, P, P, P, SZ, P]),
         "moe_dispatch_plan_noalloc_scratch_bytes": (SZ, []),
+        "moe_router_tiles": (I64, [I64, I32]),
+        "moe_router_topk_tiles": (ctypes.c_int, [P, P, P, I64, I64, I32, I32, I32, U32, P, P, P, P, P, P]),
+        "moe_dispatch_plan_tiles": (ctypes.c_int, [P, P, P, I64, I32, I32, I64, F32, P, P, P, P, P, P]),
         "moe_permute": (ctypes.c_int, [P, I64, I32, P, P, I32, I64, P, P]),
         "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P, SZ, P]),
         "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
@@ -260,6 +264,56 @@ def moe_dispatch_plan_aux(topk_idx, probs, E: int, capacity: int, alpha: float, 
                                        _ptr(counts), _ptr(offsets), _ptr(dest), _ptr(src), _ptr(loss),
                                        _ptr(workspace), _ws_size(workspace), _stream(stream)))
     return counts, offsets, dest, src, loss
+
+
+def moe_router_tiles(T: int, E: int) -> int:
+    return lib().moe_router_tiles(T, E)
+
+
+def moe_router_topk_tiles(x, w_gate, bias, k: int, flags: int = 0, want_probs: bool = True,
+                          want_colsum: bool = True, topk_idx=None, topk_w=None, probs=None,
+                          tile_counts=None, tile_colsum=None, stream=None):
+    """The bf16 router that also counts each token tile's choices per expert
+    (and sums its softmax columns in double); returns topk_idx, topk_w, probs,
+    tile_counts, tile_colsum."""
+    T, d = x.shape
+    E = w_gate.shape[0]
+    n = max(moe_router_tiles(T, E), 1)
+    topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+    topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    if want_probs and probs is None:
+        probs = _empty((T, E), torch.float32, x)
+    tile_counts = _empty((n, E), torch.int32, x) if tile_counts is None else tile_counts
+    if want_colsum and tile_colsum is None:
+        tile_colsum = _empty((n, E), torch.float64, x)
+    _check(lib().moe_router_topk_tiles(_ptr(x), _ptr(w_gate), _ptr(bias), T, d, E, k, dtype_code(x.dtype), flags,
+                                       _ptr(topk_idx), _ptr(topk_w), _ptr(probs), _ptr(tile_counts),
+                                       _ptr(tile_colsum), _stream(stream)))
+    return topk_idx, topk_w, probs, tile_counts, tile_colsum
+
+
+def moe_dispatch_plan_tiles(topk_idx, tile_counts, tile_colsum, E: int, capacity: int, alpha: float = 0.0,
+                            counts=None, offsets=None, dest=None, src=None, loss=None, stream=None):
+    """moe_dispatch_plan (and, with tile_colsum, the aux loss) from the
+    router's per-tile counts; returns counts, offsets, dest, src, loss."""
+    T, k = topk_idx.shape
+    rows = moe_rows_max(T, k, E, capacity)
+    counts = _empty((E,), torch.int32, topk_idx) if counts is None else counts
+    offsets = _empty((E + 1,), torch.int32, topk_idx) if offsets is None else offsets
+    dest = _empty((T, k), torch.int32, topk_idx) if dest is None else dest
+    src = _empty((max(rows, 1),), torch.int32, topk_idx) if src is None else src
+    if tile_colsum is not None and loss is None:
+        loss = _empty((1,), torch.float32, topk_idx)
+    _check(lib().moe_dispatch_plan_tiles(_ptr(topk_idx), _ptr(tile_counts), _ptr(tile_colsum), T, k, E, capacity,
+                                         alpha, _ptr(counts), _ptr(offsets), _ptr(dest), _ptr(src),
+                                         _ptr(loss if tile_colsum is not None else None), _stream(stream)))
+    return counts, offsets, dest, src, (loss if tile_colsum is not None else None)
+
+
+def tiles_eligible(dtype, T: int, E: int) -> bool:
+    """Whether the router can hand the dispatch plan its per-tile counts:
+    bf16 and at most 8192 (tile, expert) count cells."""
+    return dtype == torch.bfloat16 and moe_router_tiles(T, E) * E <= 8192
 
 
 def moe_dispatch_plan_noalloc(topk_idx, E: int, capacity: int, counts, offsets, dest, src,
@@ -572,6 +626,12 @@ class MoEBuffers:
         self.ws_plan_aux = (z((max(moe_dispatch_plan_aux_workspace_bytes(T, k, E), 8),), torch.uint8)
                             if self.probs is not None else None)
         self.ws_aux = z((max(moe_aux_loss_workspace_bytes(T, E), 8),), torch.uint8)
+        # the router's per-tile counts (and column sums) for the plan that
+        # needs no histogram pass (bf16, few enough tile x expert cells)
+        nt = max(moe_router_tiles(T, E), 1)
+        self.tiles = routed and tiles_eligible(dtype, T, E)
+        self.tile_counts = z((nt, E), torch.int32) if self.tiles else None
+        self.tile_colsum = z((nt, E), torch.float64) if (self.tiles and self.probs is not None) else None
         self.used_idx, self.used_w = self.topk_idx, self.topk_w
         nb = moe_ffn_workspace_bytes(dtype)
         self.ws_ffn = z((nb,), torch.uint8) if nb > 0 else None
@@ -602,11 +662,17 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     if bufs is None:
         bufs = MoEBuffers(T, d, d_ff, E, k, capacity, x.dtype, x.device, routed,
                           save_for_backward=save_for_backward, w2_f16=w2_f16 is not None)
+    # the plain bf16 router can count its tiles' choices for the plan
+    tiles = (routed and bufs.tiles and temperature == 1.0 and noise is None and bufs.lse is None)
     if routed:
         if temperature != 1.0 or noise is not None or bufs.lse is not None:
             moe_router_topk_ex(x, w_gate, bias, k, flags, temperature, noise,
                                bufs.probs is not None, bufs.lse is not None, bufs.topk_idx,
                                bufs.topk_w, bufs.probs, bufs.lse, stream)
+        elif tiles:
+            moe_router_topk_tiles(x, w_gate, bias, k, flags, bufs.probs is not None, bufs.tile_colsum is not None,
+                                  bufs.topk_idx, bufs.topk_w, bufs.probs, bufs.tile_counts, bufs.tile_colsum,
+                                  stream)
         else:
             moe_router_topk(x, w_gate, bias, k, flags, bufs.probs is not None, bufs.topk_idx,
                             bufs.topk_w, bufs.probs, stream)
@@ -627,8 +693,12 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
 
     # the dispatch plan, with the aux loss folded in where the router's
     # probabilities are kept
-    aux_done = routed and bufs.probs is not None and bufs.ws_plan_aux is not None
-    if aux_done:
+    aux_done = routed and bufs.probs is not None and (bufs.ws_plan_aux is not None or tiles)
+    if tiles:
+        moe_dispatch_plan_tiles(idx, bufs.tile_counts, bufs.tile_colsum, E, capacity, alpha, bufs.counts,
+                                bufs.offsets, bufs.dest, bufs.src, bufs.loss if bufs.tile_colsum is not None
+                                else None, stream)
+    elif aux_done:
         moe_dispatch_plan_aux(idx, bufs.probs, E, capacity, alpha, bufs.counts, bufs.offsets, bufs.dest,
                               bufs.src, bufs.loss, bufs.ws_plan_aux, stream)
     else:

@@ -382,3 +382,25 @@ def test_bench_probe_library_exports_and_argument_checks():
     assert L.probe_mfma_loop(None, 1, ctypes.c_void_p(16), 1, None) == -1
     assert L.probe_mfma_loop(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), 1, None) == -1
     assert L.probe_mfma_loop(ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 0, None) == -1
+
+
+def test_router_tiles_and_plan_tiles_argument_errors():
+    L = ops.lib()
+    assert L.moe_router_tiles(0, 8) == 0 and L.moe_router_tiles(8192, 0) == 0 and L.moe_router_tiles(1, 257) == 0
+    assert L.moe_router_tiles(8192, 8) == 512 and L.moe_router_tiles(16384, 64) == 256
+    assert L.moe_router_tiles(17, 16) == 2 and L.moe_router_tiles(100, 100) == 7
+    p = ctypes.c_void_p(4096)
+    # f32: the tile outputs come from the bf16 router only
+    assert L.moe_router_topk_tiles(p, p, None, 16, 64, 8, 2, 0, 0, p, p, None, p, None, None) == -2
+    assert L.moe_router_topk_tiles(p, p, None, 16, 64, 8, 9, 1, 0, p, p, None, p, None, None) == -3   # k > E
+    assert L.moe_router_topk_tiles(p, p, None, 16, 64, 8, 2, 1, 0, p, p, None, None, None, None) == -1   # no counts
+    assert L.moe_router_topk_tiles(p, p, None, 16, 64, 8, 2, 1, 0, p, p, None, p, ctypes.c_void_p(4100),
+                                   None) == -6   # colsum alignment
+    assert L.moe_router_topk_tiles(p, p, None, 0, 64, 8, 2, 1, 0, None, None, None, None, None, None) == 0
+    # plan from tiles: colsum and loss go together; too many cells; alignment
+    assert L.moe_dispatch_plan_tiles(p, p, p, 16, 2, 8, 4, 0.01, p, p, p, p, None, None) == -1
+    assert L.moe_dispatch_plan_tiles(p, p, None, 16, 2, 8, 4, 0.0, p, p, p, p, p, None) == -1
+    assert L.moe_dispatch_plan_tiles(p, p, None, 20000, 2, 8, 4, 0.0, p, p, p, p, None, None) == -3
+    assert L.moe_dispatch_plan_tiles(p, ctypes.c_void_p(4100), None, 16, 2, 8, 4, 0.0, p, p, p, p, None,
+                                     None) == -6
+    assert L.moe_dispatch_plan_tiles(p, None, None, 16, 2, 8, 4, 0.0, p, p, p, p, None, None) == -1

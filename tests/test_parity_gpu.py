@@ -298,6 +298,61 @@ def test_plan_aux_equals_plan_then_aux_loss(T, E, k, cf, seed):
     assert abs(lg - want) <= 1e-5 * abs(want) + 1e-12
 
 
+@pytest.mark.parametrize("T,E,k,d,cf,seed", [(300, 6, 2, 256, 1.25, 11), (17, 8, 2, 128, 1.0, 12),
+                                             (1, 4, 1, 64, 1.25, 13), (4096, 16, 2, 1024, 1.0, 14),
+                                             (8192, 8, 2, 512, 1.25, 15), (1000, 40, 3, 256, 1.0, 16),
+                                             (8192, 64, 2, 256, 1.25, 17), (777, 100, 4, 128, 0.0, 18),
+                                             (0, 8, 2, 64, 1.25, 19)])
+def test_router_tiles_and_plan_tiles(T, E, k, d, cf, seed):
+    """The bf16 router's per-tile outputs and the plan built from them:
+    routing bit-identical to moe_router_topk; tile counts equal to a host
+    histogram of topk_idx per tile; tile column sums equal to the probabilities
+    summed per tile (to double rounding of float32 values); the plan bit for
+    bit moe_dispatch_plan's; the loss to double rounding of moe_dispatch_plan_aux
+    and to the oracle's 1e-5 (cf 0: no dropping)."""
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((max(T, 1), d)).astype(np.float32))[:T].to(torch.bfloat16).to("cuda:0")
+    wg = torch.from_numpy((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)).to(torch.bfloat16).to("cuda:0")
+    bias = torch.from_numpy(rng.standard_normal(E).astype(np.float32) * 0.1).to("cuda:0")
+    C = ops.moe_capacity(T, E, cf)
+    alpha = 0.01
+    ri, rw, rp = ops.moe_router_topk(x, wg, bias, k)
+    ti, tw, tp, tc, ts = ops.moe_router_topk_tiles(x, wg, bias, k)
+    torch.cuda.synchronize()
+    assert torch.equal(ti, ri) and torch.equal(tw, rw) and torch.equal(tp, rp)
+    tile = 64 if 17 <= E <= 64 else 16   # as include/moe.h documents
+    n = ops.moe_router_tiles(T, E)
+    assert n == (T + tile - 1) // tile
+    idx_h, p_h = host(ri).astype(np.int64), host(rp).astype(np.float64)
+    want_c = np.zeros((n, E), np.int64)
+    want_s = np.zeros((n, E), np.float64)
+    for t in range(T):
+        want_c[t // tile] += np.bincount(idx_h[t], minlength=E)
+        want_s[t // tile] += p_h[t]
+    if T:
+        np.testing.assert_array_equal(host(tc)[:n], want_c)
+        np.testing.assert_allclose(host(ts)[:n], want_s, rtol=1e-12, atol=1e-12)
+    ref = ops.moe_dispatch_plan(ri, E, C)
+    got = ops.moe_dispatch_plan_tiles(ti, tc, ts, E, C, alpha)
+    aux = ops.moe_dispatch_plan_aux(ri, rp, E, C, alpha)
+    torch.cuda.synchronize()
+    R = int(host(ref[1])[-1])
+    for a, b in zip(got[:3], ref[:3]):
+        assert torch.equal(a, b)
+    assert torch.equal(got[3][:R], ref[3][:R])
+    lg, la = float(host(got[4])[0]), float(host(aux[4])[0])
+    want = O.aux_loss(p_h, host(ref[0]), k, alpha) if T else 0.0
+    say("  T=%d E=%d: tiles %.9g plan_aux %.9g oracle %.9g" % (T, E, lg, la, want))
+    assert abs(lg - la) <= 2e-7 * abs(la) + 1e-12
+    assert abs(lg - want) <= 1e-5 * abs(want) + 1e-12
+    # without column sums: the plan alone
+    got2 = ops.moe_dispatch_plan_tiles(ti, tc, None, E, C)
+    torch.cuda.synchronize()
+    for a, b in zip(got2[:3], ref[:3]):
+        assert torch.equal(a, b)
+    assert got2[4] is None
+
+
 def test_dispatch_ignores_invalid_and_repeated_ids():
     """Ids outside [0,E) and repeats inside a token are skipped. Expected plan:
     the oracle's, with every skipped slot sent to an extra expert E placed
