@@ -34,6 +34,10 @@
 //     then the next stage has landed and every wave holds the last slice's
 //     fragments, so the stage two ahead is issued into the freed slot and the
 //     next stage's first fragments are read while the fourth slice's MFMAs run;
+//   * the k-slices are laid out instruction by instruction: after each MFMA
+//     comes at most one LDS read of the next slice's fragments (in the order
+//     its MFMAs need them), one memory load and, for converting kinds, one
+//     fragment's conversion, each fenced so the compiler keeps the order;
 //   * K-contiguous operand in LDS: a tile row is 8 chunks of 16 B; logical
 //     chunk c of row r sits at chunk c ^ ((r >> 1) & 7). A fragment read
 //     touches 16 consecutive rows at one logical chunk per LDS cycle, which
@@ -497,45 +501,92 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     }
   };
 
+  // Reads of one slice in the order the next slice's MFMAs need them (tile
+  // (m / 4, m % 4) for MFMA m): A0, B0 .. B3, A1 .. A3, a k-major fragment
+  // as two reads (its lower and upper four k-values).
+  constexpr int kPA = AKM ? 2 : 1, kPB = BKM ? 2 : 1;
+  constexpr int kNR = MI * kPA + NI * kPB;   // reads per slice
+  auto read_one = [&](int S, int kk, int fs, int r) __attribute__((always_inline)) {
+    const char* const base = reinterpret_cast<const char*>(L(S));
+    const int c = fr_x ^ (kk * 2);
+    bool isa;
+    int idx, part;
+    if (r < kPA) {
+      isa = true, idx = 0, part = r;
+    } else if (r < kPA + NI * kPB) {
+      isa = false, idx = (r - kPA) / kPB, part = (r - kPA) % kPB;
+    } else {
+      isa = true, idx = 1 + (r - kPA - NI * kPB) / kPA, part = (r - kPA - NI * kPB) % kPA;
+    }
+    if (isa) {
+      if constexpr (AKM) {
+        const uint2 v = ds_read_tr(base + tr_a + kk * 8192 + idx * 256 + part * 2048);
+        if (part == 0) fa[fs][idx].x = v.x, fa[fs][idx].y = v.y;
+        else fa[fs][idx].z = v.x, fa[fs][idx].w = v.y;
+      } else {
+        fa[fs][idx] = L(S)[fr_a + c + idx * 32 * kCpr];
+      }
+    } else {
+      if constexpr (BKM) {
+        const uint2 v = ds_read_tr(base + tr_b + kk * 8192 + idx * 256 + part * 2048);
+        if (part == 0) fb[fs][idx].x = v.x, fb[fs][idx].y = v.y;
+        else fb[fs][idx].z = v.x, fb[fs][idx].w = v.y;
+      } else {
+        fb[fs][idx] = L(S)[fr_b + c + idx * 32 * kCpr];
+      }
+    }
+  };
+  // position of read r in a slice, and of B fragment j's conversion
+  auto read_pos = [](int r) { return (r * 16) / kNR; };
+  auto conv_pos = [&](int j) {
+    const int last = read_pos(kPA + j * kPB + kPB - 1);   // B fragment j's last read
+    return last + 6 < 16 ? last + 6 : 15;
+  };
+
   f32x16 acc[MI][NI];
-  // 16 MFMAs of fragment set fs; converting kinds convert set cs between them.
-  // ND (a compile-time count) loads j0 .. j0+ND-1 of stage kt (slot S) are
-  // issued between them as well, one after every 16/ND-th MFMA.
-  auto mfma_block = [&](int fs, int cs, auto nd_c, int kt, int S, int j0) __attribute__((always_inline)) {
+  // 16 MFMAs of set fs laid out one by one: after MFMA m (tile (m / 4, m % 4))
+  // come, where the plan puts them, one read of the next slice (slot rS,
+  // k-slice rkk >= 0, into set fs ^ 1), one load (ND of them, loads l0 .. of
+  // stage lkt into slot lS, spread evenly) and, for converting kinds, the
+  // conversion of one B fragment of set fs ^ 1 once its read has landed; each
+  // piece is fenced so the compiler keeps the order.
+  auto xblock = [&](int fs, int rS, int rkk, auto nd_c, int lkt, int lS, int l0) __attribute__((always_inline)) {
     constexpr int ND = decltype(nd_c)::value;
-    if constexpr (ND > 0) issue_range(cur, kt, S, j0, j0 + ND);
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int m = 0; m < 16; ++m) {
+      const int i = m >> 2, j = m & 3;
+      if constexpr (!F16)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[fs][i]),
+                                                            __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[fs][i]),
+                                                           __builtin_bit_cast(f16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (rkk >= 0) {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        if constexpr (!F16)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[fs][i]), __builtin_bit_cast(bf16x8, fb[fs][j]),
-              acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, fa[fs][i]), __builtin_bit_cast(f16x8, fb[fs][j]),
-              acc[i][j], 0, 0, 0);
+        for (int r = 0; r < kNR; ++r)
+          if (read_pos(r) == m) {
+            read_one(rS, rkk, fs ^ 1, r);
+            __builtin_amdgcn_sched_barrier(0);
+          }
       }
-    if constexpr (CVT != kCvtNone) {
-      conv_fb(cs);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if constexpr (ND > 0) {
 #pragma unroll
-      for (int q = 0; q < 12; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        if (ND > 0 && q * ND % 12 < ND) {
-          __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+        for (int v = 0; v < ND; ++v)
+          if ((v * 16) / ND + (ND < 16 ? 1 : 0) == m) {
+            issue_range(cur, lkt, lS, l0 + v, l0 + v + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
       }
-    } else if constexpr (ND > 0) {
+      if constexpr (CVT != kCvtNone) {
+        if (rkk >= 0) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if ((q + 15) * ND % 16 < ND) {   // after MFMA 1, 1 + 16/ND, ...
-          __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          for (int jc = 0; jc < NI; ++jc)
+            if (conv_pos(jc) == m) {
+              if constexpr (CVT == kCvtBf16ToF16) fb[fs ^ 1][jc] = bf16x8_to_f16x8(fb[fs ^ 1][jc]);
+              else fb[fs ^ 1][jc] = f16x8_to_bf16x8(fb[fs ^ 1][jc]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
         }
       }
     }
@@ -548,17 +599,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   auto slices012 = [&](int S, int kt, auto pend_c) __attribute__((always_inline)) {
     constexpr bool PEND = decltype(pend_c)::value;
     using L01 = std::conditional_t<PEND, SliceLoads, NoLoads>;
-    read_frags(S, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(0, 1, L01{}, kt + 1, S ^ 1, kSpread0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(S, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(1, 0, L01{}, kt + 1, S ^ 1, kSpread0 + kSpreadPer);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(S, 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(0, 1, NoLoads{}, 0, 0, 0);
+    xblock(0, S, 1, L01{}, kt + 1, S ^ 1, kSpread0);
+    xblock(1, S, 2, L01{}, kt + 1, S ^ 1, kSpread0 + kSpreadPer);
+    xblock(0, S, 3, NoLoads{}, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   // Loads of stage kt+1 (slot S^1) a steady boundary left, issued at once
@@ -567,9 +611,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     if (pend) issue_range(cur, kt + 1, S ^ 1, kSpread0, kLoadsPerStage);
     pend = false;
   };
-  auto slice3 = [&]() __attribute__((always_inline)) {
+  // The fourth slice with the next stage's first fragments read from slot
+  // rS (rS < 0: none, the last slice of a unit).
+  auto slice3 = [&](int rS) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(1, 0, NoLoads{}, 0, 0, 0);
+    xblock(1, rS < 0 ? 0 : rS, rS < 0 ? -1 : 0, NoLoads{}, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -581,33 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   // follows during the next stage's first two slices.
   auto boundary = [&](int kt, int S) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_range(cur, kt + 2, S, 0, kSpread0);
-    read_frags(S ^ 1, 0, 0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        if constexpr (!F16)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[1][i]), __builtin_bit_cast(bf16x8, fb[1][j]), acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, fa[1][i]), __builtin_bit_cast(f16x8, fb[1][j]), acc[i][j], 0, 0, 0);
-      }
-    conv_fb(0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-      if (q * kSpread0 % 16 < kSpread0) {
-        __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);   // SALU (DMA setup)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
-      }
-      if (q >= 2 && q < 6) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU (read addresses)
-        __builtin_amdgcn_sched_group_barrier(0x100, AKM || BKM ? 3 : 2, 0);   // DS read
-      }
-      if (CVT != kCvtNone && q >= 8) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // conversion
-    }
+    xblock(1, S ^ 1, 0, std::integral_constant<int, kSpread0>{}, kt + 2, S, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   // Steady stage: stage kt+1 needs no zero fill and stage kt+2 belongs to this tile.
@@ -637,8 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       MOE_BARRIER();
     }
     issue(cur, kt + 2, S);
-    read_frags(S ^ 1, 0, 0);
-    slice3();
+    slice3(S ^ 1);
   };
 
   auto emit = [&](int c_e, int grow, int gcol, const float4& a, const float4& b) {
@@ -866,10 +885,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       make_ctx(u.tile, cur);
       issue(cur, u.klo, 0);
     }
-    read_frags(1, 0, 0);
-    slice3();
+    slice3(1);
     slices012(1, kt + 1, std::false_type{});
-    slice3();
+    slice3(-1);
 
     MOE_BARRIER();   // every wave is done reading slot 1
     // A whole tile leaves through the per-wave epilogue, after the next unit's
