@@ -234,6 +234,27 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
   __shared__ double s_red[kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = nchunks * E;
+  // Workgroup 0 (the one that forms the aux loss, the launch's longest) adds
+  // up its share of the column sums first, so those loads overlap the count
+  // loads and the masks: thread (ee = tid % E, g = tid / E) adds the rows g,
+  // g + G, ... of expert ee, eight in flight; the G group sums are added in
+  // g order below.
+  double part = 0.0;
+  if constexpr (AUX) {
+    const int G = kThreads / E;
+    const int ee = tid % E, g = tid / E;
+    if (blockIdx.x == 0 && g < G) {
+      constexpr int U = 8;
+      for (int c0 = g; c0 < nchunks; c0 += U * G) {
+        double v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = colsum[static_cast<int64_t>(min(c0 + u * G, nchunks - 1)) * E + ee];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (c0 + u * G < nchunks) part += v[u];
+      }
+    }
+  }
   // all chunk counts, 16 bytes per load where the count is a multiple of 4
   if ((n & 3) == 0) {
     const int4* c4 = reinterpret_cast<const int4*>(chunk_cnt);
@@ -295,22 +316,7 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
     if (e == 0) offsets[0] = 0;
     if constexpr (AUX) {
       double term = 0.0;
-      // thread (ee = tid % E, g = tid / E) adds the chunk sums g, g + G, ...
-      // of expert ee, eight in flight; the G group sums are added in g order
       const int G = kThreads / E;
-      const int ee = tid % E, g = tid / E;
-      double part = 0.0;
-      if (g < G) {
-        constexpr int U = 8;
-        for (int c0 = g; c0 < nchunks; c0 += U * G) {
-          double v[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) v[u] = colsum[static_cast<int64_t>(min(c0 + u * G, nchunks - 1)) * E + ee];
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            if (c0 + u * G < nchunks) part += v[u];
-        }
-      }
       s_red[tid] = part;
       __syncthreads();
       if (e < E && T > 0) {
