@@ -117,7 +117,15 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
 }
 
 // bf16: MFMA logits, LDS reduction over the four d-slices, then softmax/top-k.
-template <int NT, int TT>
+// WLU > 0 (one 16-expert tile, one token tile, d = 512 WLU): the gate weight
+// is staged once per workgroup in LDS by LDS-DMA (rows kWlPad bytes apart
+// beyond d, so the 16 rows of a fragment read fall on distinct banks) and
+// each wave issues all of its x loads at once, no gate-weight loads among
+// them; the MFMAs run in the same order as the other form's, so the logits
+// are bit-identical to it.
+constexpr int kWlPad = 16;
+constexpr int kWlMaxBytes = 64 * 1024;   // gate weight staged in LDS at most
+template <int NT, int TT, int WLU>
 __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, const float* __restrict__ noise, float temperature,
@@ -143,6 +151,52 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[tt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  constexpr bool WL = WLU > 0;
+  if constexpr (WL) {
+    static_assert(NT == 1 && TT == 1, "one expert tile, one token tile");
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_wg[];
+    const int64_t rs = d * 2 + kWlPad;   // bytes per staged row
+    // the gate weight goes to LDS by LDS-DMA (no registers): wave-wide load
+    // j carries bytes 1024 j .. +1023 of the weight, inside one row (2 d is a
+    // multiple of 1024); then every x load of this wave is issued
+    {
+      const int64_t wbytes = static_cast<int64_t>(E) * d * 2;
+      const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(wg), 0, static_cast<int>(wbytes), 0x00020000);
+      const int njobs = static_cast<int>(wbytes / 1024);
+      for (int j = wave; j < njobs; j += 4) {
+        const int64_t off = static_cast<int64_t>(j) * 1024;
+        unsigned char* dst = s_wg + (off / (d * 2)) * rs + off % (d * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 static_cast<uint32_t>(lane) * 16u, static_cast<uint32_t>(off), 0, 0);
+      }
+    }
+    // d = 512 WLU: every one of the 4 WLU loads is in range, so the wait
+    // below counts exactly the x loads younger than the weight's DMA
+    bf16x8 a[WLU][4];
+#pragma unroll
+    for (int u = 0; u < WLU; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int col = wave * kChunk + u * 4 * kChunk + s * 32 + g * 8;
+        a[u][s] = *reinterpret_cast<const bf16x8*>(xrow[0] + col);
+      }
+    // the weight's DMA is older than the x loads: wait for it alone, then
+    // every wave's share is in LDS after the barrier
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((WLU * 4) & 15) | (((WLU * 4) >> 4) << 14));
+    __syncthreads();
+    const unsigned char* const brow = s_wg + static_cast<int64_t>(min(r, E - 1)) * rs;
+#pragma unroll
+    for (int u = 0; u < WLU; ++u) {
+      const int c0 = wave * kChunk + u * 4 * kChunk;
+      bf16x8 b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(brow + (c0 + s * 32 + g * 8) * 2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s], b[s], acc[0][0], 0, 0, 0);
+    }
+  }
   const uint16_t* wrow[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) wrow[n] = wg + static_cast<int64_t>(min(n * 16 + r, E - 1)) * d;
@@ -154,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
   // columns 32 s .. 32 s + 31 and lane group g the eight from 32 s + 8 g, so
   // the four groups of a row read 64 contiguous bytes.
   constexpr int U = (NT * (TT + 1)) <= 4 ? 4 : ((NT * (TT + 1)) <= 8 ? 2 : 1);
-  for (int64_t c00 = static_cast<int64_t>(wave) * kChunk; c00 < d; c00 += 4 * U * kChunk) {
+  for (int64_t c00 = static_cast<int64_t>(wave) * kChunk; !WL && c00 < d; c00 += 4 * U * kChunk) {
     bf16x8 a[U][TT][4], b[U][NT][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -265,8 +319,26 @@ hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
   constexpr int TT = router_tiles<NT>();
   const dim3 grid(static_cast<unsigned>((a.T + kTok * TT - 1) / (kTok * TT))), block(kThreads);
   const dim3 grid_f32(static_cast<unsigned>((a.T + kTok - 1) / kTok));
-  if (a.dtype == 1)
-    hipLaunchKernelGGL((router_bf16_kernel<NT, TT>), grid, block, 0, s,
+  // the staged-weight form for one expert tile with the weight within 64 KiB
+  // where it measured faster: d = 4096 (8 experts: router 21.8 -> 20.2 us with
+  // cold caches); at d = 1024 (16 experts) it measured slower (9.6 -> 10.1 us),
+  // the weight being as many bytes per workgroup as its tokens' rows
+  const int wlu = (NT == 1 && TT == 1 && static_cast<int64_t>(a.E) * a.d * 2 <= kWlMaxBytes && a.d == 4096)
+                      ? 8 : 0;
+  const size_t lds = static_cast<size_t>(a.E) * static_cast<size_t>(a.d * 2 + kWlPad);
+  auto launch_wl = [&](auto u_c) {
+    constexpr int WU = decltype(u_c)::value;
+    hipLaunchKernelGGL((router_bf16_kernel<NT, TT, WU>), grid, block, lds, s,
+                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,
+                       a.noise, a.temperature, a.T, a.d, a.E, a.k, a.flags, a.topk_idx, a.topk_w,
+                       a.probs, a.lse, a.tile_cnt, a.tile_colsum);
+  };
+  if (a.dtype == 1 && wlu > 0) {
+    if constexpr (NT == 1 && TT == 1) {
+      launch_wl(std::integral_constant<int, 8>{});
+    }
+  } else if (a.dtype == 1)
+    hipLaunchKernelGGL((router_bf16_kernel<NT, TT, 0>), grid, block, 0, s,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,
                        a.noise, a.temperature, a.T, a.d, a.E, a.k, a.flags, a.topk_idx, a.topk_w,
                        a.probs, a.lse, a.tile_cnt, a.tile_colsum);
