@@ -67,6 +67,10 @@ def parse(argv=None):
                     help="time the vendor library's dense bf16 GEMM (torch.matmul -> hipBLASLt) on the "
                          "workload's expert-GEMM shape (all kept rows as one M) instead of the layer: a "
                          "reference for the clock and matrix-core busy fraction, not the metric")
+    ap.add_argument("--path", default="auto", choices=["auto", "frag", "gather", "rows"],
+                    help="activation layout of a bf16 forward: what the layer picks (auto), the "
+                         "fragment-ordered copy (frag), row-major with the permute folded into the "
+                         "up-projection (gather) or row-major with x_perm stored (rows)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps, as a "
                          "known-size reference for memory-traffic counters")
@@ -489,8 +493,10 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     given_idx = dev(inp["topk_idx"], False) if not cfg.routed else None
     given_w = dev(inp["topk_w"], False) if not cfg.routed else None
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
+    frag, gather = {"auto": (None, None), "frag": (True, False), "gather": (False, True),
+                    "rows": (False, False)}[args.path if bf else "auto"]
     b = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, x.dtype, x.device, cfg.routed,
-                       w2_f16=bf)
+                       w2_f16=bf, frag=frag, gather=gather)
     # inference weight format: W2 in fp16, converted once (the kernels would
     # otherwise round each W2 value to fp16 in registers on every step, the
     # same way); the report counts values that lost bits or overflowed
@@ -506,6 +512,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     stream = torch.cuda.current_stream()
 
     names = ["router", "dispatch_plan", "permute", "up_gelu", "down", "combine"]
+    if b.gather:
+        names.remove("permute")   # no launch of its own: the up-projection reads x through src
 
     # routed bf16 layers with few enough (tile, expert) cells: the router counts
     # its token tiles' choices and sums their softmax columns, and the plan (with
@@ -534,9 +542,10 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
             ops.moe_dispatch_plan(idx, cfg.E, C, b.counts, b.offsets, b.dest, b.src, b.ws_dispatch)
 
     def k_permute():
+        # (with b.gather the up-projection reads x through src: no launch here)
         if b.frag:
             ops.moe_permute_frag(x, b.src, b.offsets, b.rows_max, b.x_frag)
-        else:
+        elif not b.gather:
             ops.moe_permute(x, b.src, b.offsets, b.rows_max, b.x_perm)
 
     def k_up():
@@ -544,6 +553,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
             ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, hfrag, True)
         elif b.frag:
             ops.moe_expert_up_gelu_frag(b.x_frag, b.offsets, w1, b.rows_max, b.h)
+        elif b.gather:
+            ops.moe_expert_up_gelu_gather(x, b.src, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
         else:
             ops.moe_expert_up_gelu(b.x_perm, b.offsets, w1, b.rows_max, b.h, b.ws_ffn)
 
@@ -559,6 +570,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
         ops.moe_combine(b.y_perm, b.dest, w, cfg.d, torch.float32, b.y)
 
     kernels = [k_router, k_plan, k_permute, k_up, k_down, k_combine]
+    if b.gather:
+        kernels.remove(k_permute)
 
     def step(ev=None):
         for i, kern in enumerate(kernels):
@@ -582,6 +595,7 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     ms_per_step = total_ms / args.steps
     per = kernel_breakdown(step, evs, len(names), torch, stream, np)
     us = dict(zip(names, (per * 1e3).tolist()))
+    us.setdefault("permute", 0.0)
 
     counts = b.counts.cpu().numpy()
     R = int(b.offsets.cpu().numpy()[-1])
@@ -590,7 +604,7 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     flops_up = 2.0 * R * d * dff
     flops_down = 2.0 * R * dff * d
     hbm = {"router": T * d * s + E * d * s + T * k * 8 + T * E * 4 if cfg.routed else 0,
-           "permute": 2 * R * d * s + R * 4,
+           "permute": 0 if b.gather else 2 * R * d * s + R * 4,
            "combine": R * d * 4 + T * d * 4 + T * k * 8}
     breakdown = {
         "router": {"us": us["router"]},
@@ -599,7 +613,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
         "dispatch_plan": {"us": us["dispatch_plan"], "bytes": T * k * 4 * 2 + R * 4 + 2 * E * 4,
                           "includes_aux_loss": bool(cfg.routed),
                           "from_router_tiles": bool(tiles)},
-        "permute": {"us": us["permute"]},
+        "permute": ({"us": us["permute"], "folded_into": "up_gelu (x read through src)"} if b.gather
+                    else {"us": us["permute"]}),
         "up_gelu": {"us": us["up_gelu"], "TFLOP/s": flops_up / (us["up_gelu"] * 1e-6) / 1e12},
         "down": {"us": us["down"], "TFLOP/s": flops_down / (us["down"] * 1e-6) / 1e12},
         "combine": {"us": us["combine"]},
@@ -650,13 +665,14 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
                               "hbm_frac": 2 * half / (t * 1e-6) / 1e9 / PEAK_HBM_GBS,
                               "what": "torch copy_ of the permute's bytes (R d s read + written) "
                                       "after the same flush"}
-        cold["permute"]["over_copy_floor"] = cold["permute"]["us"] / t
+        if "permute" in cold:
+            cold["permute"]["over_copy_floor"] = cold["permute"]["us"] / t
         del ca, cb
     del flush_buf
 
     dom = "up_gelu" if us["up_gelu"] >= us["down"] else "down"
     dom_frag = b.frag and (dom == "up_gelu" or hfrag is not None)
-    dom_which = ("up" if dom == "up_gelu" else
+    dom_which = (("up_gather" if b.gather else "up") if dom == "up_gelu" else
                  "down" if hfrag is not None or w2h is None else "down_f16w")
     dom_kernel = ("frag_gemm_kernel<%s>" % ("up_frag" if hfrag is not None else "up_rows")
                   if dom_frag and dom == "up_gelu" else
@@ -681,7 +697,9 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
                    "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
                    "max_over_mean_load": float(counts.max() / counts.mean()),
                    "activation_layout": ("fragment-ordered x and h" if hfrag is not None else
-                                         "fragment-ordered x" if b.frag else "row-major"),
+                                         "fragment-ordered x" if b.frag else
+                                         "row-major, the permute folded into the up-projection "
+                                         "(x read through src)" if b.gather else "row-major"),
                    "w2_storage": ("fp16, converted once from the bf16 weights (round to nearest "
                                   "even; %d values lost low bits, %d overflowed)" % tuple(w2_report)
                                   if bf else "f32"),

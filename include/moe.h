@@ -264,6 +264,22 @@ int moe_expert_down(const void* h, const int32_t* offsets, int32_t E,
                     int32_t dtype, float* y_perm, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/* The permute folded into the up-projection, for bf16 layers without a
+ * backward (EP tutorial 5.3's packed rows are never stored): h[r] =
+ * fp16(gelu_tanh(W1[e] . x[src[r]])) for every expert e and row r in
+ * [offsets[e], offsets[e+1]) -- the h of moe_permute followed by
+ * moe_expert_up_gelu, bit for bit, with the same workspace argument.
+ *   x [T, d] bf16 token rows (device, 16-byte aligned, T * d * 2 < 2^31),
+ *   src [rows_max] int32 and offsets [E+1] as moe_dispatch_plan writes them
+ *   (device, read only by the kernel; an src entry outside [0, T) reads zeros
+ *   or another row of x, never memory outside x), the other arguments as for
+ *   moe_expert_up_gelu with dtype MOE_BF16.
+ * Errors: those of moe_expert_up_gelu; MOE_ERR_ARG for T < 0 or a NULL src
+ *   when rows_max > 0; MOE_ERR_SHAPE when x holds 2^31 bytes or more. */
+int moe_expert_up_gelu_gather(const void* x, int64_t T, const int32_t* src, const int32_t* offsets,
+                              int32_t E, int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                              void* h, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* W2 stored in fp16, for bf16 layers (an inference-time weight format; the
  * down-projection of moe_expert_down converts every bf16 W2 value to fp16 in
  * registers before the fp16 x fp16 products, this does it once up front).

@@ -413,6 +413,20 @@ int moe_expert_up_gelu(const void* x_perm, const int32_t* offsets, int32_t E, in
                     "moe_expert_up_gelu launch");
 }
 
+int moe_expert_up_gelu_gather(const void* x, int64_t T, const int32_t* src, const int32_t* offsets,
+                              int32_t E, int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                              void* h, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_ffn(x, offsets, E, rows_max, d, d_ff, w1, MOE_BF16, h));
+  MOE_TRY(check_ffn_ws(MOE_BF16, workspace, workspace_bytes));
+  if (T < 0) return fail(MOE_ERR_ARG, "T = %lld must be >= 0", static_cast<long long>(T));
+  if (T * d > 0x3fffffffLL)
+    return fail(MOE_ERR_SHAPE, "moe_expert_up_gelu_gather needs T * d * 2 < 2^31 bytes of x");
+  if (rows_max > 0) MOE_NONNULL(src);
+  return hip_status(moe::launch_up_gelu_gather(x, T, src, offsets, E, rows_max, d, d_ff, w1, h, workspace,
+                                               stream),
+                    "moe_expert_up_gelu_gather launch");
+}
+
 int64_t moe_frag_rows(int64_t rows_max, int32_t E) {
   if (rows_max < 0 || E < 1 || E > MOE_MAX_E) return -1;
   return moe::frag_rows(rows_max, E);

@@ -111,12 +111,15 @@ enum Epi { kEpiGelu, kEpiF32, kEpiDGelu };
 // One kind of product: operand layouts (k-major = stored [K][M or N]), the
 // tile list (row- or K-segmented), the MFMA input type, the conversion of B
 // and the epilogue.
-template <bool A_KM, bool B_KM, bool SEG_K, bool F16, int CVT_B, int EPI, bool SAVE_Z>
+// GATHER: A's rows are read through a row map (A row r = token gsrc[r]).
+template <bool A_KM, bool B_KM, bool SEG_K, bool F16, int CVT_B, int EPI, bool SAVE_Z, bool GATHER = false>
 struct GemmOp {
   static constexpr bool kAKM = A_KM, kBKM = B_KM, kSegK = SEG_K, kF16 = F16, kSaveZ = SAVE_Z;
+  static constexpr bool kGather = GATHER;
   static constexpr int kCvt = CVT_B, kEpi = EPI;
 };
 using OpUp = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, false>;
+using OpUpG = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, false, true>;
 using OpUpZ = GemmOp<false, false, false, false, kCvtNone, kEpiGelu, true>;
 using OpDown = GemmOp<false, false, false, true, kCvtBf16ToF16, kEpiF32, false>;
 using OpDownF16 = GemmOp<false, false, false, true, kCvtNone, kEpiF32, false>;
@@ -136,6 +139,7 @@ __device__ __forceinline__ void store16(const uint4& v, __amdgpu_buffer_rsrc_t r
 struct Ctx {
   __amdgpu_buffer_rsrc_t a, b;
   int m0, n0, seg1, e;
+  uint32_t ga[kLoadsA];   // gathered A: this lane's row byte offsets, one per A load of a stage
 };
 
 // Four consecutive k-values of one column from the k-major LDS tile (see the
@@ -226,8 +230,10 @@ template <class Op>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int M, int N,
     int K, const uint16_t* __restrict__ B, void* __restrict__ Cout, uint16_t* __restrict__ Z,
-    float* __restrict__ part, int max_split) {
+    float* __restrict__ part, int max_split, const int32_t* __restrict__ gsrc, int a_bytes) {
   constexpr bool AKM = Op::kAKM, BKM = Op::kBKM, SEGK = Op::kSegK, F16 = Op::kF16;
+  constexpr bool GATHER = Op::kGather;
+  static_assert(!GATHER || (!AKM && !SEGK), "the row map applies to a K-contiguous, row-segmented A");
   constexpr int CVT = Op::kCvt, EPI = Op::kEpi;
   // Both operands K-contiguous: chunks past K hold the next row's values and
   // are zeroed; a k-major operand reads zeros past K (the buffer ends there),
@@ -402,9 +408,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
       c.seg1 = __builtin_amdgcn_readfirstlane(s_off[te + 1]);
       c.m0 = __builtin_amdgcn_readfirstlane(s_off[te] + tl.mi * BM);
       c.n0 = __builtin_amdgcn_readfirstlane(tl.nt * BN);
-      const int a_rows = min(c.seg1 - c.m0, BM);
-      c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A + static_cast<int64_t>(c.m0) * K),
-                                              0, static_cast<int>(a_rows * a_rb), 0x00020000);
+      if constexpr (GATHER) {
+        // A is the token matrix itself (a_bytes long): the tile's row i is
+        // token gsrc[m0 + i]. Each lane keeps the byte offset of its row in
+        // each of the stage's A loads; rows past the segment get an offset
+        // past the buffer, so their loads return zeros.
+        c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, a_bytes, 0x00020000);
+        const uint32_t chunk = static_cast<uint32_t>((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16u;
+#pragma unroll
+        for (int jj = 0; jj < kLoadsA; ++jj) {
+          const int r = c.m0 + (jj * kWaves + wave) * kRowsPerLoad + (lane >> 3);
+          c.ga[jj] = r < c.seg1 ? static_cast<uint32_t>(gsrc[r]) * a_rb + chunk : 0x80000000u;
+        }
+      } else {
+        const int a_rows = min(c.seg1 - c.m0, BM);
+        c.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A + static_cast<int64_t>(c.m0) * K),
+                                                0, static_cast<int>(a_rows * a_rb), 0x00020000);
+      }
       if constexpr (BKM) {
         // B_e is [K][N]: the tile's columns start at n0 of every k-row; the
         // buffer ends after k-row K - 1.
@@ -428,9 +448,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
     for (int jj = j0; jj < j1; ++jj) {
       if (jj < kLoadsA) {
         const int blk = jj * kWaves + wave;
-        const uint32_t so = AKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * a_rb)
-                                : (blk * kRowsPerLoad * a_rb + static_cast<uint32_t>(kt) * BK * 2u);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16, ld_voff_a, so, 0, 0);
+        if constexpr (GATHER) {
+          // the k offset goes into the lane offset, which the range check covers
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16,
+                                                   c.ga[jj] + static_cast<uint32_t>(kt) * BK * 2u, 0, 0, 0);
+        } else {
+          const uint32_t so = AKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * a_rb)
+                                  : (blk * kRowsPerLoad * a_rb + static_cast<uint32_t>(kt) * BK * 2u);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a, (lds_ptr_t)(dst + blk * kWave), 16, ld_voff_a, so, 0, 0);
+        }
       } else {
         const int blk = (jj - kLoadsA) * kWaves + wave;
         const uint32_t so = BKM ? (static_cast<uint32_t>(2 * blk + kt * BK) * b_rb)
@@ -984,10 +1010,11 @@ int ffn_mfma_grid() { return (device_cu_count() + 7) / 8 * 8; }
 
 template <class Op>
 void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int E, int M, int N,
-               int K, const void* B, void* C, void* Z, float* part, int max_split) {
+               int K, const void* B, void* C, void* Z, float* part, int max_split,
+               const int32_t* gsrc = nullptr, int a_bytes = 0) {
   hipLaunchKernelGGL(gemm_mfma_kernel<Op>, g, dim3(kThreads), 0, s, static_cast<const uint16_t*>(A),
                      offsets, E, M, N, K, static_cast<const uint16_t*>(B), C,
-                     static_cast<uint16_t*>(Z), part, max_split);
+                     static_cast<uint16_t*>(Z), part, max_split, gsrc, a_bytes);
   // A tile can split only into pieces of >= 16 stages: with fewer than 32
   // stages per tile nothing is split and there is nothing to add up.
   const int nk2 = (((K + BK - 1) / BK) + 1) & ~1;
@@ -1013,7 +1040,7 @@ size_t ffn_mfma_workspace_bytes() {
 
 hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
                             int64_t rows_max, int M, int N, int K, const void* B, void* C,
-                            void* Z, void* ws, hipStream_t s) {
+                            void* Z, void* ws, hipStream_t s, const int32_t* gsrc, int64_t a_rows) {
   const bool seg_k = kind == GemmKind::kDw2 || kind == GemmKind::kDw1;
   const int grid_max = ffn_mfma_grid();
   int64_t g = grid_max;
@@ -1042,6 +1069,10 @@ hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets
     case GemmKind::kUp:
       if (Z != nullptr) launch_op<OpUpZ>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split);
       else launch_op<OpUp>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split);
+      break;
+    case GemmKind::kUpGather:
+      launch_op<OpUpG>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split, gsrc,
+                       static_cast<int>(a_rows * K * 2));
       break;
     case GemmKind::kDown: launch_op<OpDown>(grid, s, A, offsets, E, M, N, K, B, C, Z, part, max_split); break;
     case GemmKind::kDownF16:

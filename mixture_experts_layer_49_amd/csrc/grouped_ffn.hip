@@ -117,6 +117,14 @@ hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int
                            static_cast<int>(d), w1, dtype, h, z, ws, s);
 }
 
+hipError_t launch_up_gelu_gather(const void* x, int64_t T, const int32_t* src, const int32_t* offsets,
+                                 int E, int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                                 void* h, void* ws, hipStream_t s) {
+  if (rows_max == 0) return hipSuccess;
+  return launch_gemm_mfma(GemmKind::kUpGather, x, offsets, E, rows_max, 0, static_cast<int>(d_ff),
+                          static_cast<int>(d), w1, h, nullptr, ws, s, src, T);
+}
+
 hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max, int64_t d,
                        int64_t d_ff, const void* w2, int dtype, float* y_perm, void* ws,
                        hipStream_t s) {

@@ -78,6 +78,10 @@ hipError_t launch_permute(const void* x, int64_t d, int elem_bytes, const int32_
 hipError_t launch_up_gelu(const void* x_perm, const int32_t* offsets, int E, int64_t rows_max,
                           int64_t d, int64_t d_ff, const void* w1, int dtype, void* h, void* z,
                           void* ws, hipStream_t s);
+// bf16: launch_up_gelu on x [T, d] read through src (row r = x[src[r]]).
+hipError_t launch_up_gelu_gather(const void* x, int64_t T, const int32_t* src, const int32_t* offsets,
+                                 int E, int64_t rows_max, int64_t d, int64_t d_ff, const void* w1,
+                                 void* h, void* ws, hipStream_t s);
 
 hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t rows_max,
                        int64_t d, int64_t d_ff, const void* w2, int dtype, float* y_perm,
@@ -87,6 +91,8 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
 // grouped by expert, K fixed):
 //   kUp:   A [R, K] bf16,  B = W1 [E, N, K] bf16 -> C = fp16 gelu(A B^T)
 //          (and, with Z, the fp16 pre-activation A B^T in Z [R, N])
+//   kUpGather: kUp with A = x [a_rows, K] bf16 read through the row map gsrc:
+//          row r of the product is x[gsrc[r]] (Z not supported)
 //   kDown: A [R, K] fp16,  B = W2 [E, N, K] bf16 -> C = A B^T f32
 //   kDownF16: as kDown with W2 stored as fp16 (no conversion in the kernel)
 //   kDh:   A [R, K] bf16,  B = W2 [E, K, N] bf16 -> C = bf16((A B) * gelu'(Z)), Z [R, N] fp16
@@ -96,10 +102,11 @@ hipError_t launch_down(const void* h, const int32_t* offsets, int E, int64_t row
 //   kDw1:  A [R, M] bf16,  B [R, N] bf16 -> C[e] = A_e^T B_e f32 [E, M, N]
 // With a workspace, output tiles of a short last round of a row-segmented
 // kind are split along K.
-enum class GemmKind { kUp, kDown, kDownF16, kDh, kDx, kDw2, kDw1 };
+enum class GemmKind { kUp, kUpGather, kDown, kDownF16, kDh, kDx, kDw2, kDw1 };
 hipError_t launch_gemm_mfma(GemmKind kind, const void* A, const int32_t* offsets, int E,
                             int64_t rows_max, int M, int N, int K, const void* B, void* C,
-                            void* Z, void* ws, hipStream_t s);
+                            void* Z, void* ws, hipStream_t s, const int32_t* gsrc = nullptr,
+                            int64_t a_rows = 0);
 inline hipError_t launch_ffn_mfma(bool up, const void* A, const int32_t* offsets, int E,
                                   int64_t rows_max, int N, int K, const void* B, void* C,
                                   void* ws, hipStream_t s) {

@@ -28,7 +28,8 @@ EXPORTS = ["moe_capacity", "moe_rows_max", "moe_router_topk", "moe_router_topk_e
            "moe_dispatch", "moe_dispatch_plan", "moe_dispatch_plan_aux",
            "moe_dispatch_plan_aux_workspace_bytes", "moe_dispatch_plan_noalloc",
            "moe_dispatch_plan_noalloc_scratch_bytes", "moe_router_tiles", "moe_router_topk_tiles",
-           "moe_dispatch_plan_tiles", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu", "moe_expert_down",
+           "moe_dispatch_plan_tiles", "moe_permute", "moe_grouped_ffn", "moe_expert_up_gelu",
+           "moe_expert_up_gelu_gather", "moe_expert_down",
            "moe_ffn_workspace_bytes", "moe_frag_rows", "moe_permute_frag", "moe_expert_up_gelu_frag",
            "moe_weights_bf16_to_f16", "moe_expert_down_f16w", "moe_expert_down_frag", "moe_combine", "moe_aux_loss_workspace_bytes", "moe_aux_loss", "moe_z_loss_workspace_bytes",
            "moe_z_loss", "moe_expert_up_gelu_z", "moe_combine_backward", "moe_expert_down_backward",
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "moe_permute": (ctypes.c_int, [P, I64, I32, P, P, I32, I64, P, P]),
         "moe_grouped_ffn": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, P, I32, P, P, P, SZ, P]),
         "moe_expert_up_gelu": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
+        "moe_expert_up_gelu_gather": (ctypes.c_int, [P, I64, P, P, I32, I64, I64, I64, P, P, P, SZ, P]),
         "moe_expert_down": (ctypes.c_int, [P, P, I32, I64, I64, I64, P, I32, P, P, SZ, P]),
         "moe_ffn_workspace_bytes": (SZ, [I32]),
         "moe_frag_rows": (I64, [I64, I32]),
@@ -358,6 +360,18 @@ def moe_expert_up_gelu(x_perm, offsets, w1, rows_max: int, h=None, workspace=Non
     return h
 
 
+def moe_expert_up_gelu_gather(x, src, offsets, w1, rows_max: int, h=None, workspace=None, stream=None):
+    """moe_permute then moe_expert_up_gelu in one kernel (bf16): the
+    up-projection reads row r as x[src[r]]."""
+    T, d = x.shape
+    E, d_ff, _ = w1.shape
+    h = _empty((max(rows_max, 1), d_ff), hidden_dtype(w1.dtype), x) if h is None else h
+    _check(lib().moe_expert_up_gelu_gather(_ptr(x), T, _ptr(src), _ptr(offsets), E, rows_max, d, d_ff,
+                                           _ptr(w1), _ptr(h), _ptr(workspace), _ws_size(workspace),
+                                           _stream(stream)))
+    return h
+
+
 def moe_expert_down(h, offsets, w2, rows_max: int, y_perm=None, workspace=None, stream=None):
     E, d, d_ff = w2.shape
     y_perm = _empty((max(rows_max, 1), d), torch.float32, h) if y_perm is None else y_perm
@@ -374,12 +388,14 @@ def moe_frag_rows(rows_max: int, E: int) -> int:
 
 def frag_eligible(dtype, d: int) -> bool:
     """Whether moe_forward takes the fragment-ordered path for this layer:
-    bf16, d a multiple of 256 and at least 2048. Measured on the workloads,
-    whole forward with fp16 W2 (x and h in fragment order): -8% at d = 4096,
-    -4% at d = 2048 (64 experts), +3% at d = 1024 (16 experts), where the
-    up-projection's short last round of tiles, which the row-major kernel
-    splits along K and this one does not, weighs more."""
-    return dtype == torch.bfloat16 and d % 256 == 0 and d >= 2048
+    bf16, d a multiple of 256 and at least 4096. Measured on the workloads,
+    whole forward with fp16 W2, against the row-major path that folds the
+    permute into the up-projection: -9% at d = 4096 (8 experts, also the
+    receiver share and the ETP share), but +1.5% at d = 2048 (64 experts) and
+    +2% at d = 1024 (16 experts), where the row-major up-projection's split
+    of a short last round of tiles along K, and its saved permute pass, weigh
+    more."""
+    return dtype == torch.bfloat16 and d % 256 == 0 and d >= 4096
 
 
 def moe_permute_frag(x, src, offsets, rows_max: int, x_frag=None, stream=None):
@@ -588,7 +604,7 @@ class MoEBuffers:
     repeated forwards allocate nothing."""
 
     def __init__(self, T, d, d_ff, E, k, capacity, dtype, device, routed=True, want_probs=True,
-                 save_for_backward=False, frag=None, w2_f16=False):
+                 save_for_backward=False, frag=None, w2_f16=False, gather=None):
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
         self.T, self.d, self.d_ff, self.E, self.k, self.capacity = T, d, d_ff, E, k, capacity
         self.rows_max = moe_rows_max(T, k, E, capacity)
@@ -607,7 +623,14 @@ class MoEBuffers:
         if frag and (save_for_backward or dtype != torch.bfloat16 or d % 256 != 0):
             raise ValueError("the fragment-ordered path needs bf16, d % 256 == 0 and no backward")
         self.frag = bool(frag)
-        self.x_perm = None if self.frag else z((R, d), dtype)
+        # the row-major bf16 forward without a backward reads x through src in
+        # the up-projection (moe_expert_up_gelu_gather): x_perm is not stored
+        if gather is None:
+            gather = not self.frag and dtype == torch.bfloat16 and not save_for_backward
+        if gather and (self.frag or save_for_backward or dtype != torch.bfloat16):
+            raise ValueError("the gathered up-projection needs the row-major bf16 path and no backward")
+        self.gather = bool(gather)
+        self.x_perm = None if (self.frag or self.gather) else z((R, d), dtype)
         self.x_frag = z((max(moe_frag_rows(self.rows_max, E), 1), d), dtype) if self.frag else None
         # forwards that will pass W2 in fp16 (w2_f16) on the fragment-ordered
         # path keep h in fragment order too when d_ff % 256 == 0: only that
@@ -648,7 +671,9 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     the router its log-sum-exp (what moe_backward needs). Without a backward,
     bf16 layers that frag_eligible() accepts run the permute and the
     up-projection on the fragment-ordered copy (bufs.frag; the same h bit for
-    bit as the row-major up-projection without a workspace). `w2_f16`, for
+    bit as the row-major up-projection without a workspace), and the other
+    bf16 layers fold the permute into the up-projection (bufs.gather: the
+    same h bit for bit, x_perm not stored). `w2_f16`, for
     bf16 layers: moe_weights_bf16_to_f16(w2), prepared once; the
     down-projection then reads it instead of converting W2 in registers
     (y_perm bit for bit the same), and on the fragment-ordered path with
@@ -717,6 +742,10 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
                 raise MoEError(-1, "these buffers keep h in fragment order: pass w2_f16")
             moe_expert_up_gelu_frag(bufs.x_frag, bufs.offsets, w1, bufs.rows_max, bufs.h, False, stream)
             down()
+    elif bufs.gather:
+        # the permute happens inside the up-projection's loads
+        moe_expert_up_gelu_gather(x, bufs.src, bufs.offsets, w1, bufs.rows_max, bufs.h, bufs.ws_ffn, stream)
+        down()
     else:
         moe_permute(x, bufs.src, bufs.offsets, bufs.rows_max, bufs.x_perm, stream)
         if bufs.z is not None:

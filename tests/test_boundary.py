@@ -198,6 +198,16 @@ def test_ffn_combine_aux_argument_errors():
     assert L.moe_expert_down(FAKE, FAKE, 8, 10, 64, 128, FAKE, 1, FAKE, FAKE, need - 1, None) == -4
     assert L.moe_expert_up_gelu(FAKE, FAKE, 8, 10, 64, 128, FAKE, 1, FAKE, FAKE, need - 1, None) == -4
     assert L.moe_grouped_ffn(FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None) == -4
+    # moe_expert_up_gelu_gather(x, T, src, offsets, E, rows_max, d, d_ff, w1, h, ws, ws_bytes, stream)
+    G = L.moe_expert_up_gelu_gather
+    assert G(FAKE, 100, FAKE, FAKE, 8, 10, 64, 130, FAKE, FAKE, None, 0, None) == -6      # d_ff % 8
+    assert G(FAKE, 100, FAKE, FAKE, 8, 10, 60, 128, FAKE, FAKE, None, 0, None) == -6      # d % 8
+    assert G(FAKE, -1, FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, None, 0, None) == -1       # T < 0
+    assert G(FAKE, 100, None, FAKE, 8, 10, 64, 128, FAKE, FAKE, None, 0, None) == -1      # src
+    assert G(FAKE, 1 << 24, FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, None, 0, None) == -3  # x of 2^31 bytes
+    assert G(FAKE, 100, FAKE, FAKE, 300, 10, 64, 128, FAKE, FAKE, None, 0, None) == -3    # E
+    assert G(FAKE, 100, FAKE, FAKE, 8, 10, 64, 128, FAKE, FAKE, FAKE, need - 1, None) == -4
+    assert G(None, 0, None, None, 8, 0, 64, 128, None, None, None, 0, None) == 0
     assert L.moe_expert_down(FAKE, FAKE, 8, 10, 64, 128, FAKE, 1, FAKE,
                              ctypes.c_void_p((1 << 20) + 8), need, None) == -6
     assert L.moe_combine(FAKE, FAKE, FAKE, 10, 9, 64, FAKE, 0, None) == -1

@@ -37,15 +37,27 @@ def test_unfrag_reads_the_documented_layout(counts, d):
 
 def test_fragment_path_choice_and_sizes():
     bf = torch.bfloat16
-    assert ops.frag_eligible(bf, 4096) and ops.frag_eligible(bf, 2048)
-    assert not ops.frag_eligible(bf, 1024) and not ops.frag_eligible(bf, 2304 + 8)
+    assert ops.frag_eligible(bf, 4096) and ops.frag_eligible(bf, 8192)
+    assert not ops.frag_eligible(bf, 2048) and not ops.frag_eligible(bf, 1024)
+    assert not ops.frag_eligible(bf, 4096 + 8)
     assert not ops.frag_eligible(torch.float32, 4096)
     # MoEBuffers on the host (sizes only): the fragment copy replaces x_perm
-    b = ops.MoEBuffers(64, 2048, 256, 4, 2, 40, bf, "cpu")
+    b = ops.MoEBuffers(64, 4096, 256, 4, 2, 40, bf, "cpu")
     assert b.frag and b.x_perm is None
-    assert b.x_frag.shape == (ops.moe_frag_rows(b.rows_max, 4), 2048)
-    assert not ops.MoEBuffers(64, 2048, 256, 4, 2, 40, bf, "cpu", save_for_backward=True).frag
+    assert b.x_frag.shape == (ops.moe_frag_rows(b.rows_max, 4), 4096)
+    assert not ops.MoEBuffers(64, 4096, 256, 4, 2, 40, bf, "cpu", save_for_backward=True).frag
     assert not ops.MoEBuffers(64, 1024, 256, 4, 2, 40, bf, "cpu").frag
+    # the row-major bf16 forward without a backward folds the permute into the
+    # up-projection (no x_perm); a backward or f32 keeps x_perm
+    g = ops.MoEBuffers(64, 1024, 256, 4, 2, 40, bf, "cpu")
+    assert g.gather and g.x_perm is None and not b.gather
+    assert not ops.MoEBuffers(64, 1024, 256, 4, 2, 40, bf, "cpu", save_for_backward=True).gather
+    assert not ops.MoEBuffers(64, 1024, 256, 4, 2, 40, torch.float32, "cpu").gather
+    assert ops.MoEBuffers(64, 1024, 256, 4, 2, 40, bf, "cpu", gather=False).x_perm is not None
+    with pytest.raises(ValueError):
+        ops.MoEBuffers(64, 1024, 256, 4, 2, 40, torch.float32, "cpu", gather=True)
+    with pytest.raises(ValueError):
+        ops.MoEBuffers(64, 2048, 256, 4, 2, 40, bf, "cpu", frag=True, gather=True)
     with pytest.raises(ValueError):
         ops.MoEBuffers(64, 2048, 256, 4, 2, 40, torch.float32, "cpu", frag=True)
     with pytest.raises(ValueError):

@@ -73,21 +73,25 @@ def gpu_tensors(inp, cfg):
     return t
 
 
-def gpu_forward(inp, cfg, flags=0, frag=None, f16w=False):
+def gpu_forward(inp, cfg, flags=0, frag=None, f16w=False, gather=None):
     """The layer forward; frag None lets moe_forward pick the path (the
-    fragment-ordered one where ops.frag_eligible), True or False forces one."""
+    fragment-ordered one where ops.frag_eligible), True or False forces one;
+    gather None lets the row-major bf16 path fold the permute into the
+    up-projection, False keeps the stored x_perm."""
     t = gpu_tensors(inp, cfg)
     C = ops.moe_capacity(cfg.T, cfg.E, cfg.cf)
     bufs = ops.MoEBuffers(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, C, t["x"].dtype, t["x"].device,
-                          cfg.routed, frag=frag, w2_f16=f16w)
+                          cfg.routed, frag=frag, w2_f16=f16w, gather=gather)
     w2h = ops.moe_weights_bf16_to_f16(t["w2"]) if f16w else None
     b = ops.moe_forward(t["x"], t["w1"], t["w2"], cfg.k, C, w_gate=t.get("w_gate"),
                         bias=t.get("bias"), topk_idx=t.get("topk_idx"),
                         topk_w=t.get("topk_w"), alpha=cfg.alpha, flags=flags, bufs=bufs, w2_f16=w2h)
     torch.cuda.synchronize()
     R = int(host(b.offsets)[-1])
-    x_perm = unfrag(b.x_frag.cpu(), host(b.offsets), cfg.d)[0] if b.frag else b.x_perm[:R]
-    out = {"C": C, "R": R, "rows_max": b.rows_max,
+    # the gathered path stores no permuted rows
+    x_perm = (unfrag(b.x_frag.cpu(), host(b.offsets), cfg.d)[0] if b.frag else
+              None if b.gather else b.x_perm[:R])
+    out = {"C": C, "R": R, "rows_max": b.rows_max, "gather": b.gather,
            "topk_idx": host(b.topk_idx) if cfg.routed else inp["topk_idx"],
            "topk_w": host(b.topk_w) if cfg.routed else inp["topk_w"],
            "counts": host(b.counts), "offsets": host(b.offsets), "dest": host(b.dest),
@@ -405,17 +409,19 @@ def oracle_forward(inp, cfg, topk_idx, topk_w, sample=None):
     return ref
 
 
-def check_layer(inp, cfg, sample=None, frag=None, f16w=False):
-    g, t = gpu_forward(inp, cfg, frag=frag, f16w=f16w)
+def check_layer(inp, cfg, sample=None, frag=None, f16w=False, gather=None):
+    g, t = gpu_forward(inp, cfg, frag=frag, f16w=f16w, gather=gather)
     ref = oracle_forward(inp, cfg, g["topk_idx"], g["topk_w"], sample)
-    say("  %s: C=%d R=%d (rows_max %d, %s path)" % (cfg.name, g["C"], g["R"], g["rows_max"],
-                                                   "fragment-ordered" if g["frag"] else "row-major"))
+    say("  %s: C=%d R=%d (rows_max %d, %s path)" % (
+        cfg.name, g["C"], g["R"], g["rows_max"],
+        "fragment-ordered" if g["frag"] else "row-major, gathered" if g["gather"] else "row-major"))
     np.testing.assert_array_equal(g["counts"], ref["counts"])
     np.testing.assert_array_equal(g["offsets"], ref["offsets"])
     np.testing.assert_array_equal(g["dest"], ref["dest"])
     np.testing.assert_array_equal(g["src"], ref["src"])
     # the permuted rows (read back from the fragment order on that path): bit-exact
-    assert torch.equal(g["x_perm"].cpu(), t["x"].cpu()[torch.from_numpy(ref["src"]).long()])
+    if g["x_perm"] is not None:
+        assert torch.equal(g["x_perm"].cpu(), t["x"].cpu()[torch.from_numpy(ref["src"]).long()])
     rows = ref["y_perm_rows"]
     if rows.size:
         close(g["y_perm"][rows], ref["y_perm"][rows], cfg.dtype, "y_perm")
@@ -445,7 +451,7 @@ FRAG_SMALL = [c for c in SMALL if c.dtype == "bf16" and c.d % 256 == 0]
 @pytest.mark.parametrize("cfg", FRAG_SMALL, ids=ids(FRAG_SMALL))
 def test_layer_small_fragment_path(cfg):
     """The layer with the fragment-ordered permute and up-projection forced
-    (moe_forward picks it by itself only from d = 2048)."""
+    (moe_forward picks it by itself only from d = 4096)."""
     g = check_layer(I.make_inputs(cfg), cfg, frag=True)
     assert g["frag"]
 
@@ -459,13 +465,17 @@ def test_layer_small_fragment_h_f16_w2(cfg):
 
 
 # Every workload at its real size, on each path, every token against the
-# oracle: "default" is what moe_forward picks (bf16 with d >= 2048: the
+# oracle: "default" is what moe_forward picks (bf16 with d >= 4096: the
 # fragment-ordered permute and up-projection, h row-major, the down-projection
-# converting bf16 W2 in registers), "frag-f16w" is the inference path the
+# converting bf16 W2 in registers; other bf16 layers: the row-major path with
+# the permute folded into the up-projection), "frag-f16w" is the inference path the
 # benchmark times (x and h in fragment order, W2 held in fp16, split
-# down-projection tiles), "row-major" is the training forward's layout.
+# down-projection tiles), "row-major" is the training forward's layout (x_perm
+# stored), "gather-f16w" the row-major inference path (the permute folded into
+# the up-projection, W2 in fp16).
 FULL_PATHS = ([(c, "default") for c in FULL] +
-              [(c, p) for c in FULL + [ETP] if c.dtype == "bf16" for p in ("frag-f16w", "row-major")] +
+              [(c, p) for c in FULL + [ETP] if c.dtype == "bf16"
+               for p in ("frag-f16w", "row-major", "gather-f16w")] +
               [(ETP, "default")])
 FULL_PATHS.sort(key=lambda cp: (FULL + [ETP]).index(cp[0]))   # one oracle run per workload
 
@@ -473,12 +483,15 @@ FULL_PATHS.sort(key=lambda cp: (FULL + [ETP]).index(cp[0]))   # one oracle run p
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg,path", FULL_PATHS, ids=["%s-%s" % (c.name, p) for c, p in FULL_PATHS])
 def test_layer_full(cfg, path):
-    frag, f16w = {"default": (None, False), "frag-f16w": (True, True), "row-major": (False, False)}[path]
-    g = check_layer(cached_inputs(cfg), cfg, frag=frag, f16w=f16w)
+    frag, f16w, gather = {"default": (None, False, None), "frag-f16w": (True, True, None),
+                          "row-major": (False, False, False), "gather-f16w": (False, True, True)}[path]
+    g = check_layer(cached_inputs(cfg), cfg, frag=frag, f16w=f16w, gather=gather)
     if path == "frag-f16w":
         assert g["frag"] and g["hfrag"] == (cfg.d_ff % 256 == 0)
     if path == "row-major":
-        assert not g["frag"]
+        assert not g["frag"] and not g["gather"]
+    if path == "gather-f16w":
+        assert g["gather"]
 
 
 def test_etp_shares_sum_to_whole_layer():
@@ -574,6 +587,33 @@ def test_ffn_halves_equal_whole():
     R = g["R"]
     assert torch.equal(h1[:R], h2[:R]) and torch.equal(y1[:R], y2[:R])
     assert np.array_equal(host(y1)[:R], g["y_perm"])
+
+
+GATHER_CASES = ["small-bf16", "ragged-bf16", "max-experts", "multi-tile", "split-k2-ragged", "split-k8",
+                "receiver", "single-token", "all-dropped", "e16-zipf-bias", "fine-grained-e64"]
+
+
+@pytest.mark.parametrize("name", GATHER_CASES)
+def test_up_gelu_gather_equals_permute_then_up(name):
+    """moe_expert_up_gelu_gather against moe_permute + moe_expert_up_gelu on
+    the same plan: h bit-identical, without and with the workspace (split
+    tiles), on ragged segments, a d tail (200), 256 experts, K = 32768 and two
+    workloads at their real sizes; rows past R are not touched."""
+    cfg = next(c for c in SMALL + FULL if c.name == name)
+    inp = cached_inputs(cfg) if cfg in FULL else I.make_inputs(cfg)
+    g, t = gpu_forward(inp, cfg, frag=False, gather=False)
+    idx = dev(g["topk_idx"].astype(np.int32), "f32")
+    _, off, _, src, xp = ops.moe_dispatch(idx, cfg.E, g["C"], t["x"])
+    rows, R = g["rows_max"], g["R"]
+    ws = torch.empty(ops.moe_ffn_workspace_bytes(torch.bfloat16), dtype=torch.uint8, device="cuda:0")
+    say("  %s: R=%d rows_max=%d" % (name, R, rows))
+    for wsa in (None, ws):
+        want = ops.moe_expert_up_gelu(xp, off, t["w1"], rows, workspace=wsa)
+        got = torch.full_like(want, 7.0)
+        ops.moe_expert_up_gelu_gather(t["x"], src, off, t["w1"], rows, h=got, workspace=wsa)
+        torch.cuda.synchronize()
+        assert torch.equal(got[:R].view(torch.int16), want[:R].view(torch.int16))
+        assert (got[R:] == 7.0).all()
 
 
 @pytest.mark.parametrize("name", ["split-k2-ragged", "split-k8", "ep8-receiver-share"])
