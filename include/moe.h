@@ -208,7 +208,7 @@ size_t moe_dispatch_plan_noalloc_scratch_bytes(void);
  *     launch and without a workspace; with tile_colsum (and a device scalar
  *     `loss`, both or neither) also the aux loss as moe_aux_loss defines it,
  *     its column sums added tile by tile in tile order. topk_idx must be the
- *     router's output the counts came from. Needs tiles x E <= 8192
+ *     router's output the counts came from. Needs tiles x E <= 16384
  *     (MOE_ERR_SHAPE otherwise: use moe_dispatch_plan). counts, offsets,
  *     dest and src are bit-identical to moe_dispatch_plan's. */
 int64_t moe_router_tiles(int64_t T, int32_t E);

@@ -12,7 +12,7 @@
 //   2. scan   per expert, an exclusive scan of the chunk counts over chunks
 //             (token order), the total count, kept = min(count, C) and the
 //             exclusive scan over experts -> offsets. While all chunk counts
-//             fit in 32 KiB of LDS (chunks x experts <= 8192: every workload
+//             fit in 64 KiB of LDS (chunks x experts <= 16384: every workload
 //             here), each place workgroup does this itself from the counts it
 //             loads whole, and workgroup 0 writes counts and offsets -- no
 //             launch of its own; beyond that, one scan workgroup.
@@ -215,11 +215,13 @@ __global__ __launch_bounds__(kThreads) void place_kernel(const int32_t* __restri
 
 // place with the scan folded in (count rows x experts <= kScanLds): every
 // workgroup loads all count rows into LDS, scans them for its own chunk's
-// bases and for the offsets; workgroup 0 writes counts and offsets and, with
-// AUX, the aux loss from the rows' column sums. A count row covers
+// bases and for the offsets; workgroup 0 writes counts and offsets. With AUX
+// the launch has one more workgroup (index nchunks, no tokens of its own)
+// that forms the aux loss from the rows' column sums and the totals, so that
+// its column-sum loads do not hold up a place workgroup. A count row covers
 // kThreads / tpc tokens: the histogram's chunks (tpc = 1) or the router's
 // token tiles (tpc = kThreads / tile tokens), so chunk c starts at row c tpc.
-constexpr int kScanLds = 8192;
+constexpr int kScanLds = 16384;
 template <bool AUX>
 __global__ __launch_bounds__(kThreads) void place_scan_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap, int nchunks, int tpc,
@@ -234,17 +236,18 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
   __shared__ double s_red[kMaxE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = nchunks * E;
-  // Workgroup 0 (the one that forms the aux loss, the launch's longest) adds
-  // up its share of the column sums first, so those loads overlap the count
-  // loads and the masks: thread (ee = tid % E, g = tid / E) adds the rows g,
-  // g + G, ... of expert ee, eight in flight; the G group sums are added in
+  const int place_wgs = static_cast<int>((T + kThreads - 1) / kThreads);
+  const bool aux_wg = AUX && static_cast<int>(blockIdx.x) == place_wgs;
+  // The aux workgroup adds up the column sums first, so those loads overlap
+  // the count loads: thread (ee = tid % E, g = tid / E) adds the rows g,
+  // g + G, ... of expert ee, sixteen in flight; the G group sums are added in
   // g order below.
   double part = 0.0;
   if constexpr (AUX) {
     const int G = kThreads / E;
     const int ee = tid % E, g = tid / E;
-    if (blockIdx.x == 0 && g < G) {
-      constexpr int U = 8;
+    if (aux_wg && g < G) {
+      constexpr int U = 16;
       for (int c0 = g; c0 < nchunks; c0 += U * G) {
         double v[U];
 #pragma unroll
@@ -255,10 +258,20 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
       }
     }
   }
-  // all chunk counts, 16 bytes per load where the count is a multiple of 4
+  // all chunk counts, 16 bytes per load where the count is a multiple of 4,
+  // sixteen loads in flight per thread before they go to LDS
   if ((n & 3) == 0) {
     const int4* c4 = reinterpret_cast<const int4*>(chunk_cnt);
-    for (int i = tid; i < n / 4; i += kThreads) reinterpret_cast<int4*>(s_cnt)[i] = c4[i];
+    const int n4 = n / 4;
+    constexpr int UL = 16;
+    for (int i0 = tid; i0 < n4; i0 += kThreads * UL) {
+      int4 v[UL];
+#pragma unroll
+      for (int u = 0; u < UL; ++u) v[u] = c4[min(i0 + u * kThreads, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < UL; ++u)
+        if (i0 + u * kThreads < n4) reinterpret_cast<int4*>(s_cnt)[i0 + u * kThreads] = v[u];
+    }
   } else {
     for (int i = tid; i < n; i += kThreads) s_cnt[i] = chunk_cnt[i];
   }
@@ -314,6 +327,8 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
       offsets[e + 1] = s_buf[cur][e];
     }
     if (e == 0) offsets[0] = 0;
+  }
+  if (aux_wg) {
     if constexpr (AUX) {
       double term = 0.0;
       const int G = kThreads / E;
@@ -409,7 +424,7 @@ hipError_t plan_impl(const int32_t* topk_idx, int64_t T, int k, int E, int64_t c
                        nullptr, nullptr);
   if (static_cast<int64_t>(nchunks) * E <= kScanLds) {
     if (aux)
-      hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
+      hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
                          nchunks, 1, chunk_cnt, counts, offsets, dest, src, colsum, alpha, loss);
     else
       hipLaunchKernelGGL(place_scan_kernel<false>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
@@ -451,7 +466,7 @@ hipError_t launch_dispatch_plan_tiles(const int32_t* topk_idx, const int32_t* ti
   const int nrows = static_cast<int>((T + tile_tokens - 1) / tile_tokens);
   const int tpc = kThreads / tile_tokens;
   if (tile_colsum != nullptr)
-    hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
+    hipLaunchKernelGGL(place_scan_kernel<true>, dim3(nchunks + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,
                        nrows, tpc, tile_cnt, counts, offsets, dest, src, tile_colsum, alpha, loss);
   else
     hipLaunchKernelGGL(place_scan_kernel<false>, dim3(nchunks), dim3(kThreads), 0, s, topk_idx, T, k, E, cap,

@@ -934,12 +934,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   }
 }
 
-// Split tiles of a row-segmented launch: workgroup b takes the quarter
-// b / 8 % 4 (64 rows) of split tile b / 32 of XCD b % 8's last round, adds
-// its S partials in split order and emits the outputs. The tile list and the
-// splits are derived from offsets[] exactly as the GEMM derived them (P
-// workgroups per XCD). The kernel boundary orders the partial stores before
-// these loads, so the pieces need no fence or ticket.
+// Split tiles of a row-segmented launch: the split tiles of XCD x's last
+// round (rem of them) are shared out over the launch's workgroups b with
+// b % 8 == x, in bands of `rows` rows (a power of two from 4 to 256, the
+// smallest with which the XCD's gridDim / 8 workgroups cover all rem tiles):
+// workgroup b takes band j % (256 / rows) of split tile j / (256 / rows),
+// j = b / 8, adds its S partials in split order and emits the outputs. The
+// tile list and the splits are derived from offsets[] exactly as the GEMM
+// derived them (P workgroups per XCD). The kernel boundary orders the partial
+// stores before these loads, so the pieces need no fence or ticket.
 template <class Op>
 __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
     const int32_t* __restrict__ offsets, int E, int N, int K, int P, int max_split,
@@ -949,43 +952,53 @@ __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
   __shared__ int s_pref[kMaxE + 1];
   __shared__ int s_tmp[kMaxE];
   build_tile_prefix(offsets, E, BM, s_pref, s_tmp);
-  const int xcd = blockIdx.x & 7, quarter = (blockIdx.x >> 3) & 3, tr = blockIdx.x >> 5;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int tiles_n = (N + BN - 1) / BN;
   const int nk2 = (((K + BK - 1) / BK) + 1) & ~1;
   const RowPlan pl = row_plan(static_cast<int64_t>(s_pref[E]) * tiles_n, xcd, P, nk2, max_split);
-  if (pl.S == 1 || tr >= pl.rem) return;
+  if (pl.S == 1) return;
+  const int per_xcd = static_cast<int>(gridDim.x >> 3);
+  int rows = 4;
+  while (rows < BM && rows * per_xcd < pl.rem * BM) rows <<= 1;
+  const int bands = BM / rows, tr = j / bands, band = j % bands;
+  if (tr >= pl.rem) return;
   const Tile tl = find_tile(s_pref, E, tiles_n, pl.r_beg + pl.full * P + tr);
   const int e0 = offsets[tl.e], seg1 = offsets[tl.e + 1];
   const int m0 = e0 + tl.mi * BM, n0 = tl.nt * BN;
-  // a quarter wholly past the segment has nothing to add (its rows were not stored)
-  if (m0 + quarter * 64 >= seg1) return;
+  const int r0 = band * rows;
+  // a band wholly past the segment has nothing to add (its rows were not stored)
+  if (m0 + r0 >= seg1) return;
   // piece si of the tile is u = si * rem + tr, at slot u of the XCD's kPiecesPerWg P
   const float* const first = part + static_cast<int64_t>(xcd * kPiecesPerWg * P + tr) * (BM * BN);
   const int64_t step = static_cast<int64_t>(pl.rem) * (BM * BN);
   const int S = pl.S;
-  // Two items per thread per pass, the values of all kMaxSplit slots loaded
-  // before any is added (slots past S re-read slot S - 1 and are not added).
-  constexpr int QU = 2;
-  constexpr int ITEMS = 64 * BN / VPC;
+  // Four items per thread per pass (two of the 8-value kinds), the values of
+  // all S pieces loaded before any is added (the piece count is uniform, so
+  // the guards are branches).
+  constexpr int QU = NV == 1 ? 4 : 2;
+  const int items = rows * (BN / VPC);
 #pragma unroll 1
-  for (int q0 = threadIdx.x; q0 < ITEMS; q0 += kThreads * QU) {
+  for (int q0 = threadIdx.x; q0 < items; q0 += kThreads * QU) {
     float4 v[kMaxSplit][QU][NV];
 #pragma unroll
-    for (int si = 0; si < kMaxSplit; ++si)
+    for (int si = 0; si < kMaxSplit; ++si) {
+      if (si < S) {
 #pragma unroll
-      for (int u = 0; u < QU; ++u) {
-        const int q = min(q0 + u * kThreads, ITEMS - 1);
-        const int row = quarter * 64 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
-        const float* src = first + min(si, S - 1) * step + row * BN + col;
-        const bool live = m0 + row < seg1;   // rows past the segment were not stored
+        for (int u = 0; u < QU; ++u) {
+          const int q = min(q0 + u * kThreads, items - 1);
+          const int row = r0 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
+          const float* src = first + si * step + row * BN + col;
+          const bool live = m0 + row < seg1;   // rows past the segment were not stored
 #pragma unroll
-        for (int h = 0; h < NV; ++h)
-          v[si][u][h] = live ? *reinterpret_cast<const float4*>(src + 4 * h) : float4{0.f, 0.f, 0.f, 0.f};
+          for (int h = 0; h < NV; ++h)
+            v[si][u][h] = live ? *reinterpret_cast<const float4*>(src + 4 * h) : float4{0.f, 0.f, 0.f, 0.f};
+        }
       }
+    }
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       const int q = q0 + u * kThreads;
-      const int row = quarter * 64 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
+      const int row = r0 + q / (BN / VPC), col = (q % (BN / VPC)) * VPC;
       float4 a = v[0][u][0], b = v[0][u][NV - 1];
 #pragma unroll
       for (int si = 1; si < kMaxSplit; ++si) {
@@ -999,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
         }
       }
       const int grow = m0 + row, gcol = n0 + col;
-      if (q < ITEMS && grow < seg1 && gcol < N)
+      if (q < items && grow < seg1 && gcol < N)
         emit_values<Op>(Cout, Z, static_cast<int64_t>(grow) * N + gcol, a, b);
     }
   }

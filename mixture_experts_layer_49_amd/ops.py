@@ -314,8 +314,8 @@ def moe_dispatch_plan_tiles(topk_idx, tile_counts, tile_colsum, E: int, capacity
 
 def tiles_eligible(dtype, T: int, E: int) -> bool:
     """Whether the router can hand the dispatch plan its per-tile counts:
-    bf16 and at most 8192 (tile, expert) count cells."""
-    return dtype == torch.bfloat16 and moe_router_tiles(T, E) * E <= 8192
+    bf16 and at most 16384 (tile, expert) count cells."""
+    return dtype == torch.bfloat16 and moe_router_tiles(T, E) * E <= 16384
 
 
 def moe_dispatch_plan_noalloc(topk_idx, E: int, capacity: int, counts, offsets, dest, src,

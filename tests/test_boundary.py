@@ -410,7 +410,7 @@ def test_router_tiles_and_plan_tiles_argument_errors():
     # plan from tiles: colsum and loss go together; too many cells; alignment
     assert L.moe_dispatch_plan_tiles(p, p, p, 16, 2, 8, 4, 0.01, p, p, p, p, None, None) == -1
     assert L.moe_dispatch_plan_tiles(p, p, None, 16, 2, 8, 4, 0.0, p, p, p, p, p, None) == -1
-    assert L.moe_dispatch_plan_tiles(p, p, None, 20000, 2, 8, 4, 0.0, p, p, p, p, None, None) == -3
+    assert L.moe_dispatch_plan_tiles(p, p, None, 40000, 2, 8, 4, 0.0, p, p, p, p, None, None) == -3
     assert L.moe_dispatch_plan_tiles(p, ctypes.c_void_p(4100), None, 16, 2, 8, 4, 0.0, p, p, p, p, None,
                                      None) == -6
     assert L.moe_dispatch_plan_tiles(p, None, None, 16, 2, 8, 4, 0.0, p, p, p, p, None, None) == -1
