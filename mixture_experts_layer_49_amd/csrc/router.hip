@@ -155,14 +155,28 @@ __device__ void softmax_topk(float (&lg)[NT], int E, int k, uint32_t flags, int6
 // are bit-identical to it.
 constexpr int kWlPad = 16;
 constexpr int kWlMaxBytes = 64 * 1024;   // gate weight staged in LDS at most
-template <int NT, int TT, int WLU>
+// WS (64 experts or fewer in four expert tiles, four token tiles, d a
+// multiple of 512): the gate weight goes through LDS one 512-column slice at
+// a time, by LDS-DMA into two slots of 64 rows kWsRow bytes apart (1 KiB of
+// the slice + 16 bytes, so the 16 rows of a fragment read fall on distinct
+// banks), issued one slice ahead together with that slice's x loads; the
+// reduction buffer then reuses the slots.
+constexpr int kWsRow = 4 * 128 * 2 + 16;
+template <int NT, int TT, int WLU, bool WS = false>
 __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, const float* __restrict__ noise, float temperature,
     int64_t T, int64_t d, int E, int k, uint32_t flags, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ probs, float* __restrict__ lse,
     int32_t* __restrict__ tile_cnt, double* __restrict__ tile_colsum) {
-  __shared__ float red[4][kTok * TT][NT * 16];
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+  // the two weight slots are separate LDS variables, so the compiler can see
+  // that reading one never aliases the DMA still filling the other
+  __shared__ __attribute__((aligned(16))) unsigned char s_w0[WS ? 64 * kWsRow : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char s_w1[WS ? 64 * kWsRow : 16];
+  __shared__ float red_s[WS ? 1 : 4][kTok * TT][NT * 16];
+  float (*const red)[kTok * TT][NT * 16] =
+      WS ? reinterpret_cast<float (*)[kTok * TT][NT * 16]>(s_w0) : red_s;
   __shared__ int s_cnt[kMaxE];
   const int tid = threadIdx.x;
   if (tile_cnt != nullptr)
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
   constexpr bool WL = WLU > 0;
   if constexpr (WL) {
     static_assert(NT == 1 && TT == 1, "one expert tile, one token tile");
-    extern __shared__ __attribute__((aligned(16))) unsigned char s_wg[];
+    unsigned char* const s_wg = s_dyn;
     const int64_t rs = d * 2 + kWlPad;   // bytes per staged row
     // the gate weight goes to LDS by LDS-DMA (no registers): wave-wide load
     // j carries bytes 1024 j .. +1023 of the weight, inside one row (2 d is a
@@ -247,8 +261,99 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
   // different column windows of their rows rather than one window of every
   // row (the per-token sums then run over the slices in that rotated order).
   // Measured at 64 experts, d = 2048: 49 -> 40 us from cold caches, 31 ->
-  // 26 us warm, with the row reductions below.
-  constexpr bool PIPE = !WL && U == 1 && NT == 4;
+  // 26 us warm, with the row reductions below; with d a multiple of 512 the
+  // WS form below takes the gate-weight loads off the waves' path as well
+  // (26.7 -> 24.0 us warm, the same logits bit for bit).
+  constexpr bool PIPE = !WL && !WS && U == 1 && NT == 4;
+  if constexpr (WS) {
+    static_assert(NT == 4 && TT == 4 && !WL, "four expert tiles, four token tiles");
+    // d % 512 == 0 (checked at launch): every x load and every weight-row
+    // piece below is in range, so each wave issues exactly 16 weight DMA
+    // loads and 16 x loads per slice and the waits count them
+    const int nsl = static_cast<int>(d / (4 * kChunk));
+    const int rot = static_cast<int>(blockIdx.x % nsl);
+    auto cof = [&](int i) -> int64_t { return static_cast<int64_t>((i + rot) % nsl) * 4 * kChunk; };
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(wg), 0, static_cast<int>(static_cast<int64_t>(E) * d * 2), 0x00020000);
+    // staged row j holds gate row min(j, E - 1): 64 rows, 16 per wave (the
+    // wave index made uniform, so offsets and LDS addresses sit in SGPRs)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto stage_w = [&](int i, unsigned char* base) __attribute__((always_inline)) {
+      const int64_t c0 = cof(i);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int row = jj * 4 + wv;
+        const uint32_t soff = static_cast<uint32_t>((static_cast<int64_t>(min(row, E - 1)) * d + c0) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(base + row * kWsRow),
+                                                 16, static_cast<uint32_t>(lane) * 16u, soff, 0, 0);
+      }
+    };
+    bf16x8 a[2][TT][4];
+    auto load_a = [&](bf16x8 (&av)[TT][4], int64_t c0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int sx = 0; sx < 4; ++sx)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          av[tt][sx] = *reinterpret_cast<const bf16x8*>(xrow[tt] + c0 + wave * kChunk + sx * 32 + g * 8);
+    };
+    auto mma = [&](const bf16x8 (&av)[TT][4], const unsigned char* slot) __attribute__((always_inline)) {
+      const unsigned char* const base = slot + (wave * kChunk + g * 8) * 2;
+      bf16x8 b[NT][4];
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int sx = 0; sx < 4; ++sx)
+          b[n][sx] = *reinterpret_cast<const bf16x8*>(base + min(n * 16 + r, E - 1) * kWsRow + sx * 64);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int sx = 0; sx < 4; ++sx)
+            acc[tt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][sx], b[n][sx], acc[tt][n], 0, 0, 0);
+    };
+    // one slice: issue the next slice's weight DMA and x loads (32 per
+    // wave), wait for everything older, then every wave's share of this
+    // slice's weight is in LDS after the barrier; the second barrier keeps
+    // the slot from being refilled while a wave still reads it
+    // (the loop below has no branch inside its body, so the compiler's own
+    // waits before the MFMAs count the loads in flight exactly)
+    auto step = [&](int i, bf16x8 (&cur)[TT][4], bf16x8 (&nxt)[TT][4], unsigned char* slot,
+                    unsigned char* other, auto has_next) __attribute__((always_inline)) {
+      if constexpr (decltype(has_next)::value) {
+        stage_w(i + 1, other);
+        load_a(nxt, cof(i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (32 & 15) | ((32 >> 4) << 14));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      // plain barriers (a release fence would also wait for the next
+      // slice's loads): the wait above covers this slice's DMA
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      mma(cur, slot);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    stage_w(0, s_w0);
+    load_a(a[0], cof(0));
+    const std::true_type more;
+    const std::false_type last;
+    int i = 0;
+    for (; i + 2 < nsl; i += 2) {
+      step(i, a[0], a[1], s_w0, s_w1, more);
+      step(i + 1, a[1], a[0], s_w1, s_w0, more);
+    }
+    if (i + 1 < nsl) {
+      step(i, a[0], a[1], s_w0, s_w1, more);
+      step(i + 1, a[1], a[0], s_w1, s_w0, last);
+    } else {
+      step(i, a[0], a[1], s_w0, s_w1, last);
+    }
+  }
   if constexpr (PIPE) {
     const int64_t cw = static_cast<int64_t>(wave) * kChunk;
     const int nsl = cw < d ? static_cast<int>((d - cw + 4 * kChunk - 1) / (4 * kChunk)) : 0;
@@ -299,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
       mma(a[1]);
     }
   }
-  for (int64_t c00 = static_cast<int64_t>(wave) * kChunk; !WL && !PIPE && c00 < d; c00 += 4 * U * kChunk) {
+  for (int64_t c00 = static_cast<int64_t>(wave) * kChunk; !WL && !WS && !PIPE && c00 < d; c00 += 4 * U * kChunk) {
     bf16x8 a[U][TT][4], b[U][NT][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -428,6 +533,12 @@ hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
     if constexpr (NT == 1 && TT == 1) {
       launch_wl(std::integral_constant<int, 8>{});
     }
+  } else if (NT == 4 && TT == 4 && a.dtype == 1 && a.d % 512 == 0) {
+    if constexpr (NT == 4 && TT == 4)
+      hipLaunchKernelGGL((router_bf16_kernel<NT, TT, 0, true>), grid, block, 0, s,
+                         static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,
+                         a.noise, a.temperature, a.T, a.d, a.E, a.k, a.flags, a.topk_idx, a.topk_w,
+                         a.probs, a.lse, a.tile_cnt, a.tile_colsum);
   } else if (a.dtype == 1)
     hipLaunchKernelGGL((router_bf16_kernel<NT, TT, 0>), grid, block, 0, s,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wg), a.bias,

@@ -49,6 +49,10 @@ SMALL = [
     # tiles): token counts that leave a ragged last workgroup, and a d tail
     I.small("router-tiles-e40", T=517, d=200, d_ff=128, E=40, k=3, cf=1.25, seed=19),
     I.small("router-tiles-e17", T=77, d=520, d_ff=64, E=17, k=2, cf=1.25, seed=20),
+    # 33..64 experts with d a multiple of 512: the gate weight staged in LDS
+    # one 512-column slice at a time (fewer than 64 rows: the rows past E
+    # repeat the last); three slices, a ragged last workgroup
+    I.small("router-ws-e48", T=300, d=1536, d_ff=128, E=48, k=2, cf=1.25, seed=22),
     # capacity 0 at a shape the fragment-ordered path takes: every slot
     # dropped, no grouped rows, every kernel of the path a no-op
     I.small("all-dropped-frag", T=64, d=256, d_ff=256, E=4, k=2, cf=0.01, seed=21),
@@ -305,7 +309,8 @@ def test_plan_aux_equals_plan_then_aux_loss(T, E, k, cf, seed):
 @pytest.mark.parametrize("T,E,k,d,cf,seed", [(300, 6, 2, 256, 1.25, 11), (17, 8, 2, 128, 1.0, 12),
                                              (1, 4, 1, 64, 1.25, 13), (4096, 16, 2, 1024, 1.0, 14),
                                              (8192, 8, 2, 512, 1.25, 15), (1000, 40, 3, 256, 1.0, 16),
-                                             (8192, 64, 2, 256, 1.25, 17), (777, 100, 4, 128, 0.0, 18),
+                                             (8192, 64, 2, 256, 1.25, 17), (1000, 64, 2, 1024, 1.25, 18),
+                                             (300, 33, 3, 512, 1.0, 19), (777, 100, 4, 128, 0.0, 18),
                                              (0, 8, 2, 64, 1.25, 19)])
 def test_router_tiles_and_plan_tiles(T, E, k, d, cf, seed):
     """The bf16 router's per-tile outputs and the plan built from them:
