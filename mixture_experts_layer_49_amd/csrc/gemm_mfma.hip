@@ -934,10 +934,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(
   }
 }
 
-// Split tiles of a row-segmented launch: the split tiles of XCD x's last
-// round (rem of them) are shared out over the launch's workgroups b with
-// b % 8 == x, in bands of `rows` rows (a power of two from 4 to 256, the
-// smallest with which the XCD's gridDim / 8 workgroups cover all rem tiles):
+// Split tiles of a row-segmented launch (two fix-up workgroups per GEMM
+// workgroup): the split tiles of XCD x's last round (rem of them) are shared
+// out over the launch's workgroups b with b % 8 == x, in bands of `rows` rows
+// (a power of two from 4 to 256, the smallest with which the XCD's
+// gridDim / 8 workgroups cover all rem tiles):
 // workgroup b takes band j % (256 / rows) of split tile j / (256 / rows),
 // j = b / 8, adds its S partials in split order and emits the outputs. The
 // tile list and the splits are derived from offsets[] exactly as the GEMM
@@ -951,17 +952,25 @@ __global__ __launch_bounds__(kThreads) void split_fixup_kernel(
   constexpr int NV = VPC / 4;
   __shared__ int s_pref[kMaxE + 1];
   __shared__ int s_tmp[kMaxE];
-  build_tile_prefix(offsets, E, BM, s_pref, s_tmp);
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int tiles_n = (N + BN - 1) / BN;
   const int nk2 = (((K + BK - 1) / BK) + 1) & ~1;
-  const RowPlan pl = row_plan(static_cast<int64_t>(s_pref[E]) * tiles_n, xcd, P, nk2, max_split);
+  // The tile count first, each wave on its own (no barrier): in launches that
+  // split nothing, or where this workgroup has no band, it ends here, before
+  // the tile prefix.
+  int tot = 0;
+  for (int e = threadIdx.x & 63; e < E; e += 64) tot += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  const RowPlan pl = row_plan(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tot)) * tiles_n, xcd, P, nk2,
+                             max_split);
   if (pl.S == 1) return;
   const int per_xcd = static_cast<int>(gridDim.x >> 3);
   int rows = 4;
   while (rows < BM && rows * per_xcd < pl.rem * BM) rows <<= 1;
   const int bands = BM / rows, tr = j / bands, band = j % bands;
   if (tr >= pl.rem) return;
+  build_tile_prefix(offsets, E, BM, s_pref, s_tmp);
   const Tile tl = find_tile(s_pref, E, tiles_n, pl.r_beg + pl.full * P + tr);
   const int e0 = offsets[tl.e], seg1 = offsets[tl.e + 1];
   const int m0 = e0 + tl.mi * BM, n0 = tl.nt * BN;
@@ -1033,7 +1042,7 @@ void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int
   const int nk2 = (((K + BK - 1) / BK) + 1) & ~1;
   if constexpr (!Op::kSegK) {
     if (max_split > 1 && nk2 >= 32)
-      hipLaunchKernelGGL(split_fixup_kernel<Op>, dim3(4 * g.x), dim3(kThreads), 0, s, offsets, E, N, K,
+      hipLaunchKernelGGL(split_fixup_kernel<Op>, dim3(2 * g.x), dim3(kThreads), 0, s, offsets, E, N, K,
                          static_cast<int>(g.x / 8), max_split, part, C, static_cast<uint16_t*>(Z));
   }
 }
@@ -1042,7 +1051,7 @@ void launch_op(dim3 g, hipStream_t s, const void* A, const int32_t* offsets, int
 
 hipError_t launch_split_fixup_down(const int32_t* offsets, int E, int N, int K, int grid, int max_split,
                                    const float* part, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(split_fixup_kernel<OpDownF16>, dim3(4 * grid), dim3(kThreads), 0, s, offsets, E, N, K, grid / 8,
+  hipLaunchKernelGGL(split_fixup_kernel<OpDownF16>, dim3(2 * grid), dim3(kThreads), 0, s, offsets, E, N, K, grid / 8,
                      max_split, part, y, nullptr);
   return hipGetLastError();
 }
