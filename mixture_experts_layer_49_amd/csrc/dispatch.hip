@@ -240,14 +240,15 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
   const bool aux_wg = AUX && static_cast<int>(blockIdx.x) == place_wgs;
   // The aux workgroup adds up the column sums first, so those loads overlap
   // the count loads: thread (ee = tid % E, g = tid / E) adds the rows g,
-  // g + G, ... of expert ee, sixteen in flight; the G group sums are added in
-  // g order below.
+  // g + G, ... of expert ee in order, sixteen in flight, thirty-two when it
+  // has more than sixteen rows (64 experts x 256 token tiles: two rounds
+  // instead of four); the G group sums are added in g order below.
   double part = 0.0;
   if constexpr (AUX) {
     const int G = kThreads / E;
     const int ee = tid % E, g = tid / E;
-    if (aux_wg && g < G) {
-      constexpr int U = 16;
+    auto add_rows = [&](auto u_c) {
+      constexpr int U = decltype(u_c)::value;
       for (int c0 = g; c0 < nchunks; c0 += U * G) {
         double v[U];
 #pragma unroll
@@ -256,6 +257,10 @@ __global__ __launch_bounds__(kThreads) void place_scan_kernel(
         for (int u = 0; u < U; ++u)
           if (c0 + u * G < nchunks) part += v[u];
       }
+    };
+    if (aux_wg && g < G) {
+      if (nchunks > 16 * G) add_rows(std::integral_constant<int, 32>{});
+      else add_rows(std::integral_constant<int, 16>{});
     }
   }
   // all chunk counts, 16 bytes per load where the count is a multiple of 4,
