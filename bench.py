@@ -186,14 +186,23 @@ def copy_probe(args, torch, device):
 def timed_steps(step, steps, torch, stream):
     """Milliseconds for `steps` back-to-back steps, bracketed by a device
     synchronisation and two events on the launch stream; nothing else is
-    recorded inside, so the figure is the whole-job time."""
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
+    recorded inside, so the figure is the whole-job time. Python's garbage
+    collector is held off meanwhile: a collection pause on the launching
+    thread would leave the GPU idle inside the timed region."""
+    import gc
+
+    gc.collect()
+    gc.disable()
+    try:
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return start.elapsed_time(stop)
 
 

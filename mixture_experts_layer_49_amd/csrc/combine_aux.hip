@@ -14,18 +14,22 @@
 namespace moe {
 namespace {
 
-// One workgroup per token row (grid-stride), float4 lanes over d. Each thread
-// takes U float4 columns per step and issues all their loads (U x KM rows)
-// before it sums, so several round trips to memory overlap. KM >= k bounds
-// the slots held in registers (2 for top-1/top-2, else kMaxK).
+// tpw token rows per workgroup (grid-stride over groups of tpw), 256 / tpw
+// threads per row, float4 lanes over d: rows of fewer than 1024 float4 share
+// a workgroup, so that each thread still has U columns of loads in flight.
+// Each thread takes U float4 columns per step and issues all their loads
+// (U x KM rows) before it sums, so several round trips to memory overlap. KM
+// >= k bounds the slots held in registers (2 for top-1/top-2, else kMaxK).
 template <bool BF16_OUT, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ topk_w, int64_t T,
-                                                      int k, int64_t d, void* __restrict__ y) {
+                                                      int k, int64_t d, void* __restrict__ y, int tpw) {
   constexpr int U = KM <= 2 ? 4 : 1;
   const int64_t dv = d / 4;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  const int tpt = static_cast<int>(blockDim.x) / tpw;   // threads per token row
+  const int ts = static_cast<int>(threadIdx.x) / tpt, tl = static_cast<int>(threadIdx.x) % tpt;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * tpw + ts; t < T; t += static_cast<int64_t>(gridDim.x) * tpw) {
     int32_t rows[KM];
     float w[KM];
 #pragma unroll
@@ -33,11 +37,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       rows[j] = j < k ? dest[t * k + j] : -1;
       w[j] = j < k ? topk_w[t * k + j] : 0.f;
     }
-    for (int64_t v0 = threadIdx.x; v0 < dv; v0 += U * static_cast<int64_t>(blockDim.x)) {
+    for (int64_t v0 = tl; v0 < dv; v0 += U * static_cast<int64_t>(tpt)) {
       float4 o[U][KM];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t v = v0 + static_cast<int64_t>(u) * blockDim.x;
+        const int64_t v = v0 + static_cast<int64_t>(u) * tpt;
 #pragma unroll
         for (int j = 0; j < KM; ++j)
           o[u][j] = (v < dv && rows[j] >= 0)
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t v = v0 + static_cast<int64_t>(u) * blockDim.x;
+        const int64_t v = v0 + static_cast<int64_t>(u) * tpt;
         if (v >= dv) break;
         // Slot order; a dropped slot is skipped (not added as zero).
         float4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -185,14 +189,20 @@ __global__ __launch_bounds__(kMaxE) void z_final_kernel(const double* __restrict
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* topk_w, int64_t T,
                           int k, int64_t d, void* y, int out_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int64_t grid = T < 65536 ? T : 65536;
+  // token rows per workgroup: enough that a row of d / 4 float4 gives each of
+  // its threads four columns (1 at d >= 4096, 4 at d = 1024), at most 32
+  int tpw = 1;
+  while (tpw < 32 && static_cast<int64_t>(256 / (2 * tpw)) * 4 >= d / 4) tpw *= 2;
+  const int64_t groups = (T + tpw - 1) / tpw;
+  const int64_t grid = groups < 65536 ? groups : 65536;
   const dim3 g(static_cast<unsigned>(grid)), b(256);
   if (k <= 2) {
-    if (out_dtype == 1) hipLaunchKernelGGL((combine_kernel<true, 2>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
-    else hipLaunchKernelGGL((combine_kernel<false, 2>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
+    if (out_dtype == 1) hipLaunchKernelGGL((combine_kernel<true, 2>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y, tpw);
+    else hipLaunchKernelGGL((combine_kernel<false, 2>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y, tpw);
   } else {
-    if (out_dtype == 1) hipLaunchKernelGGL((combine_kernel<true, kMaxK>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
-    else hipLaunchKernelGGL((combine_kernel<false, kMaxK>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y);
+    if (out_dtype == 1)
+      hipLaunchKernelGGL((combine_kernel<true, kMaxK>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y, tpw);
+    else hipLaunchKernelGGL((combine_kernel<false, kMaxK>), g, b, 0, s, y_perm, dest, topk_w, T, k, d, y, tpw);
   }
   return hipGetLastError();
 }
