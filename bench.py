@@ -197,12 +197,15 @@ def timed_steps(step, steps, torch, stream):
         torch.cuda.synchronize()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
+        h0 = time.perf_counter()
         for _ in range(steps):
             step()
+        host = time.perf_counter() - h0
         stop.record(stream)
         torch.cuda.synchronize()
     finally:
         gc.enable()
+    timed_steps.host_us_per_step = host * 1e6 / max(steps, 1)
     return start.elapsed_time(stop)
 
 
@@ -702,6 +705,9 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
         "value": T * args.steps / (total_ms * 1e-3),
         "unit": "tokens/s" if cfg.routed else "rows/s",
         "ms_per_step": ms_per_step,
+        # host time to enqueue one step (the binding's argument marshalling and
+        # the launches); at or above ms_per_step the step would be launch-bound
+        "host_enqueue_us_per_step": timed_steps.host_us_per_step,
         "config": {"workload": cfg.name, "T": T, "d": d, "d_ff": dff, "E": E, "k": k,
                    "capacity_factor": cfg.cf, "capacity": C, "kept_rows": R,
                    "max_over_mean_load": float(counts.max() / counts.mean()),
