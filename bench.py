@@ -31,6 +31,7 @@ gradients, gate backward, gate weight gradients, dispatch^T).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -188,10 +189,11 @@ def timed_steps(step, steps, torch, stream):
     synchronisation and two events on the launch stream; nothing else is
     recorded inside, so the figure is the whole-job time. Python's garbage
     collector is held off meanwhile: a collection pause on the launching
-    thread would leave the GPU idle inside the timed region."""
+    thread would leave the GPU idle inside the timed region (the callers
+    collect before their warm-up steps, so no long host pause sits between
+    those and the timed steps either: an idle GPU lowers its clock)."""
     import gc
 
-    gc.collect()
     gc.disable()
     try:
         torch.cuda.synchronize()
@@ -291,6 +293,7 @@ def bench_backward(args, cfg, inp, ops, torch, np):
         rec(15)
 
     copy_probe(args, torch, x.device)
+    gc.collect()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -594,13 +597,16 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
             ev[len(kernels)].record(stream)
 
     copy_probe(args, torch, x.device)
+    # one set of boundary events per step of the second pass, all on the
+    # launch stream (made before the warm-up, so that nothing but the
+    # synchronisation separates the warm-up from the timed steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    gc.collect()
     ramp = clock_ramp(step, torch, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # one set of boundary events per timed step, all on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
     total_ms = timed_steps(step, args.steps, torch, stream)
     after = measure_clock(step, kernels, torch, stream, x.device)
     ceiling = measure_mfma_ceiling(torch, stream, x.device)
