@@ -313,8 +313,11 @@ size_t moe_ffn_workspace_bytes(int32_t dtype);
 
 /* The expert FFN of bf16 layers on fragment-ordered activations (inference:
  * moe_permute_frag, then moe_expert_up_gelu_frag with MOE_ORDER_FRAG, then
- * moe_expert_down_frag; the same h and y_perm, bit for bit, as the row-major
- * calls without a workspace). The fragment-ordered copy of x_perm holds
+ * moe_expert_down_frag). The products are those of the row-major calls,
+ * added in float32 in the matrix cores' 16 x 16 x 32 steps instead of
+ * 32 x 32 x 16 ones: h and y_perm equal the row-major calls' (without a
+ * workspace) up to float32 summation order; on every shape tested they were
+ * equal bit for bit. The fragment-ordered copy of x_perm holds
  * the permuted rows of EP tutorial 5.3 laid out for the matrix cores: each
  * expert segment is padded with zero rows to a multiple of 32 (padded segment
  * e starts at pad[e] = sum over e' < e of roundup(offsets[e'+1] - offsets[e'],
@@ -339,8 +342,8 @@ size_t moe_ffn_workspace_bytes(int32_t dtype);
  * moe_expert_down_frag: y_perm[r] = W2[e] . h[r] (float32, row-major
  *   [rows_max, d], rows >= offsets[E] not touched; ETP page w2) from h in
  *   fragment order and w2_f16 = moe_weights_bf16_to_f16(W2) [E, d, d_ff];
- *   d_ff a multiple of 256. Without a workspace, bit-identical to
- *   moe_expert_down_f16w without one; with moe_ffn_workspace_bytes of
+ *   d_ff a multiple of 256. Without a workspace, equal to
+ *   moe_expert_down_f16w without one as above; with moe_ffn_workspace_bytes of
  *   workspace, the tiles of a short last round are split along K (pieces of
  *   whole 256-deep quads, so the sums may round differently from the
  *   row-major kernel's splits; fixed order, deterministic).

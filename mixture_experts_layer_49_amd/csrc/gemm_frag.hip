@@ -20,19 +20,23 @@
 //
 // frag_gemm_kernel<KIND>: C = A B[e]^T over the segments, A fragment-ordered,
 // B = W1 or W2 [E, N, K] K-contiguous. 256 x 256 tiles, four waves as 4 x 1
-// (wave w: rows 64 w .. +63, all 256 columns, 2 x 8 accumulator tiles of
-// 32 x 32). Each wave loads its A fragments straight into registers (1 KiB
-// contiguous per wave load, four stages of register buffers, issued three
-// stages ahead); only B goes through LDS, in a ring of four 32 KiB slots
-// filled by LDS-DMA three stages ahead. One barrier per 64-deep stage. The
-// k-loop is laid out instruction by instruction: each MFMA is followed by at
-// most one LDS fragment read and one memory load, so neither kind arrives in
-// bursts that hold up the next MFMA. Tiles continue across a workgroup's units: the last three stages of a tile
-// prefetch the next tile's first three, so those loads are in flight during
-// the per-wave epilogue. The kinds (below) differ in the MFMA input type and
-// the epilogue; every MFMA sees the same operands in the same order as the
-// row-major GEMM's, so the results are bit-identical to it without a
-// workspace.
+// (wave w: rows 64 w .. +63, all 256 columns, 4 x 16 accumulator tiles of
+// 16 x 16, v_mfma_f32_16x16x32 on bf16 or fp16: per flop it moves half the
+// accumulator data of the 32 x 32 x 16 form, and under the chip's power cap
+// an MFMA-only loop of it holds a clock about 14% higher at the same issue
+// rate). Each wave loads its A fragments (16 rows x 32 k: four 256-byte runs
+// of the 32-row x 16-k blocks) straight into registers, four stages of
+// register buffers issued three stages ahead; only B goes through LDS, in a
+// ring of four 32 KiB slots filled by LDS-DMA three stages ahead. One barrier
+// per 64-deep stage. The k-loop is laid out instruction by instruction: each
+// MFMA is followed by at most one LDS fragment read and one memory load, so
+// neither kind arrives in bursts that hold up the next MFMA. Tiles continue
+// across a workgroup's units: the last three stages of a tile prefetch the
+// next tile's first three, so those loads are in flight during the per-wave
+// epilogue. The kinds (below) differ in the MFMA input type and the epilogue.
+// The products are those of the row-major GEMM (32 x 32 x 16 MFMAs), added
+// in float32; on every shape tested the results were equal to its own bit
+// for bit, without a workspace.
 #include "ffn_common.h"
 #include "gemm_frag.h"
 
@@ -47,15 +51,18 @@ typedef unsigned int u32x4v __attribute__((__vector_size__(16)));
 constexpr int FBM = 256, FBN = 256, FBK = 64;
 constexpr int kFT = 256;                       // threads
 constexpr int kFW = kFT / kWave;               // waves (4)
-constexpr int FMI = 2, FNI = 8;                // 32 x 32 accumulator tiles per wave
+constexpr int FMI = 4, FNI = 16;               // 16 x 16 accumulator tiles per wave (64 x 256)
 constexpr int kFABuf = 4;                      // A register buffers (stages)
 constexpr int kFCpr = FBK / 8;                 // 16-byte chunks per W1 row of a stage (8)
 constexpr int kFSlotU4 = FBN * kFCpr;          // uint4 per LDS slot (32 KiB)
 constexpr int kFBLoads = FBN / 8 / kFW;        // LDS-DMA loads per wave per stage (8)
-constexpr int kFAFrag = FMI * 4;               // A fragments per wave per stage (8)
-constexpr int kFEpiP = 136;                    // floats per row of a wave's epilogue buffer (8 rows)
-constexpr int kFFragP = 40;                    // the same for the fragment epilogue (32 rows)
-static_assert(8 * kFEpiP <= 32 * kFFragP, "one per-wave buffer serves both epilogues");
+constexpr int kFAFrag = FMI * 2;               // A fragments per wave per stage (8): 4 row blocks x 2 k-slices
+constexpr int kFBRing = 4;                     // B fragments held in registers, read three ahead
+constexpr int kFMf = FMI * FNI * 2;            // MFMAs per wave per stage (128)
+constexpr int kFEpiP = 68;                     // floats per row of the row-major epilogue's staging (16 rows)
+constexpr int kFFragP = 20;                    // the same for the fragment epilogue (32 rows)
+constexpr int kFEpiFloats = 16 * kFEpiP;       // per-wave staging buffer
+static_assert(32 * kFFragP <= kFEpiFloats, "one per-wave buffer serves both epilogues");
 constexpr int kFragMaxSplit = 8;               // as the row-major GEMM (its fix-up kernel sums up to 8)
 
 #define FR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -206,6 +213,32 @@ __device__ __forceinline__ void fr_store16(const uint4& v, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
 }
 
+// One 16 x 16 x 32 MFMA accumulating in place (the accumulator tied to the
+// destination in the same accumulation registers). Written as inline assembly
+// because the compiler, given sixty-four 4-register accumulators, chose
+// separate destination registers and moved accumulators through VGPRs in the
+// loop. The compiler does not know these are MFMAs, so the kernel adds the
+// wait states the hardware needs where other instructions meet them: after
+// the accumulators are set to zero (before the k-loop) and before the
+// epilogue reads the results.
+template <bool F16>
+__device__ __forceinline__ void mfma16_acc(f32x4& acc, const uint4& a, const uint4& b) {
+  const u32x4v av = __builtin_bit_cast(u32x4v, a), bv = __builtin_bit_cast(u32x4v, b);
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(av), "v"(bv));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(av), "v"(bv));
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order, at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     const uint16_t* __restrict__ Afrag, const int32_t* __restrict__ offsets, int E, int N, int K,
@@ -221,7 +254,7 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pad[kMaxE + 1];
   __shared__ int s_tmp[kMaxE];
-  __shared__ float s_epi[kFW][32 * kFFragP];   // per-wave epilogue staging
+  __shared__ float s_epi[kFW][kFEpiFloats];   // per-wave epilogue staging
   auto SL = [&](int S) -> uint4* { return S == 0 ? sb0 : (S == 1 ? sb1 : (S == 2 ? sb2 : sb3)); };
   const int tid = threadIdx.x;
   for (int e = tid; e <= E; e += kFT) s_off[e] = offsets[e];
@@ -244,14 +277,20 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
   if (n_units == 0) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int l32 = lane & 31, hl = lane >> 5;
   const uint32_t b_rb = static_cast<uint32_t>(K) * 2u;
   const uint32_t a_blk = static_cast<uint32_t>(K) * 64u;   // bytes per 32-row block of x_frag
   // LDS-DMA of W1: wave-wide load j fills rows 8 (4 j + wave) + lane / 8 of
   // the slot at physical chunk lane % 8, fetching logical chunk
   // (lane % 8) ^ ((row >> 1) & 7); fragment reads undo the XOR.
   const uint32_t ld_voff_b = (lane >> 3) * b_rb + (((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16u);
-  const int fr_x = hl ^ ((l32 >> 1) & 7);
+  // A fragment of 16 rows x 32 k (lane l: row l % 16, k = 8 (l / 16) .. +7)
+  // out of the 32-row x 16-k blocks of x_frag: the lane's 16 bytes sit at
+  // unit (row % 32) + 32 ((k / 8) % 2) of 16-k block k / 16. Per lane:
+  const uint32_t a_voff = (static_cast<uint32_t>((lane & 15) + 32 * ((lane >> 4) & 1)) * 16u) +
+                          static_cast<uint32_t>(lane >> 5) * 1024u;
+  // B fragment (16 W1 rows x 32 k: lane l row l % 16, logical chunk 4 s + l / 16)
+  // in a slot: uint4 (b_base ^ 4 s) + 128 j for column block j, k-slice s.
+  const int b_base = (lane & 15) * kFCpr + ((lane >> 4) ^ ((lane & 15) >> 1));
 
   // Unit q: a whole tile of round q, or (q >= full) piece pc = (q - full) P + w
   // of the last round: k-range pc / rem (in quads of stages) of tile pc % rem.
@@ -287,45 +326,35 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
                                             0, static_cast<int>(b_rows * b_rb), 0x00020000);
   };
 
-  uint4 fa[kFABuf][kFAFrag];   // [stage buffer][4 i + slice]
-  uint4 fb[2][FNI];
-  f32x16 acc[FMI][FNI];
+  uint4 fa[kFABuf][kFAFrag];   // [stage buffer][4 s + i]: k-slice s, 16-row block i
+  uint4 fb[kFBRing];           // B fragments, fragment f of a stage in fb[f % 4]
+  f32x4 acc[FMI][FNI];
 
-  // A fragments f0 .. f1-1 (f = 4 i + slice) of stage kt into buffer AB.
-  auto issue_a = [&](const FCtx& c, int kt, auto ab_c, int f0, int f1) __attribute__((always_inline)) {
+  // A fragment v = 4 s + i of stage kt into buffer AB: rows 16 i .. +15 of the
+  // wave's 64 (32-row block 2 wave + i / 2, its half i % 2), k = 64 kt + 32 s ..
+  auto issue_a = [&](const FCtx& c, int kt, auto ab_c, int v) __attribute__((always_inline)) {
     constexpr int AB = decltype(ab_c)::value;
-#pragma unroll
-    for (int f = f0; f < f1; ++f) {
-      const int i = f >> 2, s = f & 3;
-      const uint32_t so = static_cast<uint32_t>(2 * wave + i) * a_blk + static_cast<uint32_t>(4 * kt + s) * 1024u;
-      fa[AB][f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-          c.a, static_cast<uint32_t>(lane) * 16u, so, 0));
-    }
+    const int s = v >> 2, i = v & 3;
+    const uint32_t so = static_cast<uint32_t>(2 * wave + (i >> 1)) * a_blk +
+                        static_cast<uint32_t>(4 * kt + 2 * s) * 1024u + static_cast<uint32_t>(i & 1) * 256u;
+    fa[AB][v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(c.a, a_voff, so, 0));
   };
-  // W1 loads j0 .. j1-1 of stage kt into slot S.
-  auto issue_b = [&](const FCtx& c, int kt, int S, int j0, int j1) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = j0; j < j1; ++j) {
-      const int blk = j * kFW + wave;
-      const uint32_t so = blk * 8 * b_rb + static_cast<uint32_t>(kt) * FBK * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(SL(S) + blk * kWave), 16, ld_voff_b, so, 0, 0);
-    }
+  // W1 load j of stage kt into slot S.
+  auto issue_b = [&](const FCtx& c, int kt, int S, int j) __attribute__((always_inline)) {
+    const int blk = j * kFW + wave;
+    const uint32_t so = blk * 8 * b_rb + static_cast<uint32_t>(kt) * FBK * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b, (lds_ptr_t)(SL(S) + blk * kWave), 16, ld_voff_b, so, 0, 0);
   };
-  // B fragment j of k-slice kk of slot S into fb[fs][j].
-  auto rd = [&](int S, int kk, int fs, int j) __attribute__((always_inline)) {
-    fb[fs][j] = SL(S)[l32 * kFCpr + (fr_x ^ (kk * 2)) + j * 32 * kFCpr];
+  // B fragment f (k-slice f / 16, column block f % 16) of slot S into the ring.
+  auto rd = [&](int S, int f) __attribute__((always_inline)) {
+    fb[f & (kFBRing - 1)] = SL(S)[(b_base ^ ((f >> 4) << 2)) + (f & 15) * 16 * kFCpr];
   };
-  // MFMA m of k-slice s: accumulator tile (m % 2, m / 2), so B fragment j is
-  // consumed by MFMAs 2 j and 2 j + 1.
-  auto mf = [&](auto ab_c, int s, int fs, int m) __attribute__((always_inline)) {
-    constexpr int AB = decltype(ab_c)::value;
-    const int i = m & 1, j = m >> 1;
-    if constexpr (DOWN)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          __builtin_bit_cast(f16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(f16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
-    else
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8, fa[AB][i * 4 + s]), __builtin_bit_cast(bf16x8, fb[fs][j]), acc[i][j], 0, 0, 0);
+  // MFMA m of a stage: fragment f = m / 4 (k-slice f / 16, column block
+  // f % 16) times A block i = m % 4; each B fragment feeds four MFMAs in a row.
+  auto mf = [&](auto ab_c, auto m_c) __attribute__((always_inline)) {
+    constexpr int AB = decltype(ab_c)::value, m = decltype(m_c)::value;
+    constexpr int f = m >> 2, i = m & 3, s = f >> 4, j = f & 15;
+    mfma16_acc<DOWN>(acc[i][j], fa[AB][4 * s + i], fb[f & (kFBRing - 1)]);
   };
 
   FCtx cur, nxt;
@@ -334,52 +363,36 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
   else nxt = cur;   // past the last unit the prefetches re-read this one (never used)
   // Prologue: the first three stages of the first unit (klo is a multiple of
   // four, so stage kt always uses slot and A buffer kt % 4).
-  issue_a(cur, cur.klo, std::integral_constant<int, 0>{}, 0, kFAFrag);
-  issue_b(cur, cur.klo, 0, 0, kFBLoads);
-  issue_a(cur, cur.klo + 1, std::integral_constant<int, 1>{}, 0, kFAFrag);
-  issue_b(cur, cur.klo + 1, 1, 0, kFBLoads);
-  issue_a(cur, cur.klo + 2, std::integral_constant<int, 2>{}, 0, kFAFrag);
-  issue_b(cur, cur.klo + 2, 2, 0, kFBLoads);
-
-  // One k-slice (16 MFMAs) in a fixed order: after MFMA m comes, for even m,
-  // the read of B fragment m / 2 of the next slice (from slot rS, k-slice
-  // rkk, into the other fb buffer) and, for m % 4 == 1, one memory load of
-  // stage pk (nA A fragments from a0, then nB W1 loads from b0). Each piece
-  // is fenced so the compiler keeps this order: every LDS read and memory
-  // instruction issues behind an MFMA that is already running, each
-  // fragment is read 16 MFMAs before its use, and a wave sends the memory
-  // pipeline one instruction per four MFMAs instead of bursts.
-  auto slice = [&](auto ab_c, auto sn_c, int s, int fs, int rS, int rkk, const FCtx& pc, int pk, int a0, int nA,
-                   int b0, int nB) __attribute__((always_inline)) {
-    constexpr int SN = decltype(sn_c)::value;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      mf(ab_c, s, fs, m);
-      __builtin_amdgcn_sched_barrier(0);
-      if ((m & 1) == 0) {
-        rd(rS, rkk, fs ^ 1, m >> 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const int vi = m >> 2;
-      if ((m & 3) == 1 && vi < nA + nB) {
-        if (vi < nA) issue_a(pc, pk, std::integral_constant<int, SN>{}, a0 + vi, a0 + vi + 1);
-        else issue_b(pc, pk, SN, b0 + vi - nA, b0 + vi - nA + 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
+  for (int v = 0; v < kFAFrag; ++v) issue_a(cur, cur.klo, std::integral_constant<int, 0>{}, v);
+#pragma unroll
+  for (int j = 0; j < kFBLoads; ++j) issue_b(cur, cur.klo, 0, j);
+#pragma unroll
+  for (int v = 0; v < kFAFrag; ++v) issue_a(cur, cur.klo + 1, std::integral_constant<int, 1>{}, v);
+#pragma unroll
+  for (int j = 0; j < kFBLoads; ++j) issue_b(cur, cur.klo + 1, 1, j);
+#pragma unroll
+  for (int v = 0; v < kFAFrag; ++v) issue_a(cur, cur.klo + 2, std::integral_constant<int, 2>{}, v);
+#pragma unroll
+  for (int j = 0; j < kFBLoads; ++j) issue_b(cur, cur.klo + 2, 2, j);
 
-  // Stage kt (slot and A buffer SB = kt % 4, compile time) of unit q. It
-  // prefetches stage kt+3 of unit q or, past the end, of unit q+1 (after the
-  // last unit: an in-bounds stage into buffers nobody reads, so every stage
-  // issues the same 16 loads): A 0-3 in slice 0, A 4-7 in slice 1, W1 0-3 in
-  // slice 2, W1 4-7 in slice 3. After slice 2 it waits for stage kt+1, whose
-  // loads are older than the 16 of stage kt+2 and the 12 of stage kt+3
-  // issued so far and, in the first two stages after a per-wave epilogue,
-  // that epilogue's NST stores. The barrier then tells every wave that stage
-  // kt+1 is in LDS and that no wave reads slot SB any more (slice 3's
-  // fragments were read during slice 2), so slice 3 may read slot S1 and
-  // its W1 loads may fill the slot of stage kt-1.
+  // Stage kt (slot and A buffer SB = kt % 4, compile time) of unit q: 128
+  // MFMAs in a fixed order, each B fragment feeding four in a row (one per A
+  // block). After MFMA m (m % 4 == 0) comes the read of B fragment m / 4 + 3
+  // into the ring (12 MFMAs before its use; the last three of the stage are
+  // the next stage's first fragments, from its slot S1), and after MFMAs 1,
+  // 9, .., 89 and 116, 120, 124, 127 one memory load each of stage kt+3 of
+  // unit q or, past the end, of unit q+1 (after the last unit: an in-bounds
+  // stage into buffers nobody reads, so every stage issues the same 16 loads):
+  // the 8 A fragments and W1 loads 0-3 before the barrier, W1 loads 4-7 after
+  // it. Every piece is fenced so the compiler keeps this order. After MFMA
+  // 116 each wave waits for stage kt+1, whose loads are older than the 16 of
+  // stage kt+2 and the 12 of stage kt+3 issued so far and, in the first two
+  // stages after a per-wave epilogue, that epilogue's NST stores; the barrier
+  // then tells every wave that stage kt+1 is in LDS and that no wave reads
+  // slot SB any more (its last fragment was read after MFMA 112), so the next
+  // stage's fragments may be read and W1 loads may fill the slot of stage
+  // kt-1 (free since the previous stage's barrier).
   int64_t q = 0;
   bool after_epi = false;
   auto stage = [&](auto sb_c, int kt) __attribute__((always_inline)) {
@@ -393,75 +406,91 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     using AB = std::integral_constant<int, SB>;
     using SNc = std::integral_constant<int, SN>;
     __builtin_amdgcn_sched_barrier(0);
-    slice(AB{}, SNc{}, 0, 0, SB, 1, pc, pk, 0, 4, 0, 0);
-    slice(AB{}, SNc{}, 1, 1, SB, 2, pc, pk, 4, 4, 0, 0);
-    slice(AB{}, SNc{}, 2, 0, SB, 3, pc, pk, 0, 0, 0, 4);
-    if (after_epi && kt - cur.klo < 2) FR_WAIT_VM(60);
-    else FR_WAIT_VM(28);
-    FR_BARRIER();
-    __builtin_amdgcn_sched_barrier(0);
-    slice(AB{}, SNc{}, 3, 1, S1, 0, pc, pk, 0, 0, 4, 4);
-    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, kFMf>([&](auto m_c) __attribute__((always_inline)) {
+      constexpr int m = decltype(m_c)::value;
+      mf(AB{}, m_c);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (m == 4 * (33 - kFBRing)) {   // before the first read of the next stage's slot
+        if (after_epi && kt - cur.klo < 2) FR_WAIT_VM(60);
+        else FR_WAIT_VM(28);
+        FR_BARRIER();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr ((m & 3) == 0) {
+        constexpr int f = (m >> 2) + kFBRing - 1;
+        if constexpr (f < 32) rd(SB, f);
+        else rd(S1, f - 32);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      constexpr int v = (m < 96 && (m & 7) == 1) ? (m >> 3)                        // 0 .. 11
+                        : (m == 116 || m == 120 || m == 124) ? 12 + (m - 116) / 4  // 12 .. 14
+                        : m == 127 ? 15 : -1;
+      if constexpr (v >= 0) {
+        if constexpr (v < kFAFrag) issue_a(pc, pk, SNc{}, v);
+        else issue_b(pc, pk, SN, v - kFAFrag);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
   };
 
-  // Per-wave epilogue of a tile: chunks of 8 rows x 128 columns of the wave's
-  // 64 x 256 block staged through its LDS buffer, then GELU, fp16 and 16-byte
-  // stores; lanes outside the output get an offset past the buffer's range
-  // and are dropped, so every lane issues exactly NST stores.
-  constexpr int ITEMS = 8 * 128 / 8 / kWave;   // 16-byte items per lane per chunk (2)
-  constexpr int NST = FMI * 4 * 2 * ITEMS;      // 32 stores per lane per tile
-  // The waits above count 32 stores after an epilogue; the register-direct
-  // fragment epilogue issues 32 too, the f32 one 64 (the waits then also
-  // cover the oldest 32 of those stores: more waiting, never less).
-  static_assert(NST == 32, "the waits above count 32 stores after an epilogue");
-  auto epilogue = [&](int c_m0, int c_n0, int c_seg1) {
+  // Per-wave epilogues. Accumulator tile (i, j) holds rows 16 i + 4 (lane / 16)
+  // + r (register r) and column 16 j + lane % 16 of the wave's 64 x 256 block.
+  // Row-major outputs go through the wave's LDS buffer in chunks of 16 rows x
+  // 64 columns (tiles (i, 4 g .. 4 g + 3)) and leave in whole 16-byte stores;
+  // lanes outside the output get an offset past the buffer's range and are
+  // dropped, so every lane issues exactly NST stores (fp16 h) or 2 NST (f32).
+  constexpr int NST = 32;   // stores per lane per tile of the fp16 epilogues
+  // The waits above count 32 stores after an epilogue; the f32 one issues 64
+  // (the waits then also cover the oldest 32 of those stores: more waiting,
+  // never less).
+  auto stage_chunk = [&](float* buf, int i, int g) __attribute__((always_inline)) {
+    const int el16 = lane & 15, eq = lane >> 4;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) buf[(4 * eq + r) * kFEpiP + 16 * jj + el16] = acc[i][4 * g + jj][r];
+  };
+  // h row-major (kFragUpRows): GELU, fp16, eight values per 16-byte store.
+  auto epilogue_rows_h = [&](const FCtx& c) {
     float* const buf = s_epi[wave];
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int el32 = ln & 31, ehl = ln >> 5;
-    const int rows_ok = min(c_seg1 - c_m0, FBM), cols_ok = min(N - c_n0, FBN);
+    const int rows_ok = min(c.seg1 - c.m0, FBM), cols_ok = min(N - c.n0, FBN);
     const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<uint16_t*>(Cout) + (static_cast<int64_t>(c_m0) * N + c_n0), 0, rows_ok * N * 2, 0x00020000);
+        static_cast<uint16_t*>(Cout) + (static_cast<int64_t>(c.m0) * N + c.n0), 0, rows_ok * N * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < FMI; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int g = 0; g < 4; ++g) {
+        stage_chunk(buf, i, g);
 #pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          // register 4 c + rr of tile (i, j) holds row 8 c + 4 (lane / 32) + rr, column 32 j + lane % 32
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              buf[(4 * ehl + rr) * kFEpiP + 32 * jj + el32] = acc[i][4 * jh + jj][4 * c + rr];
-#pragma unroll
-          for (int it = 0; it < ITEMS; ++it) {
-            const int f = ln + kWave * it;
-            const int row = f >> 4, col = (f & 15) << 3;
-            const float4 a = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col);
-            const float4 b = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col + 4);
-            const int trow = 64 * wave + 32 * i + 8 * c + row, tcol = 128 * jh + col;
-            const uint32_t voff = (trow < rows_ok && tcol < cols_ok)
-                                      ? static_cast<uint32_t>((trow * N + tcol) * 2) : 0x80000000u;
-            const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
-            const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
-            const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
-            const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
-            fr_store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
-                       out, voff);
-          }
+        for (int it = 0; it < 2; ++it) {
+          const int f = ln + kWave * it;
+          const int row = f >> 3, col = (f & 7) << 3;
+          const float4 a = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col);
+          const float4 b = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col + 4);
+          const int trow = 64 * wave + 16 * i + row, tcol = 64 * g + col;
+          const uint32_t voff = (trow < rows_ok && tcol < cols_ok)
+                                    ? static_cast<uint32_t>((trow * N + tcol) * 2) : 0x80000000u;
+          const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
+          const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
+          const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
+          const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
+          fr_store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
+                     out, voff);
         }
+      }
   };
 
-  // h in fragment order: each 32 x 32 accumulator tile goes through the
-  // wave's LDS buffer (rows 40 floats apart: the two half-waves of a write sit
-  // 32 banks apart), then lane l reads row l % 32, columns 8 (l / 32) .. +7 and
-  // 16 + 8 (l / 32) .. +7 -- unit l of the tile's two fragments -- applies
-  // GELU and fp16 and writes each with one 16-byte store (1 KiB per wave
-  // store). Blocks past the padded segment are past the buffer's range and
-  // dropped; rows inside the last block but past the segment hold GELU(0) = 0
-  // (their A rows are zero). 32 stores per lane per tile, as NST.
+  // h in fragment order: each 32-row x 16-column block of h (accumulator
+  // tiles (2 p, q) and (2 p + 1, q)) goes through the wave's LDS buffer (rows
+  // 20 floats apart: the four row groups of a write land on distinct banks),
+  // then lane l reads row l % 32, columns 8 (l / 32) .. +7 -- unit l of the
+  // block -- applies GELU and fp16 and writes it with one 16-byte store (1 KiB
+  // per wave store). Blocks past the padded segment are past the buffer's
+  // range and dropped; rows inside the last block but past the segment hold
+  // GELU(0) = 0 (their A rows are zero). 32 stores per lane per tile, as NST.
   auto epilogue_frag = [&](const FCtx& c) {
     float* const buf = s_epi[wave];
     const uint32_t h_blk = static_cast<uint32_t>(N) * 64u;   // bytes per 32-row block of h
@@ -470,41 +499,38 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
         static_cast<int>(c.blocks * h_blk), 0x00020000);
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int el32 = ln & 31, ehl = ln >> 5;
+    const int el16 = ln & 15, eq = ln >> 4;
     const uint32_t lo = static_cast<uint32_t>(ln) * 16u;
 #pragma unroll
-    for (int i = 0; i < FMI; ++i)
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int j = 0; j < FNI; ++j) {
-        // register r of tile (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+      for (int qb = 0; qb < FNI; ++qb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) buf[(8 * (r >> 2) + 4 * ehl + (r & 3)) * kFFragP + el32] = acc[i][j][r];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const float4 a = *reinterpret_cast<const float4*>(buf + el32 * kFFragP + 16 * p + 8 * ehl);
-          const float4 b = *reinterpret_cast<const float4*>(buf + el32 * kFFragP + 16 * p + 8 * ehl + 4);
-          const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
-          const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
-          const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
-          const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
-          const uint32_t kg = static_cast<uint32_t>(c.n0 + 32 * j + 16 * p) / 16u;
-          const uint32_t so = static_cast<uint32_t>(2 * wave + i) * h_blk + kg * 1024u;
-          fr_store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
-                     out, lo, so);
+        for (int r = 0; r < 4; ++r) {
+          buf[(4 * eq + r) * kFFragP + el16] = acc[2 * p][qb][r];
+          buf[(16 + 4 * eq + r) * kFFragP + el16] = acc[2 * p + 1][qb][r];
         }
+        const float4 a = *reinterpret_cast<const float4*>(buf + (ln & 31) * kFFragP + 8 * (ln >> 5));
+        const float4 b = *reinterpret_cast<const float4*>(buf + (ln & 31) * kFFragP + 8 * (ln >> 5) + 4);
+        const f16x2 p0 = {static_cast<_Float16>(gelu_tanh_fast(a.x)), static_cast<_Float16>(gelu_tanh_fast(a.y))};
+        const f16x2 p1 = {static_cast<_Float16>(gelu_tanh_fast(a.z)), static_cast<_Float16>(gelu_tanh_fast(a.w))};
+        const f16x2 p2 = {static_cast<_Float16>(gelu_tanh_fast(b.x)), static_cast<_Float16>(gelu_tanh_fast(b.y))};
+        const f16x2 p3 = {static_cast<_Float16>(gelu_tanh_fast(b.z)), static_cast<_Float16>(gelu_tanh_fast(b.w))};
+        const uint32_t so = static_cast<uint32_t>(2 * wave + p) * h_blk +
+                            static_cast<uint32_t>((c.n0 >> 4) + qb) * 1024u;
+        fr_store16(uint4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                         __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)},
+                   out, lo, so);
       }
   };
 
-  // f32 output (down-projection): as the row-major h epilogue, eight values
-  // per item in two 16-byte stores; a split piece writes its 256 x 256
-  // partial sum (the rows inside the segment), row-major, to its workspace
-  // slot xcd * 2 P + piece.
+  // f32 output (down-projection): four values per 16-byte store; a split
+  // piece writes its 256 x 256 partial sum (the rows inside the segment),
+  // row-major, to its workspace slot xcd * 2 P + piece.
   auto epilogue_down = [&](const FCtx& c) {
     float* const buf = s_epi[wave];
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int el32 = ln & 31, ehl = ln >> 5;
     const bool piece = c.tail >= 0;
     const int pitch = piece ? FBN : N;
     // a piece stores only the rows inside the segment (the fix-up reads no others)
@@ -515,29 +541,20 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < FMI; ++i)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
+      for (int g = 0; g < 4; ++g) {
+        stage_chunk(buf, i, g);
 #pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              buf[(4 * ehl + rr) * kFEpiP + 32 * jj + el32] = acc[i][4 * jh + jj][4 * cc + rr];
-#pragma unroll
-          for (int it = 0; it < ITEMS; ++it) {
-            const int f = ln + kWave * it;
-            const int row = f >> 4, col = (f & 15) << 3;
-            const float4 a = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col);
-            const float4 b = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col + 4);
-            const int trow = 64 * wave + 32 * i + 8 * cc + row, tcol = 128 * jh + col;
-            const bool ok = trow < rows_ok && tcol < cols_ok;
-            const uint32_t voff = ok ? static_cast<uint32_t>((trow * pitch + tcol) * 4) : 0x80000000u;
-            fr_store16(uint4{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w)},
-                       out, voff);
-            fr_store16(uint4{__float_as_uint(b.x), __float_as_uint(b.y), __float_as_uint(b.z), __float_as_uint(b.w)},
-                       out, ok ? voff + 16u : 0x80000000u);
-          }
+        for (int it = 0; it < 4; ++it) {
+          const int f = ln + kWave * it;
+          const int row = f >> 4, col = (f & 15) << 2;
+          const float4 a = *reinterpret_cast<const float4*>(buf + row * kFEpiP + col);
+          const int trow = 64 * wave + 16 * i + row, tcol = 64 * g + col;
+          const bool ok = trow < rows_ok && tcol < cols_ok;
+          const uint32_t voff = ok ? static_cast<uint32_t>((trow * pitch + tcol) * 4) : 0x80000000u;
+          fr_store16(uint4{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w)},
+                     out, voff);
         }
+      }
   };
 
   for (;;) {
@@ -547,14 +564,16 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     else FR_WAIT_VM(32);
     FR_BARRIER();
 #pragma unroll
-    for (int j = 0; j < FNI; ++j) rd(0, 0, 0, j);
+    for (int f = 0; f < kFBRing - 1; ++f) rd(0, f);
 #pragma unroll
     for (int i = 0; i < FMI; ++i)
 #pragma unroll
-      for (int j = 0; j < FNI; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int j = 0; j < FNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int kt = cur.klo; kt < cur.khi; kt += 4) {
+      // The accumulator writes that set them to zero come before the loop
+      // (the compiler places them ahead of its header): wait states before
+      // the first MFMAs read them.
+      asm volatile("s_nop 2" ::: "memory");
       stage(std::integral_constant<int, 0>{}, kt);
       stage(std::integral_constant<int, 1>{}, kt + 1);
       stage(std::integral_constant<int, 2>{}, kt + 2);
@@ -564,8 +583,11 @@ __global__ __launch_bounds__(kFT, 1) void frag_gemm_kernel(
     ++q;
     const bool has_next = q < n_units;
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");   // the stores stay after the prefetches
-    if constexpr (KIND == kFragUpRows) epilogue(done.m0, done.n0, done.seg1);
+    // the last MFMAs' results are complete before the epilogue reads them
+    // (more wait states than the longest 16 x 16 x 32 MFMA needs)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // also: the stores stay after the prefetches
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KIND == kFragUpRows) epilogue_rows_h(done);
     else if constexpr (HFRAG) epilogue_frag(done);
     else epilogue_down(done);
     if (!has_next) {

@@ -1,9 +1,13 @@
 """GPU: the fragment-ordered permute and up-projection against the row-major
 ones, on the same segments. The permuted rows are bit-exact (read back through
-the layout's definition, padding rows zero), h is bit-identical to
-moe_expert_up_gelu without a workspace (the same MFMA operands in the same
-order), and rows past the segments are left alone. The row-major up-projection
-is itself checked against the oracle by the layer parity tests."""
+the layout's definition, padding rows zero), and rows past the segments are
+left alone. The fragment-ordered GEMM multiplies with 16 x 16 x 32 MFMAs and
+the row-major one with 32 x 32 x 16 MFMAs: the same products, added in float32
+in another order, so h agrees with moe_expert_up_gelu's to one fp16 rounding
+step (plus the absolute change of a reordered float32 sum near zero) and y_perm
+to float32 summation order. The row-major GEMM is itself checked against the
+oracle by the layer parity tests, and so is the fragment-ordered path at every
+workload's full size."""
 import numpy as np
 import pytest
 import torch
@@ -15,6 +19,37 @@ pytestmark = pytest.mark.gpu
 
 SENT_H = 0x7E55     # an fp16 NaN pattern no result has
 SENT_X = 0x5A5A
+
+
+def fp16_close(got, ref, what):
+    """got and ref (fp16, same shape) agree to one fp16 rounding step of ref
+    plus 2^-17: the float32 sums of d products behind them differ only in the
+    order of their additions, which moves the pre-activation by about
+    sqrt(d) 2^-24 of the partial sums' size and gelu by at most 1.13 times
+    that; after the fp16 rounding, values next to a rounding boundary move by
+    one step, and near zero (fp16 subnormals, step 2^-24) by that absolute
+    change. Few values may move at all."""
+    a, b = got.double().cpu(), ref.double().cpu()
+    assert torch.isfinite(a).all() == torch.isfinite(b).all()
+    step = torch.where(b.abs() < 2.0 ** -14, torch.full_like(b, 2.0 ** -24),
+                       torch.exp2(torch.floor(torch.log2(b.abs().clamp_min(2.0 ** -14)))) * 2.0 ** -10)
+    diff = (a - b).abs()
+    bad = diff > step * 1.0001 + 2.0 ** -17
+    moved = (diff > 0).double().mean().item() if diff.numel() else 0.0
+    say("  %s: %.4f%% of values differ, max|diff| %.3g, %d beyond the bound"
+        % (what, 100 * moved, diff.max().item() if diff.numel() else 0.0, int(bad.sum())))
+    assert not bad.any(), "%s differs by more than one fp16 step" % what
+    assert moved < 0.02, "%s: %.4f of the values differ" % (what, moved)
+
+
+def f32_close(got, ref, what, tol=1e-4):
+    """float32 results of the same products summed in another order: max|diff|
+    within tol of the reference's RMS."""
+    a, b = got.double().cpu(), ref.double().cpu()
+    rms = b.pow(2).mean().sqrt().item() if b.numel() else 0.0
+    err = ((a - b).abs().max().item() / rms) if rms > 0 else (a - b).abs().max().item() if a.numel() else 0.0
+    say("  %s: max|diff|/rms %.2e" % (what, err))
+    assert err <= tol, "%s: max|diff|/rms %.3e" % (what, err)
 
 
 def run_case(counts, d, d_ff, slack=17, seed=0):
@@ -45,12 +80,7 @@ def run_case(counts, d, d_ff, slack=17, seed=0):
     assert torch.equal(rows, x.cpu()[src.cpu()[:R].long()]), "permuted rows differ"
     assert (pads.view(torch.int16) == 0).all(), "padding rows are not zero"
     assert (x_frag.view(torch.int16)[pad_total:].cpu() == SENT_X).all(), "rows past the padded segments written"
-    same = torch.equal(h[:R].view(torch.int16), h_ref[:R].view(torch.int16))
-    if not same:
-        diff = (h[:R].float() - h_ref[:R].float()).abs()
-        bad = torch.nonzero(diff > 0)
-        say("  %d values differ, first at %s" % (bad.shape[0], bad[:4].tolist()))
-    assert same, "h differs from the row-major up-projection"
+    fp16_close(h[:R], h_ref[:R], "h (row-major) vs the row-major GEMM's")
     assert (h[R:].view(torch.int16) == SENT_H).all(), "rows past offsets[E] written"
     if d_ff % 256 == 0:
         # h in fragment order: the same values, padding rows zero, nothing past the padded segments;
@@ -64,11 +94,14 @@ def run_case(counts, d, d_ff, slack=17, seed=0):
         ops.moe_expert_down_frag(hf, off, w2h, rows_max, y_perm=y)
         torch.cuda.synchronize()
         hrows, hpads, hpt = unfrag(hf.cpu(), counts_to_offsets(counts), d_ff)
-        assert torch.equal(hrows.view(torch.int16), h_ref[:R].cpu().view(torch.int16)), "fragment-ordered h differs"
+        assert torch.equal(hrows.view(torch.int16), h[:R].cpu().view(torch.int16)), \
+            "fragment-ordered h differs from the same kernel's row-major h"
         assert (hpads.view(torch.int16) == 0).all(), "padding rows of h are not zero"
         assert (hf.view(torch.int16)[hpt:].cpu() == SENT_H).all(), "rows past the padded segments of h written"
-        assert torch.equal(y[:R].view(torch.int32), y_ref[:R].view(torch.int32)), \
-            "down-projection from fragment-ordered h differs: max|diff| %.3g" % (y[:R] - y_ref[:R]).abs().max().item()
+        # the down-projection from fragment-ordered h against the row-major one
+        # on the row-major kernel's h: both the h values (one fp16 step apart
+        # in a few places) and the summation order differ
+        f32_close(y[:R], y_ref[:R], "y_perm from fragment-ordered h", tol=1e-3)
         assert torch.isnan(y[R:]).all(), "rows past offsets[E] of y_perm written"
     return R
 
@@ -253,11 +286,12 @@ def test_down_f16w_equals_in_register_conversion(counts, d, d_ff):
 
 
 @pytest.mark.parametrize("frag,hfrag", [(False, False), (True, False), (True, True)])
-def test_forward_with_f16_w2_is_bit_identical(frag, hfrag):
+def test_forward_with_f16_w2(frag, hfrag):
     """The layer forward given moe_weights_bf16_to_f16(W2) against the same
-    forward converting W2 in registers: the same y, bit for bit (with h
-    row-major, and on the fragment-ordered path also with h kept in
-    fragment order)."""
+    forward converting W2 in registers: with h row-major (both forwards run
+    the same kernels) the same y, bit for bit; with h kept in fragment order
+    (the down-projection then runs the fragment-ordered GEMM, whose float32
+    sums are added in another order) y to float32 summation order."""
     from mixture_experts_layer_49_amd import inputs as I
     from parity_helpers import dev
     cfg = I.small("f16w", T=600, d=256, d_ff=512, E=4, k=2, cf=1.25, seed=71)
@@ -272,7 +306,10 @@ def test_forward_with_f16_w2_is_bit_identical(frag, hfrag):
         assert (b.h_frag is not None) == (hfrag and w2h is not None)
         torch.cuda.synchronize()
         ys.append(b.y.clone())
-    assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32))
+    if hfrag:
+        f32_close(ys[1], ys[0], "y with h in fragment order", tol=1e-4)
+    else:
+        assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32))
 
 
 @pytest.mark.parametrize("counts,d,d_ff", [([1283, 1250, 1301, 1222, 1279, 1340, 1197, 1368], 4096, 16384),
