@@ -434,12 +434,14 @@ def cold_us(fn, flush, torch, stream, reps=10):
     return t[len(t) // 2]
 
 
-def measure_mfma_ceiling(torch, stream, device, iters=20000, reps=5):
+def measure_mfma_ceiling(torch, stream, device, form="32x32x16", iters=20000, reps=5):
     """The matrix-core ceiling under the power cap: libmoe_bench.so's MFMA-only
-    loop (v_mfma_f32_32x32x16_bf16 on register operands, one workgroup of four
-    waves per CU, no memory traffic), a few warm launches then `reps` timed
-    ones; its TFLOP/s, the fraction of the nominal peak and the clock it held
-    (shader-clock against 100 MHz ticks over workgroup 0's loop)."""
+    loop (form "32x32x16": v_mfma_f32_32x32x16_bf16, 16 accumulators;
+    "16x16x32": v_mfma_f32_16x16x32_bf16, 64 accumulators, twice the
+    iterations; operands in registers, one workgroup of four waves per CU, no
+    memory traffic), a few warm launches then `reps` timed ones; its TFLOP/s,
+    the fraction of the nominal peak and the clock it held (shader-clock
+    against 100 MHz ticks over workgroup 0's loop)."""
     import ctypes
 
     L = bench_lib()
@@ -447,10 +449,12 @@ def measure_mfma_ceiling(torch, stream, device, iters=20000, reps=5):
     out = torch.empty(grid * 256, dtype=torch.float32, device=device)
     clk = torch.zeros(2, dtype=torch.int64, device=device)
     strm = ctypes.c_void_p(stream.cuda_stream)
+    small = form == "16x16x32"
+    fn = L.probe_mfma_loop16 if small else L.probe_mfma_loop
+    n_it = 2 * iters if small else iters
 
     def launch():
-        if L.probe_mfma_loop(ctypes.c_void_p(out.data_ptr()), iters, ctypes.c_void_p(clk.data_ptr()), grid,
-                             strm) != 0:
+        if fn(ctypes.c_void_p(out.data_ptr()), n_it, ctypes.c_void_p(clk.data_ptr()), grid, strm) != 0:
             raise RuntimeError("probe_mfma_loop failed")
 
     for _ in range(3):
@@ -463,12 +467,13 @@ def measure_mfma_ceiling(torch, stream, device, iters=20000, reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    flop = float(grid) * 4 * iters * 16 * 32768.0
+    flop = float(grid) * 4 * n_it * (64 * 16384.0 if small else 16 * 32768.0)
     c = clk.cpu().numpy().astype(float)
     tf = flop / (ms * 1e-3) / 1e12
     return {"TFLOP/s": tf, "frac": tf / PEAK_MFMA_TFLOPS, "sclk_mhz": 100.0 * c[0] / c[1],
-            "what": "v_mfma_f32_32x32x16_bf16 on register operands, no memory traffic, one workgroup "
-                    "of 4 waves per CU (%d), %.2f ms per launch" % (grid, ms)}
+            "what": "v_mfma_f32_%s_bf16 on register operands, %d accumulators, no memory traffic, one "
+                    "workgroup of 4 waves per CU (%d), %.2f ms per launch"
+                    % (form, 64 if small else 16, grid, ms)}
 
 
 def bench_lib():
@@ -483,8 +488,9 @@ def bench_lib():
     L.probe_stream_read.restype = ctypes.c_int
     L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
-    L.probe_mfma_loop.restype = ctypes.c_int
-    L.probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    for fn in (L.probe_mfma_loop, L.probe_mfma_loop16):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return L
 
 
@@ -609,7 +615,9 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
     torch.cuda.synchronize()
     total_ms = timed_steps(step, args.steps, torch, stream)
     after = measure_clock(step, kernels, torch, stream, x.device)
-    ceiling = measure_mfma_ceiling(torch, stream, x.device)
+    # both MFMA forms: the fragment-ordered GEMM multiplies with 16x16x32, the
+    # row-major one with 32x32x16
+    ceilings = {f: measure_mfma_ceiling(torch, stream, x.device, f) for f in ("16x16x32", "32x32x16")}
     ms_per_step = total_ms / args.steps
     per = kernel_breakdown(step, evs, len(names), torch, stream, np)
     us = dict(zip(names, (per * 1e3).tolist()))
@@ -696,6 +704,8 @@ def forward_workload(args, name, ops, torch, np, I, want_cpu):
                   if dom_frag and dom == "up_gelu" else
                   "frag_gemm_kernel<down>" if dom_frag else "grouped_gemm_mfma<%s>" % dom_which)
     achieved = breakdown[dom]["TFLOP/s"]
+    ceiling = dict(ceilings["16x16x32" if dom_frag else "32x32x16"])
+    ceiling["other_form"] = ceilings["32x32x16" if dom_frag else "16x16x32"]
     ffn_tflops = (flops_up + flops_down) / ((us["up_gelu"] + us["down"]) * 1e-6) / 1e12
     fam = "gemm_frag" if dom_frag else "gemm_mfma"
     under = profiled_sclk(dom_which, cfg.name, fam)

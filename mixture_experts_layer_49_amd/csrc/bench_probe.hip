@@ -17,6 +17,10 @@
 // (grid x 256 floats) so nothing is optimised away. Workgroup 0 also records
 // the shader-clock and 100 MHz ticks over its loop in clk[0..1]. Flops per
 // launch: grid x 4 x iters x 16 x 32768.
+// probe_mfma_loop16: the same with v_mfma_f32_16x16x32_bf16, 64 independent
+// accumulators of 16 x 16 (the form the fragment-ordered expert GEMM uses;
+// per flop it moves half the accumulator data, and the power cap lets it run
+// at a higher clock). Flops per launch: grid x 4 x iters x 64 x 16384.
 //
 // probe_stream_read: every byte of [p, p + bytes) is read once with 16-byte
 // vector loads, U of them in flight per thread, grid-stride over 16-byte
@@ -76,6 +80,8 @@ __global__ __launch_bounds__(64) void clock_kernel(unsigned long long* __restric
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t lcg_operand(unsigned s) {
   bf16x8_t v;
@@ -118,6 +124,43 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out,
   }
 }
 
+__global__ __launch_bounds__(256) void mfma_loop16_kernel(float* __restrict__ out, int iters,
+                                                          unsigned long long* __restrict__ clk) {
+  const unsigned seed = blockIdx.x * 1000u + threadIdx.x * 7u;
+  u32x4_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_bit_cast(u32x4_t, lcg_operand(seed + i));
+    b[i] = __builtin_bit_cast(u32x4_t, lcg_operand(seed + 100u + i));
+  }
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  f32x4_t acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = f32x4_t{};
+  for (int it = 0; it < iters; ++it) {
+    // wait states between the accumulator writes that set them to zero
+    // (placed ahead of the loop) and the first MFMAs reading them
+    asm volatile("s_nop 2" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 64; ++i)   // accumulate in place (inline assembly: see the expert GEMM)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i]) : "v"(a[i & 3]), "v"(b[(i >> 2) & 3]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // results complete before they are read
+  __builtin_amdgcn_sched_barrier(0);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += acc[i][r];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,6 +173,11 @@ int probe_mfma_loop(float* out, int iters, unsigned long long* clk, int grid, hi
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+int probe_mfma_loop16(float* out, int iters, unsigned long long* clk, int grid, hipStream_t stream) {
+  if (out == nullptr || clk == nullptr || iters < 1 || grid < 1) return -1;
+  hipLaunchKernelGGL(mfma_loop16_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, out, iters, clk);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // out: device, two uint64 words (shader-clock ticks, 100 MHz ticks).
 int probe_clock(unsigned long long* out, int ticks, hipStream_t stream) {

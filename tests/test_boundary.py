@@ -374,16 +374,17 @@ def test_backward_argument_errors():
 
 def test_bench_probe_library_exports_and_argument_checks():
     """libmoe_bench.so (the benchmark's measurement kernels) loads, exports its
-    three probes, and rejects bad arguments before any launch."""
+    four probes, and rejects bad arguments before any launch."""
     path = os.path.join(os.path.dirname(ops.LIB_PATH), "libmoe_bench.so")
     if not os.path.exists(path):
         pytest.skip("libmoe_bench.so not built")
     L = ctypes.CDLL(path)
-    for name in ("probe_stream_read", "probe_clock", "probe_mfma_loop"):
+    for name in ("probe_stream_read", "probe_clock", "probe_mfma_loop", "probe_mfma_loop16"):
         assert hasattr(L, name), name
     L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.probe_mfma_loop16.argtypes = L.probe_mfma_loop.argtypes
     assert L.probe_stream_read(None, 16, None, 1, None) == -1
     assert L.probe_stream_read(ctypes.c_void_p(16), 15, ctypes.c_void_p(16), 1, None) == -1   # not a multiple of 16
     assert L.probe_stream_read(ctypes.c_void_p(8), 16, ctypes.c_void_p(16), 1, None) == -1    # misaligned
@@ -392,6 +393,10 @@ def test_bench_probe_library_exports_and_argument_checks():
     assert L.probe_mfma_loop(None, 1, ctypes.c_void_p(16), 1, None) == -1
     assert L.probe_mfma_loop(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), 1, None) == -1
     assert L.probe_mfma_loop(ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 0, None) == -1
+    for fn in (L.probe_mfma_loop, L.probe_mfma_loop16):
+        assert fn(None, 1, ctypes.c_void_p(16), 1, None) == -1
+        assert fn(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), 1, None) == -1
+        assert fn(ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 0, None) == -1
 
 
 def test_router_tiles_and_plan_tiles_argument_errors():
