@@ -670,13 +670,14 @@ def moe_forward(x, w1, w2, k: int, capacity: int, w_gate=None, bias=None, topk_i
     `save_for_backward` the up-projection also keeps the pre-activation and
     the router its log-sum-exp (what moe_backward needs). Without a backward,
     bf16 layers that frag_eligible() accepts run the permute and the
-    up-projection on the fragment-ordered copy (bufs.frag; the same h bit for
-    bit as the row-major up-projection without a workspace), and the other
+    up-projection on the fragment-ordered copy (bufs.frag; 16x16x32 MFMAs:
+    h equal to the row-major up-projection's without a workspace up to
+    float32 summation order, bit for bit on every shape tested), and the other
     bf16 layers fold the permute into the up-projection (bufs.gather: the
     same h bit for bit, x_perm not stored). `w2_f16`, for
     bf16 layers: moe_weights_bf16_to_f16(w2), prepared once; the
     down-projection then reads it instead of converting W2 in registers
-    (y_perm bit for bit the same), and on the fragment-ordered path with
+    (y_perm bit for bit the same on the row-major kernel), and on the fragment-ordered path with
     d_ff % 256 == 0 and buffers made with w2_f16=True, h stays in fragment
     order (bufs.h_frag) for a down-projection that loads it straight into
     registers (bufs.h is then not allocated). Nothing here allocates when
