@@ -391,10 +391,10 @@ def frag_eligible(dtype, d: int) -> bool:
     bf16, d a multiple of 256 and at least 4096. Measured on the workloads,
     whole forward with fp16 W2, against the row-major path that folds the
     permute into the up-projection: -9% at d = 4096 (8 experts, also the
-    receiver share and the ETP share), but +1.5% at d = 2048 (64 experts) and
-    +2% at d = 1024 (16 experts), where the row-major up-projection's split
-    of a short last round of tiles along K, and its saved permute pass, weigh
-    more."""
+    receiver share and the ETP share; more since the fragment GEMM moved to
+    16x16x32 MFMAs), +2% at d = 2048 (64 experts: the fragment-order permute
+    pass costs more than the GEMMs gain), -1.7% at d = 1024 (16 experts,
+    within the spread between boxes; left on the row-major path)."""
     return dtype == torch.bfloat16 and d % 256 == 0 and d >= 4096
 
 
